@@ -1,0 +1,604 @@
+// C ABI of the library: argument checks, buffer carving and the order of
+// kernel launches for each entry point. Every launch goes to the caller's
+// stream; nothing here allocates device memory or synchronises (except
+// nc_read_status).
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+
+static thread_local std::string g_last_error;
+
+nc_status record_hip_error(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return NC_ERR_HIP;
+}
+
+namespace {
+
+constexpr size_t kStatusBytes = 256;
+
+struct Dims {
+  long M;
+  int B, T, d, H, G, D, F, V, L, QKV, HD, QK;
+  float eps, cap, base;
+  int dtype;
+  size_t es;  // bytes per stored element
+};
+
+nc_status make_dims(const nc_config* c, Dims* o, bool need_depth) {
+  if (!c) return NC_ERR_INVALID_ARG;
+  if (c->dtype != NC_BF16 && c->dtype != NC_F32) return NC_ERR_UNSUPPORTED;
+  if (c->d_model <= 0 || c->n_head <= 0 || c->head_dim <= 0 || c->n_kv_head <= 0 || c->d_ff <= 0 || c->vocab <= 0 ||
+      c->batch <= 0 || c->seq_len <= 0 || (need_depth && c->depth <= 0) || c->depth < 0)
+    return NC_ERR_SHAPE;
+  if (c->n_head % c->n_kv_head != 0) return NC_ERR_SHAPE;
+  if (!(c->softcap > 0.f) || !(c->rope_base > 0.f) || !(c->norm_eps >= 0.f)) return NC_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return NC_ERR_UNSUPPORTED;
+  if (c->d_model % 64 != 0 || c->d_model > 2048 || c->d_ff % 64 != 0 || c->vocab % 8 != 0) return NC_ERR_UNSUPPORTED;
+  long M = (long)c->batch * c->seq_len;
+  if (M > 0x7fffffffL || c->batch > 65535 || c->n_kv_head > 65535) return NC_ERR_UNSUPPORTED;
+  long qkv = (long)(c->n_head + 2 * c->n_kv_head) * c->head_dim;
+  if (qkv * c->d_model > 0x7fffffffL || (long)c->d_ff * c->d_model > 0x7fffffffL ||
+      (long)c->vocab * c->d_model > 0x7fffffffL || M * c->d_ff > 0x7fffffffL || M * qkv > 0x7fffffffL)
+    return NC_ERR_UNSUPPORTED;
+  o->M = M;
+  o->B = c->batch;
+  o->T = c->seq_len;
+  o->d = c->d_model;
+  o->H = c->n_head;
+  o->G = c->n_kv_head;
+  o->D = c->head_dim;
+  o->F = c->d_ff;
+  o->V = c->vocab;
+  o->L = c->depth;
+  o->QKV = (int)qkv;
+  o->HD = c->n_head * c->head_dim;
+  o->QK = (c->n_head + c->n_kv_head) * c->head_dim;
+  o->eps = c->norm_eps;
+  o->cap = c->softcap;
+  o->base = c->rope_base;
+  o->dtype = c->dtype;
+  o->es = c->dtype == NC_BF16 ? 2 : 4;
+  return NC_OK;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sequential carving of a caller buffer into 256-byte aligned pieces.
+struct Carver {
+  char* p;
+  size_t used = 0;
+  explicit Carver(void* base) : p(static_cast<char*>(base)) {}
+  template <typename U>
+  U* take(size_t n) {
+    U* r = reinterpret_cast<U*>(p ? p + used : nullptr);
+    used += align_up(n * sizeof(U), 256);
+    return r;
+  }
+};
+
+template <typename T>
+struct BlockSaved {
+  float *r1, *lse, *r2, *cs, *sn;
+  T *h1, *qkv, *qk, *o, *x1, *h2, *u;
+};
+template <typename T>
+BlockSaved<T> carve_block_saved(Carver& c, const Dims& m, bool table) {
+  BlockSaved<T> s;
+  s.r1 = c.take<float>(m.M);
+  s.h1 = c.take<T>(m.M * m.d);
+  s.qkv = c.take<T>(m.M * m.QKV);
+  s.qk = c.take<T>(m.M * m.QK);
+  s.o = c.take<T>(m.M * m.HD);
+  s.lse = c.take<float>(m.M * m.H);
+  s.x1 = c.take<T>(m.M * m.d);
+  s.r2 = c.take<float>(m.M);
+  s.h2 = c.take<T>(m.M * m.d);
+  s.u = c.take<T>(m.M * m.F);
+  s.cs = table ? c.take<float>((size_t)m.T * m.D / 2) : nullptr;
+  s.sn = table ? c.take<float>((size_t)m.T * m.D / 2) : nullptr;
+  return s;
+}
+
+template <typename T>
+struct BlockScratch {
+  T *du, *dh, *dx1, *dy, *dqkv;
+  float *delta, *partial;
+  size_t partial_elems;
+};
+size_t block_partial_elems(const Dims& m) {
+  size_t a = gemm_dw_partial_elems((int)m.M, m.d, m.F);
+  size_t b = gemm_dw_partial_elems((int)m.M, m.F, m.d);
+  size_t c = gemm_dw_partial_elems((int)m.M, m.d, m.HD);
+  size_t e = gemm_dw_partial_elems((int)m.M, m.QKV, m.d);
+  size_t r = a;
+  if (b > r) r = b;
+  if (c > r) r = c;
+  if (e > r) r = e;
+  return r;
+}
+template <typename T>
+BlockScratch<T> carve_block_scratch(Carver& c, const Dims& m) {
+  BlockScratch<T> s;
+  s.du = c.take<T>(m.M * m.F);
+  s.dh = c.take<T>(m.M * m.d);
+  s.dx1 = c.take<T>(m.M * m.d);
+  s.dy = c.take<T>(m.M * m.HD);
+  s.dqkv = c.take<T>(m.M * m.QKV);
+  s.delta = c.take<float>(m.M * m.H);
+  s.partial_elems = block_partial_elems(m);
+  s.partial = c.take<float>(s.partial_elems ? s.partial_elems : 1);
+  return s;
+}
+
+template <typename T>
+struct HeadSaved {
+  T *xf, *z;
+  float *rf, *lse, *zt;
+  int* nv;
+};
+template <typename T>
+HeadSaved<T> carve_head_saved(Carver& c, const Dims& m) {
+  HeadSaved<T> s;
+  s.xf = c.take<T>(m.M * m.d);
+  s.rf = c.take<float>(m.M);
+  s.z = c.take<T>((size_t)m.M * m.V);
+  s.lse = c.take<float>(m.M);
+  s.zt = c.take<float>(m.M);
+  s.nv = c.take<int>(1);
+  return s;
+}
+
+template <typename T>
+struct HeadScratch {
+  float *part, *block_sums, *partial;
+  int* block_counts;
+  T* dxf;
+  size_t partial_elems;
+};
+template <typename T>
+HeadScratch<T> carve_head_scratch(Carver& c, const Dims& m) {
+  HeadScratch<T> s;
+  s.part = c.take<float>(m.M * lmhead_tiles(m.V));
+  s.block_sums = c.take<float>(xent_loss_blocks((int)m.M));
+  s.block_counts = c.take<int>(xent_loss_blocks((int)m.M));
+  s.dxf = c.take<T>(m.M * m.d);
+  s.partial_elems = gemm_dw_partial_elems((int)m.M, m.V, m.d);
+  s.partial = c.take<float>(s.partial_elems ? s.partial_elems : 1);
+  return s;
+}
+
+struct EmbedScratch {
+  float* de;
+  void* sort;
+};
+EmbedScratch carve_embed_scratch(Carver& c, const Dims& m) {
+  EmbedScratch s;
+  s.de = c.take<float>(m.M * m.d);
+  s.sort = c.take<char>(embed_sort_bytes((int)m.M, m.V, m.d));
+  return s;
+}
+
+size_t block_saved_bytes(const Dims& m, bool table) {
+  Carver c(nullptr);
+  if (m.es == 2) carve_block_saved<bf16>(c, m, table);
+  else carve_block_saved<float>(c, m, table);
+  return c.used;
+}
+size_t head_saved_bytes(const Dims& m) {
+  Carver c(nullptr);
+  if (m.es == 2) carve_head_saved<bf16>(c, m);
+  else carve_head_saved<float>(c, m);
+  return c.used;
+}
+// Scratch after the status word: the largest of the entry points' needs.
+size_t scratch_body_bytes(const Dims& m) {
+  Carver a(nullptr), b(nullptr), e(nullptr);
+  if (m.es == 2) {
+    carve_block_scratch<bf16>(a, m);
+    carve_head_scratch<bf16>(b, m);
+  } else {
+    carve_block_scratch<float>(a, m);
+    carve_head_scratch<float>(b, m);
+  }
+  carve_embed_scratch(e, m);
+  size_t r = a.used;
+  if (b.used > r) r = b.used;
+  if (e.used > r) r = e.used;
+  return r;
+}
+
+size_t param_offsets(const Dims& m, size_t* off) {
+  size_t o = 0;
+  off[0] = o;
+  o += (size_t)m.V * m.d;
+  for (int l = 0; l < m.L; ++l) {
+    off[1 + 4 * l] = o;
+    o += (size_t)m.QKV * m.d;
+    off[2 + 4 * l] = o;
+    o += (size_t)m.d * m.HD;
+    off[3 + 4 * l] = o;
+    o += (size_t)m.F * m.d;
+    off[4 + 4 * l] = o;
+    o += (size_t)m.d * m.F;
+  }
+  off[1 + 4 * m.L] = o;
+  o += (size_t)m.V * m.d;
+  return o;
+}
+
+size_t model_workspace_bytes(const Dims& m) {
+  size_t b = kStatusBytes;
+  b += 2 * align_up((size_t)m.T * m.D / 2 * sizeof(float), 256);
+  b += (size_t)(m.L + 1) * align_up((size_t)m.M * m.d * m.es, 256);
+  b += align_up((size_t)m.M * sizeof(float), 256);
+  b += (size_t)m.L * block_saved_bytes(m, false);
+  b += head_saved_bytes(m);
+  b += align_up((size_t)m.M * m.d * m.es, 256);
+  b += scratch_body_bytes(m);
+  return b;
+}
+
+// ------------------------------------------------------------ typed steps
+
+template <typename T>
+struct BlockW {
+  const T *wqkv, *wo, *w1, *w2;
+};
+
+template <typename T>
+nc_status block_fwd_t(const Dims& m, const BlockW<T>& w, const T* x, T* x_out, const BlockSaved<T>& s,
+                      const float* cs, const float* sn, hipStream_t st) {
+  const int M = (int)m.M;
+  NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.h1, s.r1, M, m.d, m.eps, nullptr, st));
+  NC_TRY(gemm_xwt<T>(s.h1, w.wqkv, s.qkv, nullptr, M, m.QKV, m.d, false, st));
+  NC_TRY(qknorm_rope_fwd<T>(s.qkv, m.QKV, s.qk, m.QK, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
+  AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
+  NC_TRY(attn_fwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, s.lse, st));
+  NC_TRY(gemm_xwt<T>(s.o, w.wo, s.x1, x, M, m.d, m.HD, false, st));
+  NC_TRY(rmsnorm_fwd<T>(s.x1, nullptr, 0, s.h2, s.r2, M, m.d, m.eps, nullptr, st));
+  NC_TRY(gemm_xwt<T>(s.h2, w.w1, s.u, nullptr, M, m.F, m.d, false, st));
+  NC_TRY(gemm_xwt<T>(s.u, w.w2, x_out, s.x1, M, m.d, m.F, true, st));
+  return NC_OK;
+}
+
+template <typename T>
+nc_status block_bwd_t(const Dims& m, const BlockW<T>& w, const T* x, const BlockSaved<T>& s, const float* cs,
+                      const float* sn, const T* dx_out, T* dx_in, const nc_block_grads& g, int acc,
+                      const BlockScratch<T>& c, hipStream_t st) {
+  (void)x;
+  const int M = (int)m.M;
+  // MLP: x_out = x1 + relu(u)^2 W2^T, u = h2 W1^T
+  NC_TRY(gemm_dw<T>(dx_out, s.u, g.w2, M, m.d, m.F, true, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dyw<T>(dx_out, w.w2, c.du, s.u, M, m.d, m.F, st));
+  NC_TRY(gemm_dw<T>(c.du, s.h2, g.w1, M, m.F, m.d, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dyw<T>(c.du, w.w1, c.dh, nullptr, M, m.F, m.d, st));
+  NC_TRY(rmsnorm_bwd<T, T>(c.dh, s.h2, s.r2, dx_out, c.dx1, M, m.d, st));
+  // attention output projection: x1 = x + o Wo^T
+  NC_TRY(gemm_dw<T>(c.dx1, s.o, g.wo, M, m.d, m.HD, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dyw<T>(c.dx1, w.wo, c.dy, nullptr, M, m.d, m.HD, st));
+  // attention, then rotation + QK norm
+  AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
+  NC_TRY(attn_bwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, c.dy, s.lse, c.delta, c.dqkv,
+                     c.dqkv + (size_t)m.H * m.D, c.dqkv + (size_t)(m.H + m.G) * m.D, m.QKV, st));
+  NC_TRY(qknorm_rope_bwd<T>(s.qkv, m.QKV, c.dqkv, m.QKV, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
+  // QKV projection and the pre-attention norm
+  NC_TRY(gemm_dw<T>(c.dqkv, s.h1, g.wqkv, M, m.QKV, m.d, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dyw<T>(c.dqkv, w.wqkv, c.dh, nullptr, M, m.QKV, m.d, st));
+  NC_TRY(rmsnorm_bwd<T, T>(c.dh, s.h1, s.r1, c.dx1, dx_in, M, m.d, st));
+  return NC_OK;
+}
+
+template <typename T>
+nc_status head_fwd_t(const Dims& m, const T* x, const T* wlm, const int32_t* tg, float* loss, const HeadSaved<T>& s,
+                     const HeadScratch<T>& c, uint32_t* status, hipStream_t st) {
+  const int M = (int)m.M;
+  NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.xf, s.rf, M, m.d, m.eps, nullptr, st));
+  NC_TRY(gemm_lmhead<T>(s.xf, wlm, s.z, M, m.V, m.d, m.cap, tg, c.part, s.zt, st));
+  NC_TRY(xent_loss(c.part, lmhead_tiles(m.V), s.zt, tg, M, m.V, s.lse, nullptr, c.block_sums, c.block_counts, loss,
+                   s.nv, status, st));
+  return NC_OK;
+}
+
+template <typename T>
+nc_status head_bwd_t(const Dims& m, const T* wlm, const int32_t* tg, const HeadSaved<T>& s, float dloss, T* dx,
+                     float* dwlm, int acc, const HeadScratch<T>& c, hipStream_t st) {
+  const int M = (int)m.M;
+  NC_TRY(xent_dz<T>(s.z, M, m.V, s.lse, tg, s.nv, dloss, m.cap, st));
+  NC_TRY(gemm_dyw<T>(s.z, wlm, c.dxf, nullptr, M, m.V, m.d, st));
+  NC_TRY(gemm_dw<T>(s.z, s.xf, dwlm, M, m.V, m.d, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(rmsnorm_bwd<T, T>(c.dxf, s.xf, s.rf, nullptr, dx, M, m.d, st));
+  return NC_OK;
+}
+
+template <typename T>
+nc_status embed_bwd_t(const Dims& m, const int32_t* idx, const T* x0, const float* r0, const T* dx0, float* dwte,
+                      int acc, const EmbedScratch& c, hipStream_t st) {
+  const int M = (int)m.M;
+  NC_TRY((rmsnorm_bwd<T, float>(dx0, x0, r0, nullptr, c.de, M, m.d, st)));
+  return embed_scatter(idx, c.de, dwte, M, m.V, m.d, acc, embed_sort_carve(c.sort, M, m.V, m.d), st);
+}
+
+template <typename T>
+nc_status model_t(const Dims& m, const T* params, const int32_t* idx, const int32_t* tg, float* loss, float* grads,
+                  float dloss, int acc, void* ws, hipStream_t st) {
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  param_offsets(m, off.data());
+  uint32_t* status = static_cast<uint32_t*>(ws);
+  Carver c(static_cast<char*>(ws) + kStatusBytes);
+  float* cs = c.take<float>((size_t)m.T * m.D / 2);
+  float* sn = c.take<float>((size_t)m.T * m.D / 2);
+  std::vector<T*> xs(m.L + 1);
+  for (int l = 0; l <= m.L; ++l) xs[l] = c.take<T>(m.M * m.d);
+  float* r0 = c.take<float>(m.M);
+  std::vector<BlockSaved<T>> sv(m.L);
+  for (int l = 0; l < m.L; ++l) sv[l] = carve_block_saved<T>(c, m, false);
+  HeadSaved<T> hs = carve_head_saved<T>(c, m);
+  T* gx = c.take<T>(m.M * m.d);
+  size_t body = c.used;
+  Carver c1(static_cast<char*>(ws) + kStatusBytes + body);
+  BlockScratch<T> bsc = carve_block_scratch<T>(c1, m);
+  Carver c2(static_cast<char*>(ws) + kStatusBytes + body);
+  HeadScratch<T> hsc = carve_head_scratch<T>(c2, m);
+  Carver c3(static_cast<char*>(ws) + kStatusBytes + body);
+  EmbedScratch esc = carve_embed_scratch(c3, m);
+
+  auto bw = [&](int l) {
+    BlockW<T> w;
+    w.wqkv = params + off[1 + 4 * l];
+    w.wo = params + off[2 + 4 * l];
+    w.w1 = params + off[3 + 4 * l];
+    w.w2 = params + off[4 + 4 * l];
+    return w;
+  };
+  auto bg = [&](int l) {
+    nc_block_grads g;
+    g.wqkv = grads + off[1 + 4 * l];
+    g.wo = grads + off[2 + 4 * l];
+    g.w1 = grads + off[3 + 4 * l];
+    g.w2 = grads + off[4 + 4 * l];
+    return g;
+  };
+
+  NC_TRY(rope_table(cs, sn, m.T, m.D, m.base, st));
+  NC_TRY(rmsnorm_fwd<T>(params + off[0], idx, m.V, xs[0], r0, (int)m.M, m.d, m.eps, status, st));
+  for (int l = 0; l < m.L; ++l) NC_TRY(block_fwd_t<T>(m, bw(l), xs[l], xs[l + 1], sv[l], cs, sn, st));
+  const T* wlm = params + off[1 + 4 * m.L];
+  NC_TRY(head_fwd_t<T>(m, xs[m.L], wlm, tg, loss, hs, hsc, status, st));
+  NC_TRY(head_bwd_t<T>(m, wlm, tg, hs, dloss, gx, grads + off[1 + 4 * m.L], acc, hsc, st));
+  for (int l = m.L - 1; l >= 0; --l) NC_TRY(block_bwd_t<T>(m, bw(l), xs[l], sv[l], cs, sn, gx, gx, bg(l), acc, bsc, st));
+  NC_TRY(embed_bwd_t<T>(m, idx, xs[0], r0, gx, grads + off[0], acc, esc, st));
+  return NC_OK;
+}
+
+}  // namespace
+}  // namespace nc
+
+using namespace nc;
+
+extern "C" {
+
+int nc_abi_version(void) { return NC_ABI_VERSION; }
+
+const char* nc_status_str(int s) {
+  switch (s) {
+    case NC_OK: return "ok";
+    case NC_ERR_INVALID_ARG: return "invalid argument";
+    case NC_ERR_SHAPE: return "bad shape";
+    case NC_ERR_ALIGN: return "misaligned buffer";
+    case NC_ERR_WORKSPACE: return "workspace too small";
+    case NC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NC_ERR_HIP: return "HIP error";
+    case NC_ERR_DEVICE_DATA: return "device data error";
+    default: return "unknown status";
+  }
+}
+
+const char* nc_last_hip_error(void) { return g_last_error.c_str(); }
+
+nc_status nc_validate(const nc_config* cfg) {
+  Dims m;
+  return make_dims(cfg, &m, true);
+}
+
+nc_status nc_param_layout(const nc_config* cfg, size_t* offsets, size_t n_offsets, size_t* n_params) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, true));
+  if (!offsets || !n_params || n_offsets < (size_t)(2 + 4 * m.L)) return NC_ERR_INVALID_ARG;
+  *n_params = param_offsets(m, offsets);
+  return NC_OK;
+}
+
+nc_status nc_query_sizes(const nc_config* cfg, nc_sizes* s) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!s) return NC_ERR_INVALID_ARG;
+  s->block_saved = block_saved_bytes(m, true);
+  s->lmhead_saved = head_saved_bytes(m);
+  s->scratch = kStatusBytes + scratch_body_bytes(m);
+  if (m.L > 0) {
+    std::vector<size_t> off(2 + 4 * (size_t)m.L);
+    s->n_params = param_offsets(m, off.data());
+    s->model_workspace = model_workspace_bytes(m);
+  } else {
+    s->n_params = 0;
+    s->model_workspace = 0;
+  }
+  return NC_OK;
+}
+
+nc_status nc_read_status(const void* scratch, uint32_t* flags, void* stream) {
+  if (!scratch || !flags) return NC_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, scratch, sizeof(v), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return record_hip_error(e, "nc_read_status copy");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return record_hip_error(e, "nc_read_status sync");
+  *flags = v;
+  return v ? NC_ERR_DEVICE_DATA : NC_OK;
+}
+
+nc_status nc_clear_status(void* scratch, void* stream) {
+  if (!scratch) return NC_ERR_INVALID_ARG;
+  if (!aligned(scratch)) return NC_ERR_ALIGN;
+  return fill_u32(static_cast<uint32_t*>(scratch), 0u, 1, static_cast<hipStream_t>(stream));
+}
+
+nc_status nc_embed_fwd(const nc_config* cfg, const int32_t* idx, const void* wte, void* x0, float* r0, void* scratch,
+                       void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!idx || !wte || !x0 || !r0 || !scratch) return NC_ERR_INVALID_ARG;
+  if (!aligned(idx) || !aligned(wte) || !aligned(x0) || !aligned(r0) || !aligned(scratch)) return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* status = static_cast<uint32_t*>(scratch);
+  if (m.es == 2)
+    return rmsnorm_fwd<bf16>(static_cast<const bf16*>(wte), idx, m.V, static_cast<bf16*>(x0), r0, (int)m.M, m.d, m.eps,
+                             status, st);
+  return rmsnorm_fwd<float>(static_cast<const float*>(wte), idx, m.V, static_cast<float*>(x0), r0, (int)m.M, m.d, m.eps,
+                            status, st);
+}
+
+nc_status nc_embed_bwd(const nc_config* cfg, const int32_t* idx, const void* x0, const float* r0, const void* dx0,
+                       float* dwte, int accumulate, void* scratch, void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!idx || !x0 || !r0 || !dx0 || !dwte || !scratch) return NC_ERR_INVALID_ARG;
+  if (!aligned(idx) || !aligned(x0) || !aligned(r0) || !aligned(dx0) || !aligned(dwte) || !aligned(scratch))
+    return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver c(static_cast<char*>(scratch) + kStatusBytes);
+  EmbedScratch e = carve_embed_scratch(c, m);
+  if (m.es == 2)
+    return embed_bwd_t<bf16>(m, idx, static_cast<const bf16*>(x0), r0, static_cast<const bf16*>(dx0), dwte,
+                             accumulate, e, st);
+  return embed_bwd_t<float>(m, idx, static_cast<const float*>(x0), r0, static_cast<const float*>(dx0), dwte,
+                            accumulate, e, st);
+}
+
+nc_status nc_block_fwd(const nc_config* cfg, const nc_block_params* w, const void* x_in, void* x_out, void* saved,
+                       void* scratch, void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!w || !w->wqkv || !w->wo || !w->w1 || !w->w2 || !x_in || !x_out || !saved || !scratch)
+    return NC_ERR_INVALID_ARG;
+  if (!aligned(w->wqkv) || !aligned(w->wo) || !aligned(w->w1) || !aligned(w->w2) || !aligned(x_in) ||
+      !aligned(x_out) || !aligned(saved) || !aligned(scratch))
+    return NC_ERR_ALIGN;
+  if (x_in == x_out) return NC_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver c(saved);
+  if (m.es == 2) {
+    BlockSaved<bf16> s = carve_block_saved<bf16>(c, m, true);
+    NC_TRY(rope_table(s.cs, s.sn, m.T, m.D, m.base, st));
+    BlockW<bf16> bw{static_cast<const bf16*>(w->wqkv), static_cast<const bf16*>(w->wo),
+                    static_cast<const bf16*>(w->w1), static_cast<const bf16*>(w->w2)};
+    return block_fwd_t<bf16>(m, bw, static_cast<const bf16*>(x_in), static_cast<bf16*>(x_out), s, s.cs, s.sn, st);
+  }
+  BlockSaved<float> s = carve_block_saved<float>(c, m, true);
+  NC_TRY(rope_table(s.cs, s.sn, m.T, m.D, m.base, st));
+  BlockW<float> bw{static_cast<const float*>(w->wqkv), static_cast<const float*>(w->wo),
+                   static_cast<const float*>(w->w1), static_cast<const float*>(w->w2)};
+  return block_fwd_t<float>(m, bw, static_cast<const float*>(x_in), static_cast<float*>(x_out), s, s.cs, s.sn, st);
+}
+
+nc_status nc_block_bwd(const nc_config* cfg, const nc_block_params* w, const void* x_in, const void* saved,
+                       const void* dx_out, void* dx_in, const nc_block_grads* grads, int accumulate, void* scratch,
+                       void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!w || !w->wqkv || !w->wo || !w->w1 || !w->w2 || !x_in || !saved || !dx_out || !dx_in || !grads ||
+      !grads->wqkv || !grads->wo || !grads->w1 || !grads->w2 || !scratch)
+    return NC_ERR_INVALID_ARG;
+  if (!aligned(w->wqkv) || !aligned(w->wo) || !aligned(w->w1) || !aligned(w->w2) || !aligned(x_in) ||
+      !aligned(saved) || !aligned(dx_out) || !aligned(dx_in) || !aligned(grads->wqkv) || !aligned(grads->wo) ||
+      !aligned(grads->w1) || !aligned(grads->w2) || !aligned(scratch))
+    return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver c(const_cast<void*>(saved));
+  Carver cs(static_cast<char*>(scratch) + kStatusBytes);
+  if (m.es == 2) {
+    BlockSaved<bf16> s = carve_block_saved<bf16>(c, m, true);
+    BlockScratch<bf16> sc = carve_block_scratch<bf16>(cs, m);
+    BlockW<bf16> bw{static_cast<const bf16*>(w->wqkv), static_cast<const bf16*>(w->wo),
+                    static_cast<const bf16*>(w->w1), static_cast<const bf16*>(w->w2)};
+    return block_bwd_t<bf16>(m, bw, static_cast<const bf16*>(x_in), s, s.cs, s.sn, static_cast<const bf16*>(dx_out),
+                             static_cast<bf16*>(dx_in), *grads, accumulate, sc, st);
+  }
+  BlockSaved<float> s = carve_block_saved<float>(c, m, true);
+  BlockScratch<float> sc = carve_block_scratch<float>(cs, m);
+  BlockW<float> bw{static_cast<const float*>(w->wqkv), static_cast<const float*>(w->wo),
+                   static_cast<const float*>(w->w1), static_cast<const float*>(w->w2)};
+  return block_bwd_t<float>(m, bw, static_cast<const float*>(x_in), s, s.cs, s.sn, static_cast<const float*>(dx_out),
+                            static_cast<float*>(dx_in), *grads, accumulate, sc, st);
+}
+
+nc_status nc_lmhead_softcap_xent_fwd(const nc_config* cfg, const void* x, const void* wlm, const int32_t* targets,
+                                     float* loss, void* saved, void* scratch, void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!x || !wlm || !targets || !loss || !saved || !scratch) return NC_ERR_INVALID_ARG;
+  if (!aligned(x) || !aligned(wlm) || !aligned(targets) || !aligned(saved) || !aligned(scratch)) return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* status = static_cast<uint32_t*>(scratch);
+  Carver c(saved);
+  Carver cs(static_cast<char*>(scratch) + kStatusBytes);
+  if (m.es == 2) {
+    HeadSaved<bf16> s = carve_head_saved<bf16>(c, m);
+    HeadScratch<bf16> sc = carve_head_scratch<bf16>(cs, m);
+    return head_fwd_t<bf16>(m, static_cast<const bf16*>(x), static_cast<const bf16*>(wlm), targets, loss, s, sc,
+                            status, st);
+  }
+  HeadSaved<float> s = carve_head_saved<float>(c, m);
+  HeadScratch<float> sc = carve_head_scratch<float>(cs, m);
+  return head_fwd_t<float>(m, static_cast<const float*>(x), static_cast<const float*>(wlm), targets, loss, s, sc,
+                           status, st);
+}
+
+nc_status nc_lmhead_softcap_xent_bwd(const nc_config* cfg, const void* x, const void* wlm, const int32_t* targets,
+                                     void* saved, float dloss, void* dx, float* dwlm, int accumulate, void* scratch,
+                                     void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, false));
+  if (!x || !wlm || !targets || !saved || !dx || !dwlm || !scratch) return NC_ERR_INVALID_ARG;
+  if (!aligned(x) || !aligned(wlm) || !aligned(targets) || !aligned(saved) || !aligned(dx) || !aligned(dwlm) ||
+      !aligned(scratch))
+    return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver c(saved);
+  Carver cs(static_cast<char*>(scratch) + kStatusBytes);
+  if (m.es == 2) {
+    HeadSaved<bf16> s = carve_head_saved<bf16>(c, m);
+    HeadScratch<bf16> sc = carve_head_scratch<bf16>(cs, m);
+    return head_bwd_t<bf16>(m, static_cast<const bf16*>(wlm), targets, s, dloss, static_cast<bf16*>(dx), dwlm,
+                            accumulate, sc, st);
+  }
+  HeadSaved<float> s = carve_head_saved<float>(c, m);
+  HeadScratch<float> sc = carve_head_scratch<float>(cs, m);
+  return head_bwd_t<float>(m, static_cast<const float*>(wlm), targets, s, dloss, static_cast<float*>(dx), dwlm,
+                           accumulate, sc, st);
+}
+
+nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const int32_t* idx, const int32_t* targets,
+                                 float* loss, float* grads, float dloss, int accumulate, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, true));
+  if (!params || !idx || !targets || !loss || !grads || !workspace) return NC_ERR_INVALID_ARG;
+  if (!aligned(params) || !aligned(idx) || !aligned(targets) || !aligned(grads) || !aligned(workspace))
+    return NC_ERR_ALIGN;
+  if (workspace_bytes < model_workspace_bytes(m)) return NC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m.es == 2)
+    return model_t<bf16>(m, static_cast<const bf16*>(params), idx, targets, loss, grads, dloss, accumulate, workspace,
+                         st);
+  return model_t<float>(m, static_cast<const float*>(params), idx, targets, loss, grads, dloss, accumulate, workspace,
+                        st);
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Shared device helpers for the gfx950 kernels: storage types, conversions,
+// wavefront reductions, the sticky device status word, launch checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/nc.h"
+
+namespace nc {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kWave = 64;
+
+// Status bits of the device status word (first 4 bytes of every scratch or
+// workspace buffer). Bits are only ever OR-ed in; they stay set until cleared.
+enum : uint32_t {
+  kStatusBadToken = 1u << 0,    // an input token id outside [0, vocab)
+  kStatusBadTarget = 1u << 1,   // a target outside [-1, vocab)
+  kStatusNonFinite = 1u << 2,   // the loss is not finite
+  kStatusNoTargets = 1u << 3,   // every target is ignored (-1)
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Elements per 16-byte vector of a storage type.
+template <typename T> struct Vec { static constexpr int n = 16 / sizeof(T); };
+
+// Load / store 16 bytes as float values.
+template <typename T> __device__ __forceinline__ void load16(const T* p, float* out);
+template <> __device__ __forceinline__ void load16<bf16>(const bf16* p, float* out) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void load16<float>(const float* p, float* out) {
+  float4 u = *reinterpret_cast<const float4*>(p);
+  out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
+}
+
+template <typename T> __device__ __forceinline__ void store16(T* p, const float* in);
+template <> __device__ __forceinline__ void store16<bf16>(bf16* p, const float* in) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+template <> __device__ __forceinline__ void store16<float>(float* p, const float* in) {
+  *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ void set_status(uint32_t* status, uint32_t bits) {
+  if (status) atomicOr(status, bits);
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Records the HIP error text for nc_last_hip_error and maps it to a status.
+nc_status record_hip_error(hipError_t e, const char* where);
+
+#define NC_LAUNCH_CHECK(where)                                        \
+  do {                                                                \
+    hipError_t e_ = hipGetLastError();                                \
+    if (e_ != hipSuccess) return ::nc::record_hip_error(e_, where);   \
+  } while (0)
+
+#define NC_TRY(...)                          \
+  do {                                       \
+    nc_status s_ = (__VA_ARGS__);            \
+    if (s_ != NC_OK) return s_;              \
+  } while (0)
+
+}  // namespace nc

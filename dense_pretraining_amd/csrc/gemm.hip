@@ -1,0 +1,100 @@
+// GEMM entry points of the block and the unembedding, built on gemm.h.
+#include "gemm.h"
+#include "kernels.h"
+
+namespace nc {
+
+namespace {
+constexpr int kTargetBlocks = 1024;  // ~4 workgroups per CU for the weight-gradient split
+
+// Number of splits of the reduction (token) axis for a weight gradient, and
+// the rows each split covers (a multiple of the tile depth).
+void dw_split(int M, int N, int K, int bk, int& nsplit, int& kper) {
+  long tiles = (long)((N + 127) / 128) * ((K + 127) / 128);
+  int s = (int)(kTargetBlocks / (tiles > 0 ? tiles : 1));
+  s = s < 1 ? 1 : (s > 16 ? 16 : s);
+  int maxs = M / 512;
+  if (s > maxs) s = maxs < 1 ? 1 : maxs;
+  kper = ((M + s - 1) / s + bk - 1) / bk * bk;
+  nsplit = (M + kper - 1) / kper;
+}
+}  // namespace
+
+size_t gemm_dw_partial_elems(int M, int N, int K) {
+  int ns, kp;
+  dw_split(M, N, K, 32, ns, kp);  // the smaller tile depth gives the most splits
+  int ns2, kp2;
+  dw_split(M, N, K, 64, ns2, kp2);
+  int s = ns > ns2 ? ns : ns2;
+  return s > 1 ? (size_t)s * N * K : 0;
+}
+
+template <typename T>
+nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_x, hipStream_t st) {
+  GemmShape s{x, w, K, K, M, N, K, K, 1};
+  EpiStore<T> e{y, N, res, N, M, N};
+  if (relu_sq_x) return launch_gemm<T, kKc, kKc, ReluSq, Identity>(s, e, st);
+  return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
+}
+
+template <typename T>
+nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* u, int M, int N, int K, hipStream_t st) {
+  // C[M,K] = A[M,N] * B where B(n=k_out, k=n_in) = W[n_in][k_out]: K-outer.
+  GemmShape s{dy, w, N, K, M, K, N, N, 1};
+  if (u) {
+    EpiDReluSq<T> e{dx, K, u, K, M, K};
+    return launch_gemm<T, kKc, kKo, Identity, Identity>(s, e, st);
+  }
+  EpiStore<T> e{dx, K, nullptr, 0, M, K};
+  return launch_gemm<T, kKc, kKo, Identity, Identity>(s, e, st);
+}
+
+template <typename T>
+nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool relu_sq_x, int accumulate,
+                  float* partial, size_t partial_elems, hipStream_t st) {
+  int nsplit, kper;
+  dw_split(M, N, K, GemmTile<T>::BK, nsplit, kper);
+  // C[N,K] = sum_m dy[m][n] x[m][k]: both operands K-outer (token axis is the reduction).
+  GemmShape s{dy, x, N, K, N, K, M, kper, nsplit};
+  if (nsplit > 1 && (partial == nullptr || partial_elems < (size_t)nsplit * N * K)) return NC_ERR_WORKSPACE;
+  EpiF32 e;
+  e.ldc = K;
+  e.M = N;
+  e.N = K;
+  if (nsplit > 1) {
+    e.C = partial;
+    e.split_stride = (long)N * K;
+    e.accumulate = 0;
+  } else {
+    e.C = dw;
+    e.split_stride = 0;
+    e.accumulate = accumulate;
+  }
+  nc_status r = relu_sq_x ? launch_gemm<T, kKo, kKo, Identity, ReluSq>(s, e, st)
+                          : launch_gemm<T, kKo, kKo, Identity, Identity>(s, e, st);
+  if (r != NC_OK || nsplit == 1) return r;
+  return splitk_reduce(partial, nsplit, (size_t)N * K, dw, accumulate, st);
+}
+
+int lmhead_tiles(int N) { return (N + 127) / 128; }
+
+template <typename T>
+nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
+                      float* part, float* zt, hipStream_t st) {
+  GemmShape s{x, w, K, K, M, N, K, K, 1};
+  EpiSoftcap<T> e{z, N, cap, targets, part, zt, lmhead_tiles(N), M, N};
+  return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
+}
+
+#define NC_INST(T)                                                                                            \
+  template nc_status gemm_xwt<T>(const T*, const T*, T*, const T*, int, int, int, bool, hipStream_t);        \
+  template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t);               \
+  template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, bool, int, float*, size_t,          \
+                                hipStream_t);                                                                 \
+  template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, const int32_t*, float*,     \
+                                    float*, hipStream_t);
+NC_INST(bf16)
+NC_INST(float)
+#undef NC_INST
+
+}  // namespace nc

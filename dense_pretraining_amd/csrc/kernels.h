@@ -1,0 +1,91 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include "common.h"
+
+namespace nc {
+
+// ------------------------------------------------------------ GEMM (gemm.hip)
+// y[M,N] = x[M,K] W[N,K]^T (+ res[M,N]); relu_sq_x applies max(x,0)^2 to x.
+template <typename T>
+nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_x, hipStream_t st);
+// dx[M,K] = dy[M,N] W[N,K]; with u given, dx = (dy W) * 2 max(u,0).
+template <typename T>
+nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* u, int M, int N, int K, hipStream_t st);
+// dW[N,K] (+)= dy[M,N]^T x[M,K] (float32), split over M when that helps fill
+// the GPU (partials in `partial`, summed in a fixed order); relu_sq_x applies
+// max(x,0)^2 to x.
+template <typename T>
+nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool relu_sq_x, int accumulate,
+                  float* partial, size_t partial_elems, hipStream_t st);
+size_t gemm_dw_partial_elems(int M, int N, int K);
+// Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N];
+// part[M, ceil(N/128)] = per-tile sums of exp(z); zt[m] = z[m][targets[m]].
+template <typename T>
+nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
+                      float* part, float* zt, hipStream_t st);
+int lmhead_tiles(int N);
+
+// ------------------------------------------------------------ rows (rows.hip)
+nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+nc_status fill_f32(float* p, float v, size_t n, hipStream_t st);
+// y = x / sqrt(mean(x^2)+eps) per row, r = the scale; with idx, row m reads x[idx[m]].
+template <typename T>
+nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int M, int d, float eps,
+                      uint32_t* status, hipStream_t st);
+// dx = (res) + r (dy - y mean(dy y)); output T or float.
+template <typename T, typename TO>
+nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO* dx, int M, int d, hipStream_t st);
+// cos/sin [T, D/2] of t * base^(-2i/D), evaluated in double.
+nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st);
+// Per token and head (H+G heads): N_D then rotate; qkv [M, ld_in] -> qk [M, ld_out].
+template <typename T>
+nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const float* cs, const float* sn, int M,
+                          int T_, int nheads, int D, float eps, hipStream_t st);
+// In place on g [M, ld_g] (first nheads*D columns): g <- N_D_bwd(R^T g) with
+// the forward recomputed from the raw qkv.
+template <typename T>
+nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float* cs, const float* sn, int M, int T_,
+                          int nheads, int D, float eps, hipStream_t st);
+// Cross-entropy: lse[m] = log(sum of part[m][:]); loss = mean over valid
+// targets of lse - zt; nv = count of valid targets; writes loss and status.
+nc_status xent_loss(const float* part, int ntiles, const float* zt, const int32_t* targets, int M, int V, float* lse,
+                    float* row_loss, float* block_sums, int* block_counts, float* loss, int* nv, uint32_t* status,
+                    hipStream_t st);
+size_t xent_loss_blocks(int M);
+// In place: z <- (exp(z - lse) - onehot) * dloss/nv * (1 - (z/c)^2) on valid rows, 0 elsewhere.
+template <typename T>
+nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, const int* nv, float dloss, float cap,
+                  hipStream_t st);
+// out (+)= sum_z partial[z] (fixed order) for float arrays of n elements.
+nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st);
+
+// ------------------------------------------------------------ attention (attn.hip)
+struct AttnArgs {
+  int B, T, H, G, D;
+  long ld_qk;  // row stride of qk (q heads then k heads)
+  long ld_v;   // row stride of the v source
+  long ld_o;   // row stride of o and dO
+  long ld_dq;  // row stride of dq
+};
+template <typename T>
+nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse, hipStream_t st);
+template <typename T>
+nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const T* dO, const float* lse, float* delta,
+                   T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st);
+
+// ------------------------------------------------------------ embedding grad (embed_bwd.hip)
+struct EmbedSortBufs {
+  int* hist;      // [n_chunks * V]
+  int* seg;       // [V + 1] segment starts (exclusive scan of counts)
+  int* perm;      // [M] token positions sorted by (id, position)
+  int* sid;       // [M] ids in sorted order
+  float* spill;   // [n_windows * 2 * d]
+};
+size_t embed_sort_bytes(int M, int V, int d);
+EmbedSortBufs embed_sort_carve(void* base, int M, int V, int d);
+// dwte[v] (+)= sum over m with idx[m] = v of de[m]; de float [M,d].
+nc_status embed_scatter(const int32_t* idx, const float* de, float* dwte, int M, int V, int d, int accumulate,
+                        const EmbedSortBufs& b, hipStream_t st);
+
+}  // namespace nc

@@ -1,0 +1,430 @@
+// Row-wise HBM-bound kernels: parameter-free RMSNorm forward/backward (also
+// fused with the embedding gather), the per-head QK norm + rotary embedding
+// forward/backward, the softcapped cross-entropy reductions, split-K sums and
+// fills. One wavefront owns one row, the row stays in registers, and the row
+// statistics are reduced with cross-lane shuffles in a fixed order.
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+namespace {
+
+template <typename T> constexpr int max_vecs() { return 2048 / Vec<T>::n / 64; }  // d <= 2048
+
+// ------------------------------------------------------------ fills
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void fill_f32_kernel(float* p, float v, size_t n) {
+  size_t n4 = n / 4;
+  float4 v4 = make_float4(v, v, v, v);
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x)
+    reinterpret_cast<float4*>(p)[i] = v4;
+  for (size_t i = n4 * 4 + blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ------------------------------------------------------------ RMSNorm
+// N(v) = v / sqrt(mean(v^2) + eps) (no gain: the architecture list on vpshk.cn
+// gives RMSNorm without learnable parameters). With GATHER, row m is the
+// embedding row idx[m] (the norm that follows the token embedding).
+template <typename T, bool GATHER>
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const T* __restrict__ x, const int32_t* __restrict__ idx,
+                                                          int V, T* __restrict__ y, float* __restrict__ r, int M,
+                                                          int d, float eps, uint32_t* status) {
+  constexpr int VE = Vec<T>::n, MAXV = max_vecs<T>();
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  long src_row = row;
+  bool zero = false;
+  if constexpr (GATHER) {
+    int id = idx[row];
+    if (id < 0 || id >= V) {
+      zero = true;
+      if (lane == 0) set_status(status, kStatusBadToken);
+      id = 0;
+    }
+    src_row = id;
+  }
+  const T* src = x + src_row * d;
+  const int nv = d / VE;
+  float v[MAXV][VE];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    int vi = lane + 64 * c;
+    if (vi < nv && !zero) {
+      load16<T>(src + vi * VE, v[c]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) ss += v[c][e] * v[c][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) v[c][e] = 0.f;
+    }
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.f / sqrtf(ss / (float)d + eps);
+  T* dst = y + (long)row * d;
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    int vi = lane + 64 * c;
+    if (vi < nv) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) v[c][e] *= rr;
+      store16<T>(dst + vi * VE, v[c]);
+    }
+  }
+  if (lane == 0) r[row] = rr;
+}
+
+// dx = res + r (dy - y mean(dy y)), written in terms of the output y.
+template <typename T, typename TO>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ y,
+                                                          const float* __restrict__ r, const T* __restrict__ res,
+                                                          TO* __restrict__ dx, int M, int d) {
+  constexpr int VE = Vec<T>::n, MAXV = max_vecs<T>();
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const long off = (long)row * d;
+  const int nv = d / VE;
+  float g[MAXV][VE], yy[MAXV][VE];
+  float dot = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    int vi = lane + 64 * c;
+    if (vi < nv) {
+      load16<T>(dy + off + vi * VE, g[c]);
+      load16<T>(y + off + vi * VE, yy[c]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) dot += g[c][e] * yy[c][e];
+    }
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float rr = r[row];
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    int vi = lane + 64 * c;
+    if (vi < nv) {
+      float o[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] = rr * (g[c][e] - yy[c][e] * dot);
+      if (res) {
+        float rs[VE];
+        load16<T>(res + off + vi * VE, rs);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o[e] += rs[e];
+      }
+      if constexpr (sizeof(TO) == sizeof(T)) {
+        store16<TO>(dx + off + vi * VE, o);
+      } else {
+        // float output from bf16 inputs: two 16-byte stores
+        store16<TO>(dx + off + vi * VE, o);
+        store16<TO>(dx + off + vi * VE + 4, o + 4);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ rotary + QK norm
+// Rotary embedding (architecture list on vpshk.cn): pair (i, i + D/2) of a
+// head at position t turns by t * base^(-2i/D). The table is evaluated in
+// double precision.
+__global__ void rope_table_kernel(float* cs, float* sn, int T, int D, float base) {
+  int P = D / 2;
+  int n = T * P;
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n; k += gridDim.x * blockDim.x) {
+    int t = k / P, i = k % P;
+    double omega = pow((double)base, -2.0 * (double)i / (double)D);
+    double ang = (double)t * omega;
+    cs[k] = (float)cos(ang);
+    sn[k] = (float)sin(ang);
+  }
+}
+
+// QK norm (parameter-free RMSNorm over each head's D values) then the
+// rotation. Lane i of a head holds the pair (i, i + D/2), so the rotation is
+// lane-local; D = 64 puts two heads in one wavefront.
+template <typename T>
+__global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(const T* __restrict__ qkv, long ld_in, T* __restrict__ qk,
+                                                              long ld_out, const float* __restrict__ cs,
+                                                              const float* __restrict__ sn, int M, int Tn, int nheads,
+                                                              int D, float eps) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= M) return;
+  const int t = m % Tn, P = D / 2, hpi = 64 / P;
+  const int sub = lane / P, i = lane % P;
+  const float c = cs[t * P + i], s = sn[t * P + i];
+  const T* src = qkv + (long)m * ld_in;
+  T* dst = qk + (long)m * ld_out;
+  for (int h0 = 0; h0 < nheads; h0 += hpi) {
+    const int h = h0 + sub;
+    const bool ok = h < nheads;
+    float a = ok ? to_f32(src[h * D + i]) : 0.f;
+    float b = ok ? to_f32(src[h * D + i + P]) : 0.f;
+    float ss = group_sum(a * a + b * b, P);
+    float rr = 1.f / sqrtf(ss / (float)D + eps);
+    a *= rr;
+    b *= rr;
+    if (ok) {
+      dst[h * D + i] = from_f32<T>(a * c - b * s);
+      dst[h * D + i + P] = from_f32<T>(a * s + b * c);
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(const T* __restrict__ qkv, long ld_in, T* __restrict__ gr,
+                                                              long ld_g, const float* __restrict__ cs,
+                                                              const float* __restrict__ sn, int M, int Tn, int nheads,
+                                                              int D, float eps) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= M) return;
+  const int t = m % Tn, P = D / 2, hpi = 64 / P;
+  const int sub = lane / P, i = lane % P;
+  const float c = cs[t * P + i], s = sn[t * P + i];
+  const T* src = qkv + (long)m * ld_in;
+  T* g = gr + (long)m * ld_g;
+  for (int h0 = 0; h0 < nheads; h0 += hpi) {
+    const int h = h0 + sub;
+    const bool ok = h < nheads;
+    float a = ok ? to_f32(src[h * D + i]) : 0.f;
+    float b = ok ? to_f32(src[h * D + i + P]) : 0.f;
+    float rr = 1.f / sqrtf(group_sum(a * a + b * b, P) / (float)D + eps);
+    float ya = a * rr, yb = b * rr;
+    float ga = ok ? to_f32(g[h * D + i]) : 0.f;
+    float gb = ok ? to_f32(g[h * D + i + P]) : 0.f;
+    // transpose rotation
+    float ua = ga * c + gb * s, ub = -ga * s + gb * c;
+    float dot = group_sum(ua * ya + ub * yb, P) / (float)D;
+    if (ok) {
+      g[h * D + i] = from_f32<T>(rr * (ua - ya * dot));
+      g[h * D + i + P] = from_f32<T>(rr * (ub - yb * dot));
+    }
+  }
+}
+
+// ------------------------------------------------------------ cross-entropy
+// Next-token cross-entropy over the softcapped logits (imeisheng.com section
+// "预训练"; softcap from the architecture list). Per row: lse = log(sum of the
+// unembedding epilogue's per-tile exp sums); loss term lse - z'[target].
+__global__ void __launch_bounds__(256) xent_rows_kernel(const float* __restrict__ part, int ntiles,
+                                                        const float* __restrict__ zt, const int32_t* __restrict__ tg,
+                                                        int M, int V, float* __restrict__ lse,
+                                                        float* __restrict__ block_sums, int* __restrict__ block_counts,
+                                                        uint32_t* status) {
+  __shared__ float ws[4];
+  __shared__ int wc[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float acc = 0.f;
+  int cnt = 0;
+  for (int k = 0; k < 8; ++k) {
+    const int m = blockIdx.x * 32 + wave * 8 + k;
+    if (m >= M) break;
+    float s = 0.f;
+    for (int t = lane; t < ntiles; t += 64) s += part[(long)m * ntiles + t];
+    s = wave_sum(s);
+    const float l = logf(s);
+    int y = tg[m];
+    if (y < -1 || y >= V) {
+      if (lane == 0) set_status(status, kStatusBadTarget);
+      y = -1;
+    }
+    if (lane == 0) lse[m] = l;
+    if (y >= 0) {
+      acc += l - zt[m];
+      cnt += 1;
+    }
+  }
+  if (lane == 0) {
+    ws[wave] = acc;
+    wc[wave] = cnt;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    block_sums[blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    block_counts[blockIdx.x] = wc[0] + wc[1] + wc[2] + wc[3];
+  }
+}
+
+__global__ void __launch_bounds__(256) xent_final_kernel(const float* __restrict__ block_sums,
+                                                         const int* __restrict__ block_counts, int nblocks,
+                                                         float* loss, int* nv, uint32_t* status) {
+  __shared__ float s[256];
+  __shared__ int c[256];
+  float a = 0.f;
+  int n = 0;
+  for (int i = threadIdx.x; i < nblocks; i += 256) {
+    a += block_sums[i];
+    n += block_counts[i];
+  }
+  s[threadIdx.x] = a;
+  c[threadIdx.x] = n;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      s[threadIdx.x] += s[threadIdx.x + w];
+      c[threadIdx.x] += c[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int count = c[0];
+    float l = count > 0 ? s[0] / (float)count : 0.f;
+    if (count == 0) set_status(status, kStatusNoTargets);
+    if (!isfinite(l)) set_status(status, kStatusNonFinite);
+    *loss = l;
+    *nv = count;
+  }
+}
+
+// dz = (softmax(z') - onehot(y)) * dloss / Nv * (1 - (z'/c)^2), in place.
+template <typename T>
+__global__ void __launch_bounds__(256) xent_dz_kernel(T* __restrict__ z, int M, int V, const float* __restrict__ lse,
+                                                      const int32_t* __restrict__ tg, const int* __restrict__ nvp,
+                                                      float dloss, float inv_cap) {
+  constexpr int VE = Vec<T>::n;
+  const int m = blockIdx.x;
+  const int y = tg[m];
+  const bool valid = y >= 0 && y < V;
+  const int nv = *nvp;
+  const float gsc = valid ? dloss / (float)nv : 0.f;
+  const float l = lse[m];
+  T* row = z + (long)m * V;
+  const int nvec = V / VE;
+  for (int vi = blockIdx.y * 1024 + threadIdx.x; vi < min(nvec, (int)(blockIdx.y + 1) * 1024); vi += 256) {
+    float v[VE];
+    load16<T>(row + vi * VE, v);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      float p = __expf(v[e] - l);
+      if (vi * VE + e == y) p -= 1.f;
+      float zc = v[e] * inv_cap;
+      v[e] = p * gsc * (1.f - zc * zc);
+    }
+    store16<T>(row + vi * VE, v);
+  }
+}
+
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int nsplit, size_t n4,
+                                                            float* __restrict__ out, int accumulate) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    float4 a = accumulate ? reinterpret_cast<const float4*>(out)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int zz = 0; zz < nsplit; ++zz) {
+      float4 p = reinterpret_cast<const float4*>(part + (size_t)zz * n4 * 4)[i];
+      a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
+    }
+    reinterpret_cast<float4*>(out)[i] = a;
+  }
+}
+
+unsigned grid_for(size_t n, size_t per_block) {
+  size_t g = (n + per_block - 1) / per_block;
+  if (g > 65536) g = 65536;
+  return (unsigned)(g ? g : 1);
+}
+
+}  // namespace
+
+nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st) {
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, p, v, n);
+  NC_LAUNCH_CHECK("fill_u32");
+  return NC_OK;
+}
+nc_status fill_f32(float* p, float v, size_t n, hipStream_t st) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n / 4 + 1, 256)), dim3(256), 0, st, p, v, n);
+  NC_LAUNCH_CHECK("fill_f32");
+  return NC_OK;
+}
+
+template <typename T>
+nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int M, int d, float eps, uint32_t* status,
+                      hipStream_t st) {
+  dim3 grid((M + 3) / 4);
+  if (idx)
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, true>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status);
+  else
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, false>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status);
+  NC_LAUNCH_CHECK("rmsnorm_fwd");
+  return NC_OK;
+}
+
+template <typename T, typename TO>
+nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO* dx, int M, int d, hipStream_t st) {
+  hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, TO>), dim3((M + 3) / 4), dim3(256), 0, st, dy, y, r, res, dx, M, d);
+  NC_LAUNCH_CHECK("rmsnorm_bwd");
+  return NC_OK;
+}
+
+nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)T * D / 2, 256)), dim3(256), 0, st, cs, sn, T, D, base);
+  NC_LAUNCH_CHECK("rope_table");
+  return NC_OK;
+}
+
+template <typename T>
+nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const float* cs, const float* sn, int M,
+                          int T_, int nheads, int D, float eps, hipStream_t st) {
+  hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, qkv, ld_in, qk, ld_out, cs, sn,
+                     M, T_, nheads, D, eps);
+  NC_LAUNCH_CHECK("qknorm_rope_fwd");
+  return NC_OK;
+}
+
+template <typename T>
+nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float* cs, const float* sn, int M, int T_,
+                          int nheads, int D, float eps, hipStream_t st) {
+  hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, qkv, ld_in, g, ld_g, cs, sn, M,
+                     T_, nheads, D, eps);
+  NC_LAUNCH_CHECK("qknorm_rope_bwd");
+  return NC_OK;
+}
+
+size_t xent_loss_blocks(int M) { return (size_t)(M + 31) / 32; }
+
+nc_status xent_loss(const float* part, int ntiles, const float* zt, const int32_t* targets, int M, int V, float* lse,
+                    float* row_loss, float* block_sums, int* block_counts, float* loss, int* nv, uint32_t* status,
+                    hipStream_t st) {
+  (void)row_loss;
+  int nb = (int)xent_loss_blocks(M);
+  hipLaunchKernelGGL(xent_rows_kernel, dim3(nb), dim3(256), 0, st, part, ntiles, zt, targets, M, V, lse, block_sums,
+                     block_counts, status);
+  NC_LAUNCH_CHECK("xent_rows");
+  hipLaunchKernelGGL(xent_final_kernel, dim3(1), dim3(256), 0, st, block_sums, block_counts, nb, loss, nv, status);
+  NC_LAUNCH_CHECK("xent_final");
+  return NC_OK;
+}
+
+template <typename T>
+nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, const int* nv, float dloss, float cap,
+                  hipStream_t st) {
+  int nvec = V / Vec<T>::n;
+  dim3 grid(M, (nvec + 1023) / 1024);
+  hipLaunchKernelGGL((xent_dz_kernel<T>), grid, dim3(256), 0, st, z, M, V, lse, targets, nv, dloss, 1.f / cap);
+  NC_LAUNCH_CHECK("xent_dz");
+  return NC_OK;
+}
+
+nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st) {
+  size_t n4 = n / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st, partial, nsplit, n4, out,
+                     accumulate);
+  NC_LAUNCH_CHECK("splitk_reduce");
+  return NC_OK;
+}
+
+#define NC_INST(T)                                                                                                  \
+  template nc_status rmsnorm_fwd<T>(const T*, const int32_t*, int, T*, float*, int, int, float, uint32_t*,         \
+                                    hipStream_t);                                                                   \
+  template nc_status rmsnorm_bwd<T, T>(const T*, const T*, const float*, const T*, T*, int, int, hipStream_t);     \
+  template nc_status qknorm_rope_fwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
+                                        float, hipStream_t);                                                        \
+  template nc_status qknorm_rope_bwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
+                                        float, hipStream_t);                                                        \
+  template nc_status xent_dz<T>(T*, int, int, const float*, const int32_t*, const int*, float, float, hipStream_t);
+NC_INST(bf16)
+NC_INST(float)
+#undef NC_INST
+template nc_status rmsnorm_bwd<bf16, float>(const bf16*, const bf16*, const float*, const bf16*, float*, int, int,
+                                            hipStream_t);
+
+}  // namespace nc

@@ -1,0 +1,236 @@
+"""ctypes binding of libnc.so: the same entry points as include/nc.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI. Torch tensors provide device memory; their data
+pointers and the current HIP stream are passed through unchanged. Loading
+fails loudly when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+from .config import Config, NC_BF16, NC_F32
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnc.so")
+
+NC_OK = 0
+STATUS_NAMES = {
+    0: "NC_OK", 1: "NC_ERR_INVALID_ARG", 2: "NC_ERR_SHAPE", 3: "NC_ERR_ALIGN", 4: "NC_ERR_WORKSPACE",
+    5: "NC_ERR_UNSUPPORTED", 6: "NC_ERR_HIP", 7: "NC_ERR_DEVICE_DATA",
+}
+STATUS_BAD_TOKEN = 0x1
+STATUS_BAD_TARGET = 0x2
+STATUS_NONFINITE_LOSS = 0x4
+STATUS_NO_TARGETS = 0x8
+
+EXPORTED = [
+    "nc_abi_version", "nc_status_str", "nc_last_hip_error", "nc_validate", "nc_param_layout",
+    "nc_query_sizes", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
+    "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
+    "nc_model_loss_and_grad",
+]
+
+
+class NcError(RuntimeError):
+    def __init__(self, code, where, detail=""):
+        self.code = code
+        msg = f"{where}: {STATUS_NAMES.get(code, code)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+class NcConfig(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("depth", "d_model", "n_head", "head_dim", "n_kv_head", "d_ff",
+                                         "vocab", "batch", "seq_len")] + [
+        ("softcap", C.c_float), ("rope_base", C.c_float), ("norm_eps", C.c_float), ("dtype", C.c_int32)]
+
+
+class NcBlockParams(C.Structure):
+    _fields_ = [("wqkv", C.c_void_p), ("wo", C.c_void_p), ("w1", C.c_void_p), ("w2", C.c_void_p)]
+
+
+class NcBlockGrads(C.Structure):
+    _fields_ = [("wqkv", C.c_void_p), ("wo", C.c_void_p), ("w1", C.c_void_p), ("w2", C.c_void_p)]
+
+
+class NcSizes(C.Structure):
+    _fields_ = [("block_saved", C.c_size_t), ("lmhead_saved", C.c_size_t), ("scratch", C.c_size_t),
+                ("model_workspace", C.c_size_t), ("n_params", C.c_size_t)]
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Loads libnc.so once; raises if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m dense_pretraining_amd.build`")
+    lib = C.CDLL(path)
+    P, I, F, S = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+    cfgp = C.POINTER(NcConfig)
+    sig = {
+        "nc_abi_version": ([], I),
+        "nc_status_str": ([I], C.c_char_p),
+        "nc_last_hip_error": ([], C.c_char_p),
+        "nc_validate": ([cfgp], I),
+        "nc_param_layout": ([cfgp, C.POINTER(S), S, C.POINTER(S)], I),
+        "nc_query_sizes": ([cfgp, C.POINTER(NcSizes)], I),
+        "nc_read_status": ([P, C.POINTER(C.c_uint32), P], I),
+        "nc_clear_status": ([P, P], I),
+        "nc_embed_fwd": ([cfgp, P, P, P, P, P, P], I),
+        "nc_embed_bwd": ([cfgp, P, P, P, P, P, I, P, P], I),
+        "nc_block_fwd": ([cfgp, C.POINTER(NcBlockParams), P, P, P, P, P], I),
+        "nc_block_bwd": ([cfgp, C.POINTER(NcBlockParams), P, P, P, P, C.POINTER(NcBlockGrads), I, P, P], I),
+        "nc_lmhead_softcap_xent_fwd": ([cfgp, P, P, P, P, P, P, P], I),
+        "nc_lmhead_softcap_xent_bwd": ([cfgp, P, P, P, P, F, P, P, I, P, P], I),
+        "nc_model_loss_and_grad": ([cfgp, P, P, P, P, P, F, I, P, S, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def to_nc_config(cfg: Config) -> NcConfig:
+    return NcConfig(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
+                    cfg.batch, cfg.seq_len, cfg.softcap, cfg.rope_base, cfg.norm_eps,
+                    NC_BF16 if cfg.dtype == "bf16" else NC_F32)
+
+
+def _check(code, where):
+    if code != NC_OK:
+        detail = ""
+        if code == 6:
+            detail = load().nc_last_hip_error().decode()
+        raise NcError(code, where, detail)
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def torch_dtype(cfg: Config):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+# ------------------------------------------------------------------ queries
+
+def validate(cfg: Config):
+    c = to_nc_config(cfg)
+    return load().nc_validate(C.byref(c))
+
+
+def query_sizes(cfg: Config) -> NcSizes:
+    c = to_nc_config(cfg)
+    s = NcSizes()
+    _check(load().nc_query_sizes(C.byref(c), C.byref(s)), "nc_query_sizes")
+    return s
+
+
+def param_layout(cfg: Config):
+    c = to_nc_config(cfg)
+    n = 2 + 4 * cfg.depth
+    offs = (C.c_size_t * n)()
+    total = C.c_size_t()
+    _check(load().nc_param_layout(C.byref(c), offs, n, C.byref(total)), "nc_param_layout")
+    return list(offs), total.value
+
+
+def read_status(scratch, stream=None):
+    """Returns the device status bits (synchronises the stream)."""
+    flags = C.c_uint32()
+    code = load().nc_read_status(_p(scratch), C.byref(flags), _stream(stream))
+    if code not in (NC_OK, 7):
+        _check(code, "nc_read_status")
+    return flags.value
+
+
+def clear_status(scratch, stream=None):
+    _check(load().nc_clear_status(_p(scratch), _stream(stream)), "nc_clear_status")
+
+
+def alloc_bytes(n, device="cuda"):
+    """A 256-byte aligned device buffer of n bytes (torch's caching allocator)."""
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+def new_scratch(cfg: Config, device="cuda"):
+    s = alloc_bytes(query_sizes(cfg).scratch, device)
+    clear_status(s)
+    return s
+
+
+# ------------------------------------------------------------------ entry points
+
+def embed_fwd(cfg, idx, wte, x0, r0, scratch, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_embed_fwd(C.byref(c), _p(idx), _p(wte), _p(x0), _p(r0), _p(scratch), _stream(stream)),
+           "nc_embed_fwd")
+
+
+def embed_bwd(cfg, idx, x0, r0, dx0, dwte, scratch, accumulate=False, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_embed_bwd(C.byref(c), _p(idx), _p(x0), _p(r0), _p(dx0), _p(dwte), int(accumulate),
+                               _p(scratch), _stream(stream)), "nc_embed_bwd")
+
+
+def _bp(w):
+    return NcBlockParams(w["wqkv"].data_ptr(), w["wo"].data_ptr(), w["w1"].data_ptr(), w["w2"].data_ptr())
+
+
+def block_fwd(cfg, w, x_in, x_out, saved, scratch, stream=None):
+    c = to_nc_config(cfg)
+    bp = _bp(w)
+    _check(load().nc_block_fwd(C.byref(c), C.byref(bp), _p(x_in), _p(x_out), _p(saved), _p(scratch),
+                               _stream(stream)), "nc_block_fwd")
+
+
+def block_bwd(cfg, w, x_in, saved, dx_out, dx_in, grads, scratch, accumulate=False, stream=None):
+    c = to_nc_config(cfg)
+    bp = _bp(w)
+    bg = NcBlockGrads(grads["wqkv"].data_ptr(), grads["wo"].data_ptr(), grads["w1"].data_ptr(),
+                      grads["w2"].data_ptr())
+    _check(load().nc_block_bwd(C.byref(c), C.byref(bp), _p(x_in), _p(saved), _p(dx_out), _p(dx_in),
+                               C.byref(bg), int(accumulate), _p(scratch), _stream(stream)), "nc_block_bwd")
+
+
+def lmhead_softcap_xent_fwd(cfg, x, wlm, targets, loss, saved, scratch, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_lmhead_softcap_xent_fwd(C.byref(c), _p(x), _p(wlm), _p(targets), _p(loss), _p(saved),
+                                             _p(scratch), _stream(stream)), "nc_lmhead_softcap_xent_fwd")
+
+
+def lmhead_softcap_xent_bwd(cfg, x, wlm, targets, saved, dloss, dx, dwlm, scratch, accumulate=False,
+                            stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_lmhead_softcap_xent_bwd(C.byref(c), _p(x), _p(wlm), _p(targets), _p(saved),
+                                             float(dloss), _p(dx), _p(dwlm), int(accumulate), _p(scratch),
+                                             _stream(stream)), "nc_lmhead_softcap_xent_bwd")
+
+
+def model_loss_and_grad(cfg, params, idx, targets, loss, grads, workspace, dloss=1.0, accumulate=False,
+                        stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_model_loss_and_grad(C.byref(c), _p(params), _p(idx), _p(targets), _p(loss), _p(grads),
+                                         float(dloss), int(accumulate), _p(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "nc_model_loss_and_grad")

@@ -1,0 +1,203 @@
+/* nc.h - C ABI of the MI355X (gfx950) nanochat pretraining step.
+ *
+ * One GPU's forward + backward through the decoder described by the
+ * architecture list of the page "安德烈·卡帕西推出nanochat：极简全栈AI训练项目"
+ * (vpshk.cn, Q&A section "卡帕西亲自揭秘背后技术"): a dense Transformer with
+ * rotary embeddings (no position table), QK norm, untied embedding and
+ * unembedding, a norm right after the token embedding, a ReLU^2 MLP,
+ * parameter-free RMSNorm, bias-free linears, multi-query attention and a
+ * logit softcap; trained by next-token cross-entropy (page "100美元成本、
+ * 8000行代码纯手搓克隆ChatGPT!" on imeisheng.com, section "预训练", which also
+ * fixes the per-GPU batch of 32 rows x 2048 tokens and the depth-20 shape of
+ * 1280 channels and 10 heads of 128).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named in the argument lists are DEVICE pointers unless marked
+ *    "host". `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *  - The caller owns all memory. The library never allocates or frees device
+ *    memory and never synchronises the stream, except nc_read_status. It keeps
+ *    no pointer after returning, beyond the kernels already queued.
+ *  - Storage type: cfg->dtype = NC_BF16 stores weights, activations and
+ *    activation gradients as bfloat16 (round to nearest even); NC_F32 stores
+ *    them as float (the check mode). Statistics, GEMM accumulation, softmax,
+ *    loss and all weight gradients are float32 in both modes.
+ *  - Layouts are row-major. Weights use the [out, in] layout of a linear
+ *    layer. M = batch * seq_len tokens; token m is row b = m / seq_len,
+ *    position t = m % seq_len. d = d_model, H = n_head, G = n_kv_head,
+ *    D = head_dim, F = d_ff, V = vocab, QKV = (H + 2G) * D.
+ *  - Wqkv is [QKV, d] = rows of Wq [H*D, d], then Wk [G*D, d], then Wv [G*D, d].
+ *  - idx and targets are int32 [M]. A target of -1 is ignored by the loss.
+ *  - Every function returns nc_status; nothing throws across the ABI. Argument
+ *    checks run before anything is queued: on error nothing was launched.
+ *    NC_ERR_HIP means a launch failed (text via nc_last_hip_error).
+ *  - Data errors found on the device (a token id outside [0,V), a target
+ *    outside [-1,V), every target ignored, a non-finite loss) set bits of a
+ *    sticky 32-bit status word kept in the first bytes of `scratch` (or of the
+ *    model `workspace`); kernels then treat a bad id as a zero row and a bad
+ *    target as ignored, with no out-of-bounds access. Read the word with
+ *    nc_read_status, clear it with nc_clear_status (clear it once after
+ *    allocating a scratch buffer).
+ *  - All buffers must be 16-byte aligned (NC_ERR_ALIGN otherwise).
+ *  - Results are deterministic: no floating-point atomics are used.
+ *  - Calls that share a scratch buffer must not run concurrently.
+ */
+#ifndef NC_H_
+#define NC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NC_ABI_VERSION 1
+
+typedef enum nc_status {
+  NC_OK = 0,
+  NC_ERR_INVALID_ARG = 1, /* null pointer or bad flag */
+  NC_ERR_SHAPE = 2,       /* inconsistent or non-positive shape */
+  NC_ERR_ALIGN = 3,       /* a buffer is not 16-byte aligned */
+  NC_ERR_WORKSPACE = 4,   /* workspace smaller than nc_query_sizes says */
+  NC_ERR_UNSUPPORTED = 5, /* shape the kernels do not implement (see nc_validate) */
+  NC_ERR_HIP = 6,         /* a HIP launch or runtime call failed */
+  NC_ERR_DEVICE_DATA = 7  /* nc_read_status found a set device status bit */
+} nc_status;
+
+typedef enum nc_dtype { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
+
+/* Device status bits (see nc_read_status). */
+#define NC_STATUS_BAD_TOKEN 0x1u
+#define NC_STATUS_BAD_TARGET 0x2u
+#define NC_STATUS_NONFINITE_LOSS 0x4u
+#define NC_STATUS_NO_TARGETS 0x8u
+
+/* Model and batch shape (host struct). softcap c: logits become c*tanh(z/c);
+ * rope_base theta: pair i of a head rotates by t * theta^(-2i/D);
+ * norm_eps: epsilon of every RMSNorm, the per-head QK norm included. */
+typedef struct nc_config {
+  int32_t depth, d_model, n_head, head_dim, n_kv_head, d_ff, vocab, batch, seq_len;
+  float softcap, rope_base, norm_eps;
+  int32_t dtype; /* nc_dtype */
+} nc_config;
+
+/* One block's weights, storage dtype: wqkv [QKV,d], wo [d,H*D], w1 [F,d], w2 [d,F]. */
+typedef struct nc_block_params {
+  const void *wqkv, *wo, *w1, *w2;
+} nc_block_params;
+
+/* One block's weight gradients, float32, same shapes as nc_block_params. */
+typedef struct nc_block_grads {
+  float *wqkv, *wo, *w1, *w2;
+} nc_block_grads;
+
+/* Buffer sizes in bytes for a configuration (see nc_query_sizes). */
+typedef struct nc_sizes {
+  size_t block_saved;     /* `saved` of nc_block_fwd/bwd (one block) */
+  size_t lmhead_saved;    /* `saved` of nc_lmhead_softcap_xent_fwd/bwd */
+  size_t scratch;         /* `scratch` of every per-function entry point */
+  size_t model_workspace; /* `workspace` of nc_model_loss_and_grad */
+  size_t n_params;        /* elements of the flat parameter buffer */
+} nc_sizes;
+
+/* ---------------------------------------------------------------- queries */
+
+int nc_abi_version(void);
+const char* nc_status_str(int status);
+/* Text of the last HIP error seen by this thread ("" if none). */
+const char* nc_last_hip_error(void);
+
+/* Checks a configuration. NC_ERR_SHAPE: a non-positive size, H % G != 0,
+ * d/H/F/V not matching. NC_ERR_UNSUPPORTED: head_dim not 64 or 128, d_model
+ * or d_ff not a multiple of 64, vocab not a multiple of 8, more than
+ * 2^31 - 1 elements in any tensor, dtype unknown. */
+nc_status nc_validate(const nc_config* cfg);
+
+/* Host outputs. offsets[0] = Wte [V,d]; for layer l (0-based)
+ * offsets[1+4l .. 4+4l] = Wqkv, Wo, W1, W2; offsets[1+4L] = Wlm [V,d].
+ * Offsets count elements of the flat parameter buffer, in which the
+ * tensors are stored back to back in this order. n_offsets must be >= 2+4L. */
+nc_status nc_param_layout(const nc_config* cfg, size_t* offsets, size_t n_offsets, size_t* n_params);
+
+nc_status nc_query_sizes(const nc_config* cfg, nc_sizes* sizes /* host */);
+
+/* Copies the status word from the start of `scratch` (or a model workspace)
+ * to *flags (host) after synchronising `stream`. Returns NC_OK when no bit is
+ * set, NC_ERR_DEVICE_DATA otherwise. */
+nc_status nc_read_status(const void* scratch, uint32_t* flags, void* stream);
+/* Queues a kernel that zeroes the status word. */
+nc_status nc_clear_status(void* scratch, void* stream);
+
+/* ------------------------------------------------------------- embedding */
+
+/* Token embedding followed by the parameter-free norm the architecture list
+ * places right after it: x0[m] = N(Wte[idx[m]]), N(v) = v / sqrt(mean(v^2) + eps).
+ * idx int32 [M]; wte [V,d]; x0 [M,d] (out); r0 float [M] (out) =
+ * 1/sqrt(mean(Wte[idx[m]]^2) + eps), kept for the backward. */
+nc_status nc_embed_fwd(const nc_config* cfg, const int32_t* idx, const void* wte, void* x0,
+                       float* r0, void* scratch, void* stream);
+
+/* Backward of nc_embed_fwd: de = N_bwd(dx0) = r0 * (dx0 - x0 * mean(dx0 * x0)),
+ * dWte[v] = sum over m with idx[m] = v of de[m], summed in increasing m for
+ * every v (deterministic). dwte float [V,d]: overwritten, or added to when
+ * accumulate != 0 (rows of ids absent from idx are then left unchanged). */
+nc_status nc_embed_bwd(const nc_config* cfg, const int32_t* idx, const void* x0, const float* r0,
+                       const void* dx0, float* dwte, int accumulate, void* scratch, void* stream);
+
+/* ----------------------------------------------------------------- block */
+
+/* One pre-norm block: h = N(x); [q|k|v] = h Wqkv^T; q, k <- RoPE(N_D(.)) per
+ * head; o = causal multi-query attention (head h uses KV head h*G/H, scale
+ * 1/sqrt(D)); x1 = x + o Wo^T; u = N(x1) W1^T; x_out = x1 + max(u,0)^2 W2^T.
+ * x_in, x_out [M,d] (must not alias). saved [block_saved bytes] receives the
+ * activations nc_block_bwd needs; it stays borrowed until that call. */
+nc_status nc_block_fwd(const nc_config* cfg, const nc_block_params* w, const void* x_in,
+                       void* x_out, void* saved, void* scratch, void* stream);
+
+/* Backward of nc_block_fwd given dx_out = dLoss/dx_out [M,d]; writes
+ * dx_in [M,d] (may alias dx_out) and the weight gradients (float32; written,
+ * or added to when accumulate != 0). x_in and saved as passed to the forward. */
+nc_status nc_block_bwd(const nc_config* cfg, const nc_block_params* w, const void* x_in,
+                       const void* saved, const void* dx_out, void* dx_in,
+                       const nc_block_grads* grads, int accumulate, void* scratch, void* stream);
+
+/* ------------------------------------------------------------ LM head + loss */
+
+/* Final norm, untied unembedding, logit softcap and next-token cross-entropy:
+ * xf = N(x); z = xf Wlm^T; z' = c tanh(z/c);
+ * loss = mean over m with targets[m] != -1 of logsumexp(z'[m]) - z'[m][targets[m]].
+ * x [M,d]; wlm [V,d]; loss: one float (device, out). saved [lmhead_saved bytes]
+ * keeps xf, the logits z' (storage dtype, [M,V]) and the row log-sum-exps. */
+nc_status nc_lmhead_softcap_xent_fwd(const nc_config* cfg, const void* x, const void* wlm,
+                                     const int32_t* targets, float* loss, void* saved,
+                                     void* scratch, void* stream);
+
+/* Backward of the above scaled by dloss: dz = (softmax(z') - onehot(target))
+ * * dloss / Nv * (1 - (z'/c)^2) on valid rows (0 on ignored rows);
+ * dWlm = dz^T xf; dx = N_bwd(dz Wlm). The logits in `saved` are overwritten
+ * by dz, so call it once per forward. dx [M,d] (out); dwlm float [V,d]
+ * (written, or added to when accumulate != 0). */
+nc_status nc_lmhead_softcap_xent_bwd(const nc_config* cfg, const void* x, const void* wlm,
+                                     const int32_t* targets, void* saved, float dloss, void* dx,
+                                     float* dwlm, int accumulate, void* scratch, void* stream);
+
+/* ---------------------------------------------------------------- model */
+
+/* The whole step: embedding, depth blocks, LM head + loss, then the backward
+ * of all of them. params: flat buffer in the storage dtype laid out as
+ * nc_param_layout says; grads: float32, same layout (written, or added to
+ * when accumulate != 0); loss: one float (device, out); dloss scales every
+ * gradient (1 for a plain step, 1/n to average n micro-steps).
+ * workspace [workspace_bytes >= model_workspace] holds every activation of
+ * the step plus scratch; its first bytes are the device status word. */
+nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const int32_t* idx,
+                                 const int32_t* targets, float* loss, float* grads, float dloss,
+                                 int accumulate, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NC_H_ */

@@ -1,0 +1,235 @@
+"""GPU path (through the C ABI) against the fp64 oracle, element by element.
+
+Shapes are small enough for the oracle to finish in seconds while spanning
+several GEMM/attention tiles and ragged tails (T = 100, 130, 70; d = 192;
+vocab = 520, 1000), GQA as well as MQA, head_dim 64 and 128, and both storage
+types: bf16 (loss rel. error <= 1e-2, per-tensor gradient rel. Frobenius
+error <= 3e-2) and the float32 check mode (<= 1e-4 for both)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dense_pretraining_amd import lib, synth
+from dense_pretraining_amd.config import Config, TINY
+from gpu_util import (TOL, ModelRun, assert_close, dev, flat_params, host, ocfg, pack_block, params,
+                      split_grads, unpack_qkv)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny": TINY,
+    "ragged": Config(depth=2, d_model=192, n_head=3, head_dim=64, n_kv_head=1, d_ff=320, vocab=520, batch=3,
+                     seq_len=100),
+    "gqa": Config(depth=1, d_model=256, n_head=4, head_dim=64, n_kv_head=2, d_ff=512, vocab=256, batch=2,
+                  seq_len=70),
+    "d128": Config(depth=2, d_model=256, n_head=2, head_dim=128, n_kv_head=1, d_ff=512, vocab=1000, batch=2,
+                   seq_len=130),
+}
+CASES = [(name, dt) for name in SHAPES for dt in ("f32", "bf16")]
+
+
+def _cfg(name, dt):
+    return SHAPES[name].with_(dtype=dt)
+
+
+def _tokens(cfg):
+    return synth.zipf_tokens(cfg.vocab, cfg.batch, cfg.seq_len)
+
+
+@pytest.mark.parametrize("name,dt", CASES)
+def test_embed_fwd_bwd(name, dt):
+    cfg = _cfg(name, dt)
+    tol = TOL[dt]
+    p = params(cfg)
+    idx, _ = _tokens(cfg)
+    M, d = cfg.tokens, cfg.d_model
+    x0_ref, r0_ref = oracle.embed_fwd(ocfg(cfg), idx.reshape(-1), p["wte"])
+    scratch = lib.new_scratch(cfg)
+    wte = dev(p["wte"], cfg)
+    idx_d = torch.from_numpy(idx.reshape(-1)).cuda()
+    x0 = torch.empty(M, d, dtype=lib.torch_dtype(cfg), device="cuda")
+    r0 = torch.empty(M, dtype=torch.float32, device="cuda")
+    lib.embed_fwd(cfg, idx_d, wte, x0, r0, scratch)
+    torch.cuda.synchronize()
+    assert_close(host(x0), x0_ref, tol["act"], "x0")
+    assert_close(host(r0), r0_ref[:, 0], tol["act"], "r0")
+    # backward from the GPU's own saved x0 (rounded like the forward stores it)
+    dx0_np = synth.normal((M, d), 1.0, np.random.default_rng(7), dt)
+    dwte = torch.empty(cfg.vocab, d, dtype=torch.float32, device="cuda")
+    lib.embed_bwd(cfg, idx_d, x0, r0, dev(dx0_np, cfg), dwte, scratch)
+    torch.cuda.synchronize()
+    ref = oracle.embed_bwd(ocfg(cfg), idx.reshape(-1), host(x0), host(r0)[:, None], dx0_np, cfg.vocab)
+    g = host(dwte)
+    assert_close(g, ref, tol["grad"], "dwte")
+    absent = np.setdiff1d(np.arange(cfg.vocab), np.unique(idx))
+    assert np.all(g[absent] == 0)
+    assert lib.read_status(scratch) == 0
+
+
+@pytest.mark.parametrize("name,dt", CASES)
+def test_block_fwd_bwd(name, dt):
+    cfg = _cfg(name, dt).with_(depth=1)
+    tol = TOL[dt]
+    p = params(cfg, fan_in=True)
+    w = p["layers"][0]
+    x_np, dy_np = synth.block_inputs(cfg.batch, cfg.seq_len, cfg.d_model, dtype=dt)
+    oc = ocfg(cfg)
+    x_ref, cache = oracle.block_fwd(oc, w, x_np)
+    dx_ref, g_ref = oracle.block_bwd(oc, w, x_np, dy_np, cache)
+
+    M, d = cfg.tokens, cfg.d_model
+    sz = lib.query_sizes(cfg)
+    saved = lib.alloc_bytes(sz.block_saved)
+    scratch = lib.new_scratch(cfg)
+    wd = {k: dev(v, cfg) for k, v in pack_block(w).items()}
+    x = dev(x_np.reshape(M, d), cfg)
+    x_out = torch.empty_like(x)
+    lib.block_fwd(cfg, wd, x, x_out, saved, scratch)
+    torch.cuda.synchronize()
+    assert_close(host(x_out), x_ref.reshape(M, d), tol["act"], "x_out")
+
+    dy = dev(dy_np.reshape(M, d), cfg)
+    dx = torch.empty_like(x)
+    gd = {k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in wd.items()}
+    lib.block_bwd(cfg, wd, x, saved, dy, dx, gd, scratch)
+    torch.cuda.synchronize()
+    assert_close(host(dx), dx_ref.reshape(M, d), tol["grad"], "dx_in")
+    gq, gk, gv = unpack_qkv(host(gd["wqkv"]), cfg)
+    assert_close(gq, g_ref["wq"], tol["grad"], "dWq")
+    assert_close(gk, g_ref["wk"], tol["grad"], "dWk")
+    assert_close(gv, g_ref["wv"], tol["grad"], "dWv")
+    assert_close(host(gd["wo"]), g_ref["wo"], tol["grad"], "dWo")
+    assert_close(host(gd["w1"]), g_ref["w1"], tol["grad"], "dW1")
+    assert_close(host(gd["w2"]), g_ref["w2"], tol["grad"], "dW2")
+
+    # dx_in may alias dx_out; accumulate adds into the gradients
+    gd2 = {k: v.clone() for k, v in gd.items()}
+    dy2 = dy.clone()
+    lib.block_bwd(cfg, wd, x, saved, dy2, dy2, gd2, scratch, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dy2, dx)
+    for k in gd:
+        torch.testing.assert_close(gd2[k], 2 * gd[k], rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("name,dt", CASES)
+def test_lmhead_softcap_xent(name, dt):
+    cfg = _cfg(name, dt)
+    tol = TOL[dt]
+    rng = np.random.default_rng(11)
+    M, d, V = cfg.tokens, cfg.d_model, cfg.vocab
+    x_np = synth.normal((M, d), 1.0, rng, dt)
+    # logits of a few units, so that the softcap bends them
+    wlm = synth.normal((V, d), 2.5 / np.sqrt(d), rng, dt)
+    _, tg = _tokens(cfg)
+    tg = tg.reshape(-1).copy()
+    tg[::7] = -1
+    oc = ocfg(cfg)
+    loss_ref, hc = oracle.lmhead_softcap_xent_fwd(oc, x_np, wlm, tg)
+    dx_ref, dwlm_ref = oracle.lmhead_softcap_xent_bwd(oc, x_np, wlm, hc, dloss=0.5)
+
+    sz = lib.query_sizes(cfg)
+    saved = lib.alloc_bytes(sz.lmhead_saved)
+    scratch = lib.new_scratch(cfg)
+    x = dev(x_np, cfg)
+    w = dev(wlm, cfg)
+    t = torch.from_numpy(tg).cuda()
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lib.lmhead_softcap_xent_fwd(cfg, x, w, t, loss, saved, scratch)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - loss_ref) <= tol["loss"] * abs(loss_ref)
+    dx = torch.empty_like(x)
+    dwlm = torch.empty(V, d, dtype=torch.float32, device="cuda")
+    lib.lmhead_softcap_xent_bwd(cfg, x, w, t, saved, 0.5, dx, dwlm, scratch)
+    torch.cuda.synchronize()
+    assert_close(host(dx), dx_ref, tol["grad"], "dx")
+    assert_close(host(dwlm), dwlm_ref, tol["grad"], "dWlm")
+    assert lib.read_status(scratch) == 0
+
+
+def _check_model(cfg, p, idx, tg, loss, grads, tol, dloss=1.0):
+    loss_ref, g_ref = oracle.model_loss_and_grad(ocfg(cfg), p, idx, tg, dloss=dloss)
+    assert abs(loss - loss_ref) <= tol["loss"] * abs(loss_ref), (loss, loss_ref)
+    g = split_grads(cfg, grads)
+    errs = {"wte": assert_close(g["wte"], g_ref["wte"], tol["grad"], "dWte"),
+            "wlm": assert_close(g["wlm"], g_ref["wlm"], tol["grad"], "dWlm")}
+    for l, (a, b) in enumerate(zip(g["layers"], g_ref["layers"])):
+        for k in a:
+            errs[f"{k}{l}"] = assert_close(a[k], b[k], tol["grad"], f"d{k}[{l}]")
+    return errs
+
+
+@pytest.mark.parametrize("name,dt", CASES)
+def test_model_loss_and_grad(name, dt):
+    cfg = _cfg(name, dt)
+    p = params(cfg)
+    idx, tg = _tokens(cfg)
+    run = ModelRun(cfg, p, idx, tg)
+    loss = run.run()
+    errs = _check_model(cfg, p, idx, tg, loss, host(run.grads), TOL[dt])
+    print(name, dt, "loss", loss, "max grad err", max(errs.values()))
+    assert run.status() == 0
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_model_deterministic_accumulate_dloss(dt):
+    cfg = SHAPES["ragged"].with_(dtype=dt)
+    p = params(cfg)
+    idx, tg = _tokens(cfg)
+    run = ModelRun(cfg, p, idx, tg)
+    l1 = run.run(dloss=0.25)
+    g1 = run.grads.clone()
+    l2 = run.run(dloss=0.25)
+    assert l1 == l2 and torch.equal(g1, run.grads), "not bitwise deterministic"
+    run.run(dloss=0.25, accumulate=True)
+    torch.testing.assert_close(run.grads, 2 * g1, rtol=1e-6, atol=0)
+    run.run(dloss=1.0)
+    torch.testing.assert_close(run.grads, 4 * g1, rtol=1e-5, atol=1e-12)
+
+
+def test_model_edge_cases():
+    cfg = SHAPES["tiny"].with_(dtype="f32")
+    p = params(cfg)
+    idx, tg = _tokens(cfg)
+    # every target ignored: loss 0, all gradients 0, status bit set
+    run = ModelRun(cfg, p, idx, np.full_like(tg, -1))
+    assert run.run() == 0.0
+    assert torch.count_nonzero(run.grads).item() == 0
+    assert run.status() & lib.STATUS_NO_TARGETS
+    # zero unembedding: loss = ln V exactly in the oracle
+    p0 = dict(p, wlm=np.zeros_like(p["wlm"]))
+    run = ModelRun(cfg, p0, idx, tg)
+    assert abs(run.run() - np.log(cfg.vocab)) < 1e-5
+    # out-of-range token and target ids: flagged, treated as zero rows / ignored
+    bad_idx = idx.copy()
+    bad_idx[0, 3] = cfg.vocab + 5
+    bad_tg = tg.copy()
+    bad_tg[1, 4] = -7
+    run = ModelRun(cfg, p, bad_idx, bad_tg)
+    loss = run.run()
+    st = run.status()
+    assert st & lib.STATUS_BAD_TOKEN and st & lib.STATUS_BAD_TARGET
+    assert np.isfinite(loss)
+
+
+def test_single_token_sequences():
+    # T = 1: attention returns v, so the gradients of Wq and Wk vanish in exact
+    # arithmetic; they must be rounding noise next to dWv, the rest as usual.
+    cfg = SHAPES["d128"].with_(dtype="f32", seq_len=1, batch=5)
+    p = params(cfg)
+    idx, tg = _tokens(cfg)
+    run = ModelRun(cfg, p, idx, tg)
+    loss = run.run()
+    loss_ref, g_ref = oracle.model_loss_and_grad(ocfg(cfg), p, idx, tg)
+    assert abs(loss - loss_ref) <= 1e-4 * abs(loss_ref)
+    g = split_grads(cfg, host(run.grads))
+    assert_close(g["wte"], g_ref["wte"], 1e-4, "dWte")
+    assert_close(g["wlm"], g_ref["wlm"], 1e-4, "dWlm")
+    for a, b in zip(g["layers"], g_ref["layers"]):
+        for k in ("wv", "wo", "w1", "w2"):
+            assert_close(a[k], b[k], 1e-4, k)
+        scale = np.max(np.abs(b["wv"]))
+        assert np.max(np.abs(a["wq"])) <= 1e-5 * scale
+        assert np.max(np.abs(a["wk"])) <= 1e-5 * scale
