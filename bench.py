@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Training-step benchmark on one MI355X.
+
+One step = nc_model_loss_and_grad: embedding + norm, all blocks, final norm,
+unembedding with logit softcap, cross-entropy, and the full backward pass,
+over one batch of seeded synthetic tokens resident in HBM.
+
+Default workload: the depth-20 model (d_model 1280, 10 query heads of 128,
+one KV head, MLP 5120, vocab 65536) at 32 rows x 2048 tokens, bf16 storage
+with fp32 accumulation -- one GPU's share of the pretraining step the
+imeisheng.com page ("预训练") describes.
+
+Prints one JSON line: tokens/s, MFU, the dominant kernel's roofline (its
+launches timed with HIP events inside the timed region) and the fp64 CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from dense_pretraining_amd import config as C  # noqa: E402
+from dense_pretraining_amd import synth  # noqa: E402
+
+METRIC = "train tokens/sec (fwd+bwd) + MFU, depth-20 B=32 T=2048 bf16, 1 MI355X"
+WORKLOADS = {
+    "depth20": (C.DEPTH20, "depth-20 decoder (d 1280, 10x128 heads, 1 KV head, MLP 5120, vocab 65536), "
+                           "32 x 2048 tokens, bf16, forward+backward"),
+    "depth30": (C.DEPTH30, "depth-30 decoder (d 1920, 15x128 heads, 1 KV head, MLP 7680, vocab 65536), "
+                           "16 x 2048 tokens, bf16, forward+backward"),
+}
+PEAK_BF16 = C.MI355X_BF16_DENSE_PEAK
+PEAK_HBM = C.MI355X_HBM_PEAK
+
+
+def flat_params(p):
+    parts = [p["wte"].reshape(-1)]
+    for w in p["layers"]:
+        parts += [np.concatenate([w["wq"], w["wk"], w["wv"]]).reshape(-1), w["wo"].reshape(-1),
+                  w["w1"].reshape(-1), w["w2"].reshape(-1)]
+    parts.append(p["wlm"].reshape(-1))
+    return np.concatenate(parts)
+
+
+def kernel_table(prof, steps):
+    rows = {}
+    for name, r in prof.items():
+        ms = r["ms"]
+        rows[name] = dict(ms_per_step=ms / steps, launches_per_step=r["launches"] / steps,
+                          tflops=(r["flops"] / (ms * 1e-3) / 1e12) if ms > 0 else 0.0,
+                          gbps=(r["bytes"] / (ms * 1e-3) / 1e9) if ms > 0 else 0.0,
+                          flops_per_launch=r["flops"] / max(r["launches"], 1),
+                          bytes_per_launch=r["bytes"] / max(r["launches"], 1))
+    return dict(sorted(rows.items(), key=lambda kv: -kv[1]["ms_per_step"]))
+
+
+def roofline(table):
+    name, r = next(iter(table.items()))
+    if r["flops_per_launch"] > 0:
+        ach = r["tflops"]
+        return name, dict(bound="mfma", achieved=round(ach, 2), peak=round(PEAK_BF16 / 1e12, 1), unit="TFLOP/s",
+                          frac=round(ach / (PEAK_BF16 / 1e12), 4), traffic=None,
+                          kernel=name, flops_per_launch=r["flops_per_launch"],
+                          avg_launch_ms=round(r["ms_per_step"] / r["launches_per_step"], 4))
+    ach = r["gbps"]
+    return name, dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
+                      frac=round(ach / (PEAK_HBM / 1e9), 4), traffic=None, kernel=name,
+                      bytes_per_launch=r["bytes_per_launch"],
+                      avg_launch_ms=round(r["ms_per_step"] / r["launches_per_step"], 4))
+
+
+def cpu_baseline(cfg, p, idx, tg, tokens):
+    """The fp64 oracle, untuned, on one sequence of `tokens` positions of the
+    same model (all blocks, full vocabulary): tokens per second."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    T = min(tokens, cfg.seq_len)
+    oc = oracle.Cfg(depth=cfg.depth, d_model=cfg.d_model, n_head=cfg.n_head, head_dim=cfg.head_dim,
+                    n_kv_head=cfg.n_kv_head, d_ff=cfg.d_ff, vocab=cfg.vocab, batch=1, seq_len=T,
+                    softcap=cfg.softcap, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
+    t0 = time.perf_counter()
+    oracle.model_loss_and_grad(oc, p, idx[:1, :T], tg[:1, :T])
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return dict(value=round(T / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"fp64 NumPy oracle, forward+backward of the same {cfg.depth}-layer model over one "
+                       f"sequence of {T} tokens (full vocabulary), {dt:.1f} s wall on {threads} BLAS threads")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="depth20")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="do not record per-kernel HIP events in the timed region")
+    a = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU data-parallel path is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dense_pretraining_amd import lib
+
+    cfg, desc = WORKLOADS[a.workload]
+    torch.cuda.set_device(0)
+    lib.load()
+    t_gen = time.perf_counter()
+    p = synth.init_params(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
+                          std=0.02, seed=0, dtype=cfg.dtype, out=np.float32)
+    idx, tg = synth.zipf_tokens(cfg.vocab, cfg.batch, cfg.seq_len)
+    params = torch.from_numpy(flat_params(p)).to("cuda", lib.torch_dtype(cfg))
+    idx_d = torch.from_numpy(idx.reshape(-1)).cuda()
+    tg_d = torch.from_numpy(tg.reshape(-1)).cuda()
+    sz = lib.query_sizes(cfg)
+    ws = lib.alloc_bytes(sz.model_workspace)
+    lib.clear_status(ws)
+    grads = torch.zeros(sz.n_params, dtype=torch.float32, device="cuda")
+    loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s; workspace {sz.model_workspace / 1e9:.1f} GB",
+          file=sys.stderr, flush=True)
+
+    def step():
+        lib.model_loss_and_grad(cfg, params, idx_d, tg_d, loss, grads, ws)
+
+    for i in range(a.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"# warmup {i + 1}/{a.warmup}", file=sys.stderr, flush=True)
+    st = lib.read_status(ws)
+    if st:
+        print(f"# device status bits set: {st:#x}", file=sys.stderr)
+
+    timing = not a.no_kernel_timing
+    torch.cuda.synchronize()
+    if timing:
+        lib.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if timing:
+        lib.profile_enable(False)
+    ms = e0.elapsed_time(e1) / a.steps
+    print(f"# timed {a.steps} steps: {ms:.2f} ms/step (wall {wall / a.steps * 1e3:.2f})", file=sys.stderr,
+          flush=True)
+
+    tokens = cfg.batch * cfg.seq_len
+    tps = tokens / (ms * 1e-3)
+    f_causal = C.flops_per_token(cfg, "causal")
+    f_palm = C.flops_per_token(cfg, "palm")
+    out = {
+        "metric": METRIC if a.workload == "depth20" else f"train tokens/sec (fwd+bwd), {a.workload}",
+        "value": round(tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded Zipf(1.1) token ids, N(0, 0.02) weights",
+        "config": {"workload": desc, "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none"},
+        "mfu": round(tps * f_causal / PEAK_BF16, 4),
+        "mfu_palm": round(tps * f_palm / PEAK_BF16, 4),
+        "loss": round(float(loss.item()), 6),
+    }
+    if timing:
+        table = kernel_table(lib.profile_summary(), a.steps)
+        name, rl = roofline(table)
+        out["roofline"] = rl
+        out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
+                              if kk in ("ms_per_step", "launches_per_step", "tflops", "gbps")}
+                          for k, v in table.items()}
+        out["kernel_ms_sum"] = round(sum(v["ms_per_step"] for v in table.values()), 3)
+    if a.cpu_tokens > 0:
+        print("# timing the CPU oracle sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, p, idx, tg, a.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -633,9 +633,16 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
   }
 }
 
+// Unmasked (query, key) pairs of causal attention over all heads and rows.
+double causal_pairs(const AttnGeom& g) { return (double)g.B * g.H * g.T * (g.T + 1.0) / 2.0; }
+
 template <typename T, int D>
 nc_status attn_fwd_impl(const AttnGeom& g, const T* qk, const T* v, T* o, float* lse, hipStream_t st) {
   int nqb = (g.T * g.n_rep + 127) / 128;
+  const double tok = (double)g.B * g.T, es = sizeof(T);
+  // S = Q K^T and O = P V: 4 D flops per pair
+  ProfScope prof(NC_NAME(T, "attn_fwd"), 4.0 * D * causal_pairs(g),
+                 es * tok * D * (2.0 * g.H + 2.0 * g.G) + 4.0 * tok * g.H, st);
   hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(nqb, g.G, g.B), dim3(256), 0, st, g, qk, v, o, lse);
   NC_LAUNCH_CHECK("attn_fwd");
   return NC_OK;
@@ -645,10 +652,19 @@ template <typename T, int D>
 nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, const T* dO, const float* lse,
                         float* delta, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st) {
   int nqb = (g.T * g.n_rep + 127) / 128;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(nqb, g.G, g.B), dim3(256), 0, st, g, qk, v, o, dO, lse, delta,
-                     dq);
-  NC_LAUNCH_CHECK("attn_bwd_dq");
+  const double tok = (double)g.B * g.T, es = sizeof(T);
+  {
+    // recompute S, then dP = dO V^T and dQ = dS K: 6 D flops per pair
+    ProfScope prof(NC_NAME(T, "attn_bwd_dq"), 6.0 * D * causal_pairs(g),
+                   es * tok * D * (4.0 * g.H + 2.0 * g.G) + 8.0 * tok * g.H, st);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(nqb, g.G, g.B), dim3(256), 0, st, g, qk, v, o, dO, lse,
+                       delta, dq);
+    NC_LAUNCH_CHECK("attn_bwd_dq");
+  }
   int nkb = (g.T + 127) / 128;
+  // recompute S and dP, then dV = P^T dO and dK = dS^T Q: 8 D flops per pair
+  ProfScope prof(NC_NAME(T, "attn_bwd_dkdv"), 8.0 * D * causal_pairs(g),
+                 es * tok * D * (2.0 * g.H + 4.0 * g.G) + 8.0 * tok * g.H, st);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(nkb, g.G, g.B), dim3(256), 0, st, g, qk, v, dO, lse, delta,
                      dk, dv, ld_dkv);
   NC_LAUNCH_CHECK("attn_bwd_dkdv");

@@ -214,6 +214,8 @@ nc_status embed_scatter(const int32_t* idx, const float* de, float* dwte, int M,
   const int nwin = (M + kWin - 1) / kWin;
   NC_TRY(fill_u32(reinterpret_cast<uint32_t*>(b.hist), 0u, (size_t)nch * V, st));
   if (!accumulate) NC_TRY(fill_f32(dwte, 0.f, (size_t)V * d, st));
+  {
+  ProfScope prof("embed_sort", 0, 4.0 * M * 5 + 8.0 * nch * V, st);
   hipLaunchKernelGGL(eb_hist_kernel, dim3((M + 255) / 256), dim3(256), 0, st, idx, M, V, b.hist);
   NC_LAUNCH_CHECK("eb_hist");
   hipLaunchKernelGGL(eb_colscan_kernel, dim3((V + 255) / 256), dim3(256), 0, st, b.hist, nch, V, b.seg);
@@ -222,9 +224,14 @@ nc_status embed_scatter(const int32_t* idx, const float* de, float* dwte, int M,
   NC_LAUNCH_CHECK("eb_scan");
   hipLaunchKernelGGL(eb_place_kernel, dim3(nch), dim3(256), 0, st, idx, M, V, b.hist, b.seg, b.perm, b.sid);
   NC_LAUNCH_CHECK("eb_place");
+  }
+  {
+  ProfScope prof("embed_window_sum", 0, 4.0 * M * d + 8.0 * M + 4.0 * (double)d * M, st);
   hipLaunchKernelGGL(eb_window_kernel, dim3(nwin), dim3(256), 0, st, de, d, b.seg, b.perm, b.sid, V, dwte, b.spill);
   NC_LAUNCH_CHECK("eb_window");
+  }
   if (nwin > 1) {
+    ProfScope prof("embed_fixup", 0, 0, st);
     hipLaunchKernelGGL(eb_fixup_kernel, dim3(nwin - 1), dim3(256), 0, st, d, b.seg, b.sid, V, dwte, b.spill);
     NC_LAUNCH_CHECK("eb_fixup");
   }

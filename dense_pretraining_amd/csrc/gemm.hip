@@ -33,6 +33,9 @@ template <typename T>
 nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_x, hipStream_t st) {
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   EpiStore<T> e{y, N, res, N, M, N};
+  const double es = sizeof(T);
+  ProfScope prof(relu_sq_x ? NC_NAME(T, "gemm_fwd_relusq") : NC_NAME(T, "gemm_fwd"), 2.0 * M * N * K,
+                 es * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
   if (relu_sq_x) return launch_gemm<T, kKc, kKc, ReluSq, Identity>(s, e, st);
   return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
 }
@@ -41,6 +44,9 @@ template <typename T>
 nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* u, int M, int N, int K, hipStream_t st) {
   // C[M,K] = A[M,N] * B where B(n=k_out, k=n_in) = W[n_in][k_out]: K-outer.
   GemmShape s{dy, w, N, K, M, K, N, N, 1};
+  const double es = sizeof(T);
+  ProfScope prof(u ? NC_NAME(T, "gemm_dx_drelusq") : NC_NAME(T, "gemm_dx"), 2.0 * M * N * K,
+                 es * ((double)M * N + (double)N * K + (double)M * K * (u ? 2 : 1)), st);
   if (u) {
     EpiDReluSq<T> e{dx, K, u, K, M, K};
     return launch_gemm<T, kKc, kKo, Identity, Identity>(s, e, st);
@@ -70,8 +76,14 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool 
     e.split_stride = 0;
     e.accumulate = accumulate;
   }
-  nc_status r = relu_sq_x ? launch_gemm<T, kKo, kKo, Identity, ReluSq>(s, e, st)
-                          : launch_gemm<T, kKo, kKo, Identity, Identity>(s, e, st);
+  nc_status r;
+  {
+    const double es = sizeof(T);
+    ProfScope prof(relu_sq_x ? NC_NAME(T, "gemm_dw_relusq") : NC_NAME(T, "gemm_dw"), 2.0 * M * N * K,
+                   es * ((double)M * N + (double)M * K) + 4.0 * N * K * (accumulate ? 2 : 1), st);
+    r = relu_sq_x ? launch_gemm<T, kKo, kKo, Identity, ReluSq>(s, e, st)
+                  : launch_gemm<T, kKo, kKo, Identity, Identity>(s, e, st);
+  }
   if (r != NC_OK || nsplit == 1) return r;
   return splitk_reduce(partial, nsplit, (size_t)N * K, dw, accumulate, st);
 }
@@ -82,6 +94,8 @@ template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
                       float* part, float* zt, hipStream_t st) {
   GemmShape s{x, w, K, K, M, N, K, K, 1};
+  ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
+                 sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N), st);
   EpiSoftcap<T> e{z, N, cap, targets, part, zt, lmhead_tiles(N), M, N};
   return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
 }

@@ -5,6 +5,23 @@
 
 namespace nc {
 
+// Times one launch with HIP events while profiling is on (prof.hip); `name`
+// must be a string literal. flops/bytes: the launch's algorithmic work.
+class ProfScope {
+ public:
+  ProfScope(const char* name, double flops, double bytes, hipStream_t st);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  int slot_;
+  hipStream_t st_;
+};
+
+template <typename T> constexpr bool is_bf16() { return sizeof(T) == 2; }
+#define NC_NAME(T, base) (is_bf16<T>() ? base "_bf16" : base "_f32")
+
 // ------------------------------------------------------------ GEMM (gemm.hip)
 // y[M,N] = x[M,K] W[N,K]^T (+ res[M,N]); relu_sq_x applies max(x,0)^2 to x.
 template <typename T>

@@ -326,11 +326,13 @@ unsigned grid_for(size_t n, size_t per_block) {
 }  // namespace
 
 nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st) {
+  ProfScope prof("fill_u32", 0, 4.0 * n, st);
   hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, p, v, n);
   NC_LAUNCH_CHECK("fill_u32");
   return NC_OK;
 }
 nc_status fill_f32(float* p, float v, size_t n, hipStream_t st) {
+  ProfScope prof("fill_f32", 0, 4.0 * n, st);
   hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n / 4 + 1, 256)), dim3(256), 0, st, p, v, n);
   NC_LAUNCH_CHECK("fill_f32");
   return NC_OK;
@@ -340,6 +342,8 @@ template <typename T>
 nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int M, int d, float eps, uint32_t* status,
                       hipStream_t st) {
   dim3 grid((M + 3) / 4);
+  ProfScope prof(idx ? NC_NAME(T, "embed_gather_rmsnorm") : NC_NAME(T, "rmsnorm_fwd"), 0,
+                 2.0 * sizeof(T) * M * d + 4.0 * M + (idx ? 4.0 * M : 0.0), st);
   if (idx)
     hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, true>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status);
   else
@@ -350,12 +354,15 @@ nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int
 
 template <typename T, typename TO>
 nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO* dx, int M, int d, hipStream_t st) {
+  ProfScope prof(sizeof(TO) != sizeof(T) ? "rmsnorm_bwd_bf16_to_f32" : NC_NAME(T, "rmsnorm_bwd"), 0,
+                 sizeof(T) * (double)M * d * (res ? 3 : 2) + sizeof(TO) * (double)M * d + 4.0 * M, st);
   hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, TO>), dim3((M + 3) / 4), dim3(256), 0, st, dy, y, r, res, dx, M, d);
   NC_LAUNCH_CHECK("rmsnorm_bwd");
   return NC_OK;
 }
 
 nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st) {
+  ProfScope prof("rope_table", 0, 4.0 * T * D, st);
   hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)T * D / 2, 256)), dim3(256), 0, st, cs, sn, T, D, base);
   NC_LAUNCH_CHECK("rope_table");
   return NC_OK;
@@ -364,6 +371,7 @@ nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t
 template <typename T>
 nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const float* cs, const float* sn, int M,
                           int T_, int nheads, int D, float eps, hipStream_t st) {
+  ProfScope prof(NC_NAME(T, "qknorm_rope_fwd"), 0, 2.0 * sizeof(T) * M * nheads * D, st);
   hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, qkv, ld_in, qk, ld_out, cs, sn,
                      M, T_, nheads, D, eps);
   NC_LAUNCH_CHECK("qknorm_rope_fwd");
@@ -373,6 +381,7 @@ nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const fl
 template <typename T>
 nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float* cs, const float* sn, int M, int T_,
                           int nheads, int D, float eps, hipStream_t st) {
+  ProfScope prof(NC_NAME(T, "qknorm_rope_bwd"), 0, 3.0 * sizeof(T) * M * nheads * D, st);
   hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, qkv, ld_in, g, ld_g, cs, sn, M,
                      T_, nheads, D, eps);
   NC_LAUNCH_CHECK("qknorm_rope_bwd");
@@ -386,6 +395,7 @@ nc_status xent_loss(const float* part, int ntiles, const float* zt, const int32_
                     hipStream_t st) {
   (void)row_loss;
   int nb = (int)xent_loss_blocks(M);
+  ProfScope prof("xent_loss", 0, 4.0 * M * ntiles + 16.0 * M, st);
   hipLaunchKernelGGL(xent_rows_kernel, dim3(nb), dim3(256), 0, st, part, ntiles, zt, targets, M, V, lse, block_sums,
                      block_counts, status);
   NC_LAUNCH_CHECK("xent_rows");
@@ -399,6 +409,7 @@ nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, 
                   hipStream_t st) {
   int nvec = V / Vec<T>::n;
   dim3 grid(M, (nvec + 1023) / 1024);
+  ProfScope prof(NC_NAME(T, "xent_dz"), 0, 2.0 * sizeof(T) * M * V + 12.0 * M, st);
   hipLaunchKernelGGL((xent_dz_kernel<T>), grid, dim3(256), 0, st, z, M, V, lse, targets, nv, dloss, 1.f / cap);
   NC_LAUNCH_CHECK("xent_dz");
   return NC_OK;
@@ -406,6 +417,7 @@ nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, 
 
 nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st) {
   size_t n4 = n / 4;
+  ProfScope prof("splitk_reduce", 0, 4.0 * n * (nsplit + (accumulate ? 2 : 1)), st);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st, partial, nsplit, n4, out,
                      accumulate);
   NC_LAUNCH_CHECK("splitk_reduce");

@@ -32,7 +32,7 @@ EXPORTED = [
     "nc_abi_version", "nc_status_str", "nc_last_hip_error", "nc_validate", "nc_param_layout",
     "nc_query_sizes", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
-    "nc_model_loss_and_grad",
+    "nc_model_loss_and_grad", "nc_profile_enable", "nc_profile_summary",
 ]
 
 
@@ -93,6 +93,8 @@ def load(path=LIB_PATH):
         "nc_lmhead_softcap_xent_fwd": ([cfgp, P, P, P, P, P, P, P], I),
         "nc_lmhead_softcap_xent_bwd": ([cfgp, P, P, P, P, F, P, P, I, P, P], I),
         "nc_model_loss_and_grad": ([cfgp, P, P, P, P, P, F, I, P, S, P], I),
+        "nc_profile_enable": ([I], I),
+        "nc_profile_summary": ([C.c_char_p, S, C.POINTER(S)], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -234,3 +236,20 @@ def model_loss_and_grad(cfg, params, idx, targets, loss, grads, workspace, dloss
                                          float(dloss), int(accumulate), _p(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream)),
            "nc_model_loss_and_grad")
+
+
+# ------------------------------------------------------------------ tracing
+
+def profile_enable(on=True):
+    _check(load().nc_profile_enable(int(on)), "nc_profile_enable")
+
+
+def profile_summary():
+    """Per-kernel {launches, ms, flops, bytes} of the launches recorded while
+    profiling was on (waits for them)."""
+    import json
+    need = C.c_size_t()
+    load().nc_profile_summary(None, 0, C.byref(need))
+    buf = C.create_string_buffer(need.value)
+    _check(load().nc_profile_summary(buf, need.value, C.byref(need)), "nc_profile_summary")
+    return json.loads(buf.value.decode())

@@ -21,16 +21,18 @@ import numpy as np
 
 
 def round_bf16(x):
-    """Round to the nearest bfloat16 (ties to even); returns float32 values."""
-    f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    r = ((u + bias) >> 16) << 16
+    """Round to the nearest bfloat16 (ties to even); returns float32 values.
+    (Finite inputs; NaN stays NaN.)"""
+    f = np.array(x, dtype=np.float32, copy=True, order="C")
     nan = np.isnan(f)
-    out = r.astype(np.uint32).view(np.float32)
+    u = f.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
     if nan.any():
-        out = np.where(nan, np.float32(np.nan), out)
-    return out
+        f[nan] = np.nan
+    return f
 
 
 def bf16_bits(x):
@@ -43,12 +45,13 @@ def from_bf16_bits(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def round_to(x, dtype):
-    """Round to the storage type ('bf16' or 'f32'); returns float64 values."""
+def round_to(x, dtype, out=np.float64):
+    """Round to the storage type ('bf16' or 'f32'); returns `out` values
+    (float64 by default; float32 holds them exactly too)."""
     if dtype == "bf16":
-        return round_bf16(x).astype(np.float64)
+        return round_bf16(x).astype(out, copy=False)
     if dtype == "f32":
-        return np.asarray(x, dtype=np.float32).astype(np.float64)
+        return np.asarray(x, dtype=np.float32).astype(out, copy=False)
     raise ValueError(dtype)
 
 
@@ -65,13 +68,15 @@ def zipf_tokens(vocab, batch, seq_len, s=1.1, seed_rank=1, seed_perm=2):
     return np.ascontiguousarray(ids[:, :seq_len]), np.ascontiguousarray(ids[:, 1:])
 
 
-def normal(shape, std, rng, dtype):
-    """std * N(0,1) of the given shape, rounded to dtype, as float64."""
-    return round_to(rng.standard_normal(shape, dtype=np.float32) * np.float32(std), dtype)
+def normal(shape, std, rng, dtype, out=np.float64):
+    """std * N(0,1) of the given shape, rounded to dtype, as `out` values."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    x *= np.float32(std)
+    return round_to(x, dtype, out)
 
 
 def init_params(depth, d_model, n_head, head_dim, n_kv_head, d_ff, vocab,
-                std=0.02, seed=0, dtype="bf16", fan_in_std=False):
+                std=0.02, seed=0, dtype="bf16", fan_in_std=False, out=np.float64):
     """Model parameters as float64 arrays holding storage-rounded values.
 
     With fan_in_std=True every matrix uses std = 1/sqrt(fan_in) instead of std.
@@ -81,7 +86,7 @@ def init_params(depth, d_model, n_head, head_dim, n_kv_head, d_ff, vocab,
 
     def draw(shape):
         sd = 1.0 / np.sqrt(shape[1]) if fan_in_std else std
-        return normal(shape, sd, rng, dtype)
+        return normal(shape, sd, rng, dtype, out)
 
     wte = draw((V, d))
     layers = []

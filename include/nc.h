@@ -196,6 +196,22 @@ nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const
                                  int accumulate, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* ---------------------------------------------------------------- tracing */
+
+/* Kernel timing. While enabled, every kernel launch of the library is
+ * bracketed by two HIP events on the launch's stream and recorded with its
+ * algorithmic work (model FLOPs, and the bytes the kernel must at least read
+ * and write). on != 0 clears the record and starts recording; on == 0 stops.
+ * Events are created by the HIP runtime when first needed and reused; no
+ * device buffer is allocated. Recording costs two event records per launch. */
+nc_status nc_profile_enable(int on);
+
+/* Waits for the recorded events and writes, into buf (host, buf_len bytes), a
+ * JSON object {"kernel": {"launches": n, "ms": t, "flops": f, "bytes": b}, ...}
+ * summed per kernel. *written (host) receives the bytes needed including the
+ * terminating NUL; NC_ERR_INVALID_ARG if buf is NULL or too small. */
+nc_status nc_profile_summary(char* buf, size_t buf_len, size_t* written);
+
 #ifdef __cplusplus
 }
 #endif
