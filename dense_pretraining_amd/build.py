@@ -34,9 +34,15 @@ FLAGS = [
 ]
 
 
+# Per-file code generation options. The attention kernels keep their MFMA
+# accumulators in VGPRs (the default heuristic moves them through AGPRs every
+# iteration there).
+FILE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, extra):
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name; that warning is harmless
     err = "\n".join(l for l in p.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -88,9 +88,60 @@ template <typename T> __device__ __forceinline__ F8<T> gld8(const T* p, bool ok)
   return pack8<T>(z);
 }
 
+// Operand fragment X[r][k0a..k0a+3 | k0b..k0b+3] for row r = r0 + lane % 16,
+// read from an LDS tile stored k-major (xt[k * LD + r], rows contiguous).
+// bf16 uses the gfx950 transposing LDS read: inside each 16-lane group,
+// source lane j reads 4 consecutive rows at k-row k0 + j/4 and the hardware
+// hands lane i the 4 k values of row r0 + i. Float (check mode) reads the 8
+// values one by one.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <typename T> __device__ __forceinline__ F8<T> ld_tr8(const T* xt, int LD, int k0a, int k0b, int r0, int lane);
+template <> __device__ __forceinline__ F8<bf16> ld_tr8<bf16>(const bf16* xt, int LD, int k0a, int k0b, int r0,
+                                                             int lane) {
+  const int j = lane & 15;
+  const int c = r0 + 4 * (j & 3);
+  v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<bf16*>(xt + (k0a + (j >> 2)) * LD + c));
+  v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<bf16*>(xt + (k0b + (j >> 2)) * LD + c));
+  uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  uint4 u = make_uint4(ua.x, ua.y, ub.x, ub.y);
+  F8<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u);
+  return f;
+}
+template <> __device__ __forceinline__ F8<float> ld_tr8<float>(const float* xt, int LD, int k0a, int k0b, int r0,
+                                                               int lane) {
+  const int r = r0 + (lane & 15);
+  F8<float> f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f.v[s] = xt[(k0a + s) * LD + r];
+    f.v[4 + s] = xt[(k0b + s) * LD + r];
+  }
+  return f;
+}
+
+// 2^x with the bare hardware instruction. Every argument here lies in
+// [-2 sqrt(D) log2(e) - log2(T), 1], far from the range where the library
+// exp2f needs its denormal rescaling.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// r / n for 0 <= r < 2^24 without an integer division.
+struct DivN {
+  int n;
+  float inv;
+  __device__ __forceinline__ int q(int r) const {
+    int x = (int)((float)r * inv);
+    x -= (x * n > r) ? 1 : 0;
+    x += ((x + 1) * n <= r) ? 1 : 0;
+    return x;
+  }
+};
+
 // ------------------------------------------------------------ tile staging
-// Row-major tile [ROWS][D] -> LDS [ROWS][D + PAD]; rows come from a row
-// address function. Transposed tile [D][ROWS + PAD] via groups of 4 rows.
+// Row-major tile [ROWS][D] -> LDS [ROWS][LD]; the row addresses come from a
+// function (nullptr = zero row).
 template <typename T, int ROWS, int D>
 struct RowTile {
   static constexpr int VE = 16 / sizeof(T);
@@ -123,62 +174,6 @@ struct RowTile {
   }
 };
 
-template <typename T, int ROWS, int D>
-struct TransTile {
-  static constexpr int VE = 16 / sizeof(T);
-  static constexpr int LD = ROWS + VE;
-  static constexpr int NQ = ROWS / 4;
-  static constexpr int N = NQ * (D / VE);
-  static constexpr int PER = (N + 255) / 256;
-  uint4 r[PER][4];
-  template <typename AddrF>
-  __device__ __forceinline__ void load(AddrF addr, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int u = tid + 256 * i;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) r[i][k] = make_uint4(0, 0, 0, 0);
-      if (u < N) {
-        int q4 = u % NQ, c = u / NQ;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const T* p = addr(4 * q4 + k);
-          if (p) r[i][k] = *reinterpret_cast<const uint4*>(p + c * VE);
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store(T* s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int u = tid + 256 * i;
-      if (u >= N) continue;
-      int q4 = u % NQ, c = u / NQ;
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[i][3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int sh = (e & 1) * 16;
-          uint32_t e0 = (w0[e >> 1] >> sh) & 0xffffu, e1 = (w1[e >> 1] >> sh) & 0xffffu;
-          uint32_t e2 = (w2[e >> 1] >> sh) & 0xffffu, e3 = (w3[e >> 1] >> sh) & 0xffffu;
-          *reinterpret_cast<uint2*>(s + (c * 8 + e) * LD + 4 * q4) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-        }
-      } else {
-        const float* f0 = reinterpret_cast<const float*>(&r[i][0]);
-        const float* f1 = reinterpret_cast<const float*>(&r[i][1]);
-        const float* f2 = reinterpret_cast<const float*>(&r[i][2]);
-        const float* f3 = reinterpret_cast<const float*>(&r[i][3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<float4*>(s + (c * 4 + e) * LD + 4 * q4) = make_float4(f0[e], f1[e], f2[e], f3[e]);
-      }
-    }
-  }
-};
-
 // Key index held in accumulator slot v by lane half lh (C layout of a 32x32
 // MFMA: rows 8*(v/4) + 4*lh + v%4).
 __device__ __forceinline__ int crow(int v, int lh) { return 8 * (v >> 2) + 4 * lh + (v & 3); }
@@ -186,7 +181,8 @@ __device__ __forceinline__ int crow(int v, int lh) { return 8 * (v >> 2) + 4 * l
 struct AttnGeom {
   int B, T, H, G, D, n_rep;
   long ld_qk, ld_v, ld_o, ld_dq;
-  int q_off_k;  // column of K head 0 inside the qk rows ((H)*D)
+  int q_off_k;  // column of K head 0 inside the qk rows (H*D)
+  float inv_rep;
 };
 
 // ============================================================ forward
@@ -196,27 +192,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
                                                           float* __restrict__ lse) {
   constexpr int BKV = 64;
   using KT = RowTile<T, BKV, D>;
-  using VT = TransTile<T, BKV, D>;
-  __shared__ __align__(16) T ks[2][BKV * KT::LD];
-  __shared__ __align__(16) T vt[2][D * VT::LD];
+  constexpr int LD = KT::LD;
+  __shared__ __align__(16) T ks[2][BKV * LD];
+  __shared__ __align__(16) T vs[2][BKV * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lh = lane >> 5, l32 = lane & 31;
+  const int g16 = (lane >> 4) & 1;
   const int nrows = g.T * g.n_rep;
   const int nqb = (nrows + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;  // longest blocks first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int per = g.G * g.B;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per);  // longest query blocks first
+  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
   const int R0 = qb * 128;
   const long tok0 = (long)b * g.T;
+  const DivN dv{g.n_rep, g.inv_rep};
 
   const int rq = R0 + 32 * wave + l32;
   const bool qok = rq < nrows;
-  const int tq = qok ? rq / g.n_rep : 0;
-  const int hq = kvh * g.n_rep + (qok ? rq % g.n_rep : 0);
-  const int t_wmax = min(g.T - 1, (R0 + 32 * wave + 31) / g.n_rep);
-  const int t_bmax = min(g.T - 1, (R0 + 127) / g.n_rep);
+  const int tq = qok ? dv.q(rq) : 0;
+  const int hq = kvh * g.n_rep + (qok ? rq - tq * g.n_rep : 0);
+  const int w_last = min(nrows - 1, R0 + 32 * wave + 31);
+  const int t_wmax = dv.q(w_last);
+  const int t_wmin = dv.q(min(nrows - 1, R0 + 32 * wave));
+  const bool wfull = R0 + 32 * wave + 31 < nrows;
+  const int t_bmax = dv.q(min(nrows - 1, R0 + 127));
   const int nkt = t_bmax / BKV + 1;
 
-  // Q as the B operand of S^T = K Q^T: lane holds d = 16*ks + 8*lh + (0..7) of its query.
+  // Q as the B operand of S^T = K Q^T: lane holds d = 16*s + 8*lh + (0..7) of its query.
   F8<T> qf[D / 16];
   const T* qrow = qk + (tok0 + tq) * g.ld_qk + (long)hq * D;
 #pragma unroll
@@ -225,8 +227,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
   const T* kbase = qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D;
   const T* vbase = vsrc + tok0 * g.ld_v + (long)kvh * D;
 
-  KT kl;
-  VT vl;
+  KT kl, vl;
   auto kaddr = [&](int kt) {
     return [=](int row) -> const T* {
       int key = kt * BKV + row;
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
   kl.load(kaddr(0), tid);
   vl.load(vaddr(0), tid);
   kl.store(ks[0], tid);
-  vl.store(vt[0], tid);
+  vl.store(vs[0], tid);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -262,7 +263,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
       vl.load(vaddr(kt + 1), tid);
     }
     const T* sk = ks[kt & 1];
-    const T* sv = vt[kt & 1];
+    const T* sv = vs[kt & 1];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int kb = kt * BKV + 32 * sub;
@@ -272,32 +273,39 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
       for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        F8<T> kf = ld_row8<T>(sk + (32 * sub + l32) * KT::LD + 16 * s + 8 * lh);
+        F8<T> kf = ld_row8<T>(sk + (32 * sub + l32) * LD + 16 * s + 8 * lh);
         mma32(sacc, kf, qf[s]);
       }
       float p[16];
+      if (wfull && kb + 31 <= t_wmin) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int key = kb + crow(v, lh);
-        float e = exp2f(sacc[v] * c1 - m0);
-        p[v] = (qok && key <= tq) ? e : 0.f;
-        lsum += p[v];
+        for (int v = 0; v < 16; ++v) {
+          p[v] = fast_exp2(sacc[v] * c1 - m0);
+          lsum += p[v];
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int key = kb + crow(v, lh);
+          float e = fast_exp2(sacc[v] * c1 - m0);
+          p[v] = (qok && key <= tq) ? e : 0.f;
+          lsum += p[v];
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         F8<T> pf = pack8<T>(p + 8 * kk);
-        const int c0 = 32 * sub + 16 * kk + 4 * lh;
+        const int k0 = 32 * sub + 16 * kk + 4 * lh;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const T* row = sv + (32 * dt + l32) * VT::LD;
-          F8<T> vf = ld_split8<T>(row + c0, row + c0 + 8);
+          F8<T> vf = ld_tr8<T>(sv, LD, k0, k0 + 8, 32 * dt + 16 * g16, lane);
           mma32(oacc[dt], vf, pf);
         }
       }
     }
     if (more) {
       kl.store(ks[(kt + 1) & 1], tid);
-      vl.store(vt[(kt + 1) & 1], tid);
+      vl.store(vs[(kt + 1) & 1], tid);
     }
     __syncthreads();
   }
@@ -310,12 +318,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float vals[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vals[i] = oacc[dt][4 * j + i] * inv;
         T* dst = orow + 32 * dt + 8 * j + 4 * lh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(vals[i]);
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(oacc[dt][4 * j + i] * inv);
       }
     if (lh == 0) lse[(tok0 + tq) * g.H + hq] = (m0 + log2f(lsum)) / kLog2e;
   }
@@ -329,25 +334,29 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
                                                              float* __restrict__ delta, T* __restrict__ dq) {
   constexpr int BKV = 64;
   using KT = RowTile<T, BKV, D>;
-  using KTT = TransTile<T, BKV, D>;
-  __shared__ __align__(16) T ks[BKV * KT::LD];
-  __shared__ __align__(16) T vs[BKV * KT::LD];
-  __shared__ __align__(16) T kt_s[D * KTT::LD];
+  constexpr int LD = KT::LD;
+  __shared__ __align__(16) T ks[2][BKV * LD];
+  __shared__ __align__(16) T vs[2][BKV * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lh = lane >> 5, l32 = lane & 31;
+  const int g16 = (lane >> 4) & 1;
   const int nrows = g.T * g.n_rep;
   const int nqb = (nrows + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int per = g.G * g.B;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per);
+  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
   const int R0 = qb * 128;
   const long tok0 = (long)b * g.T;
+  const DivN dv{g.n_rep, g.inv_rep};
 
   const int rq = R0 + 32 * wave + l32;
   const bool qok = rq < nrows;
-  const int tq = qok ? rq / g.n_rep : 0;
-  const int hq = kvh * g.n_rep + (qok ? rq % g.n_rep : 0);
-  const int t_wmax = min(g.T - 1, (R0 + 32 * wave + 31) / g.n_rep);
-  const int t_bmax = min(g.T - 1, (R0 + 127) / g.n_rep);
+  const int tq = qok ? dv.q(rq) : 0;
+  const int hq = kvh * g.n_rep + (qok ? rq - tq * g.n_rep : 0);
+  const int t_wmax = dv.q(min(nrows - 1, R0 + 32 * wave + 31));
+  const int t_wmin = dv.q(min(nrows - 1, R0 + 32 * wave));
+  const bool wfull = R0 + 32 * wave + 31 < nrows;
+  const int t_bmax = dv.q(min(nrows - 1, R0 + 127));
   const int nkt = t_bmax / BKV + 1;
 
   const long qi = (tok0 + tq) * g.H + hq;
@@ -373,7 +382,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
   const T* kbase = qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D;
   const T* vbase = vsrc + tok0 * g.ld_v + (long)kvh * D;
   KT kl, vl;
-  KTT ktl;
   auto kaddr = [&](int kt) {
     return [=](int row) -> const T* {
       int key = kt * BKV + row;
@@ -395,10 +403,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
 
   kl.load(kaddr(0), tid);
   vl.load(vaddr(0), tid);
-  ktl.load(kaddr(0), tid);
-  kl.store(ks, tid);
-  vl.store(vs, tid);
-  ktl.store(kt_s, tid);
+  kl.store(ks[0], tid);
+  vl.store(vs[0], tid);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -406,8 +412,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
     if (more) {
       kl.load(kaddr(kt + 1), tid);
       vl.load(vaddr(kt + 1), tid);
-      ktl.load(kaddr(kt + 1), tid);
     }
+    const T* sk = ks[kt & 1];
+    const T* sv = vs[kt & 1];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int kb = kt * BKV + 32 * sub;
@@ -417,35 +424,37 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
       for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        F8<T> kf = ld_row8<T>(ks + (32 * sub + l32) * KT::LD + 16 * s + 8 * lh);
+        F8<T> kf = ld_row8<T>(sk + (32 * sub + l32) * LD + 16 * s + 8 * lh);
         mma32(sacc, kf, qf[s]);
-        F8<T> vf = ld_row8<T>(vs + (32 * sub + l32) * KT::LD + 16 * s + 8 * lh);
+        F8<T> vf = ld_row8<T>(sv + (32 * sub + l32) * LD + 16 * s + 8 * lh);
         mma32(pacc, vf, df[s]);
       }
       float ds[16];
+      if (wfull && kb + 31 <= t_wmin) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int key = kb + crow(v, lh);
-        float p = exp2f(sacc[v] * c1 - lse2);
-        ds[v] = (qok && key <= tq) ? p * (pacc[v] - dlt) : 0.f;
+        for (int v = 0; v < 16; ++v) ds[v] = fast_exp2(sacc[v] * c1 - lse2) * (pacc[v] - dlt);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int key = kb + crow(v, lh);
+          float p = fast_exp2(sacc[v] * c1 - lse2);
+          ds[v] = (qok && key <= tq) ? p * (pacc[v] - dlt) : 0.f;
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         F8<T> sf = pack8<T>(ds + 8 * kk);
-        const int c0 = 32 * sub + 16 * kk + 4 * lh;
+        const int k0 = 32 * sub + 16 * kk + 4 * lh;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const T* row = kt_s + (32 * dt + l32) * KTT::LD;
-          F8<T> kf = ld_split8<T>(row + c0, row + c0 + 8);
+          F8<T> kf = ld_tr8<T>(sk, LD, k0, k0 + 8, 32 * dt + 16 * g16, lane);
           mma32(dqacc[dt], kf, sf);
         }
       }
     }
-    __syncthreads();
     if (more) {
-      kl.store(ks, tid);
-      vl.store(vs, tid);
-      ktl.store(kt_s, tid);
+      kl.store(ks[(kt + 1) & 1], tid);
+      vl.store(vs[(kt + 1) & 1], tid);
     }
     __syncthreads();
   }
@@ -463,6 +472,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
 }
 
 // ============================================================ backward: dK/dV pass
+// Block: 128 keys (4 waves x 32). Query rows of all heads sharing the KV head
+// stream through LDS in tiles of 32 flattened rows, with each row's position,
+// LSE and Delta staged beside them.
 template <typename T, int D>
 __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const T* __restrict__ qk,
                                                                const T* __restrict__ vsrc, const T* __restrict__ dO,
@@ -471,22 +483,23 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
                                                                T* __restrict__ dv, long ld_dkv) {
   constexpr int BQ = 32;
   using QT = RowTile<T, BQ, D>;
-  using QTT = TransTile<T, BQ, D>;
-  __shared__ __align__(16) T qs[2][BQ * QT::LD];
-  __shared__ __align__(16) T qt[2][D * QTT::LD];
-  __shared__ __align__(16) T ds_[2][BQ * QT::LD];
-  __shared__ __align__(16) T dt_[2][D * QTT::LD];
+  constexpr int LD = QT::LD;
+  __shared__ __align__(16) T qs[2][BQ * LD];
+  __shared__ __align__(16) T ds_[2][BQ * LD];
   __shared__ float sl[2][BQ], sd[2][BQ];
+  __shared__ int st[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lh = lane >> 5, l32 = lane & 31;
-  const int nkb = (g.T + 127) / 128;
-  const int kblk = nkb - 1 - blockIdx.x;  // most query rows first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int g16 = (lane >> 4) & 1;
+  const int per = g.G * g.B;
+  const int kblk = (int)(blockIdx.x / per);  // key block 0 sees every query row: first
+  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
   const long tok0 = (long)b * g.T;
   const int kb0 = kblk * 128;
   const int key = kb0 + 32 * wave + l32;  // this lane's key
   const bool kok = key < g.T;
   const int kw0 = kb0 + 32 * wave;
+  const DivN dvn{g.n_rep, g.inv_rep};
 
   // own K and V rows as B operands (lane: key, 8 consecutive d)
   F8<T> kf[D / 16], vf[D / 16];
@@ -505,7 +518,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
     return [=](int row) -> const T* {
       int r = r_start + tile * BQ + row;
       if (r >= nrows) return nullptr;
-      int t = r / g.n_rep, h = kvh * g.n_rep + r % g.n_rep;
+      int t = dvn.q(r), h = kvh * g.n_rep + (r - t * g.n_rep);
       return qk + (tok0 + t) * g.ld_qk + (long)h * D;
     };
   };
@@ -513,27 +526,37 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
     return [=](int row) -> const T* {
       int r = r_start + tile * BQ + row;
       if (r >= nrows) return nullptr;
-      int t = r / g.n_rep, h = kvh * g.n_rep + r % g.n_rep;
+      int t = dvn.q(r), h = kvh * g.n_rep + (r - t * g.n_rep);
       return dO + (tok0 + t) * g.ld_o + (long)h * D;
     };
   };
-  auto stats = [&](int tile, int buf) {
+  // per-row staging of (lse * log2 e, Delta, position) by threads < BQ
+  float pl = 0.f, pd = 0.f;
+  int pt = -1;
+  auto stats_load = [&](int tile) {
     if (tid < BQ) {
       int r = r_start + tile * BQ + tid;
-      float l = 0.f, d = 0.f;
+      pl = 0.f;
+      pd = 0.f;
+      pt = -1;
       if (r < nrows) {
-        int t = r / g.n_rep, h = kvh * g.n_rep + r % g.n_rep;
+        int t = dvn.q(r), h = kvh * g.n_rep + (r - t * g.n_rep);
         long i = (tok0 + t) * g.H + h;
-        l = lse[i] * kLog2e;
-        d = delta[i];
+        pl = lse[i] * kLog2e;
+        pd = delta[i];
+        pt = t;
       }
-      sl[buf][tid] = l;
-      sd[buf][tid] = d;
+    }
+  };
+  auto stats_store = [&](int buf) {
+    if (tid < BQ) {
+      sl[buf][tid] = pl;
+      sd[buf][tid] = pd;
+      st[buf][tid] = pt;
     }
   };
 
   QT ql, dl;
-  QTT qtl, dtl;
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
@@ -544,13 +567,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
   if (ntiles > 0) {
     ql.load(qaddr(0), tid);
     dl.load(daddr(0), tid);
-    qtl.load(qaddr(0), tid);
-    dtl.load(daddr(0), tid);
+    stats_load(0);
     ql.store(qs[0], tid);
     dl.store(ds_[0], tid);
-    qtl.store(qt[0], tid);
-    dtl.store(dt_[0], tid);
-    stats(0, 0);
+    stats_store(0);
   }
   __syncthreads();
 
@@ -560,11 +580,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
     if (more) {
       ql.load(qaddr(it + 1), tid);
       dl.load(daddr(it + 1), tid);
-      qtl.load(qaddr(it + 1), tid);
-      dtl.load(daddr(it + 1), tid);
+      stats_load(it + 1);
     }
     const int rq0 = r_start + it * BQ;
-    const int t_tmax = min(g.T - 1, (rq0 + BQ - 1) / g.n_rep);
+    const int t_tmax = dvn.q(min(nrows - 1, rq0 + BQ - 1));
     if (t_tmax >= kw0) {
       f32x16 sacc, pacc;
 #pragma unroll
@@ -573,37 +592,42 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
       const T* sdo = ds_[buf];
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        F8<T> qa = ld_row8<T>(sq + l32 * QT::LD + 16 * s + 8 * lh);
+        F8<T> qa = ld_row8<T>(sq + l32 * LD + 16 * s + 8 * lh);
         mma32(sacc, qa, kf[s]);
-        F8<T> da = ld_row8<T>(sdo + l32 * QT::LD + 16 * s + 8 * lh);
+        F8<T> da = ld_row8<T>(sdo + l32 * LD + 16 * s + 8 * lh);
         mma32(pacc, da, vf[s]);
       }
       // sacc[v] = S[query crow(v,lh)][key l32]
       float p[16], dsv[16];
+      const bool full = kok && rq0 + BQ <= nrows && dvn.q(rq0) >= kw0 + 31;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int qr = crow(v, lh);
-        int r = rq0 + qr;
-        int t = r / g.n_rep;
-        bool ok = kok && r < nrows && key <= t;
-        float pv = exp2f(sacc[v] * c1 - sl[buf][qr]);
-        p[v] = ok ? pv : 0.f;
-        dsv[v] = ok ? pv * (pacc[v] - sd[buf][qr]) : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int q0 = 8 * j + 4 * lh;
+        const float4 l4 = *reinterpret_cast<const float4*>(&sl[buf][q0]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sd[buf][q0]);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
+        int4 t4 = make_int4(0, 0, 0, 0);
+        if (!full) t4 = *reinterpret_cast<const int4*>(&st[buf][q0]);
+        const int ta[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * j + i;
+          float pv = fast_exp2(sacc[v] * c1 - la[i]);
+          if (!full) pv = (kok && key <= ta[i]) ? pv : 0.f;
+          p[v] = pv;
+          dsv[v] = pv * (pacc[v] - da[i]);
+        }
       }
-      const T* sqt = qt[buf];
-      const T* sdt = dt_[buf];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         F8<T> pf = pack8<T>(p + 8 * kk);
         F8<T> sf = pack8<T>(dsv + 8 * kk);
-        const int c0 = 16 * kk + 4 * lh;
+        const int k0 = 16 * kk + 4 * lh;
 #pragma unroll
         for (int dti = 0; dti < D / 32; ++dti) {
-          const T* drw = sdt + (32 * dti + l32) * QTT::LD;
-          F8<T> da = ld_split8<T>(drw + c0, drw + c0 + 8);
+          F8<T> da = ld_tr8<T>(sdo, LD, k0, k0 + 8, 32 * dti + 16 * g16, lane);
           mma32(dvacc[dti], da, pf);
-          const T* qrw = sqt + (32 * dti + l32) * QTT::LD;
-          F8<T> qa = ld_split8<T>(qrw + c0, qrw + c0 + 8);
+          F8<T> qa = ld_tr8<T>(sq, LD, k0, k0 + 8, 32 * dti + 16 * g16, lane);
           mma32(dkacc[dti], qa, sf);
         }
       }
@@ -611,9 +635,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
     if (more) {
       ql.store(qs[buf ^ 1], tid);
       dl.store(ds_[buf ^ 1], tid);
-      qtl.store(qt[buf ^ 1], tid);
-      dtl.store(dt_[buf ^ 1], tid);
-      stats(it + 1, buf ^ 1);
+      stats_store(buf ^ 1);
     }
     __syncthreads();
   }
@@ -643,7 +665,7 @@ nc_status attn_fwd_impl(const AttnGeom& g, const T* qk, const T* v, T* o, float*
   // S = Q K^T and O = P V: 4 D flops per pair
   ProfScope prof(NC_NAME(T, "attn_fwd"), 4.0 * D * causal_pairs(g),
                  es * tok * D * (2.0 * g.H + 2.0 * g.G) + 4.0 * tok * g.H, st);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(nqb, g.G, g.B), dim3(256), 0, st, g, qk, v, o, lse);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(nqb * g.G * g.B), dim3(256), 0, st, g, qk, v, o, lse);
   NC_LAUNCH_CHECK("attn_fwd");
   return NC_OK;
 }
@@ -657,7 +679,7 @@ nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, 
     // recompute S, then dP = dO V^T and dQ = dS K: 6 D flops per pair
     ProfScope prof(NC_NAME(T, "attn_bwd_dq"), 6.0 * D * causal_pairs(g),
                    es * tok * D * (4.0 * g.H + 2.0 * g.G) + 8.0 * tok * g.H, st);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(nqb, g.G, g.B), dim3(256), 0, st, g, qk, v, o, dO, lse,
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(nqb * g.G * g.B), dim3(256), 0, st, g, qk, v, o, dO, lse,
                        delta, dq);
     NC_LAUNCH_CHECK("attn_bwd_dq");
   }
@@ -665,8 +687,8 @@ nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, 
   // recompute S and dP, then dV = P^T dO and dK = dS^T Q: 8 D flops per pair
   ProfScope prof(NC_NAME(T, "attn_bwd_dkdv"), 8.0 * D * causal_pairs(g),
                  es * tok * D * (2.0 * g.H + 4.0 * g.G) + 8.0 * tok * g.H, st);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(nkb, g.G, g.B), dim3(256), 0, st, g, qk, v, dO, lse, delta,
-                     dk, dv, ld_dkv);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(nkb * g.G * g.B), dim3(256), 0, st, g, qk, v, dO, lse,
+                     delta, dk, dv, ld_dkv);
   NC_LAUNCH_CHECK("attn_bwd_dkdv");
   return NC_OK;
 }
@@ -676,6 +698,7 @@ AttnGeom make_geom(const AttnArgs& a) {
   g.B = a.B; g.T = a.T; g.H = a.H; g.G = a.G; g.D = a.D; g.n_rep = a.H / a.G;
   g.ld_qk = a.ld_qk; g.ld_v = a.ld_v; g.ld_o = a.ld_o; g.ld_dq = a.ld_dq;
   g.q_off_k = a.H * a.D;
+  g.inv_rep = 1.0f / (float)g.n_rep;
   return g;
 }
 
