@@ -163,7 +163,7 @@ struct HeadScratch {
 template <typename T>
 HeadScratch<T> carve_head_scratch(Carver& c, const Dims& m) {
   HeadScratch<T> s;
-  s.part = c.take<float>(m.M * lmhead_tiles(m.V));
+  s.part = c.take<float>(m.M * lmhead_tiles(m.V, m.es == 2));
   s.block_sums = c.take<float>(xent_loss_blocks((int)m.M));
   s.block_counts = c.take<int>(xent_loss_blocks((int)m.M));
   s.dxf = c.take<T>(m.M * m.d);
@@ -299,7 +299,7 @@ nc_status head_fwd_t(const Dims& m, const T* x, const T* wlm, const int32_t* tg,
   const int M = (int)m.M;
   NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.xf, s.rf, M, m.d, m.eps, nullptr, st));
   NC_TRY(gemm_lmhead<T>(s.xf, wlm, s.z, M, m.V, m.d, m.cap, tg, c.part, s.zt, st));
-  NC_TRY(xent_loss(c.part, lmhead_tiles(m.V), s.zt, tg, M, m.V, s.lse, nullptr, c.block_sums, c.block_counts, loss,
+  NC_TRY(xent_loss(c.part, lmhead_tiles(m.V, m.es == 2), s.zt, tg, M, m.V, s.lse, nullptr, c.block_sums, c.block_counts, loss,
                    s.nv, status, st));
   return NC_OK;
 }

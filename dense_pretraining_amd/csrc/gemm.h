@@ -6,16 +6,20 @@
 //   forward     y  = x W^T   A = x  [M,K] (K contiguous), B = W  [N,K] (K contiguous)
 //   input grad  dx = dy W    A = dy [M,K] (K contiguous), B = W  [K,N] (K outer)
 //   weight grad dW = dy^T x  A = dy [K,M] (K outer),      B = x  [K,N] (K outer)
-// Both operands are staged in LDS as [row][k] so that each lane's MFMA
-// fragment (8 consecutive k of one row) is one 16-byte LDS read; a K-outer
-// operand is transposed while it is written to LDS.
+// A K-contiguous operand is staged in LDS as [row][k] and each lane's MFMA
+// fragment (8 consecutive k of one row) is one 16-byte LDS read. A K-outer
+// operand is copied to LDS as it lies in memory, [k][row], and the fragment
+// is gathered with two gfx950 transposing LDS reads (ds_read_b64_tr_b16), so
+// neither layout costs a register transpose.
 //
-// Block tile 128 x 128 (x BK), 256 threads = 4 wavefronts in a 2 x 2 grid,
-// each owning 64 x 64 of C as 4 x 4 MFMA tiles of 16 x 16. bf16 storage uses
-// v_mfma_f32_16x16x32_bf16 (BK = 64); float storage (check mode) uses eight
-// v_mfma_f32_16x16x4_f32 per 32-wide k chunk (BK = 32). The MFMA's first
-// source is the B fragment so that each lane ends up holding 4 consecutive
-// columns of one row of C (lane l: row l%16, columns 4*(l/16)..+3).
+// bf16: block tile 256 x 256 x 64, 256 threads = 4 wavefronts in a 2 x 2
+// grid, each owning 128 x 128 of C as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16
+// (256 fp32 accumulators per lane, kept in AGPRs). Per 16-deep k step a wave
+// reads 8 fragments (8 KB) for 16 MFMAs, 64 B of LDS per CU clock at full
+// MFMA rate. Float storage (check mode) runs the same code on 128 x 128 x 32
+// tiles with eight 32x32x2 f32 MFMAs per fragment pair.
+// The MFMA's first source is the B fragment, so each lane ends up holding
+// one row of C and runs of 4 consecutive columns.
 // Tiles are walked in groups of 8 M-tiles, and each XCD (workgroups are
 // dispatched round-robin over the 8 XCDs) gets a contiguous range of the
 // walk, so that tiles sharing operand rows share an L2.
@@ -42,10 +46,10 @@ struct ReluSq {
 
 template <typename T> struct GemmTile;
 template <> struct GemmTile<bf16> {
-  static constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+  static constexpr int BM = 256, BN = 256, BK = 64, WTM = 4, WTN = 4;
 };
 template <> struct GemmTile<float> {
-  static constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 4;
+  static constexpr int BM = 128, BN = 128, BK = 32, WTM = 2, WTN = 2;
 };
 
 struct GemmShape {
@@ -78,43 +82,94 @@ __device__ __forceinline__ void gemm_tile_coords(int tiles_m, int tiles_n, int& 
   tn = in_group / gm;
 }
 
+// ---------------------------------------------------------------- fragments
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mfma32(f32x16& c, const Frag<bf16>& b, const Frag<bf16>& a) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b.v, a.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma32(f32x16& c, const Frag<float>& b, const Frag<float>& a) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(b.v[s], a.v[s], c, 0, 0, 0);
+}
+
+// 8 consecutive k of one row from a [row][k] tile.
+template <typename T> __device__ __forceinline__ Frag<T> frag_row(const T* p);
+template <> __device__ __forceinline__ Frag<bf16> frag_row<bf16>(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_row<float>(const float* p) {
+  Frag<float> f;
+  float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w; f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  return f;
+}
+
+typedef short gemm_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) gemm_v4i16 gemm_lds_v4i16;
+
+// Row r0 + lane%16, k = k0 .. k0+7, from a [k][row] tile (row stride LD).
+// Transposing read: inside each 16-lane group, source lane j points at k row
+// k0 + j/4, rows r0 + 4*(j%4) .. +3, and lane i receives the 4 k values of
+// row r0 + i (layout measured on the device).
+template <typename T> __device__ __forceinline__ Frag<T> frag_col(const T* xt, int LD, int k0, int r0, int lane);
+template <> __device__ __forceinline__ Frag<bf16> frag_col<bf16>(const bf16* xt, int LD, int k0, int r0, int lane) {
+  const int j = lane & 15;
+  const bf16* p = xt + (k0 + (j >> 2)) * LD + r0 + 4 * (j & 3);
+  gemm_v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((gemm_lds_v4i16*)const_cast<bf16*>(p));
+  gemm_v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((gemm_lds_v4i16*)const_cast<bf16*>(p + 4 * LD));
+  uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  uint4 u = make_uint4(ua.x, ua.y, ub.x, ub.y);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u);
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> frag_col<float>(const float* xt, int LD, int k0, int r0,
+                                                                    int lane) {
+  const int r = r0 + (lane & 15);
+  Frag<float> f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f.v[s] = xt[(k0 + s) * LD + r];
+  return f;
+}
+
 // ---------------------------------------------------------------- loaders
 
-// Global -> register stage of one operand tile (ROWS x BK), then -> LDS.
+// One operand tile (ROWS x BK) : global -> registers -> LDS.
 template <typename T, int Layout, int ROWS, typename Tr>
 struct OperandLoader {
   static constexpr int BK = GemmTile<T>::BK;
-  static constexpr int LDK = GemmTile<T>::LDK;
   static constexpr int VE = Vec<T>::n;  // elements per 16 B
-  // Kc: ROWS * (BK / VE) vectors; Ko: (BK / 4) k-groups x (ROWS / VE) row vectors, 4 loads each
-  static constexpr int NLOAD = 4;
+  // LDS row stride: [row][k] rows of BK + 16 B; [k][row] rows of ROWS + 32 B
+  static constexpr int LD = Layout == kKc ? BK + VE : ROWS + 2 * VE;
+  static constexpr int SIZE = Layout == kKc ? ROWS * LD : BK * LD;
+  static constexpr int NV = ROWS * BK / VE;
+  static constexpr int NLOAD = NV / 256;
+  static_assert(NV % 256 == 0, "tile must split evenly over 256 threads");
   uint4 r[NLOAD];
 
   __device__ __forceinline__ void load(const T* __restrict__ g, long ld, int row0, int nrows, int k0, int kend,
                                        int tid) {
-    if constexpr (Layout == kKc) {
-      constexpr int VPR = BK / VE;  // vectors per row (8)
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        int v = tid + 256 * i;
-        int row = v / VPR, kv = v % VPR;
-        int gr = row0 + row, gk = k0 + kv * VE;
-        if (gr < nrows && gk < kend)
-          r[i] = *reinterpret_cast<const uint4*>(g + (long)gr * ld + gk);
-        else
-          r[i] = make_uint4(0, 0, 0, 0);
-      }
-    } else {
-      constexpr int NKG = BK / 4;  // k groups of 4 lines
-      int kg = tid % NKG, rv = tid / NKG;
-      int gr = row0 + rv * VE;
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        int gk = k0 + kg * 4 + i;
-        if (gk < kend && gr < nrows)
-          r[i] = *reinterpret_cast<const uint4*>(g + (long)gk * ld + gr);
-        else
-          r[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < NLOAD; ++i) {
+      const int v = tid + 256 * i;
+      if constexpr (Layout == kKc) {
+        constexpr int VPR = BK / VE;
+        const int row = v / VPR, kv = v % VPR;
+        const int gr = row0 + row, gk = k0 + kv * VE;
+        r[i] = (gr < nrows && gk < kend) ? *reinterpret_cast<const uint4*>(g + (long)gr * ld + gk)
+                                         : make_uint4(0, 0, 0, 0);
+      } else {
+        constexpr int VPL = ROWS / VE;
+        const int kl = v / VPL, rv = v % VPL;
+        const int gk = k0 + kl, gr = row0 + rv * VE;
+        r[i] = (gk < kend && gr < nrows) ? *reinterpret_cast<const uint4*>(g + (long)gk * ld + gr)
+                                         : make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -133,80 +188,47 @@ struct OperandLoader {
     }
   }
 
-  __device__ __forceinline__ void store(T* __restrict__ s, int tid) {
-    if constexpr (Layout == kKc) {
-      constexpr int VPR = BK / VE;
+  __device__ __forceinline__ void store(T* __restrict__ s, int tid) const {
 #pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        int v = tid + 256 * i;
-        int row = v / VPR, kv = v % VPR;
-        *reinterpret_cast<uint4*>(s + row * LDK + kv * VE) = r[i];
-      }
-    } else {
-      constexpr int NKG = BK / 4;
-      int kg = tid % NKG, rv = tid / NKG;
-      if constexpr (sizeof(T) == 2) {
-        // r[kk] holds rows rv*8 + 0..7 of k-line kk; write 4 k values per row.
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          int sh = (i & 1) * 16;
-          uint32_t e0 = (w0[i >> 1] >> sh) & 0xffffu, e1 = (w1[i >> 1] >> sh) & 0xffffu;
-          uint32_t e2 = (w2[i >> 1] >> sh) & 0xffffu, e3 = (w3[i >> 1] >> sh) & 0xffffu;
-          uint2 o = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-          *reinterpret_cast<uint2*>(s + (rv * 8 + i) * LDK + kg * 4) = o;
-        }
+    for (int i = 0; i < NLOAD; ++i) {
+      const int v = tid + 256 * i;
+      if constexpr (Layout == kKc) {
+        constexpr int VPR = BK / VE;
+        *reinterpret_cast<uint4*>(s + (v / VPR) * LD + (v % VPR) * VE) = r[i];
       } else {
-        const float* f0 = reinterpret_cast<const float*>(&r[0]);
-        const float* f1 = reinterpret_cast<const float*>(&r[1]);
-        const float* f2 = reinterpret_cast<const float*>(&r[2]);
-        const float* f3 = reinterpret_cast<const float*>(&r[3]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<float4*>(s + (rv * 4 + i) * LDK + kg * 4) = make_float4(f0[i], f1[i], f2[i], f3[i]);
-        }
+        constexpr int VPL = ROWS / VE;
+        *reinterpret_cast<uint4*>(s + (v / VPL) * LD + (v % VPL) * VE) = r[i];
       }
+    }
+  }
+
+  // Fragment of tile row `row` (0..ROWS), k = k0..k0+7, for this lane
+  // (row = base + lane % 32 in the caller).
+  __device__ __forceinline__ static Frag<T> frag(const T* s, int row_base, int k0, int lane) {
+    if constexpr (Layout == kKc) {
+      return frag_row<T>(s + (row_base + (lane & 31)) * LD + k0);
+    } else {
+      return frag_col<T>(s, LD, k0, row_base + 16 * ((lane >> 4) & 1), lane);
     }
   }
 };
 
-// ---------------------------------------------------------------- MFMA core
+// ---------------------------------------------------------------- kernel
 
-template <typename T> struct Frag;
-template <> struct Frag<bf16> {
-  bf16x8 v;
-  __device__ __forceinline__ void read(const bf16* s) { v = *reinterpret_cast<const bf16x8*>(s); }
-};
-template <> struct Frag<float> {
-  float v[8];
-  __device__ __forceinline__ void read(const float* s) {
-    float4 a = *reinterpret_cast<const float4*>(s);
-    float4 b = *reinterpret_cast<const float4*>(s + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-
-__device__ __forceinline__ void mfma_acc(f32x4& c, const Frag<bf16>& b, const Frag<bf16>& a) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.v, a.v, c, 0, 0, 0);
-}
-__device__ __forceinline__ void mfma_acc(f32x4& c, const Frag<float>& b, const Frag<float>& a) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(b.v[s], a.v[s], c, 0, 0, 0);
-}
-
-// Per-lane view of the finished tile handed to an epilogue.
+template <typename T>
 struct TileAcc {
-  f32x4 c[4][4];  // c[i][j][v] = C[row(i)][col(j) + v]
+  static constexpr int WTM = GemmTile<T>::WTM, WTN = GemmTile<T>::WTN;
+  // c[i][j][4*g + e] = C[m_base + 32 i][n_base + 32 j + 8 g + e]
+  f32x16 c[WTM][WTN];
 };
 
 template <typename T, int LA, int LB, typename TrA, typename TrB, typename Epi>
-__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmShape s, Epi epi) {
+__global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   using Cfg = GemmTile<T>;
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, LDK = Cfg::LDK;
-  __shared__ __align__(16) T smem[2][(BM + BN) * LDK];
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WTM = Cfg::WTM, WTN = Cfg::WTN;
+  using LoadA = OperandLoader<T, LA, BM, TrA>;
+  using LoadB = OperandLoader<T, LB, BN, TrB>;
+  __shared__ __align__(16) T smem[2][LoadA::SIZE + LoadB::SIZE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -220,17 +242,19 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmShape s, Epi epi) {
 
   const T* __restrict__ A = static_cast<const T*>(s.A);
   const T* __restrict__ B = static_cast<const T*>(s.B);
-  OperandLoader<T, LA, BM, TrA> la;
-  OperandLoader<T, LB, BN, TrB> lb;
+  LoadA la;
+  LoadB lb;
 
-  TileAcc acc;
+  TileAcc<T> acc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc.c[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WTN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
 
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const int frow = lane & 15, fk = (lane >> 4) * 8;
+  const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
+  const int kl = 8 * (lane >> 5);  // this lane's k offset inside a 16-deep step
 
   if (nk > 0) {
     la.load(A, s.lda, m0, s.M, kbeg, kend, tid);
@@ -238,7 +262,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmShape s, Epi epi) {
     la.transform();
     lb.transform();
     la.store(smem[0], tid);
-    lb.store(smem[0] + BM * LDK, tid);
+    lb.store(smem[0] + LoadA::SIZE, tid);
   }
   __syncthreads();
 
@@ -249,34 +273,37 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmShape s, Epi epi) {
       lb.load(B, s.ldb, n0, s.N, kbeg + (kt + 1) * BK, kend, tid);
     }
     const T* sa = smem[kt & 1];
-    const T* sb = sa + BM * LDK;
+    const T* sb = sa + LoadA::SIZE;
 #pragma unroll
-    for (int kc = 0; kc < BK; kc += 32) {
-      Frag<T> fa[4], fb[4];
+    for (int kk = 0; kk < BK; kk += 16) {
+      Frag<T> fa[WTM], fb[WTN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i].read(sa + (wm + 16 * i + frow) * LDK + kc + fk);
+      for (int i = 0; i < WTM; ++i) fa[i] = LoadA::frag(sa, wm + 32 * i, kk + kl, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j].read(sb + (wn + 16 * j + frow) * LDK + kc + fk);
+      for (int j = 0; j < WTN; ++j) fb[j] = LoadB::frag(sb, wn + 32 * j, kk + kl, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WTM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_acc(acc.c[i][j], fb[j], fa[i]);
+        for (int j = 0; j < WTN; ++j) mfma32(acc.c[i][j], fb[j], fa[i]);
     }
     if (more) {
       la.transform();
       lb.transform();
       la.store(smem[(kt + 1) & 1], tid);
-      lb.store(smem[(kt + 1) & 1] + BM * LDK, tid);
+      lb.store(smem[(kt + 1) & 1] + LoadA::SIZE, tid);
     }
     __syncthreads();
   }
 
-  epi(acc, m0 + wm + frow, n0 + wn + (lane >> 4) * 4, z, lane, wave, reinterpret_cast<float*>(&smem[0][0]));
+  epi(acc, m0 + wm + (lane & 31), n0 + wn + 4 * (lane >> 5), m0, n0, z, lane, wave,
+      reinterpret_cast<float*>(&smem[0][0]));
 }
 
 // ---------------------------------------------------------------- epilogues
-// Called with row_base = first row of this lane (add 16*i), col_base = first
-// of its 4 columns (add 16*j). `red` is LDS scratch usable after a barrier.
+// Called by every thread with m_base = this lane's row (add 32*i) and
+// n_base = its first column (add 32*j + 8*g for the run of 4 columns held
+// in c[i][j][4g..4g+3]); m0/n0 = the block tile's origin. `red` is LDS
+// scratch usable after a barrier.
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v);
@@ -300,6 +327,20 @@ template <> __device__ __forceinline__ void load4<float>(const float* p, float* 
   v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
 }
 
+// Visit every run of 4 columns this lane holds: f(row, col, float v[4]).
+template <typename T, typename F>
+__device__ __forceinline__ void for_each_run(TileAcc<T>& a, int m_base, int n_base, F f) {
+#pragma unroll
+  for (int i = 0; i < TileAcc<T>::WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < TileAcc<T>::WTN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4] = {a.c[i][j][4 * g], a.c[i][j][4 * g + 1], a.c[i][j][4 * g + 2], a.c[i][j][4 * g + 3]};
+        f(m_base + 32 * i, n_base + 32 * j + 8 * g, v);
+      }
+}
+
 // C = acc (+ residual). Output in the storage type.
 template <typename T>
 struct EpiStore {
@@ -308,25 +349,18 @@ struct EpiStore {
   const T* res;  // optional residual, same layout as C
   long ldr;
   int M, N;
-  __device__ __forceinline__ void operator()(TileAcc& a, int row_base, int col_base, int, int, int, float*) const {
+  template <typename TT>
+  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int, int, int, int, int, float*) const {
+    for_each_run<TT>(a, mb, nb, [&](int row, int col, float* v) {
+      if (row >= M || col >= N) return;
+      if (res) {
+        float r[4];
+        load4<T>(res + (long)row * ldr + col, r);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = row_base + 16 * i;
-      if (row >= M) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int col = col_base + 16 * j;
-        if (col >= N) continue;
-        float v[4] = {a.c[i][j][0], a.c[i][j][1], a.c[i][j][2], a.c[i][j][3]};
-        if (res) {
-          float r[4];
-          load4<T>(res + (long)row * ldr + col, r);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += r[e];
-        }
-        store4<T>(C + (long)row * ldc + col, v);
+        for (int e = 0; e < 4; ++e) v[e] += r[e];
       }
-    }
+      store4<T>(C + (long)row * ldc + col, v);
+    });
   }
 };
 
@@ -338,22 +372,16 @@ struct EpiDReluSq {
   const T* u;
   long ldu;
   int M, N;
-  __device__ __forceinline__ void operator()(TileAcc& a, int row_base, int col_base, int, int, int, float*) const {
+  template <typename TT>
+  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int, int, int, int, int, float*) const {
+    for_each_run<TT>(a, mb, nb, [&](int row, int col, float* v) {
+      if (row >= M || col >= N) return;
+      float uu[4];
+      load4<T>(u + (long)row * ldu + col, uu);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = row_base + 16 * i;
-      if (row >= M) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int col = col_base + 16 * j;
-        if (col >= N) continue;
-        float uu[4], v[4];
-        load4<T>(u + (long)row * ldu + col, uu);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = a.c[i][j][e] * 2.f * fmaxf(uu[e], 0.f);
-        store4<T>(C + (long)row * ldc + col, v);
-      }
-    }
+      for (int e = 0; e < 4; ++e) v[e] *= 2.f * fmaxf(uu[e], 0.f);
+      store4<T>(C + (long)row * ldc + col, v);
+    });
   }
 };
 
@@ -365,31 +393,26 @@ struct EpiF32 {
   long split_stride;
   int accumulate;
   int M, N;
-  __device__ __forceinline__ void operator()(TileAcc& a, int row_base, int col_base, int z, int, int, float*) const {
+  template <typename TT>
+  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int, int, int z, int, int,
+                                             float*) const {
     float* base = C + (long)z * split_stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = row_base + 16 * i;
-      if (row >= M) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int col = col_base + 16 * j;
-        if (col >= N) continue;
-        float* p = base + (long)row * ldc + col;
-        float4 v = make_float4(a.c[i][j][0], a.c[i][j][1], a.c[i][j][2], a.c[i][j][3]);
-        if (accumulate) {
-          float4 o = *reinterpret_cast<float4*>(p);
-          v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-        }
-        *reinterpret_cast<float4*>(p) = v;
+    for_each_run<TT>(a, mb, nb, [&](int row, int col, float* v) {
+      if (row >= M || col >= N) return;
+      float* p = base + (long)row * ldc + col;
+      float4 o = make_float4(v[0], v[1], v[2], v[3]);
+      if (accumulate) {
+        float4 q = *reinterpret_cast<float4*>(p);
+        o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
       }
-    }
+      *reinterpret_cast<float4*>(p) = o;
+    });
   }
 };
 
 // Unembedding epilogue: z' = c tanh(z / c) (the logit softcap of the
 // architecture list), stored in the storage type; per row, the sum of
-// exp(z') over this tile's 128 columns goes to part[row * n_tiles + tile]
+// exp(z') over this tile's BN columns goes to part[row * n_tiles + tile]
 // (|z'| <= c, so no running maximum is needed in float32); the float32 z'
 // of the target column goes to zt[row].
 template <typename T>
@@ -402,55 +425,52 @@ struct EpiSoftcap {
   float* zt;
   int n_tiles;
   int M, N;
-  __device__ __forceinline__ void operator()(TileAcc& a, int row_base, int col_base, int, int lane, int wave,
-                                             float* red) const {
+  template <typename TT>
+  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int m0, int n0, int, int lane,
+                                             int wave, float* red) const {
+    constexpr int WTM = TileAcc<TT>::WTM, BM = GemmTile<TT>::BM, BN = GemmTile<TT>::BN;
     const float two_over_c = 2.f / cap;
-    float rowsum[4];
+    float rowsum[WTM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = row_base + 16 * i;
+    for (int i = 0; i < WTM; ++i) {
       rowsum[i] = 0.f;
-      int tgt = (row < M) ? targets[row] : -1;
+      const int row = mb + 32 * i;
+      const int tgt = row < M ? targets[row] : -1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int col = col_base + 16 * j;
-        float v[4];
+      for (int j = 0; j < TileAcc<TT>::WTN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // c tanh(x/c) = c - 2c / (exp(2x/c) + 1)
-          float ex = __expf(a.c[i][j][e] * two_over_c);
-          v[e] = cap - 2.f * cap / (ex + 1.f);
-        }
-        if (row < M && col < N) {
-          store4<T>(Z + (long)row * ldz + col, v);
+        for (int g = 0; g < 4; ++g) {
+          const int col = nb + 32 * j + 8 * g;
+          float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            rowsum[i] += __expf(v[e]);
-            if (col + e == tgt) zt[row] = v[e];
+            // c tanh(x/c) = c - 2c / (exp(2x/c) + 1)
+            float ex = __expf(a.c[i][j][4 * g + e] * two_over_c);
+            v[e] = cap - 2.f * cap / (ex + 1.f);
+          }
+          if (row < M && col < N) {
+            store4<T>(Z + (long)row * ldz + col, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              rowsum[i] += __expf(v[e]);
+              if (col + e == tgt) zt[row] = v[e];
+            }
           }
         }
-      }
-      // sum over the 4 lane groups holding the other columns of this row
-      rowsum[i] += __shfl_xor(rowsum[i], 16, 64);
+      // the other half of this row's columns sits in lane ^ 32
       rowsum[i] += __shfl_xor(rowsum[i], 32, 64);
     }
     __syncthreads();  // operand LDS is free now
-    const int wn_idx = wave & 1, wm = (wave >> 1) * 64;
-    if (lane < 16) {
+    const int wn_idx = wave & 1, wm = (wave >> 1) * (BM / 2);
+    if (lane < 32) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wn_idx * 128 + wm + 16 * i + lane] = rowsum[i];
+      for (int i = 0; i < WTM; ++i) red[wn_idx * BM + wm + 32 * i + lane] = rowsum[i];
     }
     __syncthreads();
-    int tid = threadIdx.x;
-    if (tid < 128) {
-      int row = (row_base - wm - (lane & 15)) + tid;  // block's first row + tid
-      (void)row;
-    }
-    if (tid < 128) {
-      int block_row0 = row_base - (wave >> 1) * 64 - (lane & 15);
-      int row = block_row0 + tid;
-      int tile = (col_base - (wave & 1) * 64 - (lane >> 4) * 4) / 128;
-      if (row < M) part[(long)row * n_tiles + tile] = red[tid] + red[128 + tid];
+    const int tid = threadIdx.x;
+    for (int r = tid; r < BM; r += 256) {
+      const int row = m0 + r;
+      if (row < M) part[(long)row * n_tiles + n0 / BN] = red[r] + red[BM + r];
     }
   }
 };

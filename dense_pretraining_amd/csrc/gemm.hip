@@ -9,8 +9,8 @@ constexpr int kTargetBlocks = 1024;  // ~4 workgroups per CU for the weight-grad
 
 // Number of splits of the reduction (token) axis for a weight gradient, and
 // the rows each split covers (a multiple of the tile depth).
-void dw_split(int M, int N, int K, int bk, int& nsplit, int& kper) {
-  long tiles = (long)((N + 127) / 128) * ((K + 127) / 128);
+void dw_split(int M, int N, int K, int bk, int bmn, int& nsplit, int& kper) {
+  long tiles = (long)((N + bmn - 1) / bmn) * ((K + bmn - 1) / bmn);
   int s = (int)(kTargetBlocks / (tiles > 0 ? tiles : 1));
   s = s < 1 ? 1 : (s > 16 ? 16 : s);
   int maxs = M / 512;
@@ -22,9 +22,9 @@ void dw_split(int M, int N, int K, int bk, int& nsplit, int& kper) {
 
 size_t gemm_dw_partial_elems(int M, int N, int K) {
   int ns, kp;
-  dw_split(M, N, K, 32, ns, kp);  // the smaller tile depth gives the most splits
+  dw_split(M, N, K, GemmTile<float>::BK, GemmTile<float>::BM, ns, kp);
   int ns2, kp2;
-  dw_split(M, N, K, 64, ns2, kp2);
+  dw_split(M, N, K, GemmTile<bf16>::BK, GemmTile<bf16>::BM, ns2, kp2);
   int s = ns > ns2 ? ns : ns2;
   return s > 1 ? (size_t)s * N * K : 0;
 }
@@ -59,7 +59,7 @@ template <typename T>
 nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool relu_sq_x, int accumulate,
                   float* partial, size_t partial_elems, hipStream_t st) {
   int nsplit, kper;
-  dw_split(M, N, K, GemmTile<T>::BK, nsplit, kper);
+  dw_split(M, N, K, GemmTile<T>::BK, GemmTile<T>::BM, nsplit, kper);
   // C[N,K] = sum_m dy[m][n] x[m][k]: both operands K-outer (token axis is the reduction).
   GemmShape s{dy, x, N, K, N, K, M, kper, nsplit};
   if (nsplit > 1 && (partial == nullptr || partial_elems < (size_t)nsplit * N * K)) return NC_ERR_WORKSPACE;
@@ -88,15 +88,19 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool 
   return splitk_reduce(partial, nsplit, (size_t)N * K, dw, accumulate, st);
 }
 
-int lmhead_tiles(int N) { return (N + 127) / 128; }
+int lmhead_tiles(int N, bool bf16_storage) {
+  const int bn = bf16_storage ? GemmTile<bf16>::BN : GemmTile<float>::BN;
+  return (N + bn - 1) / bn;
+}
 
 template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
                       float* part, float* zt, hipStream_t st) {
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
-                 sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N), st);
-  EpiSoftcap<T> e{z, N, cap, targets, part, zt, lmhead_tiles(N), M, N};
+                 sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
+                 st);
+  EpiSoftcap<T> e{z, N, cap, targets, part, zt, lmhead_tiles(N, is_bf16<T>()), M, N};
   return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
 }
 

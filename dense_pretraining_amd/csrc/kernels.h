@@ -37,11 +37,11 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool 
                   float* partial, size_t partial_elems, hipStream_t st);
 size_t gemm_dw_partial_elems(int M, int N, int K);
 // Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N];
-// part[M, ceil(N/128)] = per-tile sums of exp(z); zt[m] = z[m][targets[m]].
+// part[M, lmhead_tiles(N)] = per-tile sums of exp(z); zt[m] = z[m][targets[m]].
 template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
                       float* part, float* zt, hipStream_t st);
-int lmhead_tiles(int N);
+int lmhead_tiles(int N, bool bf16_storage);
 
 // ------------------------------------------------------------ rows (rows.hip)
 nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
