@@ -46,7 +46,7 @@ struct ReluSq {
 
 template <typename T> struct GemmTile;
 template <> struct GemmTile<bf16> {
-  static constexpr int BM = 256, BN = 256, BK = 64, WTM = 4, WTN = 4;
+  static constexpr int BM = 256, BN = 256, BK = 32, WTM = 4, WTN = 4;
 };
 template <> struct GemmTile<float> {
   static constexpr int BM = 128, BN = 128, BK = 32, WTM = 2, WTN = 2;
@@ -299,6 +299,258 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
       reinterpret_cast<float*>(&smem[0][0]));
 }
 
+// ---------------------------------------------------------------- bf16: direct-to-LDS pipeline
+// The bf16 path streams operand tiles straight from HBM into LDS with
+// buffer_load_dwordx4 ... lds (gfx950): no staging registers, so k-tile t+3
+// is fetched while tile t is multiplied (4-stage LDS ring of 256x32 tiles,
+// 128 KB). Each load instruction of a wavefront fills 1 KB of LDS, lane i at
+// byte 16*i; the 16-byte chunks are XOR-swizzled on the way in so that the
+// fragment reads (b128 for K-contiguous, transposing b64 for K-outer tiles)
+// hit distinct banks. Out-of-range lanes get an offset beyond the buffer
+// record, which the hardware turns into zeros: ragged M/N/K need no branch.
+// The ReLU^2 operand transform is applied to fragments after the LDS read.
+
+constexpr int kDmaBK = 32;
+constexpr int kDmaStages = 4;
+constexpr unsigned kDmaRecords = 0x7ffffff0u;  // buffer record size (bytes)
+constexpr unsigned kDmaOOB = 0x7ffffff0u;      // offset that reads as zero
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int dma_swz_row(int r) { return ((r >> 2) & 3) ^ (r & 2); }  // K-contiguous chunks
+__device__ __forceinline__ int dma_swz_k(int k) { return (5 * (k & 3)) & 31; }          // K-outer chunks
+
+template <int Layout>
+struct DmaOperand {
+  // tile: 256 rows x 32 k of bf16 = 16 KB; per wavefront 4 load instructions.
+  static constexpr int ELEMS = 256 * kDmaBK;
+  // Per-lane byte offsets of the 4 loads inside a tile (rows beyond the matrix
+  // already point out of the record); they do not change from tile to tile:
+  // the k advance goes into soffset (K contiguous) or the record base (K outer).
+  unsigned off[4];
+  int kpos[4];  // k of each load inside the tile (for the ragged last tile)
+  const bf16* g;
+  long ld;
+  int row0;
+
+  __device__ __forceinline__ void init(const bf16* g_, long ld_, int row0_, int nrows, int wave, int lane) {
+    g = g_;
+    ld = ld_;
+    row0 = row0_;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 4 * wave + q;
+      if constexpr (Layout == kKc) {
+        const int row = 16 * c + (lane >> 2);  // 1 KB chunk = 16 rows of 32 k
+        const int kc = (lane & 3) ^ dma_swz_row(row);
+        kpos[q] = 8 * kc;
+        off[q] = row0 + row < nrows ? (unsigned)(((long)row * ld + 8 * kc) * 2) : kDmaOOB;
+      } else {
+        const int kl = 2 * c + (lane >> 5);  // 1 KB chunk = 2 k lines of 256 rows
+        const int rc = (lane & 31) ^ dma_swz_k(kl);
+        kpos[q] = kl;
+        off[q] = row0 + 8 * rc < nrows ? (unsigned)(((long)kl * ld + 8 * rc) * 2) : kDmaOOB;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void issue(bf16* lds, int k0, int kend, int wave) const {
+    const bool full = k0 + kDmaBK <= kend;
+    if constexpr (Layout == kKc) {
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g + (long)row0 * ld),
+                                                                    (short)0, (int)kDmaRecords, 0x00020000);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const unsigned o = (full || k0 + kpos[q] < kend) ? off[q] : kDmaOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * (4 * wave + q)), 16, o,
+                                                 (unsigned)(k0 * 2), 0, 0);
+      }
+    } else {
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g + (long)k0 * ld + row0),
+                                                                    (short)0, (int)kDmaRecords, 0x00020000);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const unsigned o = (full || k0 + kpos[q] < kend) ? off[q] : kDmaOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * (4 * wave + q)), 16, o, 0, 0, 0);
+      }
+    }
+  }
+
+  // Fragment of tile row row_base + lane%32, k = kk + 8*(lane/32) .. +7.
+  __device__ __forceinline__ static Frag<bf16> frag(const bf16* lds, int row_base, int kk, int lane) {
+    if constexpr (Layout == kKc) {
+      const int r = row_base + (lane & 31);
+      const int kc = (kk >> 3) + (lane >> 5);
+      return frag_row<bf16>(lds + r * kDmaBK + 8 * (kc ^ dma_swz_row(r)));
+    } else {
+      const int j = lane & 15;
+      const int r = row_base + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const int rc = r >> 3, half = (r >> 2) & 1;
+      const int ka = kk + 8 * (lane >> 5) + (j >> 2);
+      const int kb = ka + 4;
+      const bf16* pa = lds + ka * 256 + 8 * (rc ^ dma_swz_k(ka)) + 4 * half;
+      const bf16* pb = lds + kb * 256 + 8 * (rc ^ dma_swz_k(kb)) + 4 * half;
+      gemm_v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((gemm_lds_v4i16*)const_cast<bf16*>(pa));
+      gemm_v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((gemm_lds_v4i16*)const_cast<bf16*>(pb));
+      uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+      uint4 u = make_uint4(ua.x, ua.y, ub.x, ub.y);
+      Frag<bf16> f;
+      f.v = __builtin_bit_cast(bf16x8, u);
+      return f;
+    }
+  }
+};
+
+template <typename Tr>
+__device__ __forceinline__ void frag_transform(Frag<bf16>& f) {
+  if constexpr (Tr::active) {
+    Tr tr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = (bf16)tr((float)f.v[e]);
+  }
+}
+
+// Ring barrier: this wave's loads older than the newest N have landed in
+// LDS and its LDS reads are done (s_waitcnt vmcnt(N) lgkmcnt(0)), then all
+// waves meet. A plain s_barrier: __syncthreads() would also drain the loads
+// that are meant to stay in flight.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int LA, int LB, typename TrA, typename TrB>
+struct DmaTile {
+  using OpA = DmaOperand<LA>;
+  using OpB = DmaOperand<LB>;
+  static constexpr int WTM = 4, WTN = 4;
+  __device__ __forceinline__ static void compute(TileAcc<bf16>& acc, const bf16* ta, const bf16* tb, int wm, int wn,
+                                                 int lane) {
+#pragma unroll
+    for (int kk = 0; kk < kDmaBK; kk += 16) {
+      Frag<bf16> fa[WTM], fb[WTN];
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        fa[i] = OpA::frag(ta, wm + 32 * i, kk, lane);
+        frag_transform<TrA>(fa[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        fb[j] = OpB::frag(tb, wn + 32 * j, kk, lane);
+        frag_transform<TrB>(fb[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) mfma32(acc.c[i][j], fb[j], fa[i]);
+    }
+  }
+};
+
+// One step of the ring: wait for tile t (stage S), then refill stage
+// (S+3)%4 with tile t+3 and multiply stage S. Each stage is its own LDS
+// array so that the compiler can tell the DMA writes from the reads. The
+// main loop runs four steps per trip while every load and wait is uniform
+// (no branches, so the accumulators stay in AGPRs); the last tiles go
+// through the same steps with their conditions.
+#define NC_DMA_STEP_FULL(t, SA, SB, NA, NB)                 \
+  {                                                         \
+    ring_barrier<16>();                                     \
+    opa.issue(NA, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
+    opb.issue(NB, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
+    Tile::compute(acc, SA, SB, wm, wn, lane);               \
+  }
+#define NC_DMA_STEP_TAIL(t, SA, SB, NA, NB)                   \
+  if ((t) < nk) {                                             \
+    const int ahead_ = nk - 1 - (t);                          \
+    if (ahead_ >= 2) ring_barrier<16>();                      \
+    else if (ahead_ == 1) ring_barrier<8>();                  \
+    else ring_barrier<0>();                                   \
+    if ((t) + 3 < nk) {                                       \
+      opa.issue(NA, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
+      opb.issue(NB, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
+    }                                                         \
+    Tile::compute(acc, SA, SB, wm, wn, lane);                 \
+  }
+
+// The whole ring in one inlined function whose stage arrays are __restrict__
+// parameters: every LDS access inside then carries alias-scope information,
+// which lets the compiler see that the reads of one stage do not depend on
+// the loads still streaming into the others (it would otherwise drain them).
+template <typename Tile>
+__device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA& opa, typename Tile::OpB& opb,
+                                         bf16* __restrict__ sa0, bf16* __restrict__ sa1, bf16* __restrict__ sa2,
+                                         bf16* __restrict__ sa3, bf16* __restrict__ sb0, bf16* __restrict__ sb1,
+                                         bf16* __restrict__ sb2, bf16* __restrict__ sb3, int nk, int kbeg, int kend,
+                                         int wave, int wm, int wn, int lane) {
+  constexpr int BK = kDmaBK;
+  if (nk > 0) {
+    opa.issue(sa0, kbeg, kend, wave);
+    opb.issue(sb0, kbeg, kend, wave);
+  }
+  if (nk > 1) {
+    opa.issue(sa1, kbeg + BK, kend, wave);
+    opb.issue(sb1, kbeg + BK, kend, wave);
+  }
+  if (nk > 2) {
+    opa.issue(sa2, kbeg + 2 * BK, kend, wave);
+    opb.issue(sb2, kbeg + 2 * BK, kend, wave);
+  }
+  int kt = 0;
+  for (; kt + 7 <= nk; kt += 4) {
+    NC_DMA_STEP_FULL(kt, sa0, sb0, sa3, sb3);
+    NC_DMA_STEP_FULL(kt + 1, sa1, sb1, sa0, sb0);
+    NC_DMA_STEP_FULL(kt + 2, sa2, sb2, sa1, sb1);
+    NC_DMA_STEP_FULL(kt + 3, sa3, sb3, sa2, sb2);
+  }
+  // at most 6 tiles left; kt is a multiple of 4, so tile kt sits in stage 0
+  NC_DMA_STEP_TAIL(kt, sa0, sb0, sa3, sb3);
+  NC_DMA_STEP_TAIL(kt + 1, sa1, sb1, sa0, sb0);
+  NC_DMA_STEP_TAIL(kt + 2, sa2, sb2, sa1, sb1);
+  NC_DMA_STEP_TAIL(kt + 3, sa3, sb3, sa2, sb2);
+  NC_DMA_STEP_TAIL(kt + 4, sa0, sb0, sa3, sb3);
+  NC_DMA_STEP_TAIL(kt + 5, sa1, sb1, sa0, sb0);
+}
+
+template <int LA, int LB, typename TrA, typename TrB, typename Epi>
+__global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) {
+  constexpr int BM = 256, BN = 256, BK = kDmaBK;
+  using Tile = DmaTile<LA, LB, TrA, TrB>;
+  constexpr int E = Tile::OpA::ELEMS;
+  __shared__ __align__(1024) bf16 sa0[E], sa1[E], sa2[E], sa3[E];
+  __shared__ __align__(1024) bf16 sb0[E], sb1[E], sb2[E], sb3[E];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int tiles_m = (s.M + BM - 1) / BM, tiles_n = (s.N + BN - 1) / BN;
+  int tm, tn, z;
+  gemm_tile_coords(tiles_m, tiles_n, tm, tn, z);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = z * s.k_split;
+  const int kend = min(s.K, kbeg + s.k_split);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  TileAcc<bf16> acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.f;
+  const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
+
+  typename Tile::OpA opa;
+  typename Tile::OpB opb;
+  opa.init(static_cast<const bf16*>(s.A), s.lda, m0, s.M, wave, lane);
+  opb.init(static_cast<const bf16*>(s.B), s.ldb, n0, s.N, wave, lane);
+  dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, nk, kbeg, kend, wave, wm, wn, lane);
+  __syncthreads();
+  epi(acc, m0 + wm + (lane & 31), n0 + wn + 4 * (lane >> 5), m0, n0, z, lane, wave, reinterpret_cast<float*>(sa0));
+}
+#undef NC_DMA_STEP_FULL
+#undef NC_DMA_STEP_TAIL
+
+
 // ---------------------------------------------------------------- epilogues
 // Called by every thread with m_base = this lane's row (add 32*i) and
 // n_base = its first column (add 32*j + 8*g for the run of 4 columns held
@@ -483,7 +735,12 @@ nc_status launch_gemm(const GemmShape& s, const Epi& epi, hipStream_t stream) {
   int tiles_m = (s.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (s.N + Cfg::BN - 1) / Cfg::BN;
   long blocks = (long)tiles_m * tiles_n * s.n_split;
   if (blocks <= 0) return NC_OK;
-  hipLaunchKernelGGL((gemm_kernel<T, LA, LB, TrA, TrB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s, epi);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((gemm_dma_kernel<LA, LB, TrA, TrB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
+                       epi);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, LA, LB, TrA, TrB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
+                       epi);
   NC_LAUNCH_CHECK("gemm");
   return NC_OK;
 }
