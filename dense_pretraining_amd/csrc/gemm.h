@@ -484,18 +484,14 @@ __device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA&
                                          bf16* __restrict__ sb2, bf16* __restrict__ sb3, int nk, int kbeg, int kend,
                                          int wave, int wm, int wn, int lane) {
   constexpr int BK = kDmaBK;
-  if (nk > 0) {
-    opa.issue(sa0, kbeg, kend, wave);
-    opb.issue(sb0, kbeg, kend, wave);
-  }
-  if (nk > 1) {
-    opa.issue(sa1, kbeg + BK, kend, wave);
-    opb.issue(sb1, kbeg + BK, kend, wave);
-  }
-  if (nk > 2) {
-    opa.issue(sa2, kbeg + 2 * BK, kend, wave);
-    opb.issue(sb2, kbeg + 2 * BK, kend, wave);
-  }
+  // unconditional: a tile beyond kend just loads zeros (keeps the compiler's
+  // per-stage bookkeeping exact at the loop entry)
+  opa.issue(sa0, kbeg, kend, wave);
+  opb.issue(sb0, kbeg, kend, wave);
+  opa.issue(sa1, kbeg + BK, kend, wave);
+  opb.issue(sb1, kbeg + BK, kend, wave);
+  opa.issue(sa2, kbeg + 2 * BK, kend, wave);
+  opb.issue(sb2, kbeg + 2 * BK, kend, wave);
   int kt = 0;
   for (; kt + 7 <= nk; kt += 4) {
     NC_DMA_STEP_FULL(kt, sa0, sb0, sa3, sb3);
