@@ -107,7 +107,7 @@ BlockSaved<T> carve_block_saved(Carver& c, const Dims& m, bool table) {
 template <typename T>
 struct BlockScratch {
   T *du, *dh, *dx1, *dy, *dqkv;
-  float *delta, *partial;
+  float *rowstat, *partial;
   size_t partial_elems;
 };
 size_t block_partial_elems(const Dims& m) {
@@ -129,7 +129,7 @@ BlockScratch<T> carve_block_scratch(Carver& c, const Dims& m) {
   s.dx1 = c.take<T>(m.M * m.d);
   s.dy = c.take<T>(m.M * m.HD);
   s.dqkv = c.take<T>(m.M * m.QKV);
-  s.delta = c.take<float>(m.M * m.H);
+  s.rowstat = c.take<float>(2 * m.M * m.H);
   s.partial_elems = block_partial_elems(m);
   s.partial = c.take<float>(s.partial_elems ? s.partial_elems : 1);
   return s;
@@ -283,7 +283,7 @@ nc_status block_bwd_t(const Dims& m, const BlockW<T>& w, const T* x, const Block
   NC_TRY(gemm_dyw<T>(c.dx1, w.wo, c.dy, nullptr, M, m.d, m.HD, st));
   // attention, then rotation + QK norm
   AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
-  NC_TRY(attn_bwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, c.dy, s.lse, c.delta, c.dqkv,
+  NC_TRY(attn_bwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, c.dy, s.lse, c.rowstat, c.dqkv,
                      c.dqkv + (size_t)m.H * m.D, c.dqkv + (size_t)(m.H + m.G) * m.D, m.QKV, st));
   NC_TRY(qknorm_rope_bwd<T>(s.qkv, m.QKV, c.dqkv, m.QKV, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
   // QKV projection and the pre-attention norm

@@ -331,7 +331,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T* __restrict__ qk,
                                                              const T* __restrict__ vsrc, const T* __restrict__ o,
                                                              const T* __restrict__ dO, const float* __restrict__ lse,
-                                                             float* __restrict__ delta, T* __restrict__ dq) {
+                                                             float2* __restrict__ rowstat, T* __restrict__ dq) {
   constexpr int BKV = 64;
   using KT = RowTile<T, BKV, D>;
   constexpr int LD = KT::LD;
@@ -375,8 +375,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
   }
   dsum += __shfl_xor(dsum, 32, 64);
   const float dlt = dsum;
-  if (qok && lh == 0) delta[qi] = dlt;
   const float lse2 = qok ? lse[qi] * kLog2e : 0.f;
+  // (lse log2 e, Delta) of each flattened row, in row order, for the dK/dV pass
+  if (qok && lh == 0) rowstat[((long)b * g.G + kvh) * nrows + rq] = make_float2(lse2, dlt);
   const float c1 = kLog2e / sqrtf((float)D);
 
   const T* kbase = qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D;
@@ -472,186 +473,339 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
 }
 
 // ============================================================ backward: dK/dV pass
-// Block: 128 keys (4 waves x 32). Query rows of all heads sharing the KV head
-// stream through LDS in tiles of 32 flattened rows, with each row's position,
-// LSE and Delta staged beside them.
-template <typename T, int D>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(AttnGeom g, const T* __restrict__ qk,
-                                                               const T* __restrict__ vsrc, const T* __restrict__ dO,
-                                                               const float* __restrict__ lse,
-                                                               const float* __restrict__ delta, T* __restrict__ dk,
-                                                               T* __restrict__ dv, long ld_dkv) {
-  constexpr int BQ = 32;
-  using QT = RowTile<T, BQ, D>;
-  constexpr int LD = QT::LD;
-  __shared__ __align__(16) T qs[2][BQ * LD];
-  __shared__ __align__(16) T ds_[2][BQ * LD];
-  __shared__ float sl[2][BQ], sd[2][BQ];
-  __shared__ int st[2][BQ];
+// Block: 128 keys, 8 waves. Waves w and w+4 share the 32 keys 32*(w%4) ..:
+//   wave w   (P side)  holds K, forms S = Q K^T and P = exp(S - lse), passes P
+//                      to its partner through LDS and accumulates dV += P^T dO;
+//   wave w+4 (dS side) holds V, forms dP = dO V^T, takes P one tile later,
+//                      dS = P (dP - Delta) and accumulates dK += dS^T Q.
+// So each wave keeps one 32-key operand and one accumulator set (half of what
+// one wave doing both needs), two waves share a SIMD, and no MFMA is repeated.
+// The flattened query rows of all heads sharing the KV head stream through a
+// 4-stage LDS ring of 32-row Q and dO tiles filled by direct-to-LDS loads
+// (XOR-swizzled 16-byte chunks: conflict-free for the row reads of S and dP
+// and for the transposing reads of dV and dK), each wave also staging its
+// own copy of the tiles' (lse log2 e, Delta) pairs. Tiles run from the last
+// query row down, so that all key blocks of a sequence start on the same rows
+// and share them in L2.
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lh = lane >> 5, l32 = lane & 31;
-  const int g16 = (lane >> 4) & 1;
+// Swizzled [rows][D] tile: 16-byte chunk c of row r sits at chunk c ^ f(r).
+// D = 128 bf16 (16 chunks a row): f(r) = 4 (r % 4) + (r / 4) % 4. Sixteen
+// consecutive rows read at one chunk hit 16 distinct chunk slots, and the
+// transposing read (rows k..k+3 x 4 chunks) covers all 64 banks once.
+// D = 64 bf16 (8 chunks, two rows per 256-byte bank line): f(r) = 4 ((r/2) % 2)
+// + (r / 4) % 4 does the same with the row parity selecting the half line.
+template <typename T, int D>
+struct Swz {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int NC = D / VE;
+  __device__ __forceinline__ static int f(int r) {
+    if constexpr (NC >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  __device__ __forceinline__ static int at(int r, int col) { return (r * NC + ((col / VE) ^ f(r))) * VE + col % VE; }
+};
+
+// Fragment X[row][c0 .. c0+7] (c0 a multiple of 8).
+template <typename T, int D>
+__device__ __forceinline__ F8<T> swz_row8(const T* t, int row, int c0) {
+  if constexpr (sizeof(T) == 2) {
+    return ld_row8<T>(t + Swz<T, D>::at(row, c0));
+  } else {
+    return ld_split8<T>(t + Swz<T, D>::at(row, c0), t + Swz<T, D>::at(row, c0 + 4));
+  }
+}
+// Fragment X[ka .. ka+3 | kb .. kb+3][c0 + lane % 16] (tile rows as k).
+template <typename T, int D>
+__device__ __forceinline__ F8<T> swz_tr8(const T* t, int ka, int kb, int c0, int lane) {
+  F8<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const int j = lane & 15;
+    const int col = c0 + 4 * (j & 3);
+    v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)const_cast<T*>(t + Swz<T, D>::at(ka + (j >> 2), col)));
+    v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)const_cast<T*>(t + Swz<T, D>::at(kb + (j >> 2), col)));
+    uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    f.v = __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
+  } else {
+    const int col = c0 + (lane & 15);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f.v[s] = t[Swz<T, D>::at(ka + s, col)];
+      f.v[4 + s] = t[Swz<T, D>::at(kb + s, col)];
+    }
+  }
+  return f;
+}
+
+template <typename T, int D>
+struct DkdvShape {
+  static constexpr int BQ = 32;                      // query rows per tile
+  static constexpr int WAVES = 8;
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int TILE = BQ * D;                // elements of one Q or dO tile
+  static constexpr int NQI = TILE / VE / 64;         // 16-byte load instructions per tile
+  static constexpr int NPW = 2 * NQI / WAVES;        // per wave, Q and dO together
+  static constexpr int NI = NPW + 1;                 // + the row statistics
+  static constexpr int STAGES = sizeof(T) == 2 ? 4 : 3;
+  static constexpr int AHEAD = STAGES - 2;           // tiles in flight beyond the one waited for
+  static constexpr int WAIT = (AHEAD - 1) * NI;
+  static_assert((2 * NQI) % WAVES == 0, "tile loads split evenly over the waves");
+};
+
+template <typename T, int D>
+struct DkdvCtx {
+  using Sh = DkdvShape<T, D>;
+  int nrows, r_start, ntiles, T_, kw0, lane, wave, kw;
+  bool kok;
+  DivN dvn;
+  int n_rep, hbase;  // first query head of the KV head
+  long ld_qk, ld_o;
+  __amdgpu_buffer_rsrc_t rq, rd, rs;
+  // per load instruction of this wave: tile row, chunk column offset, operand
+  int lrow[Sh::NPW], lcol[Sh::NPW], lblk[Sh::NPW];
+  bool ldo[Sh::NPW];
+
+  __device__ __forceinline__ int row0(int s) const { return r_start + Sh::BQ * (ntiles - 1 - s); }
+
+  // Loads of the tile processed at step s into one ring stage.
+  __device__ __forceinline__ void issue(int s, T* __restrict__ sq, T* __restrict__ sd, float* __restrict__ ss) const {
+    const int rq0 = row0(s);
+    const bool live = s < ntiles;
+#pragma unroll
+    for (int i = 0; i < Sh::NPW; ++i) {
+      const int r = rq0 + lrow[i];
+      unsigned off = kDmaOOB;
+      if (live && r < nrows) {
+        const int t = dvn.q(r), h = hbase + (r - t * n_rep);
+        off = (unsigned)((((long)t * (ldo[i] ? ld_o : ld_qk)) + (long)h * D + lcol[i]) * (long)sizeof(T));
+      }
+      T* dst = (ldo[i] ? sd : sq) + lblk[i] * 64 * Sh::VE;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ldo[i] ? rd : rq, (lds_void*)dst, 16, off, 0, 0, 0);
+    }
+    const int e = 2 * rq0 + lane;  // float index into this tile's (lse2, Delta) pairs
+    const unsigned soff = (live && e < 2 * nrows) ? (unsigned)e * 4u : kDmaOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(ss + 64 * wave), 4, soff, 0, 0, 0);
+  }
+
+  // Tile of step s has no unmasked pair for this wave's keys.
+  __device__ __forceinline__ bool skip(int s) const {
+    if (s < 0 || s >= ntiles) return true;
+    const int rq0 = row0(s);
+    return dvn.q(min(nrows - 1, rq0 + Sh::BQ - 1)) < kw0;
+  }
+  __device__ __forceinline__ bool full(int s) const {
+    const int rq0 = row0(s);
+    return kw0 + 32 <= T_ && rq0 + Sh::BQ <= nrows && dvn.q(rq0) >= kw0 + 31;
+  }
+};
+
+// P side: S = Q K^T, P, hand P over, dV += P^T dO.
+template <typename T, int D>
+__device__ __forceinline__ void dkdv_tile_p(const DkdvCtx<T, D>& c, int s, const T* __restrict__ sq,
+                                            const T* __restrict__ sdo, const float* __restrict__ st, F8<T>* pb,
+                                            f32x16* acc, const F8<T>* kf, float c1) {
+  if (c.skip(s)) return;
+  const int lane = c.lane, lh = lane >> 5, l32 = lane & 31, g16 = (lane >> 4) & 1;
+  f32x16 sacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) mma32(sacc, swz_row8<T, D>(sq, l32, 16 * k + 8 * lh), kf[k]);
+  const float* sw = st + 64 * c.wave;
+  const bool full = c.full(s);
+  const int rq0 = c.row0(s), key = c.kw0 + l32;
+  float p[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q0 = 8 * j + 4 * lh;
+    const float4 a = *reinterpret_cast<const float4*>(sw + 2 * q0);
+    const float4 b = *reinterpret_cast<const float4*>(sw + 2 * q0 + 4);
+    const float la[4] = {a.x, a.z, b.x, b.z};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float pv = fast_exp2(sacc[4 * j + i] * c1 - la[i]);
+      if (!full) {
+        const int r = rq0 + q0 + i;
+        pv = (c.kok & (r < c.nrows) & (key <= c.dvn.q(r))) ? pv : 0.f;
+      }
+      p[4 * j + i] = pv;
+    }
+  }
+  const F8<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
+  pb[(2 * c.kw) * 64 + lane] = pf0;
+  pb[(2 * c.kw + 1) * 64 + lane] = pf1;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int k0 = 16 * kk + 4 * lh;
+#pragma unroll
+    for (int dti = 0; dti < D / 32; ++dti)
+      mma32(acc[dti], swz_tr8<T, D>(sdo, k0, k0 + 8, 32 * dti + 16 * g16, lane), kk ? pf1 : pf0);
+  }
+}
+
+// dS side: dP = dO V^T, dS = P (dP - Delta), dK += dS^T Q.
+template <typename T, int D>
+__device__ __forceinline__ void dkdv_tile_ds(const DkdvCtx<T, D>& c, int s, const T* __restrict__ sq,
+                                             const T* __restrict__ sdo, const float* __restrict__ st,
+                                             const F8<T>* pb, f32x16* acc, const F8<T>* vf) {
+  if (c.skip(s)) return;
+  const int lane = c.lane, lh = lane >> 5, l32 = lane & 31, g16 = (lane >> 4) & 1;
+  f32x16 pacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) pacc[v] = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) mma32(pacc, swz_row8<T, D>(sdo, l32, 16 * k + 8 * lh), vf[k]);
+  const float* sw = st + 64 * c.wave;
+  const F8<T> pf0 = pb[(2 * c.kw) * 64 + lane], pf1 = pb[(2 * c.kw + 1) * 64 + lane];
+  float ds[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q0 = 8 * j + 4 * lh;
+    const float4 a = *reinterpret_cast<const float4*>(sw + 2 * q0);
+    const float4 b = *reinterpret_cast<const float4*>(sw + 2 * q0 + 4);
+    const float da[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = 4 * j + i;
+      const float pv = to_f32((v < 8 ? pf0 : pf1).v[v & 7]);
+      ds[v] = pv * (pacc[v] - da[i]);
+    }
+  }
+  const F8<T> sf0 = pack8<T>(ds), sf1 = pack8<T>(ds + 8);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int k0 = 16 * kk + 4 * lh;
+#pragma unroll
+    for (int dti = 0; dti < D / 32; ++dti)
+      mma32(acc[dti], swz_tr8<T, D>(sq, k0, k0 + 8, 32 * dti + 16 * g16, lane), kk ? sf1 : sf0);
+  }
+}
+
+// One ring step s: wait for the tile of step s, refill the stage two tiles
+// ahead, then the P side works on tile s and the dS side on tile s - 1 (whose
+// P was handed over before this step's barrier).
+#define NC_DKDV_STEP(S_, CUR, PRV, NXT)                                                            \
+  {                                                                                                \
+    const int s_ = (S_);                                                                           \
+    ring_barrier<Sh::WAIT>();                                                                      \
+    c.issue(s_ + Sh::AHEAD, q##NXT, d##NXT, t##NXT);                                              \
+    if constexpr (ROLE == 0) dkdv_tile_p<T, D>(c, s_, q##CUR, d##CUR, t##CUR, pb + (s_ & 1) * 512, \
+                                               acc, kv, c1);                                      \
+    else dkdv_tile_ds<T, D>(c, s_ - 1, q##PRV, d##PRV, t##PRV, pb + ((s_ - 1) & 1) * 512, acc, kv); \
+  }
+
+template <int ROLE, typename T, int D>
+__device__ __forceinline__ void dkdv_ring(const DkdvCtx<T, D>& c, f32x16* acc, const F8<T>* kv, F8<T>* pb,
+                                          float c1, T* __restrict__ q0, T* __restrict__ q1, T* __restrict__ q2,
+                                          T* __restrict__ q3, T* __restrict__ d0, T* __restrict__ d1,
+                                          T* __restrict__ d2, T* __restrict__ d3, float* __restrict__ t0,
+                                          float* __restrict__ t1, float* __restrict__ t2, float* __restrict__ t3) {
+  using Sh = DkdvShape<T, D>;
+  const int nsteps = c.ntiles + 1;  // the dS side trails by one tile
+  c.issue(0, q0, d0, t0);
+  if constexpr (Sh::STAGES == 4) {
+    c.issue(1, q1, d1, t1);
+    int s = 0;
+    for (; s + 4 <= nsteps; s += 4) {
+      NC_DKDV_STEP(s, 0, 3, 2);
+      NC_DKDV_STEP(s + 1, 1, 0, 3);
+      NC_DKDV_STEP(s + 2, 2, 1, 0);
+      NC_DKDV_STEP(s + 3, 3, 2, 1);
+    }
+    if (s < nsteps) NC_DKDV_STEP(s, 0, 3, 2);
+    if (s + 1 < nsteps) NC_DKDV_STEP(s + 1, 1, 0, 3);
+    if (s + 2 < nsteps) NC_DKDV_STEP(s + 2, 2, 1, 0);
+  } else {
+    int s = 0;
+    for (; s + 3 <= nsteps; s += 3) {
+      NC_DKDV_STEP(s, 0, 2, 1);
+      NC_DKDV_STEP(s + 1, 1, 0, 2);
+      NC_DKDV_STEP(s + 2, 2, 1, 0);
+    }
+    if (s < nsteps) NC_DKDV_STEP(s, 0, 2, 1);
+    if (s + 1 < nsteps) NC_DKDV_STEP(s + 1, 1, 0, 2);
+  }
+  // the last refills target tiles past the end; let them land before exit
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));
+}
+#undef NC_DKDV_STEP
+
+template <typename T, int D>
+__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const T* __restrict__ qk,
+                                                               const T* __restrict__ vsrc, const T* __restrict__ dO,
+                                                               const float2* __restrict__ rowstat,
+                                                               T* __restrict__ dk, T* __restrict__ dv, long ld_dkv) {
+  using Sh = DkdvShape<T, D>;
+  __shared__ __align__(16) T q0[Sh::TILE], q1[Sh::TILE], q2[Sh::TILE], q3[Sh::STAGES == 4 ? Sh::TILE : 1];
+  __shared__ __align__(16) T d0[Sh::TILE], d1[Sh::TILE], d2[Sh::TILE], d3[Sh::STAGES == 4 ? Sh::TILE : 1];
+  __shared__ __align__(16) float t0[64 * Sh::WAVES], t1[64 * Sh::WAVES], t2[64 * Sh::WAVES],
+      t3[Sh::STAGES == 4 ? 64 * Sh::WAVES : 1];
+  __shared__ __align__(16) F8<T> pb[2 * 512];  // P hand-over: [parity][key group][half][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63, lh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets and buffer resources
   const int per = g.G * g.B;
   const int kblk = (int)(blockIdx.x / per);  // key block 0 sees every query row: first
   const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
   const long tok0 = (long)b * g.T;
   const int kb0 = kblk * 128;
-  const int key = kb0 + 32 * wave + l32;  // this lane's key
-  const bool kok = key < g.T;
-  const int kw0 = kb0 + 32 * wave;
-  const DivN dvn{g.n_rep, g.inv_rep};
+  const int role = wave >> 2;
 
-  // own K and V rows as B operands (lane: key, 8 consecutive d)
-  F8<T> kf[D / 16], vf[D / 16];
-  const T* krow = qk + (tok0 + (kok ? key : 0)) * g.ld_qk + g.q_off_k + (long)kvh * D;
-  const T* vrow = vsrc + (tok0 + (kok ? key : 0)) * g.ld_v + (long)kvh * D;
+  DkdvCtx<T, D> c;
+  c.lane = lane;
+  c.wave = wave;
+  c.kw = wave & 3;
+  c.kw0 = kb0 + 32 * c.kw;
+  c.T_ = g.T;
+  c.kok = c.kw0 + l32 < g.T;
+  c.dvn = DivN{g.n_rep, g.inv_rep};
+  c.n_rep = g.n_rep;
+  c.hbase = kvh * g.n_rep;
+  c.nrows = g.T * g.n_rep;
+  c.r_start = (kb0 * g.n_rep) / Sh::BQ * Sh::BQ;
+  c.ntiles = c.r_start < c.nrows ? (c.nrows - c.r_start + Sh::BQ - 1) / Sh::BQ : 0;
+  c.ld_qk = g.ld_qk;
+  c.ld_o = g.ld_o;
+  c.rq = dma_rsrc(qk + tok0 * g.ld_qk);
+  c.rd = dma_rsrc(dO + tok0 * g.ld_o);
+  c.rs = dma_rsrc(rowstat + ((long)b * g.G + kvh) * c.nrows);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kf[s] = gld8<T>(krow + 16 * s + 8 * lh, kok);
-    vf[s] = gld8<T>(vrow + 16 * s + 8 * lh, kok);
+  for (int i = 0; i < Sh::NPW; ++i) {
+    const int ins = wave * Sh::NPW + i;  // Q tile instructions first, then dO
+    const int blk = ins % Sh::NQI;
+    const int u = 64 * blk + lane;       // chunk slot inside the tile
+    const int row = u / Swz<T, D>::NC, pc = u % Swz<T, D>::NC;
+    c.ldo[i] = ins >= Sh::NQI;
+    c.lblk[i] = blk;
+    c.lrow[i] = row;
+    c.lcol[i] = (pc ^ Swz<T, D>::f(row)) * Sh::VE;
   }
 
-  const int nrows = g.T * g.n_rep;
-  const int r_start = (kb0 * g.n_rep) / BQ * BQ;
-  const int ntiles = r_start < nrows ? (nrows - r_start + BQ - 1) / BQ : 0;
-  auto qaddr = [&](int tile) {
-    return [=](int row) -> const T* {
-      int r = r_start + tile * BQ + row;
-      if (r >= nrows) return nullptr;
-      int t = dvn.q(r), h = kvh * g.n_rep + (r - t * g.n_rep);
-      return qk + (tok0 + t) * g.ld_qk + (long)h * D;
-    };
-  };
-  auto daddr = [&](int tile) {
-    return [=](int row) -> const T* {
-      int r = r_start + tile * BQ + row;
-      if (r >= nrows) return nullptr;
-      int t = dvn.q(r), h = kvh * g.n_rep + (r - t * g.n_rep);
-      return dO + (tok0 + t) * g.ld_o + (long)h * D;
-    };
-  };
-  // per-row staging of (lse * log2 e, Delta, position) by threads < BQ
-  float pl = 0.f, pd = 0.f;
-  int pt = -1;
-  auto stats_load = [&](int tile) {
-    if (tid < BQ) {
-      int r = r_start + tile * BQ + tid;
-      pl = 0.f;
-      pd = 0.f;
-      pt = -1;
-      if (r < nrows) {
-        int t = dvn.q(r), h = kvh * g.n_rep + (r - t * g.n_rep);
-        long i = (tok0 + t) * g.H + h;
-        pl = lse[i] * kLog2e;
-        pd = delta[i];
-        pt = t;
-      }
-    }
-  };
-  auto stats_store = [&](int buf) {
-    if (tid < BQ) {
-      sl[buf][tid] = pl;
-      sd[buf][tid] = pd;
-      st[buf][tid] = pt;
-    }
-  };
-
-  QT ql, dl;
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  // own 32 keys: K (P side) or V (dS side) as B operands, 8 consecutive d per lane
+  const int key = c.kw0 + l32;
+  F8<T> kv[D / 16];
+  const T* src = role == 0 ? qk + (tok0 + (c.kok ? key : 0)) * g.ld_qk + g.q_off_k + (long)kvh * D
+                           : vsrc + (tok0 + (c.kok ? key : 0)) * g.ld_v + (long)kvh * D;
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) kv[k] = gld8<T>(src + 16 * k + 8 * lh, c.kok);
+  f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { dkacc[i][v] = 0.f; dvacc[i][v] = 0.f; }
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
   const float c1 = kLog2e / sqrtf((float)D);
 
-  if (ntiles > 0) {
-    ql.load(qaddr(0), tid);
-    dl.load(daddr(0), tid);
-    stats_load(0);
-    ql.store(qs[0], tid);
-    dl.store(ds_[0], tid);
-    stats_store(0);
-  }
-  __syncthreads();
+  if (role == 0) dkdv_ring<0, T, D>(c, acc, kv, pb, c1, q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3);
+  else dkdv_ring<1, T, D>(c, acc, kv, pb, c1, q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const bool more = it + 1 < ntiles;
-    const int buf = it & 1;
-    if (more) {
-      ql.load(qaddr(it + 1), tid);
-      dl.load(daddr(it + 1), tid);
-      stats_load(it + 1);
-    }
-    const int rq0 = r_start + it * BQ;
-    const int t_tmax = dvn.q(min(nrows - 1, rq0 + BQ - 1));
-    if (t_tmax >= kw0) {
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
-      const T* sq = qs[buf];
-      const T* sdo = ds_[buf];
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        F8<T> qa = ld_row8<T>(sq + l32 * LD + 16 * s + 8 * lh);
-        mma32(sacc, qa, kf[s]);
-        F8<T> da = ld_row8<T>(sdo + l32 * LD + 16 * s + 8 * lh);
-        mma32(pacc, da, vf[s]);
-      }
-      // sacc[v] = S[query crow(v,lh)][key l32]
-      float p[16], dsv[16];
-      const bool full = kok && rq0 + BQ <= nrows && dvn.q(rq0) >= kw0 + 31;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q0 = 8 * j + 4 * lh;
-        const float4 l4 = *reinterpret_cast<const float4*>(&sl[buf][q0]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&sd[buf][q0]);
-        const float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
-        int4 t4 = make_int4(0, 0, 0, 0);
-        if (!full) t4 = *reinterpret_cast<const int4*>(&st[buf][q0]);
-        const int ta[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = 4 * j + i;
-          float pv = fast_exp2(sacc[v] * c1 - la[i]);
-          if (!full) pv = (kok && key <= ta[i]) ? pv : 0.f;
-          p[v] = pv;
-          dsv[v] = pv * (pacc[v] - da[i]);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        F8<T> pf = pack8<T>(p + 8 * kk);
-        F8<T> sf = pack8<T>(dsv + 8 * kk);
-        const int k0 = 16 * kk + 4 * lh;
-#pragma unroll
-        for (int dti = 0; dti < D / 32; ++dti) {
-          F8<T> da = ld_tr8<T>(sdo, LD, k0, k0 + 8, 32 * dti + 16 * g16, lane);
-          mma32(dvacc[dti], da, pf);
-          F8<T> qa = ld_tr8<T>(sq, LD, k0, k0 + 8, 32 * dti + 16 * g16, lane);
-          mma32(dkacc[dti], qa, sf);
-        }
-      }
-    }
-    if (more) {
-      ql.store(qs[buf ^ 1], tid);
-      dl.store(ds_[buf ^ 1], tid);
-      stats_store(buf ^ 1);
-    }
-    __syncthreads();
-  }
-
-  if (kok) {
-    const float sc = 1.f / sqrtf((float)D);
-    T* ko = dk + (tok0 + key) * ld_dkv + (long)kvh * D;
-    T* vo = dv + (tok0 + key) * ld_dkv + (long)kvh * D;
+  if (c.kok) {
+    const float sc = role == 0 ? 1.f : 1.f / sqrtf((float)D);
+    T* out = (role == 0 ? dv : dk) + (tok0 + key) * ld_dkv + (long)kvh * D;
 #pragma unroll
     for (int dti = 0; dti < D / 32; ++dti)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int d = 32 * dti + crow(v, lh);
-        ko[d] = from_f32<T>(dkacc[dti][v] * sc);
-        vo[d] = from_f32<T>(dvacc[dti][v]);
-      }
+      for (int v = 0; v < 16; ++v) out[32 * dti + crow(v, lh)] = from_f32<T>(acc[dti][v] * sc);
   }
 }
 
@@ -672,23 +826,27 @@ nc_status attn_fwd_impl(const AttnGeom& g, const T* qk, const T* v, T* o, float*
 
 template <typename T, int D>
 nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, const T* dO, const float* lse,
-                        float* delta, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st) {
+                        float* rowstat, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st) {
+  // the dK/dV ring addresses one sequence of Q and dO through 32-bit offsets
+  if ((double)g.T * (double)(g.ld_qk > g.ld_o ? g.ld_qk : g.ld_o) * sizeof(T) >= (double)kDmaOOB)
+    return NC_ERR_UNSUPPORTED;
   int nqb = (g.T * g.n_rep + 127) / 128;
   const double tok = (double)g.B * g.T, es = sizeof(T);
+  float2* rs = reinterpret_cast<float2*>(rowstat);
   {
     // recompute S, then dP = dO V^T and dQ = dS K: 6 D flops per pair
     ProfScope prof(NC_NAME(T, "attn_bwd_dq"), 6.0 * D * causal_pairs(g),
-                   es * tok * D * (4.0 * g.H + 2.0 * g.G) + 8.0 * tok * g.H, st);
+                   es * tok * D * (4.0 * g.H + 2.0 * g.G) + 12.0 * tok * g.H, st);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(nqb * g.G * g.B), dim3(256), 0, st, g, qk, v, o, dO, lse,
-                       delta, dq);
+                       rs, dq);
     NC_LAUNCH_CHECK("attn_bwd_dq");
   }
   int nkb = (g.T + 127) / 128;
   // recompute S and dP, then dV = P^T dO and dK = dS^T Q: 8 D flops per pair
   ProfScope prof(NC_NAME(T, "attn_bwd_dkdv"), 8.0 * D * causal_pairs(g),
                  es * tok * D * (2.0 * g.H + 4.0 * g.G) + 8.0 * tok * g.H, st);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(nkb * g.G * g.B), dim3(256), 0, st, g, qk, v, dO, lse,
-                     delta, dk, dv, ld_dkv);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(nkb * g.G * g.B), dim3(512), 0, st, g, qk, v, dO, rs, dk,
+                     dv, ld_dkv);
   NC_LAUNCH_CHECK("attn_bwd_dkdv");
   return NC_OK;
 }
@@ -714,10 +872,10 @@ nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse,
 
 template <typename T>
 nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const T* dO, const float* lse,
-                   float* delta, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st) {
+                   float* rowstat, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st) {
   AttnGeom g = make_geom(a);
-  if (a.D == 128) return attn_bwd_impl<T, 128>(g, qk, v, o, dO, lse, delta, dq, dk, dv, ld_dkv, st);
-  if (a.D == 64) return attn_bwd_impl<T, 64>(g, qk, v, o, dO, lse, delta, dq, dk, dv, ld_dkv, st);
+  if (a.D == 128) return attn_bwd_impl<T, 128>(g, qk, v, o, dO, lse, rowstat, dq, dk, dv, ld_dkv, st);
+  if (a.D == 64) return attn_bwd_impl<T, 64>(g, qk, v, o, dO, lse, rowstat, dq, dk, dv, ld_dkv, st);
   return NC_ERR_UNSUPPORTED;
 }
 

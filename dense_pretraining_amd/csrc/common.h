@@ -80,6 +80,30 @@ __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bits) {
   if (status) atomicOr(status, bits);
 }
 
+// ---------------------------------------------------------------- direct-to-LDS loads
+// buffer_load_* ... lds (gfx950) writes lane i's data at the LDS address in
+// M0 plus i times the access size, whatever the source address. A buffer
+// resource with a 2 GiB record turns any offset at or past kDmaOOB into a
+// zero read, so out-of-range lanes need no branch.
+constexpr unsigned kDmaRecords = 0x7ffffff0u;  // buffer record size (bytes)
+constexpr unsigned kDmaOOB = 0x7ffffff0u;      // offset that reads as zero
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kDmaRecords, 0x00020000);
+}
+
+// Ring barrier: this wave's loads older than the newest N have landed in
+// LDS and its LDS reads are done (s_waitcnt vmcnt(N) lgkmcnt(0)), then all
+// waves meet. A plain s_barrier: __syncthreads() would also drain the loads
+// that are meant to stay in flight.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Records the HIP error text for nc_last_hip_error and maps it to a status.

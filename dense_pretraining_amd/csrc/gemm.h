@@ -312,9 +312,6 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
 
 constexpr int kDmaBK = 32;
 constexpr int kDmaStages = 4;
-constexpr unsigned kDmaRecords = 0x7ffffff0u;  // buffer record size (bytes)
-constexpr unsigned kDmaOOB = 0x7ffffff0u;      // offset that reads as zero
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int dma_swz_row(int r) { return ((r >> 2) & 3) ^ (r & 2); }  // K-contiguous chunks
 __device__ __forceinline__ int dma_swz_k(int k) { return (5 * (k & 3)) & 31; }          // K-outer chunks
@@ -356,8 +353,7 @@ struct DmaOperand {
   __device__ __forceinline__ void issue(bf16* lds, int k0, int kend, int wave) const {
     const bool full = k0 + kDmaBK <= kend;
     if constexpr (Layout == kKc) {
-      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g + (long)row0 * ld),
-                                                                    (short)0, (int)kDmaRecords, 0x00020000);
+      __amdgpu_buffer_rsrc_t rs = dma_rsrc(g + (long)row0 * ld);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const unsigned o = (full || k0 + kpos[q] < kend) ? off[q] : kDmaOOB;
@@ -365,8 +361,7 @@ struct DmaOperand {
                                                  (unsigned)(k0 * 2), 0, 0);
       }
     } else {
-      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(g + (long)k0 * ld + row0),
-                                                                    (short)0, (int)kDmaRecords, 0x00020000);
+      __amdgpu_buffer_rsrc_t rs = dma_rsrc(g + (long)k0 * ld + row0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const unsigned o = (full || k0 + kpos[q] < kend) ? off[q] : kDmaOOB;
@@ -407,16 +402,6 @@ __device__ __forceinline__ void frag_transform(Frag<bf16>& f) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) f.v[e] = (bf16)tr((float)f.v[e]);
   }
-}
-
-// Ring barrier: this wave's loads older than the newest N have landed in
-// LDS and its LDS reads are done (s_waitcnt vmcnt(N) lgkmcnt(0)), then all
-// waves meet. A plain s_barrier: __syncthreads() would also drain the loads
-// that are meant to stay in flight.
-template <int N>
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
 }
 
 template <int LA, int LB, typename TrA, typename TrB>
