@@ -84,7 +84,7 @@ struct Carver {
 template <typename T>
 struct BlockSaved {
   float *r1, *lse, *r2, *cs, *sn;
-  T *h1, *qkv, *qk, *o, *x1, *h2, *u;
+  T *h1, *qkv, *qk, *o, *x1, *h2, *act;  // act = max(h2 W1^T, 0)^2
 };
 template <typename T>
 BlockSaved<T> carve_block_saved(Carver& c, const Dims& m, bool table) {
@@ -98,7 +98,7 @@ BlockSaved<T> carve_block_saved(Carver& c, const Dims& m, bool table) {
   s.x1 = c.take<T>(m.M * m.d);
   s.r2 = c.take<float>(m.M);
   s.h2 = c.take<T>(m.M * m.d);
-  s.u = c.take<T>(m.M * m.F);
+  s.act = c.take<T>(m.M * m.F);
   s.cs = table ? c.take<float>((size_t)m.T * m.D / 2) : nullptr;
   s.sn = table ? c.take<float>((size_t)m.T * m.D / 2) : nullptr;
   return s;
@@ -261,8 +261,8 @@ nc_status block_fwd_t(const Dims& m, const BlockW<T>& w, const T* x, T* x_out, c
   NC_TRY(attn_fwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, s.lse, st));
   NC_TRY(gemm_xwt<T>(s.o, w.wo, s.x1, x, M, m.d, m.HD, false, st));
   NC_TRY(rmsnorm_fwd<T>(s.x1, nullptr, 0, s.h2, s.r2, M, m.d, m.eps, nullptr, st));
-  NC_TRY(gemm_xwt<T>(s.h2, w.w1, s.u, nullptr, M, m.F, m.d, false, st));
-  NC_TRY(gemm_xwt<T>(s.u, w.w2, x_out, s.x1, M, m.d, m.F, true, st));
+  NC_TRY(gemm_xwt<T>(s.h2, w.w1, s.act, nullptr, M, m.F, m.d, true, st));
+  NC_TRY(gemm_xwt<T>(s.act, w.w2, x_out, s.x1, M, m.d, m.F, false, st));
   return NC_OK;
 }
 
@@ -272,14 +272,14 @@ nc_status block_bwd_t(const Dims& m, const BlockW<T>& w, const T* x, const Block
                       const BlockScratch<T>& c, hipStream_t st) {
   (void)x;
   const int M = (int)m.M;
-  // MLP: x_out = x1 + relu(u)^2 W2^T, u = h2 W1^T
-  NC_TRY(gemm_dw<T>(dx_out, s.u, g.w2, M, m.d, m.F, true, acc, c.partial, c.partial_elems, st));
-  NC_TRY(gemm_dyw<T>(dx_out, w.w2, c.du, s.u, M, m.d, m.F, st));
-  NC_TRY(gemm_dw<T>(c.du, s.h2, g.w1, M, m.F, m.d, false, acc, c.partial, c.partial_elems, st));
+  // MLP: x_out = x1 + act W2^T, act = max(h2 W1^T, 0)^2
+  NC_TRY(gemm_dw<T>(dx_out, s.act, g.w2, M, m.d, m.F, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dyw<T>(dx_out, w.w2, c.du, s.act, M, m.d, m.F, st));
+  NC_TRY(gemm_dw<T>(c.du, s.h2, g.w1, M, m.F, m.d, acc, c.partial, c.partial_elems, st));
   NC_TRY(gemm_dyw<T>(c.du, w.w1, c.dh, nullptr, M, m.F, m.d, st));
   NC_TRY(rmsnorm_bwd<T, T>(c.dh, s.h2, s.r2, dx_out, c.dx1, M, m.d, st));
   // attention output projection: x1 = x + o Wo^T
-  NC_TRY(gemm_dw<T>(c.dx1, s.o, g.wo, M, m.d, m.HD, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dw<T>(c.dx1, s.o, g.wo, M, m.d, m.HD, acc, c.partial, c.partial_elems, st));
   NC_TRY(gemm_dyw<T>(c.dx1, w.wo, c.dy, nullptr, M, m.d, m.HD, st));
   // attention, then rotation + QK norm
   AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
@@ -287,7 +287,7 @@ nc_status block_bwd_t(const Dims& m, const BlockW<T>& w, const T* x, const Block
                      c.dqkv + (size_t)m.H * m.D, c.dqkv + (size_t)(m.H + m.G) * m.D, m.QKV, st));
   NC_TRY(qknorm_rope_bwd<T>(s.qkv, m.QKV, c.dqkv, m.QKV, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
   // QKV projection and the pre-attention norm
-  NC_TRY(gemm_dw<T>(c.dqkv, s.h1, g.wqkv, M, m.QKV, m.d, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dw<T>(c.dqkv, s.h1, g.wqkv, M, m.QKV, m.d, acc, c.partial, c.partial_elems, st));
   NC_TRY(gemm_dyw<T>(c.dqkv, w.wqkv, c.dh, nullptr, M, m.QKV, m.d, st));
   NC_TRY(rmsnorm_bwd<T, T>(c.dh, s.h1, s.r1, c.dx1, dx_in, M, m.d, st));
   return NC_OK;
@@ -310,7 +310,7 @@ nc_status head_bwd_t(const Dims& m, const T* wlm, const int32_t* tg, const HeadS
   const int M = (int)m.M;
   NC_TRY(xent_dz<T>(s.z, M, m.V, s.lse, tg, s.nv, dloss, m.cap, st));
   NC_TRY(gemm_dyw<T>(s.z, wlm, c.dxf, nullptr, M, m.V, m.d, st));
-  NC_TRY(gemm_dw<T>(s.z, s.xf, dwlm, M, m.V, m.d, false, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dw<T>(s.z, s.xf, dwlm, M, m.V, m.d, acc, c.partial, c.partial_elems, st));
   NC_TRY(rmsnorm_bwd<T, T>(c.dxf, s.xf, s.rf, nullptr, dx, M, m.d, st));
   return NC_OK;
 }

@@ -31,19 +31,6 @@ namespace nc {
 
 enum OperandLayout { kKc = 0, kKo = 1 };
 
-struct Identity {
-  static constexpr bool active = false;
-  __device__ __forceinline__ float operator()(float x) const { return x; }
-};
-// a = max(u, 0)^2: the ReLU^2 activation applied while an operand is loaded.
-struct ReluSq {
-  static constexpr bool active = true;
-  __device__ __forceinline__ float operator()(float x) const {
-    float r = fmaxf(x, 0.f);
-    return r * r;
-  }
-};
-
 template <typename T> struct GemmTile;
 template <> struct GemmTile<bf16> {
   static constexpr int BM = 256, BN = 256, BK = 32, WTM = 4, WTN = 4;
@@ -141,7 +128,7 @@ template <> __device__ __forceinline__ Frag<float> frag_col<float>(const float* 
 // ---------------------------------------------------------------- loaders
 
 // One operand tile (ROWS x BK) : global -> registers -> LDS.
-template <typename T, int Layout, int ROWS, typename Tr>
+template <typename T, int Layout, int ROWS>
 struct OperandLoader {
   static constexpr int BK = GemmTile<T>::BK;
   static constexpr int VE = Vec<T>::n;  // elements per 16 B
@@ -170,20 +157,6 @@ struct OperandLoader {
         const int gk = k0 + kl, gr = row0 + rv * VE;
         r[i] = (gk < kend && gr < nrows) ? *reinterpret_cast<const uint4*>(g + (long)gk * ld + gr)
                                          : make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void transform() {
-    if constexpr (Tr::active) {
-      Tr tr;
-#pragma unroll
-      for (int i = 0; i < NLOAD; ++i) {
-        float f[VE];
-        load16<T>(reinterpret_cast<const T*>(&r[i]), f);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) f[e] = tr(f[e]);
-        store16<T>(reinterpret_cast<T*>(&r[i]), f);
       }
     }
   }
@@ -222,12 +195,266 @@ struct TileAcc {
   f32x16 c[WTM][WTN];
 };
 
-template <typename T, int LA, int LB, typename TrA, typename TrB, typename Epi>
+// ---------------------------------------------------------------- epilogues
+// The accumulators leave through LDS: each wave owns a 32-row x (32*WTN)
+// float32 slab (16-byte chunks XOR-swizzled by row, so both the column-wise
+// writes and the row-wise reads are conflict-free). Phase 1 runs in the
+// accumulator layout, where a lane holds one row and runs of 4 columns
+// (epi.pre may transform the values and keep per-row state); phase 2 reads
+// the slab back so that 16 consecutive lanes cover 64 consecutive columns of
+// one row, and epi.post writes 4 values per lane: each store instruction
+// fills whole 128-byte lines of 4 rows instead of touching 32 rows.
+
+struct EpiCtx {
+  int m0, n0;     // block tile origin
+  int wm, wn;     // wave sub-tile origin inside the block tile
+  int z;          // K split
+  int lane, wave;
+  float* red;     // LDS scratch beside the slabs (2 * BM floats)
+};
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v);
+template <> __device__ __forceinline__ void store4<bf16>(bf16* p, const float* v) {
+  bf16x4 o;
+  o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* v);
+template <> __device__ __forceinline__ void load4<bf16>(const bf16* p, float* v) {
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void load4<float>(const float* p, float* v) {
+  float4 u = *reinterpret_cast<const float4*>(p);
+  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+}
+
+// A wave's LDS instructions execute in order, and the compiler keeps the slab
+// writes and reads (lane-dependent addresses it cannot tell apart) in program
+// order, so no fence is needed between the two phases.
+
+template <int WTM, int WTN, typename Epi>
+__device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi& epi, const EpiCtx& x,
+                                                float* slab) {
+  constexpr int NCH = 8 * WTN;  // 16-byte chunks per slab row
+  const int lane = x.lane, lr = lane & 31, h = lane >> 5;
+  const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) {
+    // the slab's other inputs (residual, activation) are fetched first, in
+    // the phase-2 layout, so that their latency hides behind phase 1
+    typename Epi::Aux aux[8][NCH / 16];
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+      for (int k = 0; k < NCH / 16; ++k)
+        aux[it][k] = epi.load_aux(r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k));
+    typename Epi::RowState rs;
+    epi.row_begin(rs, r0 + 32 * i + lr);
+#pragma unroll
+    for (int j = 0; j < WTN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4] = {c[i][j][4 * g], c[i][j][4 * g + 1], c[i][j][4 * g + 2], c[i][j][4 * g + 3]};
+        const int cc = 8 * j + 2 * g + h;
+        epi.pre(rs, r0 + 32 * i + lr, c0 + 4 * cc, v);
+        *reinterpret_cast<float4*>(slab + 4 * (lr * NCH + (cc ^ (lr & 15)))) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    epi.row_end(rs, x, i);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rr = 4 * it + (lane >> 4);
+#pragma unroll
+      for (int k = 0; k < NCH / 16; ++k) {
+        const int cc = (lane & 15) + 16 * k;
+        const float4 q = *reinterpret_cast<const float4*>(slab + 4 * (rr * NCH + (cc ^ (rr & 15))));
+        float v[4] = {q.x, q.y, q.z, q.w};
+        epi.post(x, r0 + 32 * i + rr, c0 + 4 * cc, v, aux[it][k]);
+      }
+    }
+  }
+}
+
+// Four values of a second [M,N] input in the storage type, fetched ahead.
+template <typename T> struct Aux4;
+template <> struct Aux4<bf16> { uint2 u; };
+template <> struct Aux4<float> { float4 u; };
+template <typename T>
+__device__ __forceinline__ Aux4<T> aux_load(const T* p, bool ok) {
+  Aux4<T> a;
+  if constexpr (sizeof(T) == 2) a.u = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0, 0);
+  else a.u = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0, 0, 0, 0);
+  return a;
+}
+template <typename T>
+__device__ __forceinline__ void aux_get(const Aux4<T>& a, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    v[0] = __uint_as_float(a.u.x << 16); v[1] = __uint_as_float(a.u.x & 0xffff0000u);
+    v[2] = __uint_as_float(a.u.y << 16); v[3] = __uint_as_float(a.u.y & 0xffff0000u);
+  } else {
+    v[0] = a.u.x; v[1] = a.u.y; v[2] = a.u.z; v[3] = a.u.w;
+  }
+}
+struct NoAux {};
+
+// Hooks of an epilogue with no per-row state and no phase-1 work.
+#define NC_EPI_NO_ROW_WORK                                                          \
+  struct RowState {};                                                               \
+  __device__ __forceinline__ void row_begin(RowState&, int) const {}                \
+  __device__ __forceinline__ void pre(RowState&, int, int, float*) const {}         \
+  __device__ __forceinline__ void row_end(RowState&, const EpiCtx&, int) const {}   \
+  __device__ __forceinline__ void finish(const EpiCtx&) const {}
+
+// C = act(acc) (+ residual), act = identity or the ReLU^2 activation
+// max(x, 0)^2. Output in the storage type.
+template <typename T, bool ReluSqOut = false>
+struct EpiStore {
+  NC_EPI_NO_ROW_WORK
+  T* C;
+  long ldc;
+  const T* res;  // optional residual, same layout as C
+  long ldr;
+  int M, N;
+  using Aux = Aux4<T>;
+  __device__ __forceinline__ Aux load_aux(int row, int col) const {
+    return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
+  }
+  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
+    if (row >= M || col >= N) return;
+    if constexpr (ReluSqOut) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r = fmaxf(v[e], 0.f);
+        v[e] = r * r;
+      }
+    }
+    if (res) {
+      float r[4];
+      aux_get<T>(a, r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += r[e];
+    }
+    store4<T>(C + (long)row * ldc + col, v);
+  }
+};
+
+// du = acc * 2 max(u, 0), the input gradient of a = max(u, 0)^2, from the
+// stored activation a: max(u, 0) = sqrt(a).
+template <typename T>
+struct EpiDReluSq {
+  NC_EPI_NO_ROW_WORK
+  T* C;
+  long ldc;
+  const T* act;  // a = max(u, 0)^2 as stored by the forward pass
+  long lda;
+  int M, N;
+  using Aux = Aux4<T>;
+  __device__ __forceinline__ Aux load_aux(int row, int col) const {
+    return aux_load<T>(act + (long)row * lda + col, row < M && col < N);
+  }
+  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
+    if (row >= M || col >= N) return;
+    float av[4];
+    aux_get<T>(a, av);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= 2.f * __builtin_sqrtf(av[e]);
+    store4<T>(C + (long)row * ldc + col, v);
+  }
+};
+
+// float32 output: a weight gradient (store or accumulate) or, with several
+// K splits, the split's partial tile at C + z * split_stride.
+struct EpiF32 {
+  NC_EPI_NO_ROW_WORK
+  float* C;
+  long ldc;
+  long split_stride;
+  int accumulate;
+  int M, N;
+  using Aux = NoAux;
+  __device__ __forceinline__ Aux load_aux(int, int) const { return Aux{}; }
+  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
+    if (row >= M || col >= N) return;
+    float* p = C + (long)x.z * split_stride + (long)row * ldc + col;
+    float4 o = make_float4(v[0], v[1], v[2], v[3]);
+    if (accumulate) {
+      const float4 q = *reinterpret_cast<const float4*>(p);
+      o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+    }
+    *reinterpret_cast<float4*>(p) = o;
+  }
+};
+
+// Unembedding epilogue: z' = c tanh(z / c) (the logit softcap of the
+// architecture list), stored in the storage type; per row, the sum of
+// exp(z') over this tile's BN columns goes to part[row * n_tiles + tile]
+// (|z'| <= c, so no running maximum is needed in float32); the float32 z'
+// of the target column goes to zt[row]. The tanh and exponentials use the
+// hardware exp2 and reciprocal: c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
+template <typename T, int BM, int BN>
+struct EpiSoftcap {
+  T* Z;
+  long ldz;
+  float cap;
+  const int32_t* targets;
+  float* part;
+  float* zt;
+  int n_tiles;
+  int M, N;
+  struct RowState {
+    float sum;
+    int tgt;
+  };
+  __device__ __forceinline__ void row_begin(RowState& rs, int row) const {
+    rs.sum = 0.f;
+    rs.tgt = row < M ? targets[row] : -1;
+  }
+  __device__ __forceinline__ void pre(RowState& rs, int row, int col, float* v) const {
+    const float k2 = 2.8853900817779268f / cap;  // 2 log2(e) / c
+    const float lg = 1.4426950408889634f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float t = __builtin_amdgcn_exp2f(v[e] * k2);
+      v[e] = cap - 2.f * cap * __builtin_amdgcn_rcpf(t + 1.f);
+    }
+    if (row < M && col < N) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rs.sum += __builtin_amdgcn_exp2f(v[e] * lg);
+      const unsigned d = (unsigned)(rs.tgt - col);
+      if (d < 4u) zt[row] = d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
+    }
+  }
+  __device__ __forceinline__ void row_end(RowState& rs, const EpiCtx& x, int i) const {
+    // the other half of this row's columns sits in lane ^ 32
+    const float s2 = rs.sum + __shfl_xor(rs.sum, 32, 64);
+    if (x.lane < 32) x.red[(x.wn ? BM : 0) + x.wm + 32 * i + x.lane] = s2;
+  }
+  using Aux = NoAux;
+  __device__ __forceinline__ Aux load_aux(int, int) const { return Aux{}; }
+  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux&) const {
+    if (row < M && col < N) store4<T>(Z + (long)row * ldz + col, v);
+  }
+  __device__ __forceinline__ void finish(const EpiCtx& x) const {
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += blockDim.x) {
+      const int row = x.m0 + r;
+      if (row < M) part[(long)row * n_tiles + x.n0 / BN] = x.red[r] + x.red[BM + r];
+    }
+  }
+};
+
+template <typename T, int LA, int LB, typename Epi>
 __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   using Cfg = GemmTile<T>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WTM = Cfg::WTM, WTN = Cfg::WTN;
-  using LoadA = OperandLoader<T, LA, BM, TrA>;
-  using LoadB = OperandLoader<T, LB, BN, TrB>;
+  using LoadA = OperandLoader<T, LA, BM>;
+  using LoadB = OperandLoader<T, LB, BN>;
   __shared__ __align__(16) T smem[2][LoadA::SIZE + LoadB::SIZE];
 
   const int tid = threadIdx.x;
@@ -259,8 +486,6 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   if (nk > 0) {
     la.load(A, s.lda, m0, s.M, kbeg, kend, tid);
     lb.load(B, s.ldb, n0, s.N, kbeg, kend, tid);
-    la.transform();
-    lb.transform();
     la.store(smem[0], tid);
     lb.store(smem[0] + LoadA::SIZE, tid);
   }
@@ -287,16 +512,18 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
         for (int j = 0; j < WTN; ++j) mfma32(acc.c[i][j], fb[j], fa[i]);
     }
     if (more) {
-      la.transform();
-      lb.transform();
       la.store(smem[(kt + 1) & 1], tid);
       lb.store(smem[(kt + 1) & 1] + LoadA::SIZE, tid);
     }
     __syncthreads();
   }
 
-  epi(acc, m0 + wm + (lane & 31), n0 + wn + 4 * (lane >> 5), m0, n0, z, lane, wave,
-      reinterpret_cast<float*>(&smem[0][0]));
+  // operand LDS is free now: one 32 x (32 WTN) float32 slab per wave, then the row-sum scratch
+  float* lds = reinterpret_cast<float*>(&smem[0][0]);
+  static_assert(sizeof(smem) >= (4 * 32 * 32 * WTN + 2 * BM) * sizeof(float), "epilogue LDS");
+  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, lds + 4 * 32 * 32 * WTN};
+  staged_epilogue<WTM, WTN>(acc.c, epi, x, lds + wave * 32 * 32 * WTN);
+  epi.finish(x);
 }
 
 // ---------------------------------------------------------------- bf16: direct-to-LDS pipeline
@@ -308,7 +535,6 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
 // fragment reads (b128 for K-contiguous, transposing b64 for K-outer tiles)
 // hit distinct banks. Out-of-range lanes get an offset beyond the buffer
 // record, which the hardware turns into zeros: ragged M/N/K need no branch.
-// The ReLU^2 operand transform is applied to fragments after the LDS read.
 
 constexpr int kDmaBK = 32;
 constexpr int kDmaStages = 4;
@@ -395,16 +621,7 @@ struct DmaOperand {
   }
 };
 
-template <typename Tr>
-__device__ __forceinline__ void frag_transform(Frag<bf16>& f) {
-  if constexpr (Tr::active) {
-    Tr tr;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f.v[e] = (bf16)tr((float)f.v[e]);
-  }
-}
-
-template <int LA, int LB, typename TrA, typename TrB>
+template <int LA, int LB>
 struct DmaTile {
   using OpA = DmaOperand<LA>;
   using OpB = DmaOperand<LB>;
@@ -415,15 +632,9 @@ struct DmaTile {
     for (int kk = 0; kk < kDmaBK; kk += 16) {
       Frag<bf16> fa[WTM], fb[WTN];
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        fa[i] = OpA::frag(ta, wm + 32 * i, kk, lane);
-        frag_transform<TrA>(fa[i]);
-      }
+      for (int i = 0; i < WTM; ++i) fa[i] = OpA::frag(ta, wm + 32 * i, kk, lane);
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        fb[j] = OpB::frag(tb, wn + 32 * j, kk, lane);
-        frag_transform<TrB>(fb[j]);
-      }
+      for (int j = 0; j < WTN; ++j) fb[j] = OpB::frag(tb, wn + 32 * j, kk, lane);
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
@@ -493,10 +704,10 @@ __device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA&
   NC_DMA_STEP_TAIL(kt + 5, sa1, sb1, sa0, sb0);
 }
 
-template <int LA, int LB, typename TrA, typename TrB, typename Epi>
+template <int LA, int LB, typename Epi>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) {
   constexpr int BM = 256, BN = 256, BK = kDmaBK;
-  using Tile = DmaTile<LA, LB, TrA, TrB>;
+  using Tile = DmaTile<LA, LB>;
   constexpr int E = Tile::OpA::ELEMS;
   __shared__ __align__(1024) bf16 sa0[E], sa1[E], sa2[E], sa3[E];
   __shared__ __align__(1024) bf16 sb0[E], sb1[E], sb2[E], sb3[E];
@@ -526,201 +737,30 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   opb.init(static_cast<const bf16*>(s.B), s.ldb, n0, s.N, wave, lane);
   dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, nk, kbeg, kend, wave, wm, wn, lane);
   __syncthreads();
-  epi(acc, m0 + wm + (lane & 31), n0 + wn + 4 * (lane >> 5), m0, n0, z, lane, wave, reinterpret_cast<float*>(sa0));
+  // the A stages become the waves' 32 x 128 float32 slabs, B stage 0 the row-sum scratch
+  static_assert(E * sizeof(bf16) == 32 * 128 * sizeof(float), "one A stage holds one slab");
+  bf16* slab = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sa3;
+  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, reinterpret_cast<float*>(sb0)};
+  staged_epilogue<4, 4>(acc.c, epi, x, reinterpret_cast<float*>(slab));
+  epi.finish(x);
 }
 #undef NC_DMA_STEP_FULL
 #undef NC_DMA_STEP_TAIL
 
 
-// ---------------------------------------------------------------- epilogues
-// Called by every thread with m_base = this lane's row (add 32*i) and
-// n_base = its first column (add 32*j + 8*g for the run of 4 columns held
-// in c[i][j][4g..4g+3]); m0/n0 = the block tile's origin. `red` is LDS
-// scratch usable after a barrier.
-
-template <typename T>
-__device__ __forceinline__ void store4(T* p, const float* v);
-template <> __device__ __forceinline__ void store4<bf16>(bf16* p, const float* v) {
-  bf16x4 o;
-  o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
-  *reinterpret_cast<bf16x4*>(p) = o;
-}
-template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, float* v);
-template <> __device__ __forceinline__ void load4<bf16>(const bf16* p, float* v) {
-  uint2 u = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-  v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-template <> __device__ __forceinline__ void load4<float>(const float* p, float* v) {
-  float4 u = *reinterpret_cast<const float4*>(p);
-  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-}
-
-// Visit every run of 4 columns this lane holds: f(row, col, float v[4]).
-template <typename T, typename F>
-__device__ __forceinline__ void for_each_run(TileAcc<T>& a, int m_base, int n_base, F f) {
-#pragma unroll
-  for (int i = 0; i < TileAcc<T>::WTM; ++i)
-#pragma unroll
-    for (int j = 0; j < TileAcc<T>::WTN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v[4] = {a.c[i][j][4 * g], a.c[i][j][4 * g + 1], a.c[i][j][4 * g + 2], a.c[i][j][4 * g + 3]};
-        f(m_base + 32 * i, n_base + 32 * j + 8 * g, v);
-      }
-}
-
-// C = acc (+ residual). Output in the storage type.
-template <typename T>
-struct EpiStore {
-  T* C;
-  long ldc;
-  const T* res;  // optional residual, same layout as C
-  long ldr;
-  int M, N;
-  template <typename TT>
-  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int, int, int, int, int, float*) const {
-    for_each_run<TT>(a, mb, nb, [&](int row, int col, float* v) {
-      if (row >= M || col >= N) return;
-      if (res) {
-        float r[4];
-        load4<T>(res + (long)row * ldr + col, r);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += r[e];
-      }
-      store4<T>(C + (long)row * ldc + col, v);
-    });
-  }
-};
-
-// du = acc * 2 max(u, 0): input grad of the ReLU^2 activation.
-template <typename T>
-struct EpiDReluSq {
-  T* C;
-  long ldc;
-  const T* u;
-  long ldu;
-  int M, N;
-  template <typename TT>
-  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int, int, int, int, int, float*) const {
-    for_each_run<TT>(a, mb, nb, [&](int row, int col, float* v) {
-      if (row >= M || col >= N) return;
-      float uu[4];
-      load4<T>(u + (long)row * ldu + col, uu);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] *= 2.f * fmaxf(uu[e], 0.f);
-      store4<T>(C + (long)row * ldc + col, v);
-    });
-  }
-};
-
-// float32 output: a weight gradient (store or accumulate) or, with several
-// K splits, the split's partial tile at C + z * split_stride.
-struct EpiF32 {
-  float* C;
-  long ldc;
-  long split_stride;
-  int accumulate;
-  int M, N;
-  template <typename TT>
-  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int, int, int z, int, int,
-                                             float*) const {
-    float* base = C + (long)z * split_stride;
-    for_each_run<TT>(a, mb, nb, [&](int row, int col, float* v) {
-      if (row >= M || col >= N) return;
-      float* p = base + (long)row * ldc + col;
-      float4 o = make_float4(v[0], v[1], v[2], v[3]);
-      if (accumulate) {
-        float4 q = *reinterpret_cast<float4*>(p);
-        o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
-      }
-      *reinterpret_cast<float4*>(p) = o;
-    });
-  }
-};
-
-// Unembedding epilogue: z' = c tanh(z / c) (the logit softcap of the
-// architecture list), stored in the storage type; per row, the sum of
-// exp(z') over this tile's BN columns goes to part[row * n_tiles + tile]
-// (|z'| <= c, so no running maximum is needed in float32); the float32 z'
-// of the target column goes to zt[row].
-template <typename T>
-struct EpiSoftcap {
-  T* Z;
-  long ldz;
-  float cap;
-  const int32_t* targets;
-  float* part;
-  float* zt;
-  int n_tiles;
-  int M, N;
-  template <typename TT>
-  __device__ __forceinline__ void operator()(TileAcc<TT>& a, int mb, int nb, int m0, int n0, int, int lane,
-                                             int wave, float* red) const {
-    constexpr int WTM = TileAcc<TT>::WTM, BM = GemmTile<TT>::BM, BN = GemmTile<TT>::BN;
-    const float two_over_c = 2.f / cap;
-    float rowsum[WTM];
-#pragma unroll
-    for (int i = 0; i < WTM; ++i) {
-      rowsum[i] = 0.f;
-      const int row = mb + 32 * i;
-      const int tgt = row < M ? targets[row] : -1;
-#pragma unroll
-      for (int j = 0; j < TileAcc<TT>::WTN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = nb + 32 * j + 8 * g;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // c tanh(x/c) = c - 2c / (exp(2x/c) + 1)
-            float ex = __expf(a.c[i][j][4 * g + e] * two_over_c);
-            v[e] = cap - 2.f * cap / (ex + 1.f);
-          }
-          if (row < M && col < N) {
-            store4<T>(Z + (long)row * ldz + col, v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              rowsum[i] += __expf(v[e]);
-              if (col + e == tgt) zt[row] = v[e];
-            }
-          }
-        }
-      // the other half of this row's columns sits in lane ^ 32
-      rowsum[i] += __shfl_xor(rowsum[i], 32, 64);
-    }
-    __syncthreads();  // operand LDS is free now
-    const int wn_idx = wave & 1, wm = (wave >> 1) * (BM / 2);
-    if (lane < 32) {
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) red[wn_idx * BM + wm + 32 * i + lane] = rowsum[i];
-    }
-    __syncthreads();
-    const int tid = threadIdx.x;
-    for (int r = tid; r < BM; r += 256) {
-      const int row = m0 + r;
-      if (row < M) part[(long)row * n_tiles + n0 / BN] = red[r] + red[BM + r];
-    }
-  }
-};
-
 // ---------------------------------------------------------------- launcher
 
-template <typename T, int LA, int LB, typename TrA, typename TrB, typename Epi>
+template <typename T, int LA, int LB, typename Epi>
 nc_status launch_gemm(const GemmShape& s, const Epi& epi, hipStream_t stream) {
   using Cfg = GemmTile<T>;
   int tiles_m = (s.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (s.N + Cfg::BN - 1) / Cfg::BN;
   long blocks = (long)tiles_m * tiles_n * s.n_split;
   if (blocks <= 0) return NC_OK;
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((gemm_dma_kernel<LA, LB, TrA, TrB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
+    hipLaunchKernelGGL((gemm_dma_kernel<LA, LB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
                        epi);
   else
-    hipLaunchKernelGGL((gemm_kernel<T, LA, LB, TrA, TrB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
+    hipLaunchKernelGGL((gemm_kernel<T, LA, LB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
                        epi);
   NC_LAUNCH_CHECK("gemm");
   return NC_OK;

@@ -30,34 +30,38 @@ size_t gemm_dw_partial_elems(int M, int N, int K) {
 }
 
 template <typename T>
-nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_x, hipStream_t st) {
+nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_out,
+                   hipStream_t st) {
   GemmShape s{x, w, K, K, M, N, K, K, 1};
-  EpiStore<T> e{y, N, res, N, M, N};
   const double es = sizeof(T);
-  ProfScope prof(relu_sq_x ? NC_NAME(T, "gemm_fwd_relusq") : NC_NAME(T, "gemm_fwd"), 2.0 * M * N * K,
+  ProfScope prof(relu_sq_out ? NC_NAME(T, "gemm_fwd_relusq") : NC_NAME(T, "gemm_fwd"), 2.0 * M * N * K,
                  es * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
-  if (relu_sq_x) return launch_gemm<T, kKc, kKc, ReluSq, Identity>(s, e, st);
-  return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
+  if (relu_sq_out) {
+    EpiStore<T, true> e{y, N, res, N, M, N};
+    return launch_gemm<T, kKc, kKc>(s, e, st);
+  }
+  EpiStore<T> e{y, N, res, N, M, N};
+  return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
 template <typename T>
-nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* u, int M, int N, int K, hipStream_t st) {
+nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st) {
   // C[M,K] = A[M,N] * B where B(n=k_out, k=n_in) = W[n_in][k_out]: K-outer.
   GemmShape s{dy, w, N, K, M, K, N, N, 1};
   const double es = sizeof(T);
-  ProfScope prof(u ? NC_NAME(T, "gemm_dx_drelusq") : NC_NAME(T, "gemm_dx"), 2.0 * M * N * K,
-                 es * ((double)M * N + (double)N * K + (double)M * K * (u ? 2 : 1)), st);
-  if (u) {
-    EpiDReluSq<T> e{dx, K, u, K, M, K};
-    return launch_gemm<T, kKc, kKo, Identity, Identity>(s, e, st);
+  ProfScope prof(act ? NC_NAME(T, "gemm_dx_drelusq") : NC_NAME(T, "gemm_dx"), 2.0 * M * N * K,
+                 es * ((double)M * N + (double)N * K + (double)M * K * (act ? 2 : 1)), st);
+  if (act) {
+    EpiDReluSq<T> e{dx, K, act, K, M, K};
+    return launch_gemm<T, kKc, kKo>(s, e, st);
   }
   EpiStore<T> e{dx, K, nullptr, 0, M, K};
-  return launch_gemm<T, kKc, kKo, Identity, Identity>(s, e, st);
+  return launch_gemm<T, kKc, kKo>(s, e, st);
 }
 
 template <typename T>
-nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool relu_sq_x, int accumulate,
-                  float* partial, size_t partial_elems, hipStream_t st) {
+nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int accumulate, float* partial,
+                  size_t partial_elems, hipStream_t st) {
   int nsplit, kper;
   dw_split(M, N, K, GemmTile<T>::BK, GemmTile<T>::BM, nsplit, kper);
   // C[N,K] = sum_m dy[m][n] x[m][k]: both operands K-outer (token axis is the reduction).
@@ -79,10 +83,9 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool 
   nc_status r;
   {
     const double es = sizeof(T);
-    ProfScope prof(relu_sq_x ? NC_NAME(T, "gemm_dw_relusq") : NC_NAME(T, "gemm_dw"), 2.0 * M * N * K,
+    ProfScope prof(NC_NAME(T, "gemm_dw"), 2.0 * M * N * K,
                    es * ((double)M * N + (double)M * K) + 4.0 * N * K * (accumulate ? 2 : 1), st);
-    r = relu_sq_x ? launch_gemm<T, kKo, kKo, Identity, ReluSq>(s, e, st)
-                  : launch_gemm<T, kKo, kKo, Identity, Identity>(s, e, st);
+    r = launch_gemm<T, kKo, kKo>(s, e, st);
   }
   if (r != NC_OK || nsplit == 1) return r;
   return splitk_reduce(partial, nsplit, (size_t)N * K, dw, accumulate, st);
@@ -100,15 +103,15 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
                  sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
                  st);
-  EpiSoftcap<T> e{z, N, cap, targets, part, zt, lmhead_tiles(N, is_bf16<T>()), M, N};
-  return launch_gemm<T, kKc, kKc, Identity, Identity>(s, e, st);
+  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, N, cap, targets, part, zt, lmhead_tiles(N, is_bf16<T>()),
+                                                   M, N};
+  return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
 #define NC_INST(T)                                                                                            \
   template nc_status gemm_xwt<T>(const T*, const T*, T*, const T*, int, int, int, bool, hipStream_t);        \
   template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t);               \
-  template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, bool, int, float*, size_t,          \
-                                hipStream_t);                                                                 \
+  template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t); \
   template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, const int32_t*, float*,     \
                                     float*, hipStream_t);
 NC_INST(bf16)

@@ -23,18 +23,20 @@ template <typename T> constexpr bool is_bf16() { return sizeof(T) == 2; }
 #define NC_NAME(T, base) (is_bf16<T>() ? base "_bf16" : base "_f32")
 
 // ------------------------------------------------------------ GEMM (gemm.hip)
-// y[M,N] = x[M,K] W[N,K]^T (+ res[M,N]); relu_sq_x applies max(x,0)^2 to x.
+// y[M,N] = act(x[M,K] W[N,K]^T) (+ res[M,N]); relu_sq_out makes act the
+// ReLU^2 activation max(.,0)^2, else the identity.
 template <typename T>
-nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_x, hipStream_t st);
-// dx[M,K] = dy[M,N] W[N,K]; with u given, dx = (dy W) * 2 max(u,0).
+nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_out,
+                   hipStream_t st);
+// dx[M,K] = dy[M,N] W[N,K]; with act = max(u,0)^2 given, dx = (dy W) * 2 sqrt(act),
+// the input gradient of the ReLU^2 activation.
 template <typename T>
-nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* u, int M, int N, int K, hipStream_t st);
+nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st);
 // dW[N,K] (+)= dy[M,N]^T x[M,K] (float32), split over M when that helps fill
-// the GPU (partials in `partial`, summed in a fixed order); relu_sq_x applies
-// max(x,0)^2 to x.
+// the GPU (partials in `partial`, summed in a fixed order).
 template <typename T>
-nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, bool relu_sq_x, int accumulate,
-                  float* partial, size_t partial_elems, hipStream_t st);
+nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int accumulate, float* partial,
+                  size_t partial_elems, hipStream_t st);
 size_t gemm_dw_partial_elems(int M, int N, int K);
 // Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N];
 // part[M, lmhead_tiles(N)] = per-tile sums of exp(z); zt[m] = z[m][targets[m]].
