@@ -78,6 +78,25 @@ def roofline(table):
                       avg_launch_ms=round(r["ms_per_step"] / r["launches_per_step"], 4))
 
 
+def measured_traffic(scope):
+    """HBM bytes per launch of `scope` from the committed counter summary
+    (profiles/*_traffic.json), or None if there is none for it or the kernel
+    sources changed since the counters were taken."""
+    import glob
+    from dense_pretraining_amd.profiling import source_hash
+
+    h = None
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))):
+        with open(f) as fh:
+            rec = json.load(fh)
+        if rec.get("scope") != scope:
+            continue
+        h = h or source_hash()
+        if rec.get("source_sha256") == h:
+            return rec["traffic_bytes_per_launch"]
+    return None
+
+
 def cpu_baseline(cfg, p, idx, tg, tokens):
     """The fp64 oracle, untuned, on one sequence of `tokens` positions of the
     same model (all blocks, full vocabulary): tokens per second."""
@@ -107,6 +126,9 @@ def main():
                     help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not record per-kernel HIP events in the timed region")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, copy this many MiB device to device once (a plain copy kernel "
+                         "of known size that calibrates the HBM byte counters of a profiling run)")
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -166,6 +188,13 @@ def main():
     print(f"# timed {a.steps} steps: {ms:.2f} ms/step (wall {wall / a.steps * 1e3:.2f})", file=sys.stderr,
           flush=True)
 
+    if a.copy_mib > 0:
+        src = torch.ones(a.copy_mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     tokens = cfg.batch * cfg.seq_len
     tps = tokens / (ms * 1e-3)
     f_causal = C.flops_per_token(cfg, "causal")
@@ -191,6 +220,8 @@ def main():
     if timing:
         table = kernel_table(lib.profile_summary(), a.steps)
         name, rl = roofline(table)
+        tb = measured_traffic(name)
+        rl["traffic"] = None if tb is None else round(tb)
         out["roofline"] = rl
         out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
                               if kk in ("ms_per_step", "launches_per_step", "tflops", "gbps")}

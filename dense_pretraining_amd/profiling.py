@@ -1,0 +1,174 @@
+"""Summaries of rocprofv3 output for the kernels of the training step.
+
+Two jobs, both reading the CSV files rocprofv3 writes with
+``--output-format csv``:
+
+* ``stats``: the ``*_kernel_stats.csv`` of a ``--kernel-trace --stats`` run
+  as a markdown table (calls, total and average time per kernel), with the
+  average launch time of one kernel checked against what bench.py measured
+  with HIP events in the same run.
+* ``traffic``: HBM bytes per launch of one kernel from two ``--pmc`` runs
+  (``FETCH_SIZE``, then ``WRITE_SIZE``, both in KiB per dispatch). Each
+  counter is first scaled by what it reads for a plain device copy of known
+  size in the same process (bench.py ``--copy-mib``), so that the figure is in
+  the copy's bytes. The result goes to a JSON file that records a hash of the
+  kernel sources; bench.py reports the figure only while that hash matches.
+
+Usage (paths are those rocprofv3 wrote):
+
+    python -m dense_pretraining_amd.profiling stats STATS_CSV --steps N \
+        --bench-log LOG --kernel REGEX --title TEXT --command TEXT > summary.md
+    python -m dense_pretraining_amd.profiling traffic --fetch CSV --write CSV \
+        --kernel REGEX --scope NAME --copy-mib MIB --command TEXT --out profiles/x.json
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and headers of the library, in name order."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(f"none of {names} in {sorted(row)}")
+
+
+def stats_table(path, steps, kernel=None, bench_ms=None, top=25):
+    rows = _rows(path)
+    out = []
+    total = 0.0
+    recs = []
+    for r in rows:
+        name = _col(r, "Name", "KernelName", "Kernel_Name")
+        calls = int(float(_col(r, "Calls")))
+        tot_ns = float(_col(r, "TotalDurationNs", "Total_Duration_Ns"))
+        recs.append((name, calls, tot_ns))
+        total += tot_ns
+    recs.sort(key=lambda t: -t[2])
+    out.append("| kernel | calls | total ms | avg us | % |")
+    out.append("|---|---:|---:|---:|---:|")
+    for name, calls, tot in recs[:top]:
+        out.append(f"| `{name}` | {calls} | {tot / 1e6:.2f} | {tot / calls / 1e3:.1f} | {100 * tot / total:.2f} |")
+    out.append("")
+    out.append(f"Sum of all kernels: {total / 1e6:.1f} ms over {steps} steps = {total / 1e6 / steps:.1f} ms/step.")
+    if kernel:
+        rx = re.compile(kernel)
+        hit = [(n, c, t) for n, c, t in recs if rx.search(n)]
+        if hit:
+            calls = sum(c for _, c, _ in hit)
+            tot = sum(t for _, _, t in hit)
+            line = (f"Dominant kernel (`{kernel}`): {calls} launches, average {tot / calls / 1e6:.4f} ms "
+                    f"per launch under rocprofv3")
+            if bench_ms is not None:
+                line += (f"; HIP events in bench.py, same run: {bench_ms:.4f} ms "
+                         f"({100 * (bench_ms / (tot / calls / 1e6) - 1):+.1f} %)")
+            out.append("")
+            out.append(line + ".")
+    return "\n".join(out)
+
+
+def counter_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, value)} for one counter."""
+    res = {}
+    for r in _rows(path):
+        if _col(r, "Counter_Name", "CounterName") != counter:
+            continue
+        did = int(float(_col(r, "Dispatch_Id", "DispatchId")))
+        name = _col(r, "Kernel_Name", "KernelName")
+        val = float(_col(r, "Counter_Value", "CounterValue"))
+        prev = res.get(did)
+        res[did] = (name, val + (prev[1] if prev else 0.0))
+    return res
+
+
+def scaled_counter(path, counter, kernel_rx, copy_bytes):
+    """Mean per-launch value of `counter` (KiB) for kernels matching
+    kernel_rx, in bytes, scaled by copy_bytes / (counter of the copy)."""
+    disp = counter_per_dispatch(path, counter)
+    rx = re.compile(kernel_rx)
+    vals = [v for n, v in disp.values() if rx.search(n)]
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel_rx} with {counter} in {path}")
+    # the copy of bench.py --copy-mib: by far the largest copy kernel the
+    # process dispatches (the others move a few bytes)
+    copies = [v for n, v in disp.values() if "copy" in n.lower() and "_ZN2nc" not in n and "nc::" not in n]
+    if not copies:
+        raise SystemExit(f"no copy kernel dispatch in {path} (run bench.py with --copy-mib)")
+    copy_kib = max(copies)
+    factor = (copy_bytes / 1024.0) / copy_kib
+    return dict(kib_per_launch=sum(vals) / len(vals), launches=len(vals), copy_kib=copy_kib, factor=factor,
+                bytes_per_launch=sum(vals) / len(vals) * 1024.0 * factor)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--steps", type=int, required=True)
+    s.add_argument("--kernel")
+    s.add_argument("--bench-log")
+    s.add_argument("--title", default="Kernel time")
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True, help="regex of the kernel symbol")
+    t.add_argument("--scope", required=True, help="bench.py kernel name the figure belongs to")
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--command", default="")
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+
+    if a.cmd == "stats":
+        bench_ms = None
+        if a.bench_log:
+            for line in open(a.bench_log):
+                if line.startswith("{"):
+                    rl = json.loads(line).get("roofline") or {}
+                    bench_ms = rl.get("avg_launch_ms")
+        print(f"# {a.title}\n")
+        if a.command:
+            print("Command (from /tmp on the MI355X, repository at $GRAFT_REPO_ROOT):\n\n```\n" + a.command + "\n```\n")
+        print(stats_table(a.csv, a.steps, a.kernel, bench_ms))
+        return 0
+
+    copy_bytes = a.copy_mib * 1024 * 1024
+    f = scaled_counter(a.fetch, "FETCH_SIZE", a.kernel, copy_bytes)
+    w = scaled_counter(a.write, "WRITE_SIZE", a.kernel, copy_bytes)
+    res = dict(scope=a.scope, kernel_regex=a.kernel, traffic_bytes_per_launch=f["bytes_per_launch"] + w["bytes_per_launch"],
+               fetch=f, write=w, copy_bytes=copy_bytes, source_sha256=source_hash(), command=a.command)
+    with open(a.out, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
