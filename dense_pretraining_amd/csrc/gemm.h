@@ -528,16 +528,15 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
 
 // ---------------------------------------------------------------- bf16: direct-to-LDS pipeline
 // The bf16 path streams operand tiles straight from HBM into LDS with
-// buffer_load_dwordx4 ... lds (gfx950): no staging registers, so k-tile t+3
-// is fetched while tile t is multiplied (4-stage LDS ring of 256x32 tiles,
-// 128 KB). Each load instruction of a wavefront fills 1 KB of LDS, lane i at
+// buffer_load_dwordx4 ... lds (gfx950): no staging registers, so k-tiles
+// t+1 .. t+4 are fetched while tile t is multiplied (5-stage LDS ring of
+// 256x32 A and B tiles, 160 KB). Each load instruction of a wavefront fills 1 KB of LDS, lane i at
 // byte 16*i; the 16-byte chunks are XOR-swizzled on the way in so that the
 // fragment reads (b128 for K-contiguous, transposing b64 for K-outer tiles)
 // hit distinct banks. Out-of-range lanes get an offset beyond the buffer
 // record, which the hardware turns into zeros: ragged M/N/K need no branch.
 
 constexpr int kDmaBK = 32;
-constexpr int kDmaStages = 4;
 
 __device__ __forceinline__ int dma_swz_row(int r) { return ((r >> 2) & 3) ^ (r & 2); }  // K-contiguous chunks
 __device__ __forceinline__ int dma_swz_k(int k) { return (5 * (k & 3)) & 31; }          // K-outer chunks
@@ -626,82 +625,108 @@ struct DmaTile {
   using OpA = DmaOperand<LA>;
   using OpB = DmaOperand<LB>;
   static constexpr int WTM = 4, WTN = 4;
-  __device__ __forceinline__ static void compute(TileAcc<bf16>& acc, const bf16* ta, const bf16* tb, int wm, int wn,
-                                                 int lane) {
+  // The fragments of one 16-deep half of a stage.
+  struct Frags {
+    Frag<bf16> a[WTM], b[WTN];
+  };
+  __device__ __forceinline__ static void load(Frags& f, const bf16* ta, const bf16* tb, int kk, int wm, int wn,
+                                              int lane) {
 #pragma unroll
-    for (int kk = 0; kk < kDmaBK; kk += 16) {
-      Frag<bf16> fa[WTM], fb[WTN];
+    for (int i = 0; i < WTM; ++i) f.a[i] = OpA::frag(ta, wm + 32 * i, kk, lane);
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) fa[i] = OpA::frag(ta, wm + 32 * i, kk, lane);
+    for (int j = 0; j < WTN; ++j) f.b[j] = OpB::frag(tb, wn + 32 * j, kk, lane);
+  }
+  __device__ __forceinline__ static void mma(TileAcc<bf16>& acc, const Frags& f) {
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) fb[j] = OpB::frag(tb, wn + 32 * j, kk, lane);
+    for (int i = 0; i < WTM; ++i)
 #pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) mfma32(acc.c[i][j], fb[j], fa[i]);
-    }
+      for (int j = 0; j < WTN; ++j) mfma32(acc.c[i][j], f.b[j], f.a[i]);
   }
 };
 
-// One step of the ring: wait for tile t (stage S), then refill stage
-// (S+3)%4 with tile t+3 and multiply stage S. Each stage is its own LDS
-// array so that the compiler can tell the DMA writes from the reads. The
-// main loop runs four steps per trip while every load and wait is uniform
-// (no branches, so the accumulators stay in AGPRs); the last tiles go
-// through the same steps with their conditions.
-#define NC_DMA_STEP_FULL(t, SA, SB, NA, NB)                 \
+// One step of the ring, for tile t in stage S (its first half already in
+// registers, f0): read the second half (f1) while multiplying f0; wait until
+// tile t+1 has landed and every wave is done with stage S; refill S with
+// tile t+4; read the first half of tile t+1 (next stage N) while multiplying
+// f1. No multiply waits for a fragment read issued just before it, and with
+// one wavefront per SIMD that is what keeps the matrix core busy. Each stage
+// is its own LDS array so that the compiler can tell the DMA writes from the
+// reads. Loads past the end of K read zeros, so every step is the same and
+// the main loop (four steps per trip, fixed stage names) has no branch.
+// The scheduler is told to put one read after each multiply: the reads of a
+// half stay ahead of the multiplies that need them (it would otherwise pull
+// those forward), and no more than a few reads are ever waited on at once.
+#define NC_DMA_STEP(t, SA, SB, NA, NB)                      \
   {                                                         \
-    ring_barrier<16>();                                     \
-    opa.issue(NA, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
-    opb.issue(NB, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
-    Tile::compute(acc, SA, SB, wm, wn, lane);               \
+    Tile::load(f1, SA, SB, 16, wm, wn, lane);               \
+    Tile::mma(acc, f0);                                     \
+    interleave_reads_with_mfma<false>();                    \
+    ring_barrier<24>();                                     \
+    opa.issue(SA, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
+    opb.issue(SB, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
+    Tile::load(f0, NA, NB, 0, wm, wn, lane);                \
+    Tile::mma(acc, f1);                                     \
+    interleave_reads_with_mfma<true>();                     \
   }
-#define NC_DMA_STEP_TAIL(t, SA, SB, NA, NB)                   \
-  if ((t) < nk) {                                             \
-    const int ahead_ = nk - 1 - (t);                          \
-    if (ahead_ >= 2) ring_barrier<16>();                      \
-    else if (ahead_ == 1) ring_barrier<8>();                  \
-    else ring_barrier<0>();                                   \
-    if ((t) + 3 < nk) {                                       \
-      opa.issue(NA, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
-      opb.issue(NB, kbeg + ((t) + 3) * kDmaBK, kend, wave);   \
-    }                                                         \
-    Tile::compute(acc, SA, SB, wm, wn, lane);                 \
+
+// Schedule the code since the last scheduling barrier as one fragment read
+// (and, after a ring barrier, one of the 8 tile loads) after each multiply
+// (16 multiplies, at most 16 reads), then fence it off: a wave never stops
+// issuing multiplies to push a burst of loads through the address unit.
+template <bool WithLoads>
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    if (WithLoads && i < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one tile load
   }
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // The whole ring in one inlined function whose stage arrays are __restrict__
 // parameters: every LDS access inside then carries alias-scope information,
 // which lets the compiler see that the reads of one stage do not depend on
 // the loads still streaming into the others (it would otherwise drain them).
+// Five 32 KB stages fill the 160 KB of LDS: tiles t+1 .. t+4 are in flight
+// while tile t is multiplied (about 2 us of lookahead at the clock the
+// matrix cores sustain), enough to ride out the operand fetches that miss L2.
 template <typename Tile>
 __device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA& opa, typename Tile::OpB& opb,
                                          bf16* __restrict__ sa0, bf16* __restrict__ sa1, bf16* __restrict__ sa2,
-                                         bf16* __restrict__ sa3, bf16* __restrict__ sb0, bf16* __restrict__ sb1,
-                                         bf16* __restrict__ sb2, bf16* __restrict__ sb3, int nk, int kbeg, int kend,
-                                         int wave, int wm, int wn, int lane) {
+                                         bf16* __restrict__ sa3, bf16* __restrict__ sa4, bf16* __restrict__ sb0,
+                                         bf16* __restrict__ sb1, bf16* __restrict__ sb2, bf16* __restrict__ sb3,
+                                         bf16* __restrict__ sb4, int nk, int kbeg, int kend, int wave, int wm, int wn,
+                                         int lane) {
   constexpr int BK = kDmaBK;
-  // unconditional: a tile beyond kend just loads zeros (keeps the compiler's
-  // per-stage bookkeeping exact at the loop entry)
+  typename Tile::Frags f0, f1;
   opa.issue(sa0, kbeg, kend, wave);
   opb.issue(sb0, kbeg, kend, wave);
   opa.issue(sa1, kbeg + BK, kend, wave);
   opb.issue(sb1, kbeg + BK, kend, wave);
   opa.issue(sa2, kbeg + 2 * BK, kend, wave);
   opb.issue(sb2, kbeg + 2 * BK, kend, wave);
+  opa.issue(sa3, kbeg + 3 * BK, kend, wave);
+  opb.issue(sb3, kbeg + 3 * BK, kend, wave);
+  opa.issue(sa4, kbeg + 4 * BK, kend, wave);
+  opb.issue(sb4, kbeg + 4 * BK, kend, wave);
+  ring_barrier<32>();  // tile 0 has landed
+  Tile::load(f0, sa0, sb0, 0, wm, wn, lane);
   int kt = 0;
-  for (; kt + 7 <= nk; kt += 4) {
-    NC_DMA_STEP_FULL(kt, sa0, sb0, sa3, sb3);
-    NC_DMA_STEP_FULL(kt + 1, sa1, sb1, sa0, sb0);
-    NC_DMA_STEP_FULL(kt + 2, sa2, sb2, sa1, sb1);
-    NC_DMA_STEP_FULL(kt + 3, sa3, sb3, sa2, sb2);
+  for (; kt + 5 <= nk; kt += 5) {
+    NC_DMA_STEP(kt, sa0, sb0, sa1, sb1);
+    NC_DMA_STEP(kt + 1, sa1, sb1, sa2, sb2);
+    NC_DMA_STEP(kt + 2, sa2, sb2, sa3, sb3);
+    NC_DMA_STEP(kt + 3, sa3, sb3, sa4, sb4);
+    NC_DMA_STEP(kt + 4, sa4, sb4, sa0, sb0);
   }
-  // at most 6 tiles left; kt is a multiple of 4, so tile kt sits in stage 0
-  NC_DMA_STEP_TAIL(kt, sa0, sb0, sa3, sb3);
-  NC_DMA_STEP_TAIL(kt + 1, sa1, sb1, sa0, sb0);
-  NC_DMA_STEP_TAIL(kt + 2, sa2, sb2, sa1, sb1);
-  NC_DMA_STEP_TAIL(kt + 3, sa3, sb3, sa2, sb2);
-  NC_DMA_STEP_TAIL(kt + 4, sa0, sb0, sa3, sb3);
-  NC_DMA_STEP_TAIL(kt + 5, sa1, sb1, sa0, sb0);
+  // kt is a multiple of 5, so tile kt sits in stage 0
+  if (kt < nk) NC_DMA_STEP(kt, sa0, sb0, sa1, sb1);
+  if (kt + 1 < nk) NC_DMA_STEP(kt + 1, sa1, sb1, sa2, sb2);
+  if (kt + 2 < nk) NC_DMA_STEP(kt + 2, sa2, sb2, sa3, sb3);
+  if (kt + 3 < nk) NC_DMA_STEP(kt + 3, sa3, sb3, sa4, sb4);
+  // the refills past the end are still landing in the stages the epilogue reuses
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));
 }
 
 template <int LA, int LB, typename Epi>
@@ -709,8 +734,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   constexpr int BM = 256, BN = 256, BK = kDmaBK;
   using Tile = DmaTile<LA, LB>;
   constexpr int E = Tile::OpA::ELEMS;
-  __shared__ __align__(1024) bf16 sa0[E], sa1[E], sa2[E], sa3[E];
-  __shared__ __align__(1024) bf16 sb0[E], sb1[E], sb2[E], sb3[E];
+  __shared__ __align__(1024) bf16 sa0[E], sa1[E], sa2[E], sa3[E], sa4[E];
+  __shared__ __align__(1024) bf16 sb0[E], sb1[E], sb2[E], sb3[E], sb4[E];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -735,7 +760,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   typename Tile::OpB opb;
   opa.init(static_cast<const bf16*>(s.A), s.lda, m0, s.M, wave, lane);
   opb.init(static_cast<const bf16*>(s.B), s.ldb, n0, s.N, wave, lane);
-  dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3, nk, kbeg, kend, wave, wm, wn, lane);
+  dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sa4, sb0, sb1, sb2, sb3, sb4, nk, kbeg, kend, wave, wm, wn,
+                 lane);
   __syncthreads();
   // the A stages become the waves' 32 x 128 float32 slabs, B stage 0 the row-sum scratch
   static_assert(E * sizeof(bf16) == 32 * 128 * sizeof(float), "one A stage holds one slab");
@@ -744,8 +770,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   staged_epilogue<4, 4>(acc.c, epi, x, reinterpret_cast<float*>(slab));
   epi.finish(x);
 }
-#undef NC_DMA_STEP_FULL
-#undef NC_DMA_STEP_TAIL
+#undef NC_DMA_STEP
 
 
 // ---------------------------------------------------------------- launcher
