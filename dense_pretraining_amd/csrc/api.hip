@@ -45,6 +45,9 @@ nc_status make_dims(const nc_config* c, Dims* o, bool need_depth) {
   if (qkv * c->d_model > 0x7fffffffL || (long)c->d_ff * c->d_model > 0x7fffffffL ||
       (long)c->vocab * c->d_model > 0x7fffffffL || M * c->d_ff > 0x7fffffffL || M * qkv > 0x7fffffffL)
     return NC_ERR_UNSUPPORTED;
+  // a weight-gradient tile of the unembedding spans 8 logit panels of M * kPanel
+  // elements, addressed with 32-bit byte offsets
+  if (M * kPanel * 8 * 2 > 0x7fffffffL) return NC_ERR_UNSUPPORTED;
   o->M = M;
   o->B = c->batch;
   o->T = c->seq_len;
@@ -146,7 +149,7 @@ HeadSaved<T> carve_head_saved(Carver& c, const Dims& m) {
   HeadSaved<T> s;
   s.xf = c.take<T>(m.M * m.d);
   s.rf = c.take<float>(m.M);
-  s.z = c.take<T>((size_t)m.M * m.V);
+  s.z = c.take<T>(logit_elems(m.M, m.V));  // column panels of kPanel
   s.lse = c.take<float>(m.M);
   s.zt = c.take<float>(m.M);
   s.nv = c.take<int>(1);
@@ -309,8 +312,8 @@ nc_status head_bwd_t(const Dims& m, const T* wlm, const int32_t* tg, const HeadS
                      float* dwlm, int acc, const HeadScratch<T>& c, hipStream_t st) {
   const int M = (int)m.M;
   NC_TRY(xent_dz<T>(s.z, M, m.V, s.lse, tg, s.nv, dloss, m.cap, st));
-  NC_TRY(gemm_dyw<T>(s.z, wlm, c.dxf, nullptr, M, m.V, m.d, st));
-  NC_TRY(gemm_dw<T>(s.z, s.xf, dwlm, M, m.V, m.d, acc, c.partial, c.partial_elems, st));
+  NC_TRY(gemm_dyw<T>(s.z, wlm, c.dxf, nullptr, M, m.V, m.d, st, (long)M * kPanel));
+  NC_TRY(gemm_dw<T>(s.z, s.xf, dwlm, M, m.V, m.d, acc, c.partial, c.partial_elems, st, (long)M * kPanel));
   NC_TRY(rmsnorm_bwd<T, T>(c.dxf, s.xf, s.rf, nullptr, dx, M, m.d, st));
   return NC_OK;
 }

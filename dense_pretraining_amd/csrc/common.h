@@ -80,6 +80,14 @@ __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bits) {
   if (status) atomicOr(status, bits);
 }
 
+// The unembedding logits (and their gradient, written in place) are stored in
+// column panels of kPanel: element (m, v) of the [M, V] matrix at
+// (v / kPanel) * M * kPanel + m * kPanel + v % kPanel. A k-tile of the input-grad
+// GEMM (k = v) is then one contiguous block, instead of 64-byte pieces of rows
+// that lie V * 2 bytes apart.
+constexpr int kPanel = 32;
+inline size_t logit_elems(long M, long V) { return (size_t)M * (size_t)((V + kPanel - 1) / kPanel * kPanel); }
+
 // ---------------------------------------------------------------- direct-to-LDS loads
 // buffer_load_* ... lds (gfx950) writes lane i's data at the LDS address in
 // M0 plus i times the access size, whatever the source address. A buffer

@@ -46,6 +46,10 @@ struct GemmShape {
   int M, N, K;
   int k_split;  // K range handled by one split (multiple of BK), K if unsplit
   int n_split;
+  // A in column panels of kPanel (the unembedding logits): element (r, c) of
+  // the stored [R, C] matrix at (c / kPanel) * a_panel + r * kPanel + c % kPanel;
+  // 0 = plain row-major with stride lda.
+  long a_panel = 0;
 };
 
 // ---------------------------------------------------------------- tile walk
@@ -141,7 +145,7 @@ struct OperandLoader {
   uint4 r[NLOAD];
 
   __device__ __forceinline__ void load(const T* __restrict__ g, long ld, int row0, int nrows, int k0, int kend,
-                                       int tid) {
+                                       int tid, long panel) {
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
       const int v = tid + 256 * i;
@@ -149,14 +153,14 @@ struct OperandLoader {
         constexpr int VPR = BK / VE;
         const int row = v / VPR, kv = v % VPR;
         const int gr = row0 + row, gk = k0 + kv * VE;
-        r[i] = (gr < nrows && gk < kend) ? *reinterpret_cast<const uint4*>(g + (long)gr * ld + gk)
-                                         : make_uint4(0, 0, 0, 0);
+        const long a = panel ? (long)(gk / kPanel) * panel + (long)gr * kPanel + gk % kPanel : (long)gr * ld + gk;
+        r[i] = (gr < nrows && gk < kend) ? *reinterpret_cast<const uint4*>(g + a) : make_uint4(0, 0, 0, 0);
       } else {
         constexpr int VPL = ROWS / VE;
         const int kl = v / VPL, rv = v % VPL;
         const int gk = k0 + kl, gr = row0 + rv * VE;
-        r[i] = (gk < kend && gr < nrows) ? *reinterpret_cast<const uint4*>(g + (long)gk * ld + gr)
-                                         : make_uint4(0, 0, 0, 0);
+        const long a = panel ? (long)(gr / kPanel) * panel + (long)gk * kPanel + gr % kPanel : (long)gk * ld + gr;
+        r[i] = (gk < kend && gr < nrows) ? *reinterpret_cast<const uint4*>(g + a) : make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -399,8 +403,8 @@ struct EpiF32 {
 // hardware exp2 and reciprocal: c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
 template <typename T, int BM, int BN>
 struct EpiSoftcap {
-  T* Z;
-  long ldz;
+  T* Z;         // [M, N] in column panels of kPanel
+  long zpanel;  // panel stride (elements): M * kPanel
   float cap;
   const int32_t* targets;
   float* part;
@@ -438,7 +442,7 @@ struct EpiSoftcap {
   using Aux = NoAux;
   __device__ __forceinline__ Aux load_aux(int, int) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux&) const {
-    if (row < M && col < N) store4<T>(Z + (long)row * ldz + col, v);
+    if (row < M && col < N) store4<T>(Z + (long)(col / kPanel) * zpanel + (long)row * kPanel + col % kPanel, v);
   }
   __device__ __forceinline__ void finish(const EpiCtx& x) const {
     __syncthreads();
@@ -484,8 +488,8 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   const int kl = 8 * (lane >> 5);  // this lane's k offset inside a 16-deep step
 
   if (nk > 0) {
-    la.load(A, s.lda, m0, s.M, kbeg, kend, tid);
-    lb.load(B, s.ldb, n0, s.N, kbeg, kend, tid);
+    la.load(A, s.lda, m0, s.M, kbeg, kend, tid, s.a_panel);
+    lb.load(B, s.ldb, n0, s.N, kbeg, kend, tid, 0);
     la.store(smem[0], tid);
     lb.store(smem[0] + LoadA::SIZE, tid);
   }
@@ -494,8 +498,8 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
     if (more) {
-      la.load(A, s.lda, m0, s.M, kbeg + (kt + 1) * BK, kend, tid);
-      lb.load(B, s.ldb, n0, s.N, kbeg + (kt + 1) * BK, kend, tid);
+      la.load(A, s.lda, m0, s.M, kbeg + (kt + 1) * BK, kend, tid, s.a_panel);
+      lb.load(B, s.ldb, n0, s.N, kbeg + (kt + 1) * BK, kend, tid, 0);
     }
     const T* sa = smem[kt & 1];
     const T* sb = sa + LoadA::SIZE;
@@ -552,25 +556,32 @@ struct DmaOperand {
   int kpos[4];  // k of each load inside the tile (for the ragged last tile)
   const bf16* g;
   long ld;
+  long panel;  // column-panel stride (elements) of a panelled operand, else 0
   int row0;
 
-  __device__ __forceinline__ void init(const bf16* g_, long ld_, int row0_, int nrows, int wave, int lane) {
+  __device__ __forceinline__ void init(const bf16* g_, long ld_, int row0_, int nrows, int wave, int lane,
+                                       long panel_) {
     g = g_;
     ld = ld_;
+    panel = panel_;
     row0 = row0_;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = 4 * wave + q;
       if constexpr (Layout == kKc) {
+        // a k-tile of a panelled operand lies inside one panel: rows kPanel apart
+        const long rs = panel ? kPanel : ld;
         const int row = 16 * c + (lane >> 2);  // 1 KB chunk = 16 rows of 32 k
         const int kc = (lane & 3) ^ dma_swz_row(row);
         kpos[q] = 8 * kc;
-        off[q] = row0 + row < nrows ? (unsigned)(((long)row * ld + 8 * kc) * 2) : kDmaOOB;
+        off[q] = row0 + row < nrows ? (unsigned)(((long)row * rs + 8 * kc) * 2) : kDmaOOB;
       } else {
         const int kl = 2 * c + (lane >> 5);  // 1 KB chunk = 2 k lines of 256 rows
         const int rc = (lane & 31) ^ dma_swz_k(kl);
         kpos[q] = kl;
-        off[q] = row0 + 8 * rc < nrows ? (unsigned)(((long)kl * ld + 8 * rc) * 2) : kDmaOOB;
+        // panelled: the 8 columns of chunk rc sit in panel rc / 4 of the tile
+        const long o = panel ? (long)(rc >> 2) * panel + (long)kl * kPanel + 8 * (rc & 3) : (long)kl * ld + 8 * rc;
+        off[q] = row0 + 8 * rc < nrows ? (unsigned)(o * 2) : kDmaOOB;
       }
     }
   }
@@ -578,15 +589,18 @@ struct DmaOperand {
   __device__ __forceinline__ void issue(bf16* lds, int k0, int kend, int wave) const {
     const bool full = k0 + kDmaBK <= kend;
     if constexpr (Layout == kKc) {
-      __amdgpu_buffer_rsrc_t rs = dma_rsrc(g + (long)row0 * ld);
+      // plain: the k advance goes into soffset; panelled: into the record base
+      __amdgpu_buffer_rsrc_t rs = dma_rsrc(panel ? g + (long)(k0 / kPanel) * panel + (long)row0 * kPanel
+                                                 : g + (long)row0 * ld);
+      const unsigned so = panel ? 0u : (unsigned)(k0 * 2);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const unsigned o = (full || k0 + kpos[q] < kend) ? off[q] : kDmaOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * (4 * wave + q)), 16, o,
-                                                 (unsigned)(k0 * 2), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * (4 * wave + q)), 16, o, so, 0, 0);
       }
     } else {
-      __amdgpu_buffer_rsrc_t rs = dma_rsrc(g + (long)k0 * ld + row0);
+      __amdgpu_buffer_rsrc_t rs = dma_rsrc(panel ? g + (long)(row0 / kPanel) * panel + (long)k0 * kPanel
+                                                 : g + (long)k0 * ld + row0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const unsigned o = (full || k0 + kpos[q] < kend) ? off[q] : kDmaOOB;
@@ -758,8 +772,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
 
   typename Tile::OpA opa;
   typename Tile::OpB opb;
-  opa.init(static_cast<const bf16*>(s.A), s.lda, m0, s.M, wave, lane);
-  opb.init(static_cast<const bf16*>(s.B), s.ldb, n0, s.N, wave, lane);
+  opa.init(static_cast<const bf16*>(s.A), s.lda, m0, s.M, wave, lane, s.a_panel);
+  opb.init(static_cast<const bf16*>(s.B), s.ldb, n0, s.N, wave, lane, 0);
   dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sa4, sb0, sb1, sb2, sb3, sb4, nk, kbeg, kend, wave, wm, wn,
                  lane);
   __syncthreads();

@@ -45,9 +45,11 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
 }
 
 template <typename T>
-nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st) {
+nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
+                   long dy_panel) {
   // C[M,K] = A[M,N] * B where B(n=k_out, k=n_in) = W[n_in][k_out]: K-outer.
   GemmShape s{dy, w, N, K, M, K, N, N, 1};
+  s.a_panel = dy_panel;
   const double es = sizeof(T);
   ProfScope prof(act ? NC_NAME(T, "gemm_dx_drelusq") : NC_NAME(T, "gemm_dx"), 2.0 * M * N * K,
                  es * ((double)M * N + (double)N * K + (double)M * K * (act ? 2 : 1)), st);
@@ -61,11 +63,12 @@ nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, i
 
 template <typename T>
 nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int accumulate, float* partial,
-                  size_t partial_elems, hipStream_t st) {
+                  size_t partial_elems, hipStream_t st, long dy_panel) {
   int nsplit, kper;
   dw_split(M, N, K, GemmTile<T>::BK, GemmTile<T>::BM, nsplit, kper);
   // C[N,K] = sum_m dy[m][n] x[m][k]: both operands K-outer (token axis is the reduction).
   GemmShape s{dy, x, N, K, N, K, M, kper, nsplit};
+  s.a_panel = dy_panel;
   if (nsplit > 1 && (partial == nullptr || partial_elems < (size_t)nsplit * N * K)) return NC_ERR_WORKSPACE;
   EpiF32 e;
   e.ldc = K;
@@ -103,15 +106,16 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
                  sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
                  st);
-  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, N, cap, targets, part, zt, lmhead_tiles(N, is_bf16<T>()),
+  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, (long)M * kPanel, cap, targets, part, zt, lmhead_tiles(N, is_bf16<T>()),
                                                    M, N};
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
 #define NC_INST(T)                                                                                            \
   template nc_status gemm_xwt<T>(const T*, const T*, T*, const T*, int, int, int, bool, hipStream_t);        \
-  template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t);               \
-  template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t); \
+  template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t, long);         \
+  template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t,  \
+                                long);                                                                        \
   template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, const int32_t*, float*,     \
                                     float*, hipStream_t);
 NC_INST(bf16)

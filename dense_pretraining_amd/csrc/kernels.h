@@ -30,15 +30,17 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
                    hipStream_t st);
 // dx[M,K] = dy[M,N] W[N,K]; with act = max(u,0)^2 given, dx = (dy W) * 2 sqrt(act),
 // the input gradient of the ReLU^2 activation.
+// dy_panel: dy stored in column panels (stride dy_panel elements), else 0.
 template <typename T>
-nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st);
+nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
+                   long dy_panel = 0);
 // dW[N,K] (+)= dy[M,N]^T x[M,K] (float32), split over M when that helps fill
 // the GPU (partials in `partial`, summed in a fixed order).
 template <typename T>
 nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int accumulate, float* partial,
-                  size_t partial_elems, hipStream_t st);
+                  size_t partial_elems, hipStream_t st, long dy_panel = 0);
 size_t gemm_dw_partial_elems(int M, int N, int K);
-// Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N];
+// Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N] in column panels;
 // part[M, lmhead_tiles(N)] = per-tile sums of exp(z); zt[m] = z[m][targets[m]].
 template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,

@@ -277,32 +277,35 @@ __global__ void __launch_bounds__(256) xent_final_kernel(const float* __restrict
   }
 }
 
-// dz = (softmax(z') - onehot(y)) * dloss / Nv * (1 - (z'/c)^2), in place.
+// dz = (softmax(z') - onehot(y)) * dloss / Nv * (1 - (z'/c)^2), in place, over
+// the column-panel layout of the logits: block (x, p) covers rows
+// [x * ROWS, (x+1) * ROWS) of panel p, each thread one 16-byte piece.
 template <typename T>
 __global__ void __launch_bounds__(256) xent_dz_kernel(T* __restrict__ z, int M, int V, const float* __restrict__ lse,
                                                       const int32_t* __restrict__ tg, const int* __restrict__ nvp,
                                                       float dloss, float inv_cap) {
   constexpr int VE = Vec<T>::n;
-  const int m = blockIdx.x;
+  constexpr int PER_ROW = kPanel / VE;  // pieces per panel row
+  constexpr int ROWS = 256 / PER_ROW;
+  const int p = blockIdx.y;
+  const int m = blockIdx.x * ROWS + threadIdx.x / PER_ROW;
+  const int v0 = p * kPanel + (threadIdx.x % PER_ROW) * VE;
+  if (m >= M || v0 >= V) return;  // V % VE == 0: a piece is wholly inside or outside
   const int y = tg[m];
   const bool valid = y >= 0 && y < V;
-  const int nv = *nvp;
-  const float gsc = valid ? dloss / (float)nv : 0.f;
+  const float gsc = valid ? dloss / (float)*nvp : 0.f;
   const float l = lse[m];
-  T* row = z + (long)m * V;
-  const int nvec = V / VE;
-  for (int vi = blockIdx.y * 1024 + threadIdx.x; vi < min(nvec, (int)(blockIdx.y + 1) * 1024); vi += 256) {
-    float v[VE];
-    load16<T>(row + vi * VE, v);
+  T* q = z + (long)p * M * kPanel + (long)m * kPanel + (v0 % kPanel);
+  float v[VE];
+  load16<T>(q, v);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      float p = __expf(v[e] - l);
-      if (vi * VE + e == y) p -= 1.f;
-      float zc = v[e] * inv_cap;
-      v[e] = p * gsc * (1.f - zc * zc);
-    }
-    store16<T>(row + vi * VE, v);
+  for (int e = 0; e < VE; ++e) {
+    float pr = __expf(v[e] - l);
+    if (v0 + e == y) pr -= 1.f;
+    const float zc = v[e] * inv_cap;
+    v[e] = pr * gsc * (1.f - zc * zc);
   }
+  store16<T>(q, v);
 }
 
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int nsplit, size_t n4,
@@ -407,8 +410,8 @@ nc_status xent_loss(const float* part, int ntiles, const float* zt, const int32_
 template <typename T>
 nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, const int* nv, float dloss, float cap,
                   hipStream_t st) {
-  int nvec = V / Vec<T>::n;
-  dim3 grid(M, (nvec + 1023) / 1024);
+  constexpr int ROWS = 256 / (kPanel / Vec<T>::n);
+  dim3 grid((M + ROWS - 1) / ROWS, (V + kPanel - 1) / kPanel);
   ProfScope prof(NC_NAME(T, "xent_dz"), 0, 2.0 * sizeof(T) * M * V + 12.0 * M, st);
   hipLaunchKernelGGL((xent_dz_kernel<T>), grid, dim3(256), 0, st, z, M, V, lse, targets, nv, dloss, 1.f / cap);
   NC_LAUNCH_CHECK("xent_dz");
