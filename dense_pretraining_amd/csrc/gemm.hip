@@ -5,16 +5,23 @@
 namespace nc {
 
 namespace {
-constexpr int kTargetBlocks = 1024;  // ~4 workgroups per CU for the weight-gradient split
+constexpr int kCUs = 256;  // MI355X compute units; one GEMM workgroup fills one
 
 // Number of splits of the reduction (token) axis for a weight gradient, and
-// the rows each split covers (a multiple of the tile depth).
+// the rows each split covers (a multiple of the tile depth). Every split
+// writes a float32 partial tile that is read back once, so the smallest count
+// is taken whose workgroups fill the GPU's rounds (the last round at least 90 %
+// busy), with at most 16 splits of at least 512 rows.
 void dw_split(int M, int N, int K, int bk, int bmn, int& nsplit, int& kper) {
-  long tiles = (long)((N + bmn - 1) / bmn) * ((K + bmn - 1) / bmn);
-  int s = (int)(kTargetBlocks / (tiles > 0 ? tiles : 1));
-  s = s < 1 ? 1 : (s > 16 ? 16 : s);
+  const long tiles = (long)((N + bmn - 1) / bmn) * ((K + bmn - 1) / bmn);
   int maxs = M / 512;
-  if (s > maxs) s = maxs < 1 ? 1 : maxs;
+  maxs = maxs < 1 ? 1 : (maxs > 16 ? 16 : maxs);
+  int s = 1;
+  for (; s < maxs; ++s) {
+    const long blocks = tiles * s;
+    const long rounds = (blocks + kCUs - 1) / kCUs;
+    if (blocks * 10 >= rounds * kCUs * 9) break;
+  }
   kper = ((M + s - 1) / s + bk - 1) / bk * bk;
   nsplit = (M + kper - 1) / kper;
 }
