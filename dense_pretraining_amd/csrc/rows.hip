@@ -144,63 +144,87 @@ __global__ void rope_table_kernel(float* cs, float* sn, int T, int D, float base
 // QK norm (parameter-free RMSNorm over each head's D values) then the
 // rotation. Lane i of a head holds the pair (i, i + D/2), so the rotation is
 // lane-local; D = 64 puts two heads in one wavefront.
-template <typename T>
+// Each (token, head) pair takes D/8 lanes; lane j holds the rotation pairs
+// 4j .. 4j+3, i.e. elements 4j.. of both halves of the head (two 8-byte
+// loads), so the rotation is lane-local and the per-head norm is a reduction
+// over D/8 lanes.
+template <typename T, int D>
 __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(const T* __restrict__ qkv, long ld_in, T* __restrict__ qk,
                                                               long ld_out, const float* __restrict__ cs,
                                                               const float* __restrict__ sn, int M, int Tn, int nheads,
-                                                              int D, float eps) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M) return;
-  const int t = m % Tn, P = D / 2, hpi = 64 / P;
-  const int sub = lane / P, i = lane % P;
-  const float c = cs[t * P + i], s = sn[t * P + i];
-  const T* src = qkv + (long)m * ld_in;
-  T* dst = qk + (long)m * ld_out;
-  for (int h0 = 0; h0 < nheads; h0 += hpi) {
-    const int h = h0 + sub;
-    const bool ok = h < nheads;
-    float a = ok ? to_f32(src[h * D + i]) : 0.f;
-    float b = ok ? to_f32(src[h * D + i + P]) : 0.f;
-    float ss = group_sum(a * a + b * b, P);
-    float rr = 1.f / sqrtf(ss / (float)D + eps);
-    a *= rr;
-    b *= rr;
-    if (ok) {
-      dst[h * D + i] = from_f32<T>(a * c - b * s);
-      dst[h * D + i + P] = from_f32<T>(a * s + b * c);
-    }
+                                                              float eps) {
+  constexpr int P = D / 2, LPH = P / 4, HPB = 256 / LPH;
+  const long pair = (long)blockIdx.x * HPB + threadIdx.x / LPH;
+  const int j = threadIdx.x % LPH;
+  if (pair >= (long)M * nheads) return;  // whole lane groups leave together
+  const int m = (int)(pair / nheads), h = (int)(pair - (long)m * nheads);
+  const int t = m % Tn;
+  const T* src = qkv + (long)m * ld_in + (long)h * D + 4 * j;
+  float a[4], b[4];
+  load4<T>(src, a);
+  load4<T>(src + P, b);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + b[e] * b[e];
+  const float rr = 1.f / sqrtf(group_sum(ss, LPH) / (float)D + eps);
+  const float4 c4 = *reinterpret_cast<const float4*>(cs + (long)t * P + 4 * j);
+  const float4 s4 = *reinterpret_cast<const float4*>(sn + (long)t * P + 4 * j);
+  const float c[4] = {c4.x, c4.y, c4.z, c4.w}, s[4] = {s4.x, s4.y, s4.z, s4.w};
+  float oa[4], ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float ya = a[e] * rr, yb = b[e] * rr;
+    oa[e] = ya * c[e] - yb * s[e];
+    ob[e] = ya * s[e] + yb * c[e];
   }
+  T* dst = qk + (long)m * ld_out + (long)h * D + 4 * j;
+  store4<T>(dst, oa);
+  store4<T>(dst + P, ob);
 }
 
-template <typename T>
+// Backward of the same map, in place on g (the gradient of the rotated,
+// normed heads on entry, of the raw heads on exit).
+template <typename T, int D>
 __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(const T* __restrict__ qkv, long ld_in, T* __restrict__ gr,
                                                               long ld_g, const float* __restrict__ cs,
                                                               const float* __restrict__ sn, int M, int Tn, int nheads,
-                                                              int D, float eps) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M) return;
-  const int t = m % Tn, P = D / 2, hpi = 64 / P;
-  const int sub = lane / P, i = lane % P;
-  const float c = cs[t * P + i], s = sn[t * P + i];
-  const T* src = qkv + (long)m * ld_in;
-  T* g = gr + (long)m * ld_g;
-  for (int h0 = 0; h0 < nheads; h0 += hpi) {
-    const int h = h0 + sub;
-    const bool ok = h < nheads;
-    float a = ok ? to_f32(src[h * D + i]) : 0.f;
-    float b = ok ? to_f32(src[h * D + i + P]) : 0.f;
-    float rr = 1.f / sqrtf(group_sum(a * a + b * b, P) / (float)D + eps);
-    float ya = a * rr, yb = b * rr;
-    float ga = ok ? to_f32(g[h * D + i]) : 0.f;
-    float gb = ok ? to_f32(g[h * D + i + P]) : 0.f;
-    // transpose rotation
-    float ua = ga * c + gb * s, ub = -ga * s + gb * c;
-    float dot = group_sum(ua * ya + ub * yb, P) / (float)D;
-    if (ok) {
-      g[h * D + i] = from_f32<T>(rr * (ua - ya * dot));
-      g[h * D + i + P] = from_f32<T>(rr * (ub - yb * dot));
-    }
+                                                              float eps) {
+  constexpr int P = D / 2, LPH = P / 4, HPB = 256 / LPH;
+  const long pair = (long)blockIdx.x * HPB + threadIdx.x / LPH;
+  const int j = threadIdx.x % LPH;
+  if (pair >= (long)M * nheads) return;
+  const int m = (int)(pair / nheads), h = (int)(pair - (long)m * nheads);
+  const int t = m % Tn;
+  const T* src = qkv + (long)m * ld_in + (long)h * D + 4 * j;
+  T* g = gr + (long)m * ld_g + (long)h * D + 4 * j;
+  float a[4], b[4], ga[4], gb[4];
+  load4<T>(src, a);
+  load4<T>(src + P, b);
+  load4<T>(g, ga);
+  load4<T>(g + P, gb);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + b[e] * b[e];
+  const float rr = 1.f / sqrtf(group_sum(ss, LPH) / (float)D + eps);
+  const float4 c4 = *reinterpret_cast<const float4*>(cs + (long)t * P + 4 * j);
+  const float4 s4 = *reinterpret_cast<const float4*>(sn + (long)t * P + 4 * j);
+  const float c[4] = {c4.x, c4.y, c4.z, c4.w}, s[4] = {s4.x, s4.y, s4.z, s4.w};
+  // transpose rotation, then the norm's backward: rr (u - y <u, y> / D)
+  float ua[4], ub[4], dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ua[e] = ga[e] * c[e] + gb[e] * s[e];
+    ub[e] = -ga[e] * s[e] + gb[e] * c[e];
+    dot += ua[e] * a[e] + ub[e] * b[e];
   }
+  dot = group_sum(dot, LPH) * rr / (float)D;  // <u, y> / D with y = x rr
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ua[e] = rr * (ua[e] - a[e] * rr * dot);
+    ub[e] = rr * (ub[e] - b[e] * rr * dot);
+  }
+  store4<T>(g, ua);
+  store4<T>(g + P, ub);
 }
 
 // ------------------------------------------------------------ cross-entropy
@@ -375,8 +399,15 @@ template <typename T>
 nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const float* cs, const float* sn, int M,
                           int T_, int nheads, int D, float eps, hipStream_t st) {
   ProfScope prof(NC_NAME(T, "qknorm_rope_fwd"), 0, 2.0 * sizeof(T) * M * nheads * D, st);
-  hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, qkv, ld_in, qk, ld_out, cs, sn,
-                     M, T_, nheads, D, eps);
+  const long pairs = (long)M * nheads;
+  if (D == 128)
+    hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, 128>), dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, st, qkv,
+                       ld_in, qk, ld_out, cs, sn, M, T_, nheads, eps);
+  else if (D == 64)
+    hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, 64>), dim3((unsigned)((pairs + 31) / 32)), dim3(256), 0, st, qkv,
+                       ld_in, qk, ld_out, cs, sn, M, T_, nheads, eps);
+  else
+    return NC_ERR_UNSUPPORTED;
   NC_LAUNCH_CHECK("qknorm_rope_fwd");
   return NC_OK;
 }
@@ -385,8 +416,15 @@ template <typename T>
 nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float* cs, const float* sn, int M, int T_,
                           int nheads, int D, float eps, hipStream_t st) {
   ProfScope prof(NC_NAME(T, "qknorm_rope_bwd"), 0, 3.0 * sizeof(T) * M * nheads * D, st);
-  hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, qkv, ld_in, g, ld_g, cs, sn, M,
-                     T_, nheads, D, eps);
+  const long pairs = (long)M * nheads;
+  if (D == 128)
+    hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T, 128>), dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, st, qkv,
+                       ld_in, g, ld_g, cs, sn, M, T_, nheads, eps);
+  else if (D == 64)
+    hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T, 64>), dim3((unsigned)((pairs + 31) / 32)), dim3(256), 0, st, qkv,
+                       ld_in, g, ld_g, cs, sn, M, T_, nheads, eps);
+  else
+    return NC_ERR_UNSUPPORTED;
   NC_LAUNCH_CHECK("qknorm_rope_bwd");
   return NC_OK;
 }
