@@ -88,39 +88,8 @@ template <typename T> __device__ __forceinline__ F8<T> gld8(const T* p, bool ok)
   return pack8<T>(z);
 }
 
-// Operand fragment X[r][k0a..k0a+3 | k0b..k0b+3] for row r = r0 + lane % 16,
-// read from an LDS tile stored k-major (xt[k * LD + r], rows contiguous).
-// bf16 uses the gfx950 transposing LDS read: inside each 16-lane group,
-// source lane j reads 4 consecutive rows at k-row k0 + j/4 and the hardware
-// hands lane i the 4 k values of row r0 + i. Float (check mode) reads the 8
-// values one by one.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-template <typename T> __device__ __forceinline__ F8<T> ld_tr8(const T* xt, int LD, int k0a, int k0b, int r0, int lane);
-template <> __device__ __forceinline__ F8<bf16> ld_tr8<bf16>(const bf16* xt, int LD, int k0a, int k0b, int r0,
-                                                             int lane) {
-  const int j = lane & 15;
-  const int c = r0 + 4 * (j & 3);
-  v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<bf16*>(xt + (k0a + (j >> 2)) * LD + c));
-  v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<bf16*>(xt + (k0b + (j >> 2)) * LD + c));
-  uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
-  uint4 u = make_uint4(ua.x, ua.y, ub.x, ub.y);
-  F8<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, u);
-  return f;
-}
-template <> __device__ __forceinline__ F8<float> ld_tr8<float>(const float* xt, int LD, int k0a, int k0b, int r0,
-                                                               int lane) {
-  const int r = r0 + (lane & 15);
-  F8<float> f;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f.v[s] = xt[(k0a + s) * LD + r];
-    f.v[4 + s] = xt[(k0b + s) * LD + r];
-  }
-  return f;
-}
 
 // 2^x with the bare hardware instruction. Every argument here lies in
 // [-2 sqrt(D) log2(e) - log2(T), 1], far from the range where the library
@@ -138,355 +107,6 @@ struct DivN {
     return x;
   }
 };
-
-// ------------------------------------------------------------ tile staging
-// Row-major tile [ROWS][D] -> LDS [ROWS][LD]; the row addresses come from a
-// function (nullptr = zero row).
-template <typename T, int ROWS, int D>
-struct RowTile {
-  static constexpr int VE = 16 / sizeof(T);
-  static constexpr int LD = D + VE;
-  static constexpr int N = ROWS * D / VE;
-  static constexpr int PER = (N + 255) / 256;
-  uint4 r[PER];
-  template <typename AddrF>
-  __device__ __forceinline__ void load(AddrF addr, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int u = tid + 256 * i;
-      r[i] = make_uint4(0, 0, 0, 0);
-      if (u < N) {
-        int row = u / (D / VE), c = u % (D / VE);
-        const T* p = addr(row);
-        if (p) r[i] = *reinterpret_cast<const uint4*>(p + c * VE);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(T* s, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int u = tid + 256 * i;
-      if (u < N) {
-        int row = u / (D / VE), c = u % (D / VE);
-        *reinterpret_cast<uint4*>(s + row * LD + c * VE) = r[i];
-      }
-    }
-  }
-};
-
-// Key index held in accumulator slot v by lane half lh (C layout of a 32x32
-// MFMA: rows 8*(v/4) + 4*lh + v%4).
-__device__ __forceinline__ int crow(int v, int lh) { return 8 * (v >> 2) + 4 * lh + (v & 3); }
-
-struct AttnGeom {
-  int B, T, H, G, D, n_rep;
-  long ld_qk, ld_v, ld_o, ld_dq;
-  int q_off_k;  // column of K head 0 inside the qk rows (H*D)
-  float inv_rep;
-};
-
-// ============================================================ forward
-template <typename T, int D>
-__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* __restrict__ qk,
-                                                          const T* __restrict__ vsrc, T* __restrict__ o,
-                                                          float* __restrict__ lse) {
-  constexpr int BKV = 64;
-  using KT = RowTile<T, BKV, D>;
-  constexpr int LD = KT::LD;
-  __shared__ __align__(16) T ks[2][BKV * LD];
-  __shared__ __align__(16) T vs[2][BKV * LD];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lh = lane >> 5, l32 = lane & 31;
-  const int g16 = (lane >> 4) & 1;
-  const int nrows = g.T * g.n_rep;
-  const int nqb = (nrows + 127) / 128;
-  const int per = g.G * g.B;
-  const int qb = nqb - 1 - (int)(blockIdx.x / per);  // longest query blocks first
-  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
-  const int R0 = qb * 128;
-  const long tok0 = (long)b * g.T;
-  const DivN dv{g.n_rep, g.inv_rep};
-
-  const int rq = R0 + 32 * wave + l32;
-  const bool qok = rq < nrows;
-  const int tq = qok ? dv.q(rq) : 0;
-  const int hq = kvh * g.n_rep + (qok ? rq - tq * g.n_rep : 0);
-  const int w_last = min(nrows - 1, R0 + 32 * wave + 31);
-  const int t_wmax = dv.q(w_last);
-  const int t_wmin = dv.q(min(nrows - 1, R0 + 32 * wave));
-  const bool wfull = R0 + 32 * wave + 31 < nrows;
-  const int t_bmax = dv.q(min(nrows - 1, R0 + 127));
-  const int nkt = t_bmax / BKV + 1;
-
-  // Q as the B operand of S^T = K Q^T: lane holds d = 16*s + 8*lh + (0..7) of its query.
-  F8<T> qf[D / 16];
-  const T* qrow = qk + (tok0 + tq) * g.ld_qk + (long)hq * D;
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) qf[s] = gld8<T>(qrow + 16 * s + 8 * lh, qok);
-
-  const T* kbase = qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D;
-  const T* vbase = vsrc + tok0 * g.ld_v + (long)kvh * D;
-
-  KT kl, vl;
-  auto kaddr = [&](int kt) {
-    return [=](int row) -> const T* {
-      int key = kt * BKV + row;
-      return key < g.T ? kbase + (long)key * g.ld_qk : nullptr;
-    };
-  };
-  auto vaddr = [&](int kt) {
-    return [=](int row) -> const T* {
-      int key = kt * BKV + row;
-      return key < g.T ? vbase + (long)key * g.ld_v : nullptr;
-    };
-  };
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
-  float lsum = 0.f;
-  const float c1 = kLog2e / sqrtf((float)D);
-  const float m0 = sqrtf((float)D) * kLog2e;  // fixed shift: |s| <= sqrt(D)
-
-  kl.load(kaddr(0), tid);
-  vl.load(vaddr(0), tid);
-  kl.store(ks[0], tid);
-  vl.store(vs[0], tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      kl.load(kaddr(kt + 1), tid);
-      vl.load(vaddr(kt + 1), tid);
-    }
-    const T* sk = ks[kt & 1];
-    const T* sv = vs[kt & 1];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kb = kt * BKV + 32 * sub;
-      if (kb > t_wmax) continue;
-      f32x16 sacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        F8<T> kf = ld_row8<T>(sk + (32 * sub + l32) * LD + 16 * s + 8 * lh);
-        mma32(sacc, kf, qf[s]);
-      }
-      float p[16];
-      if (wfull && kb + 31 <= t_wmin) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          p[v] = fast_exp2(sacc[v] * c1 - m0);
-          lsum += p[v];
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          int key = kb + crow(v, lh);
-          float e = fast_exp2(sacc[v] * c1 - m0);
-          p[v] = (qok && key <= tq) ? e : 0.f;
-          lsum += p[v];
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        F8<T> pf = pack8<T>(p + 8 * kk);
-        const int k0 = 32 * sub + 16 * kk + 4 * lh;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          F8<T> vf = ld_tr8<T>(sv, LD, k0, k0 + 8, 32 * dt + 16 * g16, lane);
-          mma32(oacc[dt], vf, pf);
-        }
-      }
-    }
-    if (more) {
-      kl.store(ks[(kt + 1) & 1], tid);
-      vl.store(vs[(kt + 1) & 1], tid);
-    }
-    __syncthreads();
-  }
-
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (qok) {
-    const float inv = 1.f / lsum;
-    T* orow = o + (tok0 + tq) * g.ld_o + (long)hq * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        T* dst = orow + 32 * dt + 8 * j + 4 * lh;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(oacc[dt][4 * j + i] * inv);
-      }
-    if (lh == 0) lse[(tok0 + tq) * g.H + hq] = (m0 + log2f(lsum)) / kLog2e;
-  }
-}
-
-// ============================================================ backward: dQ pass (+ Delta)
-template <typename T, int D>
-__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T* __restrict__ qk,
-                                                             const T* __restrict__ vsrc, const T* __restrict__ o,
-                                                             const T* __restrict__ dO, const float* __restrict__ lse,
-                                                             float2* __restrict__ rowstat, T* __restrict__ dq) {
-  constexpr int BKV = 64;
-  using KT = RowTile<T, BKV, D>;
-  constexpr int LD = KT::LD;
-  __shared__ __align__(16) T ks[2][BKV * LD];
-  __shared__ __align__(16) T vs[2][BKV * LD];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lh = lane >> 5, l32 = lane & 31;
-  const int g16 = (lane >> 4) & 1;
-  const int nrows = g.T * g.n_rep;
-  const int nqb = (nrows + 127) / 128;
-  const int per = g.G * g.B;
-  const int qb = nqb - 1 - (int)(blockIdx.x / per);
-  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
-  const int R0 = qb * 128;
-  const long tok0 = (long)b * g.T;
-  const DivN dv{g.n_rep, g.inv_rep};
-
-  const int rq = R0 + 32 * wave + l32;
-  const bool qok = rq < nrows;
-  const int tq = qok ? dv.q(rq) : 0;
-  const int hq = kvh * g.n_rep + (qok ? rq - tq * g.n_rep : 0);
-  const int t_wmax = dv.q(min(nrows - 1, R0 + 32 * wave + 31));
-  const int t_wmin = dv.q(min(nrows - 1, R0 + 32 * wave));
-  const bool wfull = R0 + 32 * wave + 31 < nrows;
-  const int t_bmax = dv.q(min(nrows - 1, R0 + 127));
-  const int nkt = t_bmax / BKV + 1;
-
-  const long qi = (tok0 + tq) * g.H + hq;
-  F8<T> qf[D / 16], df[D / 16];
-  const T* qrow = qk + (tok0 + tq) * g.ld_qk + (long)hq * D;
-  const T* drow = dO + (tok0 + tq) * g.ld_o + (long)hq * D;
-  const T* orow = o + (tok0 + tq) * g.ld_o + (long)hq * D;
-  float dsum = 0.f;
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    qf[s] = gld8<T>(qrow + 16 * s + 8 * lh, qok);
-    df[s] = gld8<T>(drow + 16 * s + 8 * lh, qok);
-    F8<T> of = gld8<T>(orow + 16 * s + 8 * lh, qok);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dsum += to_f32(df[s].v[e]) * to_f32(of.v[e]);
-  }
-  dsum += __shfl_xor(dsum, 32, 64);
-  const float dlt = dsum;
-  const float lse2 = qok ? lse[qi] * kLog2e : 0.f;
-  // (lse log2 e, Delta) of each flattened row, in row order, for the dK/dV pass
-  if (qok && lh == 0) rowstat[((long)b * g.G + kvh) * nrows + rq] = make_float2(lse2, dlt);
-  const float c1 = kLog2e / sqrtf((float)D);
-
-  const T* kbase = qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D;
-  const T* vbase = vsrc + tok0 * g.ld_v + (long)kvh * D;
-  KT kl, vl;
-  auto kaddr = [&](int kt) {
-    return [=](int row) -> const T* {
-      int key = kt * BKV + row;
-      return key < g.T ? kbase + (long)key * g.ld_qk : nullptr;
-    };
-  };
-  auto vaddr = [&](int kt) {
-    return [=](int row) -> const T* {
-      int key = kt * BKV + row;
-      return key < g.T ? vbase + (long)key * g.ld_v : nullptr;
-    };
-  };
-
-  f32x16 dqacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) dqacc[i][v] = 0.f;
-
-  kl.load(kaddr(0), tid);
-  vl.load(vaddr(0), tid);
-  kl.store(ks[0], tid);
-  vl.store(vs[0], tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      kl.load(kaddr(kt + 1), tid);
-      vl.load(vaddr(kt + 1), tid);
-    }
-    const T* sk = ks[kt & 1];
-    const T* sv = vs[kt & 1];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kb = kt * BKV + 32 * sub;
-      if (kb > t_wmax) continue;
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        F8<T> kf = ld_row8<T>(sk + (32 * sub + l32) * LD + 16 * s + 8 * lh);
-        mma32(sacc, kf, qf[s]);
-        F8<T> vf = ld_row8<T>(sv + (32 * sub + l32) * LD + 16 * s + 8 * lh);
-        mma32(pacc, vf, df[s]);
-      }
-      float ds[16];
-      if (wfull && kb + 31 <= t_wmin) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) ds[v] = fast_exp2(sacc[v] * c1 - lse2) * (pacc[v] - dlt);
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          int key = kb + crow(v, lh);
-          float p = fast_exp2(sacc[v] * c1 - lse2);
-          ds[v] = (qok && key <= tq) ? p * (pacc[v] - dlt) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        F8<T> sf = pack8<T>(ds + 8 * kk);
-        const int k0 = 32 * sub + 16 * kk + 4 * lh;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          F8<T> kf = ld_tr8<T>(sk, LD, k0, k0 + 8, 32 * dt + 16 * g16, lane);
-          mma32(dqacc[dt], kf, sf);
-        }
-      }
-    }
-    if (more) {
-      kl.store(ks[(kt + 1) & 1], tid);
-      vl.store(vs[(kt + 1) & 1], tid);
-    }
-    __syncthreads();
-  }
-
-  if (qok) {
-    const float sc = 1.f / sqrtf((float)D);
-    T* out = dq + (tok0 + tq) * g.ld_dq + (long)hq * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[32 * dt + 8 * j + 4 * lh + i] = from_f32<T>(dqacc[dt][4 * j + i] * sc);
-  }
-}
-
-// ============================================================ backward: dK/dV pass
-// Block: 128 keys, 8 waves. Waves w and w+4 share the 32 keys 32*(w%4) ..:
-//   wave w   (P side)  holds K, forms S = Q K^T and P = exp(S - lse), passes P
-//                      to its partner through LDS and accumulates dV += P^T dO;
-//   wave w+4 (dS side) holds V, forms dP = dO V^T, takes P one tile later,
-//                      dS = P (dP - Delta) and accumulates dK += dS^T Q.
-// So each wave keeps one 32-key operand and one accumulator set (half of what
-// one wave doing both needs), two waves share a SIMD, and no MFMA is repeated.
-// The flattened query rows of all heads sharing the KV head stream through a
-// 4-stage LDS ring of 32-row Q and dO tiles filled by direct-to-LDS loads
-// (XOR-swizzled 16-byte chunks: conflict-free for the row reads of S and dP
-// and for the transposing reads of dV and dK), each wave also staging its
-// own copy of the tiles' (lse log2 e, Delta) pairs. Tiles run from the last
-// query row down, so that all key blocks of a sequence start on the same rows
-// and share them in L2.
 
 // Swizzled [rows][D] tile: 16-byte chunk c of row r sits at chunk c ^ f(r).
 // D = 128 bf16 (16 chunks a row): f(r) = 4 (r % 4) + (r / 4) % 4. Sixteen
@@ -537,6 +157,366 @@ __device__ __forceinline__ F8<T> swz_tr8(const T* t, int ka, int kb, int c0, int
   }
   return f;
 }
+
+// ------------------------------------------------------------ tile staging
+// Row-major tile [ROWS][D] -> LDS in the swizzled layout above, staged
+// through registers; the row addresses come from a function (nullptr = zero row).
+template <typename T, int ROWS, int D>
+struct RowTile {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int ELEMS = ROWS * D;
+  static constexpr int N = ROWS * D / VE;
+  static constexpr int PER = (N + 255) / 256;
+  uint4 r[PER];
+  template <typename AddrF>
+  __device__ __forceinline__ void load(AddrF addr, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int u = tid + 256 * i;
+      r[i] = make_uint4(0, 0, 0, 0);
+      if (u < N) {
+        int row = u / (D / VE), c = u % (D / VE);
+        const T* p = addr(row);
+        if (p) r[i] = *reinterpret_cast<const uint4*>(p + c * VE);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int u = tid + 256 * i;
+      if (u < N) {
+        int row = u / (D / VE), c = u % (D / VE);
+        *reinterpret_cast<uint4*>(s + Swz<T, D>::at(row, c * VE)) = r[i];
+      }
+    }
+  }
+};
+
+// K and V tiles of 64 keys streamed straight into LDS (buffer_load ... lds),
+// in the swizzled layout, through a 2-stage ring: tile t+1 loads while tile
+// t is used, and no registers hold data in flight. Keys at or past T read as
+// zeros.
+template <typename T, int D>
+struct KvDma {
+  static constexpr int BKV = 64;
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int TILE = BKV * D;        // elements of one K or V tile
+  static constexpr int NI = TILE / VE / 64;   // 1 KB loads per tile
+  static constexpr int NPW = 2 * NI / 4;      // per wave, K and V together
+  static_assert((2 * NI) % 4 == 0, "tile loads split evenly over 4 waves");
+  const T* kbase;
+  const T* vbase;
+  long ldk, ldv;
+  int T_;
+  unsigned off[NPW];
+  int row[NPW], blk[NPW];
+  bool isv[NPW];
+
+  __device__ __forceinline__ void init(const T* kb, long ldk_, const T* vb, long ldv_, int Tn, int wave, int lane) {
+    kbase = kb;
+    vbase = vb;
+    ldk = ldk_;
+    ldv = ldv_;
+    T_ = Tn;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int ins = wave * NPW + i;  // K instructions first, then V
+      isv[i] = ins >= NI;
+      blk[i] = ins % NI;
+      const int u = 64 * blk[i] + lane;  // chunk slot inside the tile
+      row[i] = u / Swz<T, D>::NC;
+      const int col = ((u % Swz<T, D>::NC) ^ Swz<T, D>::f(row[i])) * VE;
+      off[i] = (unsigned)(((long)row[i] * (isv[i] ? ldv : ldk) + col) * (long)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, T* __restrict__ sk, T* __restrict__ sv) const {
+    const long key0 = (long)kt * BKV;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const unsigned o = key0 + row[i] < T_ ? off[i] : kDmaOOB;
+      __amdgpu_buffer_rsrc_t rs = dma_rsrc(isv[i] ? vbase + key0 * ldv : kbase + key0 * ldk);
+      T* dst = (isv[i] ? sv : sk) + blk[i] * 64 * VE;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, o, 0, 0, 0);
+    }
+  }
+};
+
+// Runs body(kt, k tile, v tile) for kt = 0 .. nkt-1 over the ring. The stages
+// are separate LDS arrays passed as __restrict__ parameters of this inlined
+// function, so the compiler can tell one stage's loads from the other
+// stage's reads.
+template <typename T, int D, typename Body>
+__device__ __forceinline__ void kv_ring(const KvDma<T, D>& dma, int nkt, T* __restrict__ k0, T* __restrict__ v0,
+                                        T* __restrict__ k1, T* __restrict__ v1, Body&& body) {
+  dma.issue(0, k0, v0);
+  int kt = 0;
+  for (; kt + 2 <= nkt; kt += 2) {
+    ring_barrier<0>();
+    dma.issue(kt + 1, k1, v1);
+    body(kt, k0, v0);
+    ring_barrier<0>();
+    dma.issue(kt + 2, k0, v0);
+    body(kt + 1, k1, v1);
+  }
+  if (kt < nkt) {
+    ring_barrier<0>();
+    dma.issue(kt + 1, k1, v1);
+    body(kt, k0, v0);
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));  // the loads past the end
+}
+
+// Key index held in accumulator slot v by lane half lh (C layout of a 32x32
+// MFMA: rows 8*(v/4) + 4*lh + v%4).
+__device__ __forceinline__ int crow(int v, int lh) { return 8 * (v >> 2) + 4 * lh + (v & 3); }
+
+struct AttnGeom {
+  int B, T, H, G, D, n_rep;
+  long ld_qk, ld_v, ld_o, ld_dq;
+  int q_off_k;  // column of K head 0 inside the qk rows (H*D)
+  float inv_rep;
+};
+
+// ============================================================ forward
+template <typename T, int D>
+__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* __restrict__ qk,
+                                                          const T* __restrict__ vsrc, T* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  using Kv = KvDma<T, D>;
+  constexpr int BKV = Kv::BKV;
+  __shared__ __align__(16) T ks0[Kv::TILE], vs0[Kv::TILE], ks1[Kv::TILE], vs1[Kv::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, lh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = (lane >> 4) & 1;
+  const int nrows = g.T * g.n_rep;
+  const int nqb = (nrows + 127) / 128;
+  const int per = g.G * g.B;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per);  // longest query blocks first
+  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
+  const int R0 = qb * 128;
+  const long tok0 = (long)b * g.T;
+  const DivN dv{g.n_rep, g.inv_rep};
+
+  const int rq = R0 + 32 * wave + l32;
+  const bool qok = rq < nrows;
+  const int tq = qok ? dv.q(rq) : 0;
+  const int hq = kvh * g.n_rep + (qok ? rq - tq * g.n_rep : 0);
+  const int w_last = min(nrows - 1, R0 + 32 * wave + 31);
+  const int t_wmax = dv.q(w_last);
+  const int t_wmin = dv.q(min(nrows - 1, R0 + 32 * wave));
+  const bool wfull = R0 + 32 * wave + 31 < nrows;
+  const int t_bmax = dv.q(min(nrows - 1, R0 + 127));
+  const int nkt = t_bmax / BKV + 1;
+
+  // Q as the B operand of S^T = K Q^T: lane holds d = 16*s + 8*lh + (0..7) of its query.
+  F8<T> qf[D / 16];
+  const T* qrow = qk + (tok0 + tq) * g.ld_qk + (long)hq * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = gld8<T>(qrow + 16 * s + 8 * lh, qok);
+
+  Kv dma;
+  dma.init(qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D, g.ld_qk, vsrc + tok0 * g.ld_v + (long)kvh * D, g.ld_v,
+           g.T, wave, lane);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float lsum = 0.f;
+  const float c1 = kLog2e / sqrtf((float)D);
+  const float m0 = sqrtf((float)D) * kLog2e;  // fixed shift: |s| <= sqrt(D)
+
+  kv_ring<T, D>(dma, nkt, ks0, vs0, ks1, vs1, [&](int kt, const T* sk, const T* sv) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kb = kt * BKV + 32 * sub;
+      if (kb > t_wmax) continue;
+      f32x16 sacc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        F8<T> kf = swz_row8<T, D>(sk, 32 * sub + l32, 16 * s + 8 * lh);
+        mma32(sacc, kf, qf[s]);
+      }
+      float p[16];
+      if (wfull && kb + 31 <= t_wmin) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          p[v] = fast_exp2(sacc[v] * c1 - m0);
+          lsum += p[v];
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int key = kb + crow(v, lh);
+          float e = fast_exp2(sacc[v] * c1 - m0);
+          p[v] = (qok && key <= tq) ? e : 0.f;
+          lsum += p[v];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        F8<T> pf = pack8<T>(p + 8 * kk);
+        const int k0 = 32 * sub + 16 * kk + 4 * lh;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          F8<T> vf = swz_tr8<T, D>(sv, k0, k0 + 8, 32 * dt + 16 * g16, lane);
+          mma32(oacc[dt], vf, pf);
+        }
+      }
+    }
+  });
+
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (qok) {
+    const float inv = 1.f / lsum;
+    T* orow = o + (tok0 + tq) * g.ld_o + (long)hq * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        T* dst = orow + 32 * dt + 8 * j + 4 * lh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(oacc[dt][4 * j + i] * inv);
+      }
+    if (lh == 0) lse[(tok0 + tq) * g.H + hq] = (m0 + log2f(lsum)) / kLog2e;
+  }
+}
+
+// ============================================================ backward: dQ pass (+ Delta)
+template <typename T, int D>
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T* __restrict__ qk,
+                                                             const T* __restrict__ vsrc, const T* __restrict__ o,
+                                                             const T* __restrict__ dO, const float* __restrict__ lse,
+                                                             float2* __restrict__ rowstat, T* __restrict__ dq) {
+  using Kv = KvDma<T, D>;
+  constexpr int BKV = Kv::BKV;
+  __shared__ __align__(16) T ks0[Kv::TILE], vs0[Kv::TILE], ks1[Kv::TILE], vs1[Kv::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, lh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = (lane >> 4) & 1;
+  const int nrows = g.T * g.n_rep;
+  const int nqb = (nrows + 127) / 128;
+  const int per = g.G * g.B;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per);
+  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
+  const int R0 = qb * 128;
+  const long tok0 = (long)b * g.T;
+  const DivN dv{g.n_rep, g.inv_rep};
+
+  const int rq = R0 + 32 * wave + l32;
+  const bool qok = rq < nrows;
+  const int tq = qok ? dv.q(rq) : 0;
+  const int hq = kvh * g.n_rep + (qok ? rq - tq * g.n_rep : 0);
+  const int t_wmax = dv.q(min(nrows - 1, R0 + 32 * wave + 31));
+  const int t_wmin = dv.q(min(nrows - 1, R0 + 32 * wave));
+  const bool wfull = R0 + 32 * wave + 31 < nrows;
+  const int t_bmax = dv.q(min(nrows - 1, R0 + 127));
+  const int nkt = t_bmax / BKV + 1;
+
+  const long qi = (tok0 + tq) * g.H + hq;
+  F8<T> qf[D / 16], df[D / 16];
+  const T* qrow = qk + (tok0 + tq) * g.ld_qk + (long)hq * D;
+  const T* drow = dO + (tok0 + tq) * g.ld_o + (long)hq * D;
+  const T* orow = o + (tok0 + tq) * g.ld_o + (long)hq * D;
+  float dsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = gld8<T>(qrow + 16 * s + 8 * lh, qok);
+    df[s] = gld8<T>(drow + 16 * s + 8 * lh, qok);
+    F8<T> of = gld8<T>(orow + 16 * s + 8 * lh, qok);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum += to_f32(df[s].v[e]) * to_f32(of.v[e]);
+  }
+  dsum += __shfl_xor(dsum, 32, 64);
+  const float dlt = dsum;
+  const float lse2 = qok ? lse[qi] * kLog2e : 0.f;
+  // (lse log2 e, Delta) of each flattened row, in row order, for the dK/dV pass
+  if (qok && lh == 0) rowstat[((long)b * g.G + kvh) * nrows + rq] = make_float2(lse2, dlt);
+  const float c1 = kLog2e / sqrtf((float)D);
+
+  Kv dma;
+  dma.init(qk + tok0 * g.ld_qk + g.q_off_k + (long)kvh * D, g.ld_qk, vsrc + tok0 * g.ld_v + (long)kvh * D, g.ld_v,
+           g.T, wave, lane);
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dqacc[i][v] = 0.f;
+
+  kv_ring<T, D>(dma, nkt, ks0, vs0, ks1, vs1, [&](int kt, const T* sk, const T* sv) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kb = kt * BKV + 32 * sub;
+      if (kb > t_wmax) continue;
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { sacc[v] = 0.f; pacc[v] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        F8<T> kf = swz_row8<T, D>(sk, 32 * sub + l32, 16 * s + 8 * lh);
+        mma32(sacc, kf, qf[s]);
+        F8<T> vf = swz_row8<T, D>(sv, 32 * sub + l32, 16 * s + 8 * lh);
+        mma32(pacc, vf, df[s]);
+      }
+      float ds[16];
+      if (wfull && kb + 31 <= t_wmin) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ds[v] = fast_exp2(sacc[v] * c1 - lse2) * (pacc[v] - dlt);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int key = kb + crow(v, lh);
+          float p = fast_exp2(sacc[v] * c1 - lse2);
+          ds[v] = (qok && key <= tq) ? p * (pacc[v] - dlt) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        F8<T> sf = pack8<T>(ds + 8 * kk);
+        const int k0 = 32 * sub + 16 * kk + 4 * lh;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          F8<T> kf = swz_tr8<T, D>(sk, k0, k0 + 8, 32 * dt + 16 * g16, lane);
+          mma32(dqacc[dt], kf, sf);
+        }
+      }
+    }
+  });
+
+  if (qok) {
+    const float sc = 1.f / sqrtf((float)D);
+    T* out = dq + (tok0 + tq) * g.ld_dq + (long)hq * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[32 * dt + 8 * j + 4 * lh + i] = from_f32<T>(dqacc[dt][4 * j + i] * sc);
+  }
+}
+
+// ============================================================ backward: dK/dV pass
+// Block: 128 keys, 8 waves. Waves w and w+4 share the 32 keys 32*(w%4) ..:
+//   wave w   (P side)  holds K, forms S = Q K^T and P = exp(S - lse), passes P
+//                      to its partner through LDS and accumulates dV += P^T dO;
+//   wave w+4 (dS side) holds V, forms dP = dO V^T, takes P one tile later,
+//                      dS = P (dP - Delta) and accumulates dK += dS^T Q.
+// So each wave keeps one 32-key operand and one accumulator set (half of what
+// one wave doing both needs), two waves share a SIMD, and no MFMA is repeated.
+// The flattened query rows of all heads sharing the KV head stream through a
+// 4-stage LDS ring of 32-row Q and dO tiles filled by direct-to-LDS loads
+// (XOR-swizzled 16-byte chunks: conflict-free for the row reads of S and dP
+// and for the transposing reads of dV and dK), each wave also staging its
+// own copy of the tiles' (lse log2 e, Delta) pairs. Tiles run from the last
+// query row down, so that all key blocks of a sequence start on the same rows
+// and share them in L2.
 
 template <typename T, int D>
 struct DkdvShape {
