@@ -34,3 +34,4 @@ from .model import (  # noqa: F401
     model_loss_and_grad,
     model_forward_logits,
 )
+from . import infer  # noqa: F401  (greedy generation with a key/value cache)
