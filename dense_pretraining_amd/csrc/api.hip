@@ -378,6 +378,156 @@ nc_status model_t(const Dims& m, const T* params, const int32_t* idx, const int3
   return NC_OK;
 }
 
+// ------------------------------------------------------------ inference
+// Workspace of nc_prefill / nc_decode_step: status word, RoPE tables for the
+// cache capacity, then the prefill buffers and the decode buffers (the same
+// bytes: one call uses one set), then what both use (final norm, logits,
+// split partials).
+template <typename T>
+struct InferBufs {
+  float *cs, *sn;
+  T *px0, *px1;  // [B*cap, d] residual streams of the prompt pass
+  BlockSaved<T> ps;
+  int32_t* rows;  // [B] the prompts' last rows
+  T *x, *h1, *qkv, *qk, *o, *x1, *h2, *act;  // one row per sequence
+  float *r, *po, *pl;
+  T* xf;
+  float *rf, *logits, *partial;
+  size_t partial_elems;
+  size_t bytes;
+};
+
+Dims prompt_dims(const Dims& m, int n_prompt) {
+  Dims p = m;
+  p.T = n_prompt;
+  p.M = (long)m.B * n_prompt;
+  return p;
+}
+
+template <typename T>
+InferBufs<T> carve_infer(void* ws, const Dims& m) {
+  InferBufs<T> b;
+  char* base = static_cast<char*>(ws);
+  Carver c(base ? base + kStatusBytes : nullptr);
+  b.cs = c.take<float>((size_t)m.T * m.D / 2);
+  b.sn = c.take<float>((size_t)m.T * m.D / 2);
+  const size_t head = c.used;
+  char* u = base ? base + kStatusBytes + head : nullptr;
+  Carver cp(u);  // prompt pass (capacity-sized)
+  b.px0 = cp.take<T>(m.M * m.d);
+  b.px1 = cp.take<T>(m.M * m.d);
+  b.ps = carve_block_saved<T>(cp, m, false);
+  b.rows = cp.take<int32_t>(m.B);
+  Carver cd(u);  // decode step
+  const long B = m.B;
+  b.x = cd.take<T>(B * m.d);
+  b.h1 = cd.take<T>(B * m.d);
+  b.qkv = cd.take<T>(B * m.QKV);
+  b.qk = cd.take<T>(B * m.QK);
+  b.o = cd.take<T>(B * m.HD);
+  b.x1 = cd.take<T>(B * m.d);
+  b.h2 = cd.take<T>(B * m.d);
+  b.act = cd.take<T>(B * m.F);
+  b.r = cd.take<float>(B);
+  const int nch = attn_decode_chunks(m.T, m.es == 2);
+  b.po = cd.take<float>((size_t)B * nch * m.H * m.D);
+  b.pl = cd.take<float>((size_t)B * nch * m.H);
+  const size_t uni = cp.used > cd.used ? cp.used : cd.used;
+  Carver cs(base ? base + kStatusBytes + head + uni : nullptr);
+  b.xf = cs.take<T>(B * m.d);
+  b.rf = cs.take<float>(B);
+  b.logits = cs.take<float>((size_t)B * m.V);
+  size_t pe = 0;
+  const int shapes[5][2] = {{m.QKV, m.d}, {m.d, m.HD}, {m.F, m.d}, {m.d, m.F}, {m.V, m.d}};
+  for (auto& nk : shapes) {
+    const size_t e = gemm_small_partial_elems((int)B, nk[0], nk[1]);
+    pe = e > pe ? e : pe;
+  }
+  b.partial = cs.take<float>(pe);
+  b.partial_elems = pe;
+  b.bytes = kStatusBytes + head + uni + cs.used;
+  return b;
+}
+
+nc_status infer_dims(const nc_config* cfg, Dims* m) {
+  NC_TRY(make_dims(cfg, m, true));
+  if (m->H / m->G > 16) return NC_ERR_UNSUPPORTED;
+  return NC_OK;
+}
+
+size_t infer_cache_bytes(const Dims& m) { return (size_t)m.L * 2 * m.B * m.T * m.G * m.D * m.es; }
+
+template <typename T>
+T* cache_at(void* cache, const Dims& m, int l, int kv) {
+  return static_cast<T*>(cache) + ((size_t)l * 2 + kv) * m.B * m.T * m.G * m.D;
+}
+
+// Final norm of one row per sequence, softcapped logits in float32, argmax.
+template <typename T>
+nc_status infer_head(const Dims& m, const T* wlm, const T* x, const int32_t* rows, long nrows, const InferBufs<T>& b,
+                     int32_t* next_tok, uint32_t* status, hipStream_t st) {
+  NC_TRY(rmsnorm_fwd<T>(x, rows, (int)nrows, b.xf, b.rf, m.B, m.d, m.eps, status, st));
+  NC_TRY(gemm_xwt_small<T>(b.xf, wlm, b.logits, true, nullptr, false, m.B, m.V, m.d, b.partial, b.partial_elems, st));
+  return argmax_softcap(b.logits, m.V, m.B, m.V, m.cap, next_tok, st);
+}
+
+template <typename T>
+nc_status prefill_t(const Dims& m, const T* params, const int32_t* idx, int n_prompt, void* cache, int32_t* next_tok,
+                    void* ws, hipStream_t st) {
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  param_offsets(m, off.data());
+  uint32_t* status = static_cast<uint32_t*>(ws);
+  const InferBufs<T> b = carve_infer<T>(ws, m);
+  const Dims p = prompt_dims(m, n_prompt);
+  NC_TRY(rope_table(b.cs, b.sn, n_prompt, m.D, m.base, st));
+  NC_TRY(rmsnorm_fwd<T>(params + off[0], idx, m.V, b.px0, b.ps.r1, (int)p.M, m.d, m.eps, status, st));
+  T* x = b.px0;
+  T* y = b.px1;
+  for (int l = 0; l < m.L; ++l) {
+    BlockW<T> w{params + off[1 + 4 * l], params + off[2 + 4 * l], params + off[3 + 4 * l], params + off[4 + 4 * l]};
+    NC_TRY(block_fwd_t<T>(p, w, x, y, b.ps, b.cs, b.sn, st));
+    NC_TRY(kv_store<T>(b.ps.qk + (size_t)m.H * m.D, m.QK, b.ps.qkv + (size_t)(m.H + m.G) * m.D, m.QKV,
+                       cache_at<T>(cache, m, l, 0), cache_at<T>(cache, m, l, 1), m.B, n_prompt, 0, m.T, m.G * m.D,
+                       st));
+    T* t = x;
+    x = y;
+    y = t;
+  }
+  NC_TRY(iota_i32(b.rows, m.B, n_prompt - 1, n_prompt, st));
+  return infer_head<T>(m, params + off[1 + 4 * m.L], x, b.rows, p.M, b, next_tok, nullptr, st);
+}
+
+template <typename T>
+nc_status decode_t(const Dims& m, const T* params, const int32_t* tok, int pos, void* cache, int32_t* next_tok,
+                   void* ws, hipStream_t st) {
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  param_offsets(m, off.data());
+  uint32_t* status = static_cast<uint32_t*>(ws);
+  const InferBufs<T> b = carve_infer<T>(ws, m);
+  const int B = m.B;
+  NC_TRY(rope_table(b.cs, b.sn, pos + 1, m.D, m.base, st));
+  NC_TRY(rmsnorm_fwd<T>(params + off[0], tok, m.V, b.x, b.r, B, m.d, m.eps, status, st));
+  for (int l = 0; l < m.L; ++l) {
+    const T* wqkv = params + off[1 + 4 * l];
+    const T* wo = params + off[2 + 4 * l];
+    const T* w1 = params + off[3 + 4 * l];
+    const T* w2 = params + off[4 + 4 * l];
+    T* ck = cache_at<T>(cache, m, l, 0);
+    T* cv = cache_at<T>(cache, m, l, 1);
+    NC_TRY(rmsnorm_fwd<T>(b.x, nullptr, 0, b.h1, b.r, B, m.d, m.eps, nullptr, st));
+    NC_TRY(gemm_xwt_small<T>(b.h1, wqkv, b.qkv, false, nullptr, false, B, m.QKV, m.d, b.partial, b.partial_elems, st));
+    NC_TRY(qknorm_rope_fwd<T>(b.qkv, m.QKV, b.qk, m.QK, b.cs, b.sn, B, 1, m.H + m.G, m.D, m.eps, st, pos));
+    NC_TRY(kv_store<T>(b.qk + (size_t)m.H * m.D, m.QK, b.qkv + (size_t)(m.H + m.G) * m.D, m.QKV, ck, cv, B, 1, pos,
+                       m.T, m.G * m.D, st));
+    NC_TRY(attn_decode<T>(b.qk, m.QK, ck, cv, B, m.H, m.G, m.D, pos + 1, m.T, b.o, m.HD, b.po, b.pl, st));
+    NC_TRY(gemm_xwt_small<T>(b.o, wo, b.x1, false, b.x, false, B, m.d, m.HD, b.partial, b.partial_elems, st));
+    NC_TRY(rmsnorm_fwd<T>(b.x1, nullptr, 0, b.h2, b.r, B, m.d, m.eps, nullptr, st));
+    NC_TRY(gemm_xwt_small<T>(b.h2, w1, b.act, false, nullptr, true, B, m.F, m.d, b.partial, b.partial_elems, st));
+    NC_TRY(gemm_xwt_small<T>(b.act, w2, b.x, false, b.x1, false, B, m.d, m.F, b.partial, b.partial_elems, st));
+  }
+  return infer_head<T>(m, params + off[1 + 4 * m.L], b.x, nullptr, B, b, next_tok, nullptr, st);
+}
+
 }  // namespace
 }  // namespace nc
 
@@ -585,6 +735,49 @@ nc_status nc_lmhead_softcap_xent_bwd(const nc_config* cfg, const void* x, const 
   HeadScratch<float> sc = carve_head_scratch<float>(cs, m);
   return head_bwd_t<float>(m, static_cast<const float*>(wlm), targets, s, dloss, static_cast<float*>(dx), dwlm,
                            accumulate, sc, st);
+}
+
+nc_status nc_infer_query_sizes(const nc_config* cfg, nc_infer_sizes* out) {
+  Dims m;
+  NC_TRY(infer_dims(cfg, &m));
+  if (!out) return NC_ERR_INVALID_ARG;
+  out->cache = infer_cache_bytes(m);
+  out->workspace = m.es == 2 ? carve_infer<bf16>(nullptr, m).bytes : carve_infer<float>(nullptr, m).bytes;
+  return NC_OK;
+}
+
+nc_status nc_prefill(const nc_config* cfg, const void* params, const int32_t* idx, int n_prompt, void* cache,
+                     int32_t* next_tok, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims m;
+  NC_TRY(infer_dims(cfg, &m));
+  if (!params || !idx || !cache || !next_tok || !workspace) return NC_ERR_INVALID_ARG;
+  if (n_prompt < 1 || n_prompt > m.T) return NC_ERR_SHAPE;
+  if (!aligned(params) || !aligned(idx) || !aligned(cache) || !aligned(next_tok) || !aligned(workspace))
+    return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m.es == 2) {
+    if (workspace_bytes < carve_infer<bf16>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
+    return prefill_t<bf16>(m, static_cast<const bf16*>(params), idx, n_prompt, cache, next_tok, workspace, st);
+  }
+  if (workspace_bytes < carve_infer<float>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
+  return prefill_t<float>(m, static_cast<const float*>(params), idx, n_prompt, cache, next_tok, workspace, st);
+}
+
+nc_status nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
+                         int32_t* next_tok, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims m;
+  NC_TRY(infer_dims(cfg, &m));
+  if (!params || !tok || !cache || !next_tok || !workspace) return NC_ERR_INVALID_ARG;
+  if (pos < 1 || pos >= m.T) return NC_ERR_SHAPE;
+  if (!aligned(params) || !aligned(tok) || !aligned(cache) || !aligned(next_tok) || !aligned(workspace))
+    return NC_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m.es == 2) {
+    if (workspace_bytes < carve_infer<bf16>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
+    return decode_t<bf16>(m, static_cast<const bf16*>(params), tok, pos, cache, next_tok, workspace, st);
+  }
+  if (workspace_bytes < carve_infer<float>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
+  return decode_t<float>(m, static_cast<const float*>(params), tok, pos, cache, next_tok, workspace, st);
 }
 
 nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const int32_t* idx, const int32_t* targets,

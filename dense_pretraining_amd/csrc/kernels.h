@@ -46,6 +46,13 @@ template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
                       float* part, float* zt, hipStream_t st);
 int lmhead_tiles(int N, bool bf16_storage);
+// y = act(x[M,K] W[N,K]^T) (+ res) for a few rows (M up to a tile): the
+// reduction is split so that enough workgroups stream W, the float32 partials
+// are summed in a fixed order; y in the storage type or float32.
+template <typename T>
+nc_status gemm_xwt_small(const T* x, const T* w, void* y, bool y_f32, const T* res, bool relu_sq, int M, int N, int K,
+                         float* partial, size_t partial_elems, hipStream_t st);
+size_t gemm_small_partial_elems(int M, int N, int K);
 
 // ------------------------------------------------------------ rows (rows.hip)
 nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
@@ -60,9 +67,10 @@ nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO*
 // cos/sin [T, D/2] of t * base^(-2i/D), evaluated in double.
 nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st);
 // Per token and head (H+G heads): N_D then rotate; qkv [M, ld_in] -> qk [M, ld_out].
+// Row m is at position pos0 + m % T_.
 template <typename T>
 nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const float* cs, const float* sn, int M,
-                          int T_, int nheads, int D, float eps, hipStream_t st);
+                          int T_, int nheads, int D, float eps, hipStream_t st, int pos0 = 0);
 // In place on g [M, ld_g] (first nheads*D columns): g <- N_D_bwd(R^T g) with
 // the forward recomputed from the raw qkv.
 template <typename T>
@@ -80,6 +88,25 @@ nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, 
                   hipStream_t st);
 // out (+)= sum_z partial[z] (fixed order) for float arrays of n elements.
 nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st);
+
+// ------------------------------------------------------------ inference (infer.hip)
+// cache[b][pos0 + t] <- rows b * Tsrc + t of k and v (G*D columns each).
+template <typename T>
+nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int B, int Tsrc, int pos0, int cap,
+                   int GD, hipStream_t st);
+// o [B, H*D] = attention of one query per head (q [B, ld_q], heads in order)
+// over keys 0..n-1 of the cache; po/pl: float scratch of
+// B * attn_decode_chunks(n) * H * (D + 1) elements.
+template <typename T>
+nc_status attn_decode(const T* q, long ldq, const T* ck, const T* cv, int B, int H, int G, int D, int n, int cap,
+                      T* o, long ldo, float* po, float* pl, hipStream_t st);
+int attn_decode_chunks(int n, bool bf16_storage);
+// out[b] = lowest index of the largest c tanh(z[b][v]/c).
+nc_status argmax_softcap(const float* z, long ldz, int B, int V, float cap, int32_t* out, hipStream_t st);
+template <typename T>
+nc_status splitk_act(const float* part, int nsplit, int M, int N, void* y, bool y_f32, const T* res, bool relu_sq,
+                     hipStream_t st);
+nc_status iota_i32(int32_t* out, int n, int start, int step, hipStream_t st);
 
 // ------------------------------------------------------------ attention (attn.hip)
 struct AttnArgs {

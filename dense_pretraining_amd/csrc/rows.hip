@@ -152,13 +152,13 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(const T* __restrict__ qkv, long ld_in, T* __restrict__ qk,
                                                               long ld_out, const float* __restrict__ cs,
                                                               const float* __restrict__ sn, int M, int Tn, int nheads,
-                                                              float eps) {
+                                                              float eps, int pos0) {
   constexpr int P = D / 2, LPH = P / 4, HPB = 256 / LPH;
   const long pair = (long)blockIdx.x * HPB + threadIdx.x / LPH;
   const int j = threadIdx.x % LPH;
   if (pair >= (long)M * nheads) return;  // whole lane groups leave together
   const int m = (int)(pair / nheads), h = (int)(pair - (long)m * nheads);
-  const int t = m % Tn;
+  const int t = pos0 + m % Tn;
   const T* src = qkv + (long)m * ld_in + (long)h * D + 4 * j;
   float a[4], b[4];
   load4<T>(src, a);
@@ -397,15 +397,15 @@ nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t
 
 template <typename T>
 nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const float* cs, const float* sn, int M,
-                          int T_, int nheads, int D, float eps, hipStream_t st) {
+                          int T_, int nheads, int D, float eps, hipStream_t st, int pos0) {
   ProfScope prof(NC_NAME(T, "qknorm_rope_fwd"), 0, 2.0 * sizeof(T) * M * nheads * D, st);
   const long pairs = (long)M * nheads;
   if (D == 128)
     hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, 128>), dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, st, qkv,
-                       ld_in, qk, ld_out, cs, sn, M, T_, nheads, eps);
+                       ld_in, qk, ld_out, cs, sn, M, T_, nheads, eps, pos0);
   else if (D == 64)
     hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, 64>), dim3((unsigned)((pairs + 31) / 32)), dim3(256), 0, st, qkv,
-                       ld_in, qk, ld_out, cs, sn, M, T_, nheads, eps);
+                       ld_in, qk, ld_out, cs, sn, M, T_, nheads, eps, pos0);
   else
     return NC_ERR_UNSUPPORTED;
   NC_LAUNCH_CHECK("qknorm_rope_fwd");
@@ -470,7 +470,7 @@ nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, 
                                     hipStream_t);                                                                   \
   template nc_status rmsnorm_bwd<T, T>(const T*, const T*, const float*, const T*, T*, int, int, hipStream_t);     \
   template nc_status qknorm_rope_fwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
-                                        float, hipStream_t);                                                        \
+                                        float, hipStream_t, int);                                                   \
   template nc_status qknorm_rope_bwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
                                         float, hipStream_t);                                                        \
   template nc_status xent_dz<T>(T*, int, int, const float*, const int32_t*, const int*, float, float, hipStream_t);

@@ -32,7 +32,8 @@ EXPORTED = [
     "nc_abi_version", "nc_status_str", "nc_last_hip_error", "nc_validate", "nc_param_layout",
     "nc_query_sizes", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
-    "nc_model_loss_and_grad", "nc_profile_enable", "nc_profile_summary",
+    "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_profile_enable",
+    "nc_profile_summary",
 ]
 
 
@@ -64,6 +65,10 @@ class NcSizes(C.Structure):
                 ("model_workspace", C.c_size_t), ("n_params", C.c_size_t)]
 
 
+class NcInferSizes(C.Structure):
+    _fields_ = [("cache", C.c_size_t), ("workspace", C.c_size_t)]
+
+
 _lib = None
 
 
@@ -93,6 +98,9 @@ def load(path=LIB_PATH):
         "nc_lmhead_softcap_xent_fwd": ([cfgp, P, P, P, P, P, P, P], I),
         "nc_lmhead_softcap_xent_bwd": ([cfgp, P, P, P, P, F, P, P, I, P, P], I),
         "nc_model_loss_and_grad": ([cfgp, P, P, P, P, P, F, I, P, S, P], I),
+        "nc_infer_query_sizes": ([cfgp, C.POINTER(NcInferSizes)], I),
+        "nc_prefill": ([cfgp, P, P, I, P, P, P, S, P], I),
+        "nc_decode_step": ([cfgp, P, P, I, P, P, P, S, P], I),
         "nc_profile_enable": ([I], I),
         "nc_profile_summary": ([C.c_char_p, S, C.POINTER(S)], I),
     }
@@ -253,3 +261,26 @@ def profile_summary():
     buf = C.create_string_buffer(need.value)
     _check(load().nc_profile_summary(buf, need.value, C.byref(need)), "nc_profile_summary")
     return json.loads(buf.value.decode())
+
+
+# ------------------------------------------------------------------ inference
+
+def infer_query_sizes(cfg: Config) -> NcInferSizes:
+    c = to_nc_config(cfg)
+    s = NcInferSizes()
+    _check(load().nc_infer_query_sizes(C.byref(c), C.byref(s)), "nc_infer_query_sizes")
+    return s
+
+
+def prefill(cfg, params, idx, n_prompt, cache, next_tok, workspace, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_prefill(C.byref(c), _p(params), _p(idx), int(n_prompt), _p(cache), _p(next_tok),
+                             _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "nc_prefill")
+
+
+def decode_step(cfg, params, tok, pos, cache, next_tok, workspace, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_decode_step(C.byref(c), _p(params), _p(tok), int(pos), _p(cache), _p(next_tok),
+                                 _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "nc_decode_step")

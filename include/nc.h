@@ -196,6 +196,43 @@ nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const
                                  int accumulate, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* ---------------------------------------------------------------- inference */
+
+/* Greedy generation with a key/value cache: a prefill pass over the prompts,
+ * then one decode step per new token (the inference engine the pages describe:
+ * imeisheng.com, feature list and the end of section "预训练"; geoz.com.cn,
+ * sections "推理与部署" and "高效推理引擎与交互界面"). cfg->batch is the number
+ * of sequences and cfg->seq_len the cache capacity in positions. Greedy
+ * decoding is a reading: the next token is the lowest id whose softcapped
+ * logit c*tanh(z/c) is largest. */
+
+/* Buffer sizes in bytes for inference (see nc_infer_query_sizes). */
+typedef struct nc_infer_sizes {
+  size_t cache;     /* K/V cache: [depth][2][batch][seq_len][n_kv_head*head_dim], storage dtype */
+  size_t workspace; /* `workspace` of nc_prefill and nc_decode_step */
+} nc_infer_sizes;
+
+/* Sizes for cfg (NC_ERR_UNSUPPORTED when n_head / n_kv_head > 16). */
+nc_status nc_infer_query_sizes(const nc_config* cfg, nc_infer_sizes* out);
+
+/* Prompt pass. idx [batch, n_prompt] token ids (device), 1 <= n_prompt <=
+ * seq_len. Fills cache positions 0 .. n_prompt-1 of every layer: K after QK
+ * norm and rotation at [l][0][b][t][:], V at [l][1][b][t][:]. next_tok
+ * [batch] (device, out): the greedy token after each prompt. params as for
+ * nc_model_loss_and_grad. workspace [workspace bytes], its first bytes the
+ * device status word (bad token ids set NC_STATUS_BAD_TOKEN and read as row 0
+ * of the embedding). */
+nc_status nc_prefill(const nc_config* cfg, const void* params, const int32_t* idx, int n_prompt, void* cache,
+                     int32_t* next_tok, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step for every sequence: tok [batch] (device) sits at position
+ * pos (0 < pos < seq_len; positions 0 .. pos-1 are already in the cache).
+ * Appends its K and V at pos and writes next_tok [batch] (device, out), the
+ * greedy token that follows. Steps of one stream are ordered; the caller feeds
+ * next_tok back as tok with pos + 1. */
+nc_status nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
+                         int32_t* next_tok, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- tracing */
 
 /* Kernel timing. While enabled, every kernel launch of the library is

@@ -114,3 +114,28 @@ def test_status_strings():
     assert L.nc_status_str(0) == b"ok"
     assert L.nc_status_str(4) == b"workspace too small"
     assert L.nc_status_str(99) == b"unknown status"
+
+
+def test_inference_arguments_checked_before_launch():
+    L = lib.load()
+    cfg = cfgmod.TINY.with_(seq_len=32)
+    c = lib.to_nc_config(cfg)
+    sz = lib.infer_query_sizes(cfg)
+    # cache: [depth][2][batch][seq_len][G*D] in the storage dtype
+    es = 2 if cfg.dtype == "bf16" else 4
+    assert sz.cache == cfg.depth * 2 * cfg.batch * cfg.seq_len * cfg.n_kv_head * cfg.head_dim * es
+    assert sz.workspace > 0
+    ok, bad = _fake(0x100000), _fake(0x100001)
+    W = sz.workspace
+    assert L.nc_prefill(C.byref(c), ok, None, 4, ok, ok, ok, W, None) == 1
+    assert L.nc_prefill(C.byref(c), ok, ok, 0, ok, ok, ok, W, None) == 2          # empty prompt
+    assert L.nc_prefill(C.byref(c), ok, ok, 33, ok, ok, ok, W, None) == 2         # beyond the capacity
+    assert L.nc_prefill(C.byref(c), ok, ok, 4, bad, ok, ok, W, None) == 3
+    assert L.nc_prefill(C.byref(c), ok, ok, 4, ok, ok, ok, W - 1, None) == 4
+    assert L.nc_decode_step(C.byref(c), ok, ok, 0, ok, ok, ok, W, None) == 2      # nothing cached yet
+    assert L.nc_decode_step(C.byref(c), ok, ok, 32, ok, ok, ok, W, None) == 2     # cache full
+    assert L.nc_decode_step(C.byref(c), ok, None, 5, ok, ok, ok, W, None) == 1
+    assert L.nc_decode_step(C.byref(c), ok, ok, 5, ok, ok, ok, W - 1, None) == 4
+    # more than 16 query heads per KV head is not implemented by the decode attention
+    wide = cfg.with_(n_head=32, d_model=256)
+    assert L.nc_infer_query_sizes(C.byref(lib.to_nc_config(wide)), C.byref(lib.NcInferSizes())) == 5
