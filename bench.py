@@ -32,6 +32,9 @@ from dense_pretraining_amd import config as C  # noqa: E402
 from dense_pretraining_amd import synth  # noqa: E402
 
 METRIC = "train tokens/sec (fwd+bwd) + MFU, depth-20 B=32 T=2048 bf16, 1 MI355X"
+INFER = dict(cfg=C.DEPTH20.with_(batch=64, seq_len=1024 + 256), prompt=1024, steps=256,
+             desc="depth-20 decoder, 64 sequences: 1024-token prefill then 256 greedy decode steps, bf16, "
+                  "one-head K/V cache")
 WORKLOADS = {
     "depth20": (C.DEPTH20, "depth-20 decoder (d 1280, 10x128 heads, 1 KV head, MLP 5120, vocab 65536), "
                            "32 x 2048 tokens, bf16, forward+backward"),
@@ -116,12 +119,123 @@ def cpu_baseline(cfg, p, idx, tg, tokens):
                        f"sequence of {T} tokens (full vocabulary), {dt:.1f} s wall on {threads} BLAS threads")
 
 
+def decode_bytes(cfg, n):
+    """HBM bytes one decode step must move at cache length n: every matrix
+    once, the embedding rows, the K/V cache read and the new K/V written."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    gd = cfg.n_kv_head * cfg.head_dim
+    return (es * (C.matmul_params(cfg) + cfg.batch * cfg.d_model)
+            + es * cfg.depth * cfg.batch * gd * 2 * (n + 1))
+
+
+def bench_infer(a, torch, lib):
+    """Greedy generation: prefill of 64 x 1024 tokens, then decode steps timed
+    as a group (HIP events on the library's stream). The timed generation runs
+    without per-kernel events; a second one, with them, gives the kernel table."""
+    cfg, n_prompt, n_steps = INFER["cfg"], INFER["prompt"], INFER["steps"]
+    torch.cuda.set_device(0)
+    lib.load()
+    p = synth.init_params(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
+                          std=0.02, seed=0, dtype=cfg.dtype, out=np.float32)
+    prompt, _ = synth.zipf_tokens(cfg.vocab, cfg.batch, n_prompt)
+    params = torch.from_numpy(flat_params(p)).to("cuda", lib.torch_dtype(cfg))
+    idx = torch.from_numpy(prompt.reshape(-1).astype(np.int32)).cuda()
+    sz = lib.infer_query_sizes(cfg)
+    cache = lib.alloc_bytes(sz.cache)
+    ws = lib.alloc_bytes(sz.workspace)
+    lib.clear_status(ws)
+    nxt = torch.zeros(cfg.batch, dtype=torch.int32, device="cuda")
+    toks = torch.zeros(cfg.batch, dtype=torch.int32, device="cuda")
+
+    def generate(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        lib.prefill(cfg, params, idx, n_prompt, cache, nxt, ws)
+        e[1].record()
+        for s in range(steps):
+            toks.copy_(nxt)
+            lib.decode_step(cfg, params, toks, n_prompt + s, cache, nxt, ws)
+        e[2].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+
+    for i in range(max(a.warmup, 1)):
+        generate(8)
+        print(f"# warmup {i + 1}", file=sys.stderr, flush=True)
+    t_pre, t_dec = generate(n_steps)
+    timing = not a.no_kernel_timing
+    if timing:
+        lib.profile_enable(True)
+        generate(n_steps)
+        lib.profile_enable(False)
+    st = lib.read_status(ws)
+    ms_step = t_dec / n_steps
+    bytes_step = sum(decode_bytes(cfg, n_prompt + s) for s in range(n_steps)) / n_steps
+    out = {
+        "metric": "decode tokens/s (greedy, KV cache), depth-20, 64 sequences, 1 MI355X",
+        "value": round(cfg.batch * n_steps / (t_dec * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded Zipf(1.1) prompts, N(0, 0.02) weights",
+        "config": {"workload": INFER["desc"], "global_batch": cfg.batch, "seq_len": cfg.seq_len,
+                   "parallelism": "none"},
+        "prefill_tokens_per_s": round(cfg.batch * n_prompt / (t_pre * 1e-3), 1),
+        "prefill_ms": round(t_pre, 3),
+        "roofline": {"bound": "hbm", "achieved": round(bytes_step / (ms_step * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(bytes_step / (ms_step * 1e-3) / PEAK_HBM, 4), "traffic": None,
+                     "kernel": "decode step (all kernels)", "bytes_per_step": round(bytes_step)},
+        "status": st,
+    }
+    if timing:
+        table = kernel_table(lib.profile_summary(), n_steps)
+        out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
+                              if kk in ("ms_per_step", "launches_per_step", "tflops", "gbps")}
+                          for k, v in table.items()}
+    if a.cpu_tokens > 0:
+        print("# timing the CPU oracle sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_infer(cfg, p, prompt, 64)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_infer(cfg, p, prompt, n_prompt, n_steps=8):
+    """The fp64 oracle's cached decode for one sequence after a short prefill
+    (untimed): decode tokens per second. The per-token cost is the weight
+    traffic of the whole model; the context length changes it little."""
+    import oracle
+    from oracle import infer
+    from threadpoolctl import threadpool_info
+
+    oc = oracle.Cfg(depth=cfg.depth, d_model=cfg.d_model, n_head=cfg.n_head, head_dim=cfg.head_dim,
+                    n_kv_head=cfg.n_kv_head, d_ff=cfg.d_ff, vocab=cfg.vocab, batch=1, seq_len=cfg.seq_len,
+                    softcap=cfg.softcap, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
+    cache, z = infer.prefill(oc, p, prompt[:1, :n_prompt])
+    tok = infer.argmax_lowest(z)
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        cache, z = infer.decode_step(oc, p, cache, tok, n_prompt + s)
+        tok = infer.argmax_lowest(z)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return dict(value=round(n_steps / dt, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"fp64 NumPy oracle, {n_steps} cached decode steps of one sequence after a {n_prompt}-token "
+                       f"prefill, {dt:.1f} s wall on {threads} BLAS threads")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="depth20")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["infer"], default="depth20",
+                    help="training step (depth20, depth30) or KV-cache generation (infer)")
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -139,6 +253,8 @@ def main():
     import torch
     from dense_pretraining_amd import lib
 
+    if a.workload == "infer":
+        return bench_infer(a, torch, lib)
     cfg, desc = WORKLOADS[a.workload]
     torch.cuda.set_device(0)
     lib.load()

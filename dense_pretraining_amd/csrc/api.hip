@@ -429,7 +429,7 @@ InferBufs<T> carve_infer(void* ws, const Dims& m) {
   b.h2 = cd.take<T>(B * m.d);
   b.act = cd.take<T>(B * m.F);
   b.r = cd.take<float>(B);
-  const int nch = attn_decode_chunks(m.T, m.es == 2);
+  const int nch = attn_decode_chunks(m.T);
   b.po = cd.take<float>((size_t)B * nch * m.H * m.D);
   b.pl = cd.take<float>((size_t)B * nch * m.H);
   const size_t uni = cp.used > cd.used ? cp.used : cd.used;
@@ -451,7 +451,7 @@ InferBufs<T> carve_infer(void* ws, const Dims& m) {
 
 nc_status infer_dims(const nc_config* cfg, Dims* m) {
   NC_TRY(make_dims(cfg, m, true));
-  if (m->H / m->G > 16) return NC_ERR_UNSUPPORTED;
+  if (m->H / m->G > 32) return NC_ERR_UNSUPPORTED;
   return NC_OK;
 }
 

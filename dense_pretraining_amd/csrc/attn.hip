@@ -196,15 +196,15 @@ struct RowTile {
 // K and V tiles of 64 keys streamed straight into LDS (buffer_load ... lds),
 // in the swizzled layout, through a 2-stage ring: tile t+1 loads while tile
 // t is used, and no registers hold data in flight. Keys at or past T read as
-// zeros.
-template <typename T, int D>
+// zeros. NW waves share the loads of a tile.
+template <typename T, int D, int NW = 4>
 struct KvDma {
   static constexpr int BKV = 64;
   static constexpr int VE = 16 / sizeof(T);
   static constexpr int TILE = BKV * D;        // elements of one K or V tile
   static constexpr int NI = TILE / VE / 64;   // 1 KB loads per tile
-  static constexpr int NPW = 2 * NI / 4;      // per wave, K and V together
-  static_assert((2 * NI) % 4 == 0, "tile loads split evenly over 4 waves");
+  static constexpr int NPW = 2 * NI / NW;     // per wave, K and V together
+  static_assert((2 * NI) % NW == 0, "tile loads split evenly over the waves");
   const T* kbase;
   const T* vbase;
   long ldk, ldv;
@@ -246,8 +246,8 @@ struct KvDma {
 // are separate LDS arrays passed as __restrict__ parameters of this inlined
 // function, so the compiler can tell one stage's loads from the other
 // stage's reads.
-template <typename T, int D, typename Body>
-__device__ __forceinline__ void kv_ring(const KvDma<T, D>& dma, int nkt, T* __restrict__ k0, T* __restrict__ v0,
+template <typename T, int D, int NW, typename Body>
+__device__ __forceinline__ void kv_ring(const KvDma<T, D, NW>& dma, int nkt, T* __restrict__ k0, T* __restrict__ v0,
                                         T* __restrict__ k1, T* __restrict__ v1, Body&& body) {
   dma.issue(0, k0, v0);
   int kt = 0;
@@ -384,6 +384,131 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
         for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(oacc[dt][4 * j + i] * inv);
       }
     if (lh == 0) lse[(tok0 + tq) * g.H + hq] = (m0 + log2f(lsum)) / kLog2e;
+  }
+}
+
+// ============================================================ decode: one query row per head
+// One new position per sequence against the key/value cache. The n_rep query
+// heads that share KV head g form the 32 columns of the score tile (unused
+// columns carry zero queries), so the forward's S^T = K Q^T and O^T = V^T P^T
+// products apply unchanged. Block (c, g, b) takes keys [c*kch, c*kch + kch)
+// through 64-key tiles; wave w takes keys 32w .. 32w+31 of each tile. With the
+// fixed shift the chunks' unnormalised sums merge by plain addition.
+template <typename T, int D, int NST>
+__global__ void __launch_bounds__(128) attn_decode_kernel(const T* __restrict__ q, long ldq, const T* __restrict__ ck,
+                                                          const T* __restrict__ cv, int H, int G, int n, int cap,
+                                                          int kch, float* __restrict__ po, float* __restrict__ pl) {
+  using Kv = KvDma<T, D, 2>;
+  constexpr int BKV = Kv::BKV;
+  __shared__ __align__(16) T ks0[Kv::TILE], vs0[Kv::TILE];
+  __shared__ __align__(16) T ks1[NST > 1 ? Kv::TILE : 8], vs1[NST > 1 ? Kv::TILE : 8];
+
+  const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = (lane >> 4) & 1;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nrep = H / G;
+  const int k_begin = c * kch;
+  const int nk = min(n, k_begin + kch) - k_begin;
+  const int nkt = (nk + BKV - 1) / BKV;
+  const bool hok = l32 < nrep;
+  const long GD = (long)G * D;
+
+  F8<T> qf[D / 16];
+  const T* qrow = q + (long)b * ldq + (long)(g * nrep + (hok ? l32 : 0)) * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qf[s] = gld8<T>(qrow + 16 * s + 8 * lh, hok);
+
+  Kv dma;
+  const long row0 = (long)b * cap + k_begin;
+  dma.init(ck + row0 * GD + (long)g * D, GD, cv + row0 * GD + (long)g * D, GD, nk, wave, lane);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[i][v] = 0.f;
+  float lsum = 0.f;
+  const float c1 = kLog2e / sqrtf((float)D);
+  const float m0 = sqrtf((float)D) * kLog2e;
+
+  auto body = [&](int kt, const T* sk, const T* sv) {
+    const int kb = kt * BKV + 32 * wave;
+    if (kb >= nk) return;
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) mma32(sacc, swz_row8<T, D>(sk, 32 * wave + l32, 16 * s + 8 * lh), qf[s]);
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float e = fast_exp2(sacc[v] * c1 - m0);
+      p[v] = kb + crow(v, lh) < nk ? e : 0.f;
+      lsum += p[v];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const F8<T> pf = pack8<T>(p + 8 * kk);
+      const int k0 = 32 * wave + 16 * kk + 4 * lh;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) mma32(oacc[dt], swz_tr8<T, D>(sv, k0, k0 + 8, 32 * dt + 16 * g16, lane), pf);
+    }
+  };
+
+  if constexpr (NST > 1) {
+    kv_ring<T, D>(dma, nkt, ks0, vs0, ks1, vs1, body);
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) {
+      if (kt) __syncthreads();  // both waves are done with the previous tile
+      dma.issue(kt, ks0, vs0);
+      ring_barrier<0>();
+      body(kt, ks0, vs0);
+    }
+  }
+  lsum += __shfl_xor(lsum, 32, 64);
+
+  // wave 1 hands its sums to wave 0 through the (now idle) K stage
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(ks0);
+  static_assert(Kv::TILE * sizeof(T) >= (D / 32) * 16 * 64 * sizeof(float), "reduction fits in one K stage");
+  if (wave == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[(dt * 16 + v) * 64 + lane] = oacc[dt][v];
+    reinterpret_cast<float*>(vs0)[lane] = lsum;
+  }
+  __syncthreads();
+  if (wave == 0 && hok) {
+    const long prow = ((long)b * gridDim.x + c) * H + (long)g * nrep + l32;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float4 o4;
+        o4.x = oacc[dt][4 * j + 0] + red[(dt * 16 + 4 * j + 0) * 64 + lane];
+        o4.y = oacc[dt][4 * j + 1] + red[(dt * 16 + 4 * j + 1) * 64 + lane];
+        o4.z = oacc[dt][4 * j + 2] + red[(dt * 16 + 4 * j + 2) * 64 + lane];
+        o4.w = oacc[dt][4 * j + 3] + red[(dt * 16 + 4 * j + 3) * 64 + lane];
+        *reinterpret_cast<float4*>(po + prow * D + 32 * dt + 8 * j + 4 * lh) = o4;
+      }
+    if (lh == 0) pl[prow] = lsum + reinterpret_cast<const float*>(vs0)[lane];
+  }
+}
+
+// o[b][h][:] = sum_c po[b][c][h][:] / sum_c pl[b][c][h], chunks in order.
+template <typename T>
+__global__ void attn_decode_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl, int H, int D,
+                                         int nchunk, T* __restrict__ o, long ldo) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  float l = 0.f;
+  for (int c = 0; c < nchunk; ++c) l += pl[((long)b * nchunk + c) * H + h];
+  const float inv = 1.f / l;
+  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
+    float acc = 0.f;
+    for (int c = 0; c < nchunk; ++c) acc += po[(((long)b * nchunk + c) * H + h) * D + dd];
+    o[(long)b * ldo + (long)h * D + dd] = from_f32<T>(acc * inv);
   }
 }
 
@@ -831,6 +956,36 @@ nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, 
   return NC_OK;
 }
 
+// Keys per decode block: one 64-key tile while the grid stays within about
+// five 2-wave blocks per CU, more tiles per block (through the 2-stage ring)
+// for longer caches.
+int decode_chunk_keys(int n, int BG) {
+  const long work = (long)BG * ((n + 63) / 64);
+  const long nt = (work + 1279) / 1280;
+  return 64 * (int)(nt < 1 ? 1 : nt);
+}
+
+template <typename T, int D>
+nc_status attn_decode_impl(const T* q, long ldq, const T* ck, const T* cv, int B, int H, int G, int n, int cap, T* o,
+                           long ldo, float* po, float* pl, hipStream_t st) {
+  const int kch = decode_chunk_keys(n, B * G);
+  const int nchunk = (n + kch - 1) / kch;
+  // reads every cached key and value once, plus the queries, writes the outputs
+  ProfScope prof(NC_NAME(T, "attn_decode"), 4.0 * D * (double)B * H * n,
+                 sizeof(T) * ((double)B * n * G * D * 2.0 + 2.0 * B * H * D), st);
+  dim3 grid(nchunk, G, B);
+  if (kch == 64)
+    hipLaunchKernelGGL((attn_decode_kernel<T, D, 1>), grid, dim3(128), 0, st, q, ldq, ck, cv, H, G, n, cap, kch, po,
+                       pl);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<T, D, 2>), grid, dim3(128), 0, st, q, ldq, ck, cv, H, G, n, cap, kch, po,
+                       pl);
+  NC_LAUNCH_CHECK("attn_decode");
+  hipLaunchKernelGGL((attn_decode_merge_kernel<T>), dim3(H, B), dim3(D), 0, st, po, pl, H, D, nchunk, o, ldo);
+  NC_LAUNCH_CHECK("attn_decode_merge");
+  return NC_OK;
+}
+
 AttnGeom make_geom(const AttnArgs& a) {
   AttnGeom g;
   g.B = a.B; g.T = a.T; g.H = a.H; g.G = a.G; g.D = a.D; g.n_rep = a.H / a.G;
@@ -858,6 +1013,23 @@ nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const
   if (a.D == 64) return attn_bwd_impl<T, 64>(g, qk, v, o, dO, lse, rowstat, dq, dk, dv, ld_dkv, st);
   return NC_ERR_UNSUPPORTED;
 }
+
+int attn_decode_chunks(int cap) { return (cap + 63) / 64; }
+
+template <typename T>
+nc_status attn_decode(const T* q, long ldq, const T* ck, const T* cv, int B, int H, int G, int D, int n, int cap,
+                      T* o, long ldo, float* po, float* pl, hipStream_t st) {
+  if (G < 1 || H % G != 0 || H / G > 32 || n < 1 || n > cap) return NC_ERR_UNSUPPORTED;
+  // the DMA tiles address 64 cache rows through 32-bit offsets
+  if (64.0 * G * D * sizeof(T) >= (double)kDmaOOB) return NC_ERR_UNSUPPORTED;
+  if (D == 128) return attn_decode_impl<T, 128>(q, ldq, ck, cv, B, H, G, n, cap, o, ldo, po, pl, st);
+  if (D == 64) return attn_decode_impl<T, 64>(q, ldq, ck, cv, B, H, G, n, cap, o, ldo, po, pl, st);
+  return NC_ERR_UNSUPPORTED;
+}
+template nc_status attn_decode<bf16>(const bf16*, long, const bf16*, const bf16*, int, int, int, int, int, int, bf16*,
+                                     long, float*, float*, hipStream_t);
+template nc_status attn_decode<float>(const float*, long, const float*, const float*, int, int, int, int, int, int,
+                                      float*, long, float*, float*, hipStream_t);
 
 template nc_status attn_fwd<bf16>(const AttnArgs&, const bf16*, const bf16*, bf16*, float*, hipStream_t);
 template nc_status attn_fwd<float>(const AttnArgs&, const float*, const float*, float*, float*, hipStream_t);

@@ -32,100 +32,6 @@ __global__ void __launch_bounds__(256) kv_store_kernel(const T* __restrict__ k, 
   *reinterpret_cast<uint4*>(cv + dst) = *reinterpret_cast<const uint4*>(v + r * ldv + (long)c * VE);
 }
 
-// One query per head against n cached keys, for the n_rep query heads that
-// share KV head g. Block (chunk c, g, b) takes keys [c*KC, c*KC + KC): it
-// stages them (K rows padded by 16 bytes so that a thread per key reads its
-// row without bank conflicts, V rows plain) and writes the unnormalised
-// partial output sum_t p[t] v[t] and sum_t p[t] per head. QK norm bounds
-// every score by sqrt(D), so p = exp(s - sqrt(D)) with a fixed shift: the
-// chunks merge by plain addition.
-constexpr int kMaxRep = 16;
-template <typename T> constexpr int decode_chunk() { return sizeof(T) == 2 ? 256 : 128; }
-
-template <typename T, int D>
-__global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ q, long ldq, const T* __restrict__ ck,
-                                                          const T* __restrict__ cv, int H, int G, int n, int cap,
-                                                          float* __restrict__ po, float* __restrict__ pl, int nchunk) {
-  constexpr int KC = decode_chunk<T>();
-  constexpr int VE = 16 / sizeof(T);
-  constexpr int KLD = D + VE;  // padded K row
-  __shared__ __align__(16) float qs[kMaxRep][D];
-  __shared__ __align__(16) float ps[kMaxRep][KC];
-  __shared__ __align__(16) T ks[KC * KLD];
-  __shared__ __align__(16) T vs[KC * D];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int nrep = H / G;
-  const int GD = G * D;
-  const float qscale = kLog2e / sqrtf((float)D);
-  for (int i = tid; i < nrep * D; i += KC) {
-    const int j = i / D, dd = i % D;
-    qs[j][dd] = to_f32(q[(long)b * ldq + (long)(g * nrep + j) * D + dd]) * qscale;
-  }
-  const int k0 = c * KC;
-  const T* kb = ck + (long)b * cap * GD + (long)g * D;
-  const T* vb = cv + (long)b * cap * GD + (long)g * D;
-  for (int i = tid; i < KC * (D / VE); i += KC) {
-    const int t = i / (D / VE), cc = i % (D / VE);
-    const int key = k0 + t;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (key < n) {
-      kv = *reinterpret_cast<const uint4*>(kb + (long)key * GD + cc * VE);
-      vv = *reinterpret_cast<const uint4*>(vb + (long)key * GD + cc * VE);
-    }
-    *reinterpret_cast<uint4*>(ks + t * KLD + cc * VE) = kv;
-    *reinterpret_cast<uint4*>(vs + t * D + cc * VE) = vv;
-  }
-  __syncthreads();
-  // scores: thread tid holds key k0 + tid
-  float s[kMaxRep];
-#pragma unroll
-  for (int j = 0; j < kMaxRep; ++j) s[j] = 0.f;
-  for (int cc = 0; cc < D / 4; ++cc) {
-    float kv[4];
-    load4<T>(ks + tid * KLD + 4 * cc, kv);
-#pragma unroll
-    for (int j = 0; j < kMaxRep; ++j) {
-      if (j < nrep) {
-        const float4 qv = *reinterpret_cast<const float4*>(&qs[j][4 * cc]);
-        s[j] += qv.x * kv[0] + qv.y * kv[1] + qv.z * kv[2] + qv.w * kv[3];
-      }
-    }
-  }
-  const bool live = k0 + tid < n;
-  const float m0 = sqrtf((float)D) * kLog2e;
-#pragma unroll
-  for (int j = 0; j < kMaxRep; ++j)
-    if (j < nrep) ps[j][tid] = live ? exp2f(s[j] - m0) : 0.f;
-  __syncthreads();
-  const long pbase = ((long)b * nchunk + c) * H + (long)g * nrep;
-  for (int i = tid; i < nrep * D; i += KC) {
-    const int j = i / D, dd = i % D;
-    float acc = 0.f;
-    for (int t = 0; t < KC; ++t) acc += ps[j][t] * to_f32(vs[t * D + dd]);
-    po[(pbase + j) * D + dd] = acc;
-  }
-  for (int j = tid; j < nrep; j += KC) {
-    float l = 0.f;
-    for (int t = 0; t < KC; ++t) l += ps[j][t];
-    pl[pbase + j] = l;
-  }
-}
-
-// o[b][h][:] = sum_c po[b][c][h][:] / sum_c pl[b][c][h], chunks in order.
-template <typename T>
-__global__ void attn_decode_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl, int H, int D,
-                                         int nchunk, T* __restrict__ o, long ldo) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  float l = 0.f;
-  for (int c = 0; c < nchunk; ++c) l += pl[((long)b * nchunk + c) * H + h];
-  const float inv = 1.f / l;
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float acc = 0.f;
-    for (int c = 0; c < nchunk; ++c) acc += po[(((long)b * nchunk + c) * H + h) * D + dd];
-    o[(long)b * ldo + (long)h * D + dd] = from_f32<T>(acc * inv);
-  }
-}
-
 // out[b] = the lowest v with c tanh(z[b][v] / c) maximal.
 __global__ void __launch_bounds__(256) argmax_softcap_kernel(const float* __restrict__ z, long ldz, int V, float cap,
                                                              int32_t* __restrict__ out) {
@@ -212,33 +118,6 @@ nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int
   return NC_OK;
 }
 
-int attn_decode_chunks(int n, bool bf16_storage) {
-  const int kc = bf16_storage ? decode_chunk<bf16>() : decode_chunk<float>();
-  return (n + kc - 1) / kc;
-}
-
-template <typename T>
-nc_status attn_decode(const T* q, long ldq, const T* ck, const T* cv, int B, int H, int G, int D, int n, int cap,
-                      T* o, long ldo, float* po, float* pl, hipStream_t st) {
-  if (H % G != 0 || H / G > kMaxRep || n < 1 || n > cap) return NC_ERR_UNSUPPORTED;
-  const int nchunk = attn_decode_chunks(n, is_bf16<T>());
-  constexpr int KC = decode_chunk<T>();
-  // reads every cached key and value once, plus the queries
-  ProfScope prof(NC_NAME(T, "attn_decode"), 4.0 * D * (double)B * H * n,
-                 sizeof(T) * ((double)B * n * G * D * 2.0 + 2.0 * B * H * D), st);
-  dim3 grid(nchunk, G, B);
-  if (D == 128)
-    hipLaunchKernelGGL((attn_decode_kernel<T, 128>), grid, dim3(KC), 0, st, q, ldq, ck, cv, H, G, n, cap, po, pl, nchunk);
-  else if (D == 64)
-    hipLaunchKernelGGL((attn_decode_kernel<T, 64>), grid, dim3(KC), 0, st, q, ldq, ck, cv, H, G, n, cap, po, pl, nchunk);
-  else
-    return NC_ERR_UNSUPPORTED;
-  NC_LAUNCH_CHECK("attn_decode");
-  hipLaunchKernelGGL((attn_decode_merge_kernel<T>), dim3(H, B), dim3(D), 0, st, po, pl, H, D, nchunk, o, ldo);
-  NC_LAUNCH_CHECK("attn_decode_merge");
-  return NC_OK;
-}
-
 nc_status argmax_softcap(const float* z, long ldz, int B, int V, float cap, int32_t* out, hipStream_t st) {
   ProfScope prof("argmax_softcap", 0, 4.0 * B * V, st);
   hipLaunchKernelGGL(argmax_softcap_kernel, dim3(B), dim3(256), 0, st, z, ldz, V, cap, out);
@@ -271,8 +150,6 @@ nc_status iota_i32(int32_t* out, int n, int start, int step, hipStream_t st) {
 
 #define NC_INST(T)                                                                                              \
   template nc_status kv_store<T>(const T*, long, const T*, long, T*, T*, int, int, int, int, int, hipStream_t); \
-  template nc_status attn_decode<T>(const T*, long, const T*, const T*, int, int, int, int, int, int, T*, long, \
-                                    float*, float*, hipStream_t);                                              \
   template nc_status splitk_act<T>(const float*, int, int, int, void*, bool, const T*, bool, hipStream_t);
 NC_INST(bf16)
 NC_INST(float)

@@ -95,12 +95,12 @@ template <typename T>
 nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int B, int Tsrc, int pos0, int cap,
                    int GD, hipStream_t st);
 // o [B, H*D] = attention of one query per head (q [B, ld_q], heads in order)
-// over keys 0..n-1 of the cache; po/pl: float scratch of
-// B * attn_decode_chunks(n) * H * (D + 1) elements.
+// over keys 0..n-1 of the cache (attn.hip; H/G <= 32); po/pl: float scratch
+// of B * attn_decode_chunks(cap) * H * (D + 1) elements.
 template <typename T>
 nc_status attn_decode(const T* q, long ldq, const T* ck, const T* cv, int B, int H, int G, int D, int n, int cap,
                       T* o, long ldo, float* po, float* pl, hipStream_t st);
-int attn_decode_chunks(int n, bool bf16_storage);
+int attn_decode_chunks(int cap);
 // out[b] = lowest index of the largest c tanh(z[b][v]/c).
 nc_status argmax_softcap(const float* z, long ldz, int B, int V, float cap, int32_t* out, hipStream_t st);
 template <typename T>

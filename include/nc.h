@@ -212,7 +212,7 @@ typedef struct nc_infer_sizes {
   size_t workspace; /* `workspace` of nc_prefill and nc_decode_step */
 } nc_infer_sizes;
 
-/* Sizes for cfg (NC_ERR_UNSUPPORTED when n_head / n_kv_head > 16). */
+/* Sizes for cfg (NC_ERR_UNSUPPORTED when n_head / n_kv_head > 32). */
 nc_status nc_infer_query_sizes(const nc_config* cfg, nc_infer_sizes* out);
 
 /* Prompt pass. idx [batch, n_prompt] token ids (device), 1 <= n_prompt <=

@@ -136,6 +136,8 @@ def test_inference_arguments_checked_before_launch():
     assert L.nc_decode_step(C.byref(c), ok, ok, 32, ok, ok, ok, W, None) == 2     # cache full
     assert L.nc_decode_step(C.byref(c), ok, None, 5, ok, ok, ok, W, None) == 1
     assert L.nc_decode_step(C.byref(c), ok, ok, 5, ok, ok, ok, W - 1, None) == 4
-    # more than 16 query heads per KV head is not implemented by the decode attention
-    wide = cfg.with_(n_head=32, d_model=256)
+    # more than 32 query heads per KV head is not implemented by the decode attention
+    assert L.nc_infer_query_sizes(C.byref(lib.to_nc_config(cfg.with_(n_head=32, d_model=256))),
+                                  C.byref(lib.NcInferSizes())) == 0
+    wide = cfg.with_(n_head=64, d_model=256)
     assert L.nc_infer_query_sizes(C.byref(lib.to_nc_config(wide)), C.byref(lib.NcInferSizes())) == 5

@@ -34,6 +34,8 @@ SHAPES = {
     "mqa_d64_bf16": _cfg(),
     "gqa_d128_bf16": _cfg(n_head=4, head_dim=128, n_kv_head=2, vocab=520, batch=2, seq_len=40),
     "mqa_d128_f32": _cfg(d_model=256, n_head=2, head_dim=128, vocab=264, batch=2, seq_len=24, dtype="f32"),
+    # 24 query heads on one KV head: 24 of the 32 score-tile columns in use
+    "rep24_d64_bf16": _cfg(n_head=24, vocab=776, batch=2, seq_len=40),
 }
 
 
@@ -156,3 +158,13 @@ def test_depth20_generation_sampled():
     for l in (0, 19):
         assert_close(gc[l, 0, :1, :260], cache[l][0], TOL["bf16"]["act"], f"K cache layer {l}")
         assert_close(gc[l, 1, :1, :260], cache[l][1], TOL["bf16"]["act"], f"V cache layer {l}")
+
+
+def test_long_cache_multi_tile_chunks():
+    """128 sequences x 2 KV heads over ~390 cached keys: the decode attention
+    gives each block two 64-key tiles (the 2-stage ring) with a ragged last
+    chunk."""
+    cfg = _cfg(d_model=128, n_head=4, n_kv_head=2, d_ff=256, vocab=512, batch=128, seq_len=400)
+    p = _params(cfg, seed=5)
+    prompt, _ = synth.zipf_tokens(cfg.vocab, cfg.batch, 389)
+    _run_and_check(cfg, p, prompt, n_steps=4, seed_note="long cache")
