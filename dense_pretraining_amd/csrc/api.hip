@@ -388,12 +388,11 @@ struct InferBufs {
   float *cs, *sn;
   T *px0, *px1;  // [B*cap, d] residual streams of the prompt pass
   BlockSaved<T> ps;
-  int32_t* rows;  // [B] the prompts' last rows
-  T *x, *h1, *qkv, *qk, *o, *x1, *h2, *act;  // one row per sequence
+  T *x, *qk, *o, *x1, *act;  // one row per sequence
   float *r, *po, *pl;
-  T* xf;
-  float *rf, *logits, *partial;
-  size_t partial_elems;
+  float* part;  // split-K partials of the few-row products
+  size_t part_elems;
+  float2* cand;  // [B][column tiles of V] logit maxima
   size_t bytes;
 };
 
@@ -417,16 +416,12 @@ InferBufs<T> carve_infer(void* ws, const Dims& m) {
   b.px0 = cp.take<T>(m.M * m.d);
   b.px1 = cp.take<T>(m.M * m.d);
   b.ps = carve_block_saved<T>(cp, m, false);
-  b.rows = cp.take<int32_t>(m.B);
   Carver cd(u);  // decode step
   const long B = m.B;
   b.x = cd.take<T>(B * m.d);
-  b.h1 = cd.take<T>(B * m.d);
-  b.qkv = cd.take<T>(B * m.QKV);
   b.qk = cd.take<T>(B * m.QK);
   b.o = cd.take<T>(B * m.HD);
   b.x1 = cd.take<T>(B * m.d);
-  b.h2 = cd.take<T>(B * m.d);
   b.act = cd.take<T>(B * m.F);
   b.r = cd.take<float>(B);
   const int nch = attn_decode_chunks(m.T);
@@ -434,17 +429,15 @@ InferBufs<T> carve_infer(void* ws, const Dims& m) {
   b.pl = cd.take<float>((size_t)B * nch * m.H);
   const size_t uni = cp.used > cd.used ? cp.used : cd.used;
   Carver cs(base ? base + kStatusBytes + head + uni : nullptr);
-  b.xf = cs.take<T>(B * m.d);
-  b.rf = cs.take<float>(B);
-  b.logits = cs.take<float>((size_t)B * m.V);
   size_t pe = 0;
   const int shapes[5][2] = {{m.QKV, m.d}, {m.d, m.HD}, {m.F, m.d}, {m.d, m.F}, {m.V, m.d}};
   for (auto& nk : shapes) {
-    const size_t e = gemm_small_partial_elems((int)B, nk[0], nk[1]);
+    const size_t e = skinny_part_elems((int)B, nk[0], nk[1]);
     pe = e > pe ? e : pe;
   }
-  b.partial = cs.take<float>(pe);
-  b.partial_elems = pe;
+  b.part = cs.take<float>(pe ? pe : 1);
+  b.part_elems = pe;
+  b.cand = cs.take<float2>((size_t)B * skinny_col_tiles(m.V));
   b.bytes = kStatusBytes + head + uni + cs.used;
   return b;
 }
@@ -462,13 +455,22 @@ T* cache_at(void* cache, const Dims& m, int l, int kv) {
   return static_cast<T*>(cache) + ((size_t)l * 2 + kv) * m.B * m.T * m.G * m.D;
 }
 
-// Final norm of one row per sequence, softcapped logits in float32, argmax.
+// Final norm of one row per sequence (row b at x + b * ldx), softcapped
+// logits, greedy choice.
 template <typename T>
-nc_status infer_head(const Dims& m, const T* wlm, const T* x, const int32_t* rows, long nrows, const InferBufs<T>& b,
-                     int32_t* next_tok, uint32_t* status, hipStream_t st) {
-  NC_TRY(rmsnorm_fwd<T>(x, rows, (int)nrows, b.xf, b.rf, m.B, m.d, m.eps, status, st));
-  NC_TRY(gemm_xwt_small<T>(b.xf, wlm, b.logits, true, nullptr, false, m.B, m.V, m.d, b.partial, b.partial_elems, st));
-  return argmax_softcap(b.logits, m.V, m.B, m.V, m.cap, next_tok, st);
+nc_status infer_head(const Dims& m, const T* wlm, const T* x, long ldx, const InferBufs<T>& b, int32_t* next_tok,
+                     hipStream_t st) {
+  NC_TRY(gemm_skinny<T>(x, ldx, wlm, m.B, m.V, m.d, true, m.eps, kSkinnyArgmax, nullptr, 0, nullptr, 0, m.cap, b.cand,
+                        b.part, b.part_elems, st));
+  return argmax_cand(b.cand, m.B, skinny_col_tiles(m.V), next_tok, st);
+}
+
+// x W^T for the decode step's rows, with the optional input norm, ReLU^2 and residual.
+template <typename T>
+nc_status decode_mm(const Dims& m, const InferBufs<T>& b, const T* x, long ldx, const T* w, int N, int K, bool norm,
+                    bool relu_sq, T* y, long ldy, const T* res, hipStream_t st) {
+  return gemm_skinny<T>(x, ldx, w, m.B, N, K, norm, m.eps, relu_sq ? kSkinnyReluSq : kSkinnyStore, y, ldy, res, ldy,
+                        0.f, nullptr, b.part, b.part_elems, st);
 }
 
 template <typename T>
@@ -493,8 +495,8 @@ nc_status prefill_t(const Dims& m, const T* params, const int32_t* idx, int n_pr
     x = y;
     y = t;
   }
-  NC_TRY(iota_i32(b.rows, m.B, n_prompt - 1, n_prompt, st));
-  return infer_head<T>(m, params + off[1 + 4 * m.L], x, b.rows, p.M, b, next_tok, nullptr, st);
+  return infer_head<T>(m, params + off[1 + 4 * m.L], x + (size_t)(n_prompt - 1) * m.d, (long)n_prompt * m.d, b,
+                       next_tok, st);
 }
 
 template <typename T>
@@ -505,7 +507,8 @@ nc_status decode_t(const Dims& m, const T* params, const int32_t* tok, int pos, 
   uint32_t* status = static_cast<uint32_t*>(ws);
   const InferBufs<T> b = carve_infer<T>(ws, m);
   const int B = m.B;
-  NC_TRY(rope_table(b.cs, b.sn, pos + 1, m.D, m.base, st));
+  NC_TRY(rope_table(b.cs, b.sn, 1, m.D, m.base, st, pos));  // the one row of position pos
+  const int qkv_split = skinny_plan(B, m.QKV, m.d).nsplit;
   NC_TRY(rmsnorm_fwd<T>(params + off[0], tok, m.V, b.x, b.r, B, m.d, m.eps, status, st));
   for (int l = 0; l < m.L; ++l) {
     const T* wqkv = params + off[1 + 4 * l];
@@ -514,18 +517,16 @@ nc_status decode_t(const Dims& m, const T* params, const int32_t* tok, int pos, 
     const T* w2 = params + off[4 + 4 * l];
     T* ck = cache_at<T>(cache, m, l, 0);
     T* cv = cache_at<T>(cache, m, l, 1);
-    NC_TRY(rmsnorm_fwd<T>(b.x, nullptr, 0, b.h1, b.r, B, m.d, m.eps, nullptr, st));
-    NC_TRY(gemm_xwt_small<T>(b.h1, wqkv, b.qkv, false, nullptr, false, B, m.QKV, m.d, b.partial, b.partial_elems, st));
-    NC_TRY(qknorm_rope_fwd<T>(b.qkv, m.QKV, b.qk, m.QK, b.cs, b.sn, B, 1, m.H + m.G, m.D, m.eps, st, pos));
-    NC_TRY(kv_store<T>(b.qk + (size_t)m.H * m.D, m.QK, b.qkv + (size_t)(m.H + m.G) * m.D, m.QKV, ck, cv, B, 1, pos,
-                       m.T, m.G * m.D, st));
+    NC_TRY(gemm_skinny<T>(b.x, m.d, wqkv, B, m.QKV, m.d, true, m.eps, kSkinnyPartial, nullptr, 0, nullptr, 0, 0.f,
+                          nullptr, b.part, b.part_elems, st));
+    NC_TRY(qkv_finish<T>(b.part, qkv_split, B, m.d, m.H, m.G, m.D, m.eps, b.cs, b.sn, b.qk, m.QK, ck, cv, pos, m.T,
+                         st));
     NC_TRY(attn_decode<T>(b.qk, m.QK, ck, cv, B, m.H, m.G, m.D, pos + 1, m.T, b.o, m.HD, b.po, b.pl, st));
-    NC_TRY(gemm_xwt_small<T>(b.o, wo, b.x1, false, b.x, false, B, m.d, m.HD, b.partial, b.partial_elems, st));
-    NC_TRY(rmsnorm_fwd<T>(b.x1, nullptr, 0, b.h2, b.r, B, m.d, m.eps, nullptr, st));
-    NC_TRY(gemm_xwt_small<T>(b.h2, w1, b.act, false, nullptr, true, B, m.F, m.d, b.partial, b.partial_elems, st));
-    NC_TRY(gemm_xwt_small<T>(b.act, w2, b.x, false, b.x1, false, B, m.d, m.F, b.partial, b.partial_elems, st));
+    NC_TRY(decode_mm<T>(m, b, b.o, m.HD, wo, m.d, m.HD, false, false, b.x1, m.d, b.x, st));
+    NC_TRY(decode_mm<T>(m, b, b.x1, m.d, w1, m.F, m.d, true, true, b.act, m.F, nullptr, st));
+    NC_TRY(decode_mm<T>(m, b, b.act, m.F, w2, m.d, m.F, false, false, b.x, m.d, b.x1, st));
   }
-  return infer_head<T>(m, params + off[1 + 4 * m.L], b.x, nullptr, B, b, next_tok, nullptr, st);
+  return infer_head<T>(m, params + off[1 + 4 * m.L], b.x, m.d, b, next_tok, st);
 }
 
 }  // namespace

@@ -104,47 +104,7 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int a
 namespace {
 // Splits of the reduction for a few-row product: enough workgroups to keep
 // every compute unit streaming W (at most 16 splits, at least 2 k-tiles each).
-void small_split(int M, int N, int K, int bk, int bmn, int& nsplit, int& kper) {
-  const long tiles = (long)((M + bmn - 1) / bmn) * ((N + bmn - 1) / bmn);
-  int s = (int)(kCUs / (tiles > 0 ? tiles : 1));
-  const int maxs = K / (2 * bk);
-  s = s > 16 ? 16 : s;
-  s = s > maxs ? maxs : s;
-  s = s < 1 ? 1 : s;
-  kper = ((K + s - 1) / s + bk - 1) / bk * bk;
-  nsplit = (K + kper - 1) / kper;
-}
 }  // namespace
-
-size_t gemm_small_partial_elems(int M, int N, int K) {
-  int ns, kp, ns2, kp2;
-  small_split(M, N, K, GemmTile<float>::BK, GemmTile<float>::BM, ns, kp);
-  small_split(M, N, K, GemmTile<bf16>::BK, GemmTile<bf16>::BM, ns2, kp2);
-  return (size_t)(ns > ns2 ? ns : ns2) * M * N;
-}
-
-template <typename T>
-nc_status gemm_xwt_small(const T* x, const T* w, void* y, bool y_f32, const T* res, bool relu_sq, int M, int N, int K,
-                         float* partial, size_t partial_elems, hipStream_t st) {
-  if (N % 4 != 0) return NC_ERR_UNSUPPORTED;
-  int nsplit, kper;
-  small_split(M, N, K, GemmTile<T>::BK, GemmTile<T>::BM, nsplit, kper);
-  if (partial == nullptr || partial_elems < (size_t)nsplit * M * N) return NC_ERR_WORKSPACE;
-  GemmShape s{x, w, K, K, M, N, K, kper, nsplit};
-  EpiF32 e;
-  e.C = partial;
-  e.ldc = N;
-  e.split_stride = (long)M * N;
-  e.accumulate = 0;
-  e.M = M;
-  e.N = N;
-  {
-    ProfScope prof(NC_NAME(T, "gemm_small"), 2.0 * M * N * K,
-                   sizeof(T) * ((double)M * K + (double)N * K) + 4.0 * M * N * nsplit, st);
-    NC_TRY((launch_gemm<T, kKc, kKc>(s, e, st)));
-  }
-  return splitk_act<T>(partial, nsplit, M, N, y, y_f32, res, relu_sq, st);
-}
 
 int lmhead_tiles(int N, bool bf16_storage) {
   const int bn = bf16_storage ? GemmTile<bf16>::BN : GemmTile<float>::BN;
@@ -168,8 +128,6 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t, long);         \
   template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t,  \
                                 long);                                                                        \
-  template nc_status gemm_xwt_small<T>(const T*, const T*, void*, bool, const T*, bool, int, int, int, float*,     \
-                                       size_t, hipStream_t);                                                       \
   template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, const int32_t*, float*,     \
                                     float*, hipStream_t);
 NC_INST(bf16)

@@ -13,8 +13,6 @@
 namespace nc {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // cache[b][pos0 + t] = src row (b * Tsrc + t), for the K and V column blocks.
 template <typename T>
 __global__ void __launch_bounds__(256) kv_store_kernel(const T* __restrict__ k, long ldk, const T* __restrict__ v,
@@ -32,80 +30,96 @@ __global__ void __launch_bounds__(256) kv_store_kernel(const T* __restrict__ k, 
   *reinterpret_cast<uint4*>(cv + dst) = *reinterpret_cast<const uint4*>(v + r * ldv + (long)c * VE);
 }
 
-// out[b] = the lowest v with c tanh(z[b][v] / c) maximal.
-__global__ void __launch_bounds__(256) argmax_softcap_kernel(const float* __restrict__ z, long ldz, int V, float cap,
-                                                             int32_t* __restrict__ out) {
-  __shared__ float wv[4];
-  __shared__ int wi[4];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float best = -INFINITY;
-  int bi = V;
-  for (int v = tid; v < V; v += 256) {
-    const float zz = cap * tanhf(z[(long)b * ldz + v] / cap);
-    if (zz > best) {  // v grows: the first maximum of this thread is kept
-      best = zz;
-      bi = v;
-    }
-  }
-  auto better = [](float a, int ia, float c, int ic) { return c > a || (c == a && ic < ia); };
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(best, m, 64);
-    const int oi = __shfl_xor(bi, m, 64);
-    if (better(best, bi, ov, oi)) {
-      best = ov;
-      bi = oi;
-    }
-  }
-  if (lane == 0) {
-    wv[wave] = best;
-    wi[wave] = bi;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < 4; ++w)
-      if (better(best, bi, wv[w], wi[w])) {
-        best = wv[w];
-        bi = wi[w];
-      }
-    out[b] = bi;
-  }
-}
+// One (sequence, head) per LPH = D/8 lanes; lane j holds elements 4j.. of
+// both halves of the head, so the rotation pairs (i, i + D/2) are lane-local.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) qkv_finish_kernel(const float* __restrict__ part, int nsplit, int B, int d,
+                                                         int H, int G, float eps, const float* __restrict__ cs,
+                                                         const float* __restrict__ sn, T* __restrict__ q, long ldq,
+                                                         T* __restrict__ ck, T* __restrict__ cv, int pos, int cap) {
+  constexpr int P = D / 2, LPH = P / 4, HPB = 256 / LPH, U = 4;
+  const int NH = H + 2 * G;
+  const long QKV = (long)NH * D;
+  const long pair = (long)blockIdx.x * HPB + threadIdx.x / LPH;
+  const int j = threadIdx.x % LPH;
+  if (pair >= (long)B * NH) return;  // whole lane groups leave together
+  const int b = (int)(pair / NH), h = (int)(pair - (long)b * NH);
 
-// y = act(sum_z part[z]) (+ res): the split partials in a fixed order.
-template <typename T, typename TO>
-__global__ void __launch_bounds__(256) splitk_act_kernel(const float* __restrict__ part, int nsplit, long n4,
-                                                         TO* __restrict__ y, const T* __restrict__ res, int relu_sq) {
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int zz = 0; zz < nsplit; ++zz) {
-      const float4 p = reinterpret_cast<const float4*>(part + (long)zz * n4 * 4)[i];
-      a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
-    }
-    float v[4] = {a.x, a.y, a.z, a.w};
-    if (relu_sq) {
+  // split-K sum in split order, loads of U splits in flight together
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, c[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* src = part + (long)b * QKV + (long)h * D + 4 * j;
+  const long zs = (long)B * QKV;
+  for (int z0 = 0; z0 < nsplit; z0 += U) {
+    float4 pa[U], pb[U];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float r = fmaxf(v[e], 0.f);
-        v[e] = r * r;
+    for (int u = 0; u < U; ++u)
+      if (z0 + u < nsplit) {
+        pa[u] = *reinterpret_cast<const float4*>(src + (z0 + u) * zs);
+        pb[u] = *reinterpret_cast<const float4*>(src + (z0 + u) * zs + P);
       }
-    }
-    if (res) {
-      float rr[4];
-      load4<T>(res + 4 * i, rr);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += rr[e];
-    }
-    store4<TO>(y + 4 * i, v);
+    for (int u = 0; u < U; ++u)
+      if (z0 + u < nsplit) {
+        a[0] += pa[u].x; a[1] += pa[u].y; a[2] += pa[u].z; a[3] += pa[u].w;
+        c[0] += pb[u].x; c[1] += pb[u].y; c[2] += pb[u].z; c[3] += pb[u].w;
+      }
   }
-}
-
-__global__ void iota_i32_kernel(int32_t* __restrict__ out, int n, int start, int step) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = start + i * step;
+  // the block's input RMSNorm, applied to the product: N(x) W^T = (x W^T) / rms(x)
+  const float* ssp = part + (long)nsplit * zs;
+  float ss = 0.f;
+  for (int zz = 0; zz < nsplit; ++zz) ss += ssp[(long)zz * B + b];
+  const float rs = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] *= rs;
+    c[e] *= rs;
+  }
+  const long GD = (long)G * D;
+  if (h >= H + G) {  // value head: stored as is
+    T* dst = cv + ((long)b * cap + pos) * GD + (long)(h - H - G) * D + 4 * j;
+    store4<T>(dst, a);
+    store4<T>(dst + P, c);
+    return;
+  }
+  float sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sq += a[e] * a[e] + c[e] * c[e];
+  const float rr = 1.f / sqrtf(group_sum(sq, LPH) / (float)D + eps);
+  const float4 c4 = *reinterpret_cast<const float4*>(cs + 4 * j);
+  const float4 s4 = *reinterpret_cast<const float4*>(sn + 4 * j);
+  const float co[4] = {c4.x, c4.y, c4.z, c4.w}, si[4] = {s4.x, s4.y, s4.z, s4.w};
+  float oa[4], ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float ya = a[e] * rr, yb = c[e] * rr;
+    oa[e] = ya * co[e] - yb * si[e];
+    ob[e] = ya * si[e] + yb * co[e];
+  }
+  T* dst = h < H ? q + (long)b * ldq + (long)h * D + 4 * j
+                 : ck + ((long)b * cap + pos) * GD + (long)(h - H) * D + 4 * j;
+  store4<T>(dst, oa);
+  store4<T>(dst + P, ob);
 }
 
 }  // namespace
+
+template <typename T>
+nc_status qkv_finish(const float* part, int nsplit, int B, int d, int H, int G, int D, float eps, const float* cs,
+                     const float* sn, T* q, long ldq, T* ck, T* cv, int pos, int cap, hipStream_t st) {
+  const long pairs = (long)B * (H + 2 * G);
+  ProfScope prof(NC_NAME(T, "qkv_finish"), 0,
+                 4.0 * nsplit * pairs * D + sizeof(T) * (double)pairs * D, st);
+  if (D == 128)
+    hipLaunchKernelGGL((qkv_finish_kernel<T, 128>), dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, st, part, nsplit,
+                       B, d, H, G, eps, cs, sn, q, ldq, ck, cv, pos, cap);
+  else if (D == 64)
+    hipLaunchKernelGGL((qkv_finish_kernel<T, 64>), dim3((unsigned)((pairs + 31) / 32)), dim3(256), 0, st, part, nsplit,
+                       B, d, H, G, eps, cs, sn, q, ldq, ck, cv, pos, cap);
+  else
+    return NC_ERR_UNSUPPORTED;
+  NC_LAUNCH_CHECK("qkv_finish");
+  return NC_OK;
+}
 
 template <typename T>
 nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int B, int Tsrc, int pos0, int cap,
@@ -118,39 +132,10 @@ nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int
   return NC_OK;
 }
 
-nc_status argmax_softcap(const float* z, long ldz, int B, int V, float cap, int32_t* out, hipStream_t st) {
-  ProfScope prof("argmax_softcap", 0, 4.0 * B * V, st);
-  hipLaunchKernelGGL(argmax_softcap_kernel, dim3(B), dim3(256), 0, st, z, ldz, V, cap, out);
-  NC_LAUNCH_CHECK("argmax_softcap");
-  return NC_OK;
-}
-
-template <typename T>
-nc_status splitk_act(const float* part, int nsplit, int M, int N, void* y, bool y_f32, const T* res, bool relu_sq,
-                     hipStream_t st) {
-  const long n4 = (long)M * N / 4;
-  const long nb = (n4 + 255) / 256;
-  const unsigned grid = (unsigned)(nb < 4096 ? nb : 4096);
-  ProfScope prof("splitk_act", 0, 4.0 * M * N * nsplit + (y_f32 ? 4.0 : (double)sizeof(T)) * M * N, st);
-  if (y_f32)
-    hipLaunchKernelGGL((splitk_act_kernel<T, float>), dim3(grid), dim3(256), 0, st, part, nsplit, n4,
-                       static_cast<float*>(y), res, relu_sq ? 1 : 0);
-  else
-    hipLaunchKernelGGL((splitk_act_kernel<T, T>), dim3(grid), dim3(256), 0, st, part, nsplit, n4, static_cast<T*>(y),
-                       res, relu_sq ? 1 : 0);
-  NC_LAUNCH_CHECK("splitk_act");
-  return NC_OK;
-}
-
-nc_status iota_i32(int32_t* out, int n, int start, int step, hipStream_t st) {
-  hipLaunchKernelGGL(iota_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, out, n, start, step);
-  NC_LAUNCH_CHECK("iota");
-  return NC_OK;
-}
-
-#define NC_INST(T)                                                                                              \
-  template nc_status kv_store<T>(const T*, long, const T*, long, T*, T*, int, int, int, int, int, hipStream_t); \
-  template nc_status splitk_act<T>(const float*, int, int, int, void*, bool, const T*, bool, hipStream_t);
+#define NC_INST(T)                                                                                                 \
+  template nc_status kv_store<T>(const T*, long, const T*, long, T*, T*, int, int, int, int, int, hipStream_t);    \
+  template nc_status qkv_finish<T>(const float*, int, int, int, int, int, int, float, const float*, const float*, T*, \
+                                   long, T*, T*, int, int, hipStream_t);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST

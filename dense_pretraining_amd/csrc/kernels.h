@@ -46,13 +46,28 @@ template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
                       float* part, float* zt, hipStream_t st);
 int lmhead_tiles(int N, bool bf16_storage);
-// y = act(x[M,K] W[N,K]^T) (+ res) for a few rows (M up to a tile): the
-// reduction is split so that enough workgroups stream W, the float32 partials
-// are summed in a fixed order; y in the storage type or float32.
+
+// ------------------------------------------------------------ few-row products (skinny.hip)
+// y = epi(diag(s) x[M,K] W[N,K]^T) (+ res), s[m] = 1/rms(x[m]) when norm, else 1.
+// epi: kSkinnyStore, kSkinnyReluSq, or kSkinnyArgmax (cand[m][t] = the largest
+// c tanh(.. / c) of row m over column tile t and its column; y unused).
+// K % 64 == 0, N % 8 == 0. part: float scratch of skinny_part_elems(M, N, K)
+// for the partial sums of a K split (none needed when that is 0).
+// kSkinnyPartial: only the float32 partial sums (and sums of squares) are
+// written to part, even unsplit, for a caller-supplied finishing kernel.
+enum { kSkinnyStore = 0, kSkinnyReluSq = 1, kSkinnyArgmax = 2, kSkinnyPartial = 3 };
+struct SkinnyPlan {
+  int mt, nmt, ntn, nsplit, kper;
+};
+SkinnyPlan skinny_plan(int M, int N, int K);
+size_t skinny_part_elems(int M, int N, int K);  // at least M * (N + 1) for kSkinnyPartial
+int skinny_col_tiles(int N);
 template <typename T>
-nc_status gemm_xwt_small(const T* x, const T* w, void* y, bool y_f32, const T* res, bool relu_sq, int M, int N, int K,
-                         float* partial, size_t partial_elems, hipStream_t st);
-size_t gemm_small_partial_elems(int M, int N, int K);
+nc_status gemm_skinny(const T* x, long ldx, const T* w, int M, int N, int K, bool norm, float eps, int epi, T* y,
+                      long ldy, const T* res, long ldres, float cap, float2* cand, float* part, size_t part_elems,
+                      hipStream_t st);
+// out[m] = the column of the largest of cand[m][0 .. ntn) (ties: lowest column).
+nc_status argmax_cand(const float2* cand, int M, int ntn, int32_t* out, hipStream_t st);
 
 // ------------------------------------------------------------ rows (rows.hip)
 nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
@@ -65,7 +80,8 @@ nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int
 template <typename T, typename TO>
 nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO* dx, int M, int d, hipStream_t st);
 // cos/sin [T, D/2] of t * base^(-2i/D), evaluated in double.
-nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st);
+// Rows t0 .. t0+T-1 of the rotation table, written to rows 0 .. T-1.
+nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st, int t0 = 0);
 // Per token and head (H+G heads): N_D then rotate; qkv [M, ld_in] -> qk [M, ld_out].
 // Row m is at position pos0 + m % T_.
 template <typename T>
@@ -94,6 +110,13 @@ nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, 
 template <typename T>
 nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int B, int Tsrc, int pos0, int cap,
                    int GD, hipStream_t st);
+// Decode step's attention inputs from the split-K partials of x W_qkv^T
+// (gemm_skinny with kSkinnyPartial, nsplit splits): sum, input RMSNorm scale,
+// QK norm and rotation (cs/sn: the table row of position pos); q heads to
+// q [B, ldq], the new key and value to position pos of the cache.
+template <typename T>
+nc_status qkv_finish(const float* part, int nsplit, int B, int d, int H, int G, int D, float eps, const float* cs,
+                     const float* sn, T* q, long ldq, T* ck, T* cv, int pos, int cap, hipStream_t st);
 // o [B, H*D] = attention of one query per head (q [B, ld_q], heads in order)
 // over keys 0..n-1 of the cache (attn.hip; H/G <= 32); po/pl: float scratch
 // of B * attn_decode_chunks(cap) * H * (D + 1) elements.
@@ -101,12 +124,6 @@ template <typename T>
 nc_status attn_decode(const T* q, long ldq, const T* ck, const T* cv, int B, int H, int G, int D, int n, int cap,
                       T* o, long ldo, float* po, float* pl, hipStream_t st);
 int attn_decode_chunks(int cap);
-// out[b] = lowest index of the largest c tanh(z[b][v]/c).
-nc_status argmax_softcap(const float* z, long ldz, int B, int V, float cap, int32_t* out, hipStream_t st);
-template <typename T>
-nc_status splitk_act(const float* part, int nsplit, int M, int N, void* y, bool y_f32, const T* res, bool relu_sq,
-                     hipStream_t st);
-nc_status iota_i32(int32_t* out, int n, int start, int step, hipStream_t st);
 
 // ------------------------------------------------------------ attention (attn.hip)
 struct AttnArgs {

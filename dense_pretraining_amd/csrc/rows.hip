@@ -129,11 +129,11 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const T* __restrict__ 
 // Rotary embedding (architecture list on vpshk.cn): pair (i, i + D/2) of a
 // head at position t turns by t * base^(-2i/D). The table is evaluated in
 // double precision.
-__global__ void rope_table_kernel(float* cs, float* sn, int T, int D, float base) {
+__global__ void rope_table_kernel(float* cs, float* sn, int T, int D, float base, int t0) {
   int P = D / 2;
   int n = T * P;
   for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n; k += gridDim.x * blockDim.x) {
-    int t = k / P, i = k % P;
+    int t = t0 + k / P, i = k % P;
     double omega = pow((double)base, -2.0 * (double)i / (double)D);
     double ang = (double)t * omega;
     cs[k] = (float)cos(ang);
@@ -388,9 +388,10 @@ nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO*
   return NC_OK;
 }
 
-nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st) {
+nc_status rope_table(float* cs, float* sn, int T, int D, float base, hipStream_t st, int t0) {
   ProfScope prof("rope_table", 0, 4.0 * T * D, st);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)T * D / 2, 256)), dim3(256), 0, st, cs, sn, T, D, base);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)T * D / 2, 256)), dim3(256), 0, st, cs, sn, T, D, base,
+                     t0);
   NC_LAUNCH_CHECK("rope_table");
   return NC_OK;
 }
