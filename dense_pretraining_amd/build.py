@@ -65,7 +65,8 @@ def build(jobs=None, extra=None, verbose=False):
     if failed:
         raise RuntimeError("hipcc compilation failed")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: an unresolved symbol (say, a kernel stub never instantiated) fails here, not at load time
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         print(p.stderr, file=sys.stderr)
