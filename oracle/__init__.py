@@ -35,3 +35,4 @@ from .model import (  # noqa: F401
     model_forward_logits,
 )
 from . import infer  # noqa: F401  (greedy generation with a key/value cache)
+from . import optim  # noqa: F401  (the optimizer step: Muon and AdamW)
