@@ -529,6 +529,69 @@ nc_status decode_t(const Dims& m, const T* params, const int32_t* tok, int pos, 
   return infer_head<T>(m, params + off[1 + 4 * m.L], b.x, m.d, b, next_tok, st);
 }
 
+// ---------------------------------------------------------------- optimizer
+// The block matrices of layer l as (offset, rows, cols) in the parameter
+// layout: Wq, Wk, Wv (row blocks of the packed projection), Wo, W1, W2.
+struct MatSpec {
+  size_t off;
+  int R, C;
+};
+void layer_matrices(const Dims& m, const size_t* off, int l, MatSpec* out) {
+  const size_t q = off[1 + 4 * l];
+  out[0] = {q, m.H * m.D, m.d};
+  out[1] = {q + (size_t)m.H * m.D * m.d, m.G * m.D, m.d};
+  out[2] = {q + (size_t)(m.H + m.G) * m.D * m.d, m.G * m.D, m.d};
+  out[3] = {off[2 + 4 * l], m.d, m.HD};
+  out[4] = {off[3 + 4 * l], m.F, m.d};
+  out[5] = {off[4 + 4 * l], m.d, m.F};
+}
+
+size_t opt_workspace_bytes(const Dims& m) {
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  param_offsets(m, off.data());
+  MatSpec ms[6];
+  layer_matrices(m, off.data(), 0, ms);
+  size_t w = 0;
+  for (const MatSpec& x : ms) {
+    const size_t b = muon_work_bytes(x.R, x.C, m.es == 2);
+    w = b > w ? b : w;
+  }
+  return w;
+}
+
+bool hparams_ok(const nc_opt_hparams* h) {
+  auto fin = [](float v) { return v == v && v < 3.0e38f && v > -3.0e38f; };
+  return h && fin(h->lr_matrix) && fin(h->lr_embed) && fin(h->lr_unembed) && h->lr_matrix >= 0.f &&
+         h->lr_embed >= 0.f && h->lr_unembed >= 0.f && h->momentum >= 0.f && h->momentum < 1.f &&
+         h->beta1 >= 0.f && h->beta1 < 1.f && h->beta2 >= 0.f && h->beta2 < 1.f && h->eps > 0.f && fin(h->eps) &&
+         h->wd_matrix >= 0.f && h->wd_adam >= 0.f && fin(h->wd_matrix) && fin(h->wd_adam) && h->step >= 1 &&
+         (h->nesterov == 0 || h->nesterov == 1);
+}
+
+template <typename T>
+nc_status opt_step_t(const Dims& m, const nc_opt_hparams& h, T* params, const float* grads, float* state, void* ws,
+                     size_t ws_bytes, hipStream_t st) {
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  const size_t n = param_offsets(m, off.data());
+  float* master = state;
+  float* s1 = state + n;
+  float* s2 = s1 + n;
+  const size_t vd = (size_t)m.V * m.d;
+  const size_t lm = off[1 + 4 * m.L];
+  NC_TRY(adamw_step<T>(grads, master, s1, s2, params, vd, h.lr_embed, h.beta1, h.beta2, h.eps, h.wd_adam, h.step,
+                       st));
+  NC_TRY(adamw_step<T>(grads + lm, master + lm, s1 + lm, s2 + vd, params + lm, vd, h.lr_unembed, h.beta1, h.beta2,
+                       h.eps, h.wd_adam, h.step, st));
+  for (int l = 0; l < m.L; ++l) {
+    MatSpec ms[6];
+    layer_matrices(m, off.data(), l, ms);
+    for (const MatSpec& x : ms)
+      NC_TRY(muon_step<T>(grads + x.off, s1 + x.off, master + x.off, params + x.off, x.R, x.C, h.lr_matrix,
+                          h.momentum, h.nesterov, h.wd_matrix, ws, ws_bytes, st));
+  }
+  return NC_OK;
+}
+
 }  // namespace
 }  // namespace nc
 
@@ -779,6 +842,46 @@ nc_status nc_decode_step(const nc_config* cfg, const void* params, const int32_t
   }
   if (workspace_bytes < carve_infer<float>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
   return decode_t<float>(m, static_cast<const float*>(params), tok, pos, cache, next_tok, workspace, st);
+}
+
+nc_status nc_opt_query_sizes(const nc_config* cfg, nc_opt_sizes* out) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, true));
+  if (!out) return NC_ERR_INVALID_ARG;
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  const size_t n = param_offsets(m, off.data());
+  out->state = 4 * (2 * n + 2 * (size_t)m.V * m.d);
+  out->workspace = opt_workspace_bytes(m);
+  return NC_OK;
+}
+
+nc_status nc_opt_init(const nc_config* cfg, const void* params, void* state, void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, true));
+  if (!params || !state) return NC_ERR_INVALID_ARG;
+  if (!aligned(params) || !aligned(state)) return NC_ERR_ALIGN;
+  std::vector<size_t> off(2 + 4 * (size_t)m.L);
+  const size_t n = param_offsets(m, off.data());
+  float* sp = static_cast<float*>(state);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t n2 = 2 * (size_t)m.V * m.d;
+  if (m.es == 2) return opt_init<bf16>(static_cast<const bf16*>(params), sp, sp + n, n, sp + 2 * n, n2, st);
+  return opt_init<float>(static_cast<const float*>(params), sp, sp + n, n, sp + 2 * n, n2, st);
+}
+
+nc_status nc_opt_step(const nc_config* cfg, const nc_opt_hparams* hp, void* params, const float* grads, void* state,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Dims m;
+  NC_TRY(make_dims(cfg, &m, true));
+  if (!hparams_ok(hp) || !params || !grads || !state || !workspace) return NC_ERR_INVALID_ARG;
+  if (!aligned(params) || !aligned(grads) || !aligned(state) || !aligned(workspace)) return NC_ERR_ALIGN;
+  if (workspace_bytes < opt_workspace_bytes(m)) return NC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m.es == 2)
+    return opt_step_t<bf16>(m, *hp, static_cast<bf16*>(params), grads, static_cast<float*>(state), workspace,
+                            workspace_bytes, st);
+  return opt_step_t<float>(m, *hp, static_cast<float*>(params), grads, static_cast<float*>(state), workspace,
+                           workspace_bytes, st);
 }
 
 nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const int32_t* idx, const int32_t* targets,

@@ -327,6 +327,31 @@ struct EpiStore {
   }
 };
 
+// y = alpha * acc + beta * res (res optional), stored in T: the steps of the
+// Newton-Schulz iteration (B = c (A A^T) + b A, X' = (X B^T) + a X).
+template <typename T>
+struct EpiAxpby {
+  NC_EPI_NO_ROW_WORK
+  T* C;
+  long ldc;
+  const T* res;
+  long ldr;
+  int M, N;
+  float alpha, beta;
+  using Aux = Aux4<T>;
+  __device__ __forceinline__ Aux load_aux(int row, int col) const {
+    return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
+  }
+  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
+    if (row >= M || col >= N) return;
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+    if (res) aux_get<T>(a, r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = alpha * v[e] + beta * r[e];
+    store4<T>(C + (long)row * ldc + col, v);
+  }
+};
+
 // du = acc * 2 max(u, 0), the input gradient of a = max(u, 0)^2, from the
 // stored activation a: max(u, 0) = sqrt(a).
 template <typename T>

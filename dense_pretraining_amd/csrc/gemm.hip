@@ -52,6 +52,17 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
 }
 
 template <typename T>
+nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int N, int K, float alpha, float beta,
+                         hipStream_t st) {
+  GemmShape s{x, w, K, K, M, N, K, K, 1};
+  const double es = sizeof(T);
+  ProfScope prof(NC_NAME(T, "gemm_ns"), 2.0 * M * N * K,
+                 es * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
+  EpiAxpby<T> e{y, N, res, N, M, N, alpha, beta};
+  return launch_gemm<T, kKc, kKc>(s, e, st);
+}
+
+template <typename T>
 nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
                    long dy_panel) {
   // C[M,K] = A[M,N] * B where B(n=k_out, k=n_in) = W[n_in][k_out]: K-outer.
@@ -125,6 +136,8 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
 
 #define NC_INST(T)                                                                                            \
   template nc_status gemm_xwt<T>(const T*, const T*, T*, const T*, int, int, int, bool, hipStream_t);        \
+  template nc_status gemm_xwt_axpby<T>(const T*, const T*, T*, const T*, int, int, int, float, float,          \
+                                       hipStream_t);                                                          \
   template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t, long);         \
   template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t,  \
                                 long);                                                                        \

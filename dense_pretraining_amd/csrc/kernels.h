@@ -31,6 +31,10 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
 // dx[M,K] = dy[M,N] W[N,K]; with act = max(u,0)^2 given, dx = (dy W) * 2 sqrt(act),
 // the input gradient of the ReLU^2 activation.
 // dy_panel: dy stored in column panels (stride dy_panel elements), else 0.
+// y[M,N] = alpha * x[M,K] w[N,K]^T + beta * res (res optional, [M,N]).
+template <typename T>
+nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int N, int K, float alpha, float beta,
+                         hipStream_t st);
 template <typename T>
 nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
                    long dy_panel = 0);
@@ -140,6 +144,21 @@ template <typename T>
 // pairs the dQ pass hands to the dK/dV pass.
 nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const T* dO, const float* lse,
                    float* rowstat, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st);
+
+// ------------------------------------------------------------ optimizer (opt.hip)
+// master = widen(params), s1 = 0 (n elements), s2 = 0 (n2 elements).
+template <typename T>
+nc_status opt_init(const T* params, float* master, float* s1, size_t n, float* s2, size_t n2, hipStream_t st);
+// AdamW over n elements (n % 4 == 0): m, v, w updated in place, p = w in the storage type.
+template <typename T>
+nc_status adamw_step(const float* g, float* w, float* m, float* v, T* p, size_t n, float lr, float beta1,
+                     float beta2, float eps, float wd, int step, hipStream_t st);
+// One Muon step of the matrix w [R, C] (float32 master, p its stored copy)
+// with gradient g and momentum mom; work: muon_work_bytes(R, C, bf16) bytes.
+template <typename T>
+nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, float lr, float mu, int nesterov,
+                    float wd, void* work, size_t work_bytes, hipStream_t st);
+size_t muon_work_bytes(int R, int C, bool bf16_storage);
 
 // ------------------------------------------------------------ embedding grad (embed_bwd.hip)
 struct EmbedSortBufs {

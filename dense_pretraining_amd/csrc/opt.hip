@@ -1,0 +1,279 @@
+// The optimizer step: AdamW for the embedding and the unembedding, Muon for
+// every block matrix (the page on vpshk.cn, Q&A "卡帕西亲自揭秘背后技术",
+// names Muon + AdamW; imeisheng.com, section "预训练", assigns Muon to the
+// matrices and AdamW to the embedding and unembedding). Muon follows its
+// published definition (K. Jordan, 2024): Nesterov momentum, then five steps
+// of the quintic Newton-Schulz map X <- a X + b (X X^T) X + c (X X^T)^2 X on
+// the update scaled to unit Frobenius norm, written for the wide orientation
+// (a matrix with more rows than columns is transposed first) so that the
+// Gram matrix is the small side squared. Here every matrix is handled in its
+// tall orientation instead (a wide one is transposed on the way in and out),
+// where the same map reads
+//   A = X^T X,  B = b A + c A^2,  X <- a X + X B     (B is symmetric).
+//
+// HBM layout of the caller's optimizer state (float32, parameter layout of
+// nc_param_layout): master weights [n_params]; s1 [n_params] holding AdamW's
+// first moment in the embedding and unembedding ranges and Muon's momentum in
+// the block matrices; s2 [2 V d] holding AdamW's second moment of the
+// embedding then of the unembedding.
+#include <cmath>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+namespace {
+
+constexpr int kNormParts = 1024;  // blocks of the momentum pass (partial sums of squares)
+constexpr int kTile = 32;         // transposing tile of the layout kernels
+
+template <typename T>
+__global__ void __launch_bounds__(256) opt_init_kernel(const T* __restrict__ p, float* __restrict__ master,
+                                                       float* __restrict__ s1, long n, float* __restrict__ s2,
+                                                       long n2) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    master[i] = to_f32(p[i]);
+    s1[i] = 0.f;
+  }
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n2; i += (long)gridDim.x * 256) s2[i] = 0.f;
+}
+
+// AdamW on n4 groups of 4: m, v updated in place, w <- w (1 - lr wd) - lr m_hat / (sqrt(v_hat) + eps),
+// p = w in the storage type. c1, c2 = 1 / (1 - beta^t).
+template <typename T>
+__global__ void __launch_bounds__(256) adamw_kernel(const float* __restrict__ g, float* __restrict__ w,
+                                                    float* __restrict__ m, float* __restrict__ v, T* __restrict__ p,
+                                                    long n4, float lr, float b1, float b2, float c1, float c2,
+                                                    float eps, float decay) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    const float4 gg = reinterpret_cast<const float4*>(g)[i];
+    float4 ww = reinterpret_cast<float4*>(w)[i], mm = reinterpret_cast<float4*>(m)[i],
+           vv = reinterpret_cast<float4*>(v)[i];
+    float ga[4] = {gg.x, gg.y, gg.z, gg.w}, wa[4] = {ww.x, ww.y, ww.z, ww.w}, ma[4] = {mm.x, mm.y, mm.z, mm.w},
+          va[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ma[e] = b1 * ma[e] + (1.f - b1) * ga[e];
+      va[e] = b2 * va[e] + (1.f - b2) * ga[e] * ga[e];
+      wa[e] = wa[e] * decay - lr * (ma[e] * c1) / (sqrtf(va[e] * c2) + eps);
+    }
+    reinterpret_cast<float4*>(w)[i] = make_float4(wa[0], wa[1], wa[2], wa[3]);
+    reinterpret_cast<float4*>(m)[i] = make_float4(ma[0], ma[1], ma[2], ma[3]);
+    reinterpret_cast<float4*>(v)[i] = make_float4(va[0], va[1], va[2], va[3]);
+    store4<T>(p + 4 * i, wa);
+  }
+}
+
+// Momentum pass: mom <- mu mom + g; the update U = g + mu mom (Nesterov) or mom;
+// part[block] = sum of U^2 over the block's elements (grid of kNormParts blocks).
+__global__ void __launch_bounds__(256) muon_mom_kernel(const float* __restrict__ g, float* __restrict__ mom, long n4,
+                                                       float mu, int nesterov, float* __restrict__ part) {
+  __shared__ float red[4];
+  float acc = 0.f;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    const float4 gg = reinterpret_cast<const float4*>(g)[i];
+    float4 mm = reinterpret_cast<float4*>(mom)[i];
+    mm.x = mu * mm.x + gg.x;
+    mm.y = mu * mm.y + gg.y;
+    mm.z = mu * mm.z + gg.z;
+    mm.w = mu * mm.w + gg.w;
+    reinterpret_cast<float4*>(mom)[i] = mm;
+    const float u0 = nesterov ? gg.x + mu * mm.x : mm.x, u1 = nesterov ? gg.y + mu * mm.y : mm.y;
+    const float u2 = nesterov ? gg.z + mu * mm.z : mm.z, u3 = nesterov ? gg.w + mu * mm.w : mm.w;
+    acc += u0 * u0 + u1 * u1 + u2 * u2 + u3 * u3;
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+// 1 / (|U|_F + 1e-7) from the momentum pass's partial sums, in a fixed order.
+__device__ __forceinline__ float inv_frobenius(const float* part, float* sh) {
+  float s = 0.f;
+  for (int i = threadIdx.x; i < kNormParts; i += 256) s += part[i];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  return 1.f / (sqrtf(sh[0] + sh[1] + sh[2] + sh[3]) + 1e-7f);
+}
+
+// X (tall layout, T) = U / |U|_F for U [R][C] (U recomputed from g and the new
+// momentum). transpose: X[c][r] = U[r][c]. One 32 x 32 tile per block.
+template <typename T>
+__global__ void __launch_bounds__(256) muon_norm_kernel(const float* __restrict__ g, const float* __restrict__ mom,
+                                                        int R, int C, int transpose, float mu, int nesterov,
+                                                        const float* __restrict__ part, T* __restrict__ X) {
+  __shared__ float sh[4];
+  __shared__ float tile[kTile][kTile + 1];
+  const float inv = inv_frobenius(part, sh);
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int j = ty; j < kTile; j += 8) {
+    const int r = r0 + j, c = c0 + tx;
+    float u = 0.f;
+    if (r < R && c < C) {
+      const long i = (long)r * C + c;
+      u = nesterov ? g[i] + mu * mom[i] : mom[i];
+    }
+    if (!transpose) {
+      if (r < R && c < C) X[(long)r * C + c] = from_f32<T>(u * inv);
+    } else {
+      tile[j][tx] = u * inv;
+    }
+  }
+  if (!transpose) return;
+  __syncthreads();
+  for (int j = ty; j < kTile; j += 8) {  // X [C][R]: row c0 + j, column r0 + tx
+    const int c = c0 + j, r = r0 + tx;
+    if (r < R && c < C) X[(long)c * R + r] = from_f32<T>(tile[tx][j]);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) cast_f32_kernel(const float* __restrict__ a, T* __restrict__ b, long n4) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    const float4 v = reinterpret_cast<const float4*>(a)[i];
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    store4<T>(b + 4 * i, f);
+  }
+}
+
+// w[r][c] <- w[r][c] decay - step X (X in the tall layout, read transposed
+// when the matrix is wide); p = w in the storage type.
+template <typename T>
+__global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, T* __restrict__ p,
+                                                         const T* __restrict__ X, int R, int C, int transpose,
+                                                         float decay, float step) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  if (transpose) {
+    for (int j = ty; j < kTile; j += 8) {  // X [C][R]: row c0 + j, column r0 + tx
+      const int c = c0 + j, r = r0 + tx;
+      tile[j][tx] = (r < R && c < C) ? to_f32(X[(long)c * R + r]) : 0.f;
+    }
+    __syncthreads();
+  }
+  for (int j = ty; j < kTile; j += 8) {
+    const int r = r0 + j, c = c0 + tx;
+    if (r >= R || c >= C) continue;
+    const long i = (long)r * C + c;
+    const float x = transpose ? tile[tx][j] : to_f32(X[i]);
+    const float nw = w[i] * decay - step * x;
+    w[i] = nw;
+    p[i] = from_f32<T>(nw);
+  }
+}
+
+unsigned grid_of(long n, long per_block, unsigned cap) {
+  const long b = (n + per_block - 1) / per_block;
+  return (unsigned)(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+}  // namespace
+
+template <typename T>
+nc_status opt_init(const T* params, float* master, float* s1, size_t n, float* s2, size_t n2, hipStream_t st) {
+  ProfScope prof("opt_init", 0, (double)n * (sizeof(T) + 8.0) + 4.0 * n2, st);
+  hipLaunchKernelGGL((opt_init_kernel<T>), dim3(grid_of((long)n, 256, 8192)), dim3(256), 0, st, params, master, s1,
+                     (long)n, s2, (long)n2);
+  NC_LAUNCH_CHECK("opt_init");
+  return NC_OK;
+}
+
+template <typename T>
+nc_status adamw_step(const float* g, float* w, float* m, float* v, T* p, size_t n, float lr, float beta1,
+                     float beta2, float eps, float wd, int step, hipStream_t st) {
+  if (n % 4 != 0) return NC_ERR_UNSUPPORTED;
+  const float c1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)step)));
+  const float c2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)step)));
+  ProfScope prof("adamw", 0, (double)n * (16.0 + 12.0 + sizeof(T)), st);
+  hipLaunchKernelGGL((adamw_kernel<T>), dim3(grid_of((long)n / 4, 256, 8192)), dim3(256), 0, st, g, w, m, v, p,
+                     (long)n / 4, lr, beta1, beta2, c1, c2, eps, 1.f - lr * wd);
+  NC_LAUNCH_CHECK("adamw");
+  return NC_OK;
+}
+
+size_t muon_work_bytes(int R, int C, bool bf16_storage) {
+  const long Rt = R > C ? R : C, Ct = R > C ? C : R;
+  const size_t es = bf16_storage ? 2 : 4;
+  const size_t part = gemm_dw_partial_elems((int)Rt, (int)Ct, (int)Ct);
+  return align_up(2 * (size_t)Rt * Ct * es, 256) + align_up(4 * (size_t)Ct * Ct, 256) +
+         align_up(2 * (size_t)Ct * Ct * es, 256) + align_up(4 * (part ? part : 1), 256) + align_up(4 * kNormParts, 256);
+}
+
+template <typename T>
+nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, float lr, float mu, int nesterov,
+                    float wd, void* work, size_t work_bytes, hipStream_t st) {
+  if (((long)R * C) % 4 != 0 || R % 4 != 0 || C % 4 != 0) return NC_ERR_UNSUPPORTED;
+  if (work_bytes < muon_work_bytes(R, C, is_bf16<T>())) return NC_ERR_WORKSPACE;
+  const bool transpose = R < C;
+  const int Rt = transpose ? C : R, Ct = transpose ? R : C;  // the tall form
+  const size_t es = sizeof(T);
+  char* q = static_cast<char*>(work);
+  T* xa = reinterpret_cast<T*>(q);
+  T* xb = xa + (size_t)Rt * Ct;
+  q += align_up(2 * (size_t)Rt * Ct * es, 256);
+  float* A = reinterpret_cast<float*>(q);
+  q += align_up(4 * (size_t)Ct * Ct, 256);
+  T* Ab = reinterpret_cast<T*>(q);
+  T* Bb = Ab + (size_t)Ct * Ct;
+  q += align_up(2 * (size_t)Ct * Ct * es, 256);
+  const size_t part_elems = gemm_dw_partial_elems(Rt, Ct, Ct);
+  float* part = reinterpret_cast<float*>(q);
+  q += align_up(4 * (part_elems ? part_elems : 1), 256);
+  float* norm_part = reinterpret_cast<float*>(q);
+
+  const long n4 = (long)R * C / 4;
+  {
+    ProfScope prof("muon_momentum", 0, 12.0 * 4 * n4, st);
+    hipLaunchKernelGGL(muon_mom_kernel, dim3(kNormParts), dim3(256), 0, st, g, mom, n4, mu, nesterov, norm_part);
+    NC_LAUNCH_CHECK("muon_momentum");
+  }
+  const dim3 tiles((C + kTile - 1) / kTile, (R + kTile - 1) / kTile);
+  {
+    ProfScope prof("muon_normalize", 0, (8.0 + es) * 4 * n4, st);
+    hipLaunchKernelGGL((muon_norm_kernel<T>), tiles, dim3(256), 0, st, g, mom, R, C, transpose ? 1 : 0, mu, nesterov,
+                       norm_part, xa);
+    NC_LAUNCH_CHECK("muon_normalize");
+  }
+  // the published coefficients (a, b, c) of the quintic map, five steps
+  const float a = 3.4445f, b = -4.7750f, c = 2.0315f;
+  T* x = xa;
+  T* xn = xb;
+  for (int it = 0; it < 5; ++it) {
+    NC_TRY(gemm_dw<T>(x, x, A, Rt, Ct, Ct, 0, part, part_elems, st));  // A = X^T X
+    {
+      ProfScope prof("cast_f32", 0, (4.0 + es) * Ct * Ct, st);
+      hipLaunchKernelGGL((cast_f32_kernel<T>), dim3(grid_of((long)Ct * Ct / 4, 256, 4096)), dim3(256), 0, st, A, Ab,
+                         (long)Ct * Ct / 4);
+      NC_LAUNCH_CHECK("cast_f32");
+    }
+    NC_TRY(gemm_xwt_axpby<T>(Ab, Ab, Bb, Ab, Ct, Ct, Ct, c, b, st));  // B = c A A^T + b A
+    NC_TRY(gemm_xwt_axpby<T>(x, Bb, xn, x, Rt, Ct, Ct, 1.f, a, st));  // X' = X B^T + a X
+    T* t = x;
+    x = xn;
+    xn = t;
+  }
+  const float scale = R > C ? std::sqrt((float)R / (float)C) : 1.f;
+  {
+    ProfScope prof("muon_apply", 0, (8.0 + 2.0 * es) * 4 * n4, st);
+    hipLaunchKernelGGL((muon_apply_kernel<T>), tiles, dim3(256), 0, st, w, p, x, R, C, transpose ? 1 : 0,
+                       1.f - lr * wd, lr * scale);
+    NC_LAUNCH_CHECK("muon_apply");
+  }
+  return NC_OK;
+}
+
+#define NC_INST(T)                                                                                                \
+  template nc_status opt_init<T>(const T*, float*, float*, size_t, float*, size_t, hipStream_t);                   \
+  template nc_status adamw_step<T>(const float*, float*, float*, float*, T*, size_t, float, float, float, float,   \
+                                   float, int, hipStream_t);                                                       \
+  template nc_status muon_step<T>(const float*, float*, float*, T*, int, int, float, float, int, float, void*,     \
+                                  size_t, hipStream_t);
+NC_INST(bf16)
+NC_INST(float)
+#undef NC_INST
+
+}  // namespace nc

@@ -32,8 +32,8 @@ EXPORTED = [
     "nc_abi_version", "nc_status_str", "nc_last_hip_error", "nc_validate", "nc_param_layout",
     "nc_query_sizes", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
-    "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_profile_enable",
-    "nc_profile_summary",
+    "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_opt_query_sizes",
+    "nc_opt_init", "nc_opt_step", "nc_profile_enable", "nc_profile_summary",
 ]
 
 
@@ -69,6 +69,16 @@ class NcInferSizes(C.Structure):
     _fields_ = [("cache", C.c_size_t), ("workspace", C.c_size_t)]
 
 
+class NcOptHparams(C.Structure):
+    _fields_ = [("lr_matrix", C.c_float), ("lr_embed", C.c_float), ("lr_unembed", C.c_float),
+                ("momentum", C.c_float), ("nesterov", C.c_int32), ("beta1", C.c_float), ("beta2", C.c_float),
+                ("eps", C.c_float), ("wd_matrix", C.c_float), ("wd_adam", C.c_float), ("step", C.c_int32)]
+
+
+class NcOptSizes(C.Structure):
+    _fields_ = [("state", C.c_size_t), ("workspace", C.c_size_t)]
+
+
 _lib = None
 
 
@@ -101,6 +111,9 @@ def load(path=LIB_PATH):
         "nc_infer_query_sizes": ([cfgp, C.POINTER(NcInferSizes)], I),
         "nc_prefill": ([cfgp, P, P, I, P, P, P, S, P], I),
         "nc_decode_step": ([cfgp, P, P, I, P, P, P, S, P], I),
+        "nc_opt_query_sizes": ([cfgp, C.POINTER(NcOptSizes)], I),
+        "nc_opt_init": ([cfgp, P, P, P], I),
+        "nc_opt_step": ([cfgp, C.POINTER(NcOptHparams), P, P, P, P, S, P], I),
         "nc_profile_enable": ([I], I),
         "nc_profile_summary": ([C.c_char_p, S, C.POINTER(S)], I),
     }
@@ -284,3 +297,29 @@ def decode_step(cfg, params, tok, pos, cache, next_tok, workspace, stream=None):
     _check(load().nc_decode_step(C.byref(c), _p(params), _p(tok), int(pos), _p(cache), _p(next_tok),
                                  _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "nc_decode_step")
+
+
+# ------------------------------------------------------------------ optimizer
+
+def opt_hparams(lr_matrix, lr_embed, lr_unembed, step, momentum=0.95, nesterov=True, beta1=0.8, beta2=0.95,
+                eps=1e-10, wd_matrix=0.0, wd_adam=0.0) -> NcOptHparams:
+    return NcOptHparams(lr_matrix, lr_embed, lr_unembed, momentum, 1 if nesterov else 0, beta1, beta2, eps,
+                        wd_matrix, wd_adam, int(step))
+
+
+def opt_query_sizes(cfg: Config) -> NcOptSizes:
+    c = to_nc_config(cfg)
+    s = NcOptSizes()
+    _check(load().nc_opt_query_sizes(C.byref(c), C.byref(s)), "nc_opt_query_sizes")
+    return s
+
+
+def opt_init(cfg, params, state, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_opt_init(C.byref(c), _p(params), _p(state), _stream(stream)), "nc_opt_init")
+
+
+def opt_step(cfg, hp: NcOptHparams, params, grads, state, workspace, stream=None):
+    c = to_nc_config(cfg)
+    _check(load().nc_opt_step(C.byref(c), C.byref(hp), _p(params), _p(grads), _p(state), _p(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)), "nc_opt_step")

@@ -233,6 +233,52 @@ nc_status nc_prefill(const nc_config* cfg, const void* params, const int32_t* id
 nc_status nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
                          int32_t* next_tok, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- optimizer
+ * The optimizer step (the page on vpshk.cn, Q&A section "卡帕西亲自揭秘背后技术",
+ * names Muon + AdamW; imeisheng.com, section "预训练": Muon for the matrices,
+ * AdamW for the embedding and the unembedding, no other trainable parameters,
+ * the learning rate scaled by 1/sqrt(d_model) and its multiplier falling
+ * linearly to 0 at the end of training). Muon is not defined on the pages;
+ * its published definition is used (K. Jordan, 2024): Nesterov momentum, then
+ * five steps of the quintic Newton-Schulz iteration with coefficients
+ * (3.4445, -4.7750, 2.0315) on the update scaled to unit Frobenius norm, the
+ * step scaled by max(1, rows/cols)^(1/2). Wq, Wk and Wv are three matrices to
+ * Muon although the parameter buffer packs them. The learning rates passed in
+ * already carry the schedule; the library holds no step counter. */
+
+typedef struct nc_opt_hparams {
+  float lr_matrix;  /* Muon, every block matrix */
+  float lr_embed;   /* AdamW, Wte */
+  float lr_unembed; /* AdamW, Wlm */
+  float momentum;   /* Muon momentum, in [0, 1) */
+  int32_t nesterov; /* 1: the Nesterov look-ahead g + momentum * buffer; 0: the buffer */
+  float beta1, beta2, eps; /* AdamW; betas in [0, 1), eps > 0 */
+  float wd_matrix, wd_adam; /* decoupled weight decay: w *= 1 - lr * wd before the update */
+  int32_t step;     /* 1-based step count, for AdamW's bias correction */
+} nc_opt_hparams;
+
+typedef struct nc_opt_sizes {
+  size_t state;     /* float32: master weights [n_params], s1 [n_params], s2 [2 vocab d_model] */
+  size_t workspace; /* scratch of nc_opt_step */
+} nc_opt_sizes;
+
+/* Sizes for cfg (depth >= 1). */
+nc_status nc_opt_query_sizes(const nc_config* cfg, nc_opt_sizes* out);
+
+/* state (device, state bytes): master = params widened to float32, moments 0.
+ * params as for nc_model_loss_and_grad. */
+nc_status nc_opt_init(const nc_config* cfg, const void* params, void* state, void* stream);
+
+/* One step: updates state from grads (device, float32, parameter layout, as
+ * written by nc_model_loss_and_grad) and writes params (device, storage dtype)
+ * = the new master weights rounded. State layout: master [n_params]; s1
+ * [n_params] holds AdamW's first moment in the Wte and Wlm ranges and Muon's
+ * momentum elsewhere; s2 [2 vocab d_model] holds AdamW's second moment of Wte
+ * then of Wlm. Hyperparameters are checked before any launch (NC_ERR_INVALID_ARG).
+ * workspace: nc_opt_sizes.workspace bytes. */
+nc_status nc_opt_step(const nc_config* cfg, const nc_opt_hparams* hp, void* params, const float* grads, void* state,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- tracing */
 
 /* Kernel timing. While enabled, every kernel launch of the library is

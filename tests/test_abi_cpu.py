@@ -141,3 +141,30 @@ def test_inference_arguments_checked_before_launch():
                                   C.byref(lib.NcInferSizes())) == 0
     wide = cfg.with_(n_head=64, d_model=256)
     assert L.nc_infer_query_sizes(C.byref(lib.to_nc_config(wide)), C.byref(lib.NcInferSizes())) == 5
+
+
+def test_optimizer_arguments_checked_before_launch():
+    L = lib.load()
+    cfg = cfgmod.TINY
+    c = lib.to_nc_config(cfg)
+    sz = lib.opt_query_sizes(cfg)
+    _, n = lib.param_layout(cfg)
+    # master [n] + s1 [n] + s2 [2 V d], all float32
+    assert sz.state == 4 * (2 * n + 2 * cfg.vocab * cfg.d_model)
+    assert sz.workspace > 0
+    ok, bad = _fake(0x100000), _fake(0x100001)
+    W = sz.workspace
+    good = lib.opt_hparams(0.02, 0.3, 0.004, 1)
+    assert L.nc_opt_step(C.byref(c), None, ok, ok, ok, ok, W, None) == 1
+    for field, value in [("lr_matrix", -1.0), ("lr_embed", float("nan")), ("momentum", 1.0), ("beta1", 1.0),
+                         ("beta2", -0.1), ("eps", 0.0), ("wd_matrix", -0.5), ("step", 0), ("nesterov", 2)]:
+        hp = lib.opt_hparams(0.02, 0.3, 0.004, 1)
+        setattr(hp, field, value)
+        assert L.nc_opt_step(C.byref(c), C.byref(hp), ok, ok, ok, ok, W, None) == 1, field
+    assert L.nc_opt_step(C.byref(c), C.byref(good), ok, None, ok, ok, W, None) == 1
+    assert L.nc_opt_step(C.byref(c), C.byref(good), ok, ok, bad, ok, W, None) == 3
+    assert L.nc_opt_step(C.byref(c), C.byref(good), ok, ok, ok, ok, W - 1, None) == 4
+    assert L.nc_opt_init(C.byref(c), None, ok, None) == 1
+    assert L.nc_opt_init(C.byref(c), ok, bad, None) == 3
+    # the optimizer needs the layers: depth 0 is a shape error
+    assert L.nc_opt_query_sizes(C.byref(lib.to_nc_config(cfg.with_(depth=0))), C.byref(lib.NcOptSizes())) == 2
