@@ -229,13 +229,126 @@ def cpu_baseline_infer(cfg, p, prompt, n_prompt, n_steps=8):
                        f"prefill, {dt:.1f} s wall on {threads} BLAS threads")
 
 
+# Hyperparameters of the optimizer benchmark. The pages fix none of them (only
+# the 1/sqrt(dim) scaling and the end-of-run decay); the time of a step does
+# not depend on their values.
+OPT_HP = dict(lr_matrix=0.02, lr_embed=0.2, lr_unembed=0.004, momentum=0.95, nesterov=True, beta1=0.8, beta2=0.95,
+              eps=1e-10, wd_matrix=0.0, wd_adam=0.0)
+
+
+def opt_flops(cfg):
+    """Newton-Schulz FLOPs of one optimizer step: per block matrix in its tall
+    orientation (R >= C), five steps of A = X^T X (2RC^2), B = bA + cA^2
+    (2C^3) and X B (2RC^2)."""
+    d, F = cfg.d_model, cfg.d_ff
+    HD, GD = cfg.n_head * cfg.head_dim, cfg.n_kv_head * cfg.head_dim
+    tot = 0
+    for R, Cc in ((HD, d), (GD, d), (GD, d), (d, HD), (F, d), (d, F)):
+        R, Cc = max(R, Cc), min(R, Cc)
+        tot += 5 * (4 * R * Cc * Cc + 2 * Cc ** 3)
+    return cfg.depth * tot
+
+
+def bench_opt(a, torch, lib):
+    """nc_opt_step at depth 20 on seeded gradients, timed with HIP events."""
+    cfg = C.DEPTH20
+    torch.cuda.set_device(0)
+    lib.load()
+    p = synth.init_params(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
+                          std=0.02, seed=0, dtype=cfg.dtype, out=np.float32)
+    params = torch.from_numpy(flat_params(p)).to("cuda", lib.torch_dtype(cfg))
+    _, n = lib.param_layout(cfg)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    grads = torch.randn(n, generator=gen, device="cuda", dtype=torch.float32) * 1e-3
+    sz = lib.opt_query_sizes(cfg)
+    state = lib.alloc_bytes(sz.state)
+    ws = lib.alloc_bytes(sz.workspace)
+    lib.opt_init(cfg, params, state)
+    step = [0]
+
+    def one():
+        step[0] += 1
+        lib.opt_step(cfg, lib.opt_hparams(step=step[0], **OPT_HP), params, grads, state, ws)
+
+    for i in range(a.warmup):
+        one()
+        torch.cuda.synchronize()
+        print(f"# warmup {i + 1}/{a.warmup}", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(a.steps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    out = {
+        "metric": "optimizer step time (Muon for the block matrices, AdamW for Wte and Wlm), depth-20, 1 MI355X",
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: N(0, 0.02) weights, N(0, 1e-3) seeded gradients",
+        "config": {"workload": "optimizer step of the depth-20 decoder (502M parameters; 120 Muon matrices, "
+                               "Newton-Schulz products in bf16; AdamW over 2 x 65536 x 1280)",
+                   "parallelism": "none"},
+        "newton_schulz_tflops": round(opt_flops(cfg) / (ms * 1e-3) / 1e12, 1),
+    }
+    if not a.no_kernel_timing:
+        lib.profile_enable(True)
+        for _ in range(a.steps):
+            one()
+        lib.profile_enable(False)
+        table = kernel_table(lib.profile_summary(), a.steps)
+        name, rl = roofline(table)
+        out["roofline"] = rl
+        out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
+                              if kk in ("ms_per_step", "launches_per_step", "tflops", "gbps")}
+                          for k, v in table.items()}
+    if a.cpu_tokens > 0:
+        print("# timing the CPU oracle sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_opt(cfg, p)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_opt(cfg, p, layers=4):
+    """The fp64 oracle on layers/depth of the step (the six Muon matrices of
+    the first ``layers`` layers and as large a share of the rows of Wte and
+    Wlm through AdamW), scaled to the whole step."""
+    from oracle import optim
+    from threadpoolctl import threadpool_info
+
+    rng = np.random.default_rng(5)
+    rows = cfg.vocab * layers // cfg.depth
+    t0 = time.perf_counter()
+    for l in range(layers):
+        for k in ("wq", "wk", "wv", "wo", "w1", "w2"):
+            W = np.asarray(p["layers"][l][k], dtype=np.float64)
+            optim.muon_update(W, rng.standard_normal(W.shape) * 1e-3, np.zeros_like(W), OPT_HP["lr_matrix"],
+                              OPT_HP["momentum"])
+    for k in ("wte", "wlm"):
+        W = np.asarray(p[k][:rows], dtype=np.float64)
+        optim.adamw_update(W, rng.standard_normal(W.shape) * 1e-3, 0 * W, 0 * W, 1, 0.2, 0.8, 0.95, 1e-10)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    scale = cfg.depth / layers
+    return dict(value=round(dt * scale * 1e3, 1), unit="ms", cores=int(threads), kind="oracle",
+                sample=f"fp64 NumPy oracle on the Muon matrices of {layers} of {cfg.depth} layers and {rows} rows "
+                       f"of Wte and Wlm (AdamW), {dt:.1f} s wall on {threads} BLAS threads, scaled x{scale:g}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["infer"], default="depth20",
-                    help="training step (depth20, depth30) or KV-cache generation (infer)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["infer", "opt"], default="depth20",
+                    help="training step (depth20, depth30), KV-cache generation (infer) or the optimizer step (opt)")
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -255,6 +368,8 @@ def main():
 
     if a.workload == "infer":
         return bench_infer(a, torch, lib)
+    if a.workload == "opt":
+        return bench_opt(a, torch, lib)
     cfg, desc = WORKLOADS[a.workload]
     torch.cuda.set_device(0)
     lib.load()

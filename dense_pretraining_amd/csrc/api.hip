@@ -553,7 +553,7 @@ size_t opt_workspace_bytes(const Dims& m) {
   layer_matrices(m, off.data(), 0, ms);
   size_t w = 0;
   for (const MatSpec& x : ms) {
-    const size_t b = muon_work_bytes(x.R, x.C, m.es == 2);
+    const size_t b = muon_work_bytes(x.R, x.C, m.L, m.es == 2);
     w = b > w ? b : w;
   }
   return w;
@@ -582,13 +582,13 @@ nc_status opt_step_t(const Dims& m, const nc_opt_hparams& h, T* params, const fl
                        st));
   NC_TRY(adamw_step<T>(grads + lm, master + lm, s1 + lm, s2 + vd, params + lm, vd, h.lr_unembed, h.beta1, h.beta2,
                        h.eps, h.wd_adam, h.step, st));
-  for (int l = 0; l < m.L; ++l) {
-    MatSpec ms[6];
-    layer_matrices(m, off.data(), l, ms);
-    for (const MatSpec& x : ms)
-      NC_TRY(muon_step<T>(grads + x.off, s1 + x.off, master + x.off, params + x.off, x.R, x.C, h.lr_matrix,
-                          h.momentum, h.nesterov, h.wd_matrix, ws, ws_bytes, st));
-  }
+  // each kind of block matrix, all layers at once: layer l's copy lies l * ls elements after layer 0's
+  const long ls = m.L > 1 ? (long)(off[5] - off[1]) : 0;
+  MatSpec ms[6];
+  layer_matrices(m, off.data(), 0, ms);
+  for (const MatSpec& x : ms)
+    NC_TRY(muon_step<T>(grads + x.off, s1 + x.off, master + x.off, params + x.off, x.R, x.C, m.L, ls, h.lr_matrix,
+                        h.momentum, h.nesterov, h.wd_matrix, ws, ws_bytes, st));
   return NC_OK;
 }
 

@@ -50,6 +50,10 @@ struct GemmShape {
   // the stored [R, C] matrix at (c / kPanel) * a_panel + r * kPanel + c % kPanel;
   // 0 = plain row-major with stride lda.
   long a_panel = 0;
+  // independent products of the same shape: problem b reads A + b * a_batch
+  // and B + b * b_batch (elements); the epilogue sees b in EpiCtx::batch
+  int batch = 1;
+  long a_batch = 0, b_batch = 0;
 };
 
 // ---------------------------------------------------------------- tile walk
@@ -215,6 +219,7 @@ struct EpiCtx {
   int z;          // K split
   int lane, wave;
   float* red;     // LDS scratch beside the slabs (2 * BM floats)
+  int batch;      // problem index of a batched launch
 };
 
 
@@ -237,7 +242,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
     for (int it = 0; it < 8; ++it)
 #pragma unroll
       for (int k = 0; k < NCH / 16; ++k)
-        aux[it][k] = epi.load_aux(r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k));
+        aux[it][k] = epi.load_aux(x, r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k));
     typename Epi::RowState rs;
     epi.row_begin(rs, r0 + 32 * i + lr);
 #pragma unroll
@@ -305,7 +310,7 @@ struct EpiStore {
   long ldr;
   int M, N;
   using Aux = Aux4<T>;
-  __device__ __forceinline__ Aux load_aux(int row, int col) const {
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
     return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
   }
   __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
@@ -338,17 +343,18 @@ struct EpiAxpby {
   long ldr;
   int M, N;
   float alpha, beta;
+  long c_batch, r_batch;  // per-problem strides of C and res in a batched launch
   using Aux = Aux4<T>;
-  __device__ __forceinline__ Aux load_aux(int row, int col) const {
-    return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
+  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
+    return aux_load<T>(res + x.batch * r_batch + (long)row * ldr + col, res != nullptr && row < M && col < N);
   }
-  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
+  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
     if (row >= M || col >= N) return;
     float r[4] = {0.f, 0.f, 0.f, 0.f};
     if (res) aux_get<T>(a, r);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = alpha * v[e] + beta * r[e];
-    store4<T>(C + (long)row * ldc + col, v);
+    store4<T>(C + x.batch * c_batch + (long)row * ldc + col, v);
   }
 };
 
@@ -363,7 +369,7 @@ struct EpiDReluSq {
   long lda;
   int M, N;
   using Aux = Aux4<T>;
-  __device__ __forceinline__ Aux load_aux(int row, int col) const {
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
     return aux_load<T>(act + (long)row * lda + col, row < M && col < N);
   }
   __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
@@ -386,7 +392,7 @@ struct EpiF32 {
   int accumulate;
   int M, N;
   using Aux = NoAux;
-  __device__ __forceinline__ Aux load_aux(int, int) const { return Aux{}; }
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
     if (row >= M || col >= N) return;
     float* p = C + (long)x.z * split_stride + (long)row * ldc + col;
@@ -444,7 +450,7 @@ struct EpiSoftcap {
     if (x.lane < 32) x.red[(x.wn ? BM : 0) + x.wm + 32 * i + x.lane] = s2;
   }
   using Aux = NoAux;
-  __device__ __forceinline__ Aux load_aux(int, int) const { return Aux{}; }
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux&) const {
     if (row < M && col < N) store4<T>(Z + (long)(col / kPanel) * zpanel + (long)row * kPanel + col % kPanel, v);
   }
@@ -470,13 +476,15 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   const int tiles_m = (s.M + BM - 1) / BM, tiles_n = (s.N + BN - 1) / BN;
   int tm, tn, z;
   gemm_tile_coords(tiles_m, tiles_n, tm, tn, z);
+  const int bi = z / s.n_split;  // batched problem, then K split
+  z -= bi * s.n_split;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = z * s.k_split;
   const int kend = min(s.K, kbeg + s.k_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
-  const T* __restrict__ A = static_cast<const T*>(s.A);
-  const T* __restrict__ B = static_cast<const T*>(s.B);
+  const T* __restrict__ A = static_cast<const T*>(s.A) + bi * s.a_batch;
+  const T* __restrict__ B = static_cast<const T*>(s.B) + bi * s.b_batch;
   LoadA la;
   LoadB lb;
 
@@ -529,7 +537,7 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   // operand LDS is free now: one 32 x (32 WTN) float32 slab per wave, then the row-sum scratch
   float* lds = reinterpret_cast<float*>(&smem[0][0]);
   static_assert(sizeof(smem) >= (4 * 32 * 32 * WTN + 2 * BM) * sizeof(float), "epilogue LDS");
-  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, lds + 4 * 32 * 32 * WTN};
+  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, lds + 4 * 32 * 32 * WTN, bi};
   staged_epilogue<WTM, WTN>(acc.c, epi, x, lds + wave * 32 * 32 * WTN);
   epi.finish(x);
 }
@@ -760,6 +768,8 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   const int tiles_m = (s.M + BM - 1) / BM, tiles_n = (s.N + BN - 1) / BN;
   int tm, tn, z;
   gemm_tile_coords(tiles_m, tiles_n, tm, tn, z);
+  const int bi = z / s.n_split;  // batched problem, then K split
+  z -= bi * s.n_split;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = z * s.k_split;
   const int kend = min(s.K, kbeg + s.k_split);
@@ -776,15 +786,15 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
 
   typename Tile::OpA opa;
   typename Tile::OpB opb;
-  opa.init(static_cast<const bf16*>(s.A), s.lda, m0, s.M, wave, lane, s.a_panel);
-  opb.init(static_cast<const bf16*>(s.B), s.ldb, n0, s.N, wave, lane, 0);
+  opa.init(static_cast<const bf16*>(s.A) + bi * s.a_batch, s.lda, m0, s.M, wave, lane, s.a_panel);
+  opb.init(static_cast<const bf16*>(s.B) + bi * s.b_batch, s.ldb, n0, s.N, wave, lane, 0);
   dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sa4, sb0, sb1, sb2, sb3, sb4, nk, kbeg, kend, wave, wm, wn,
                  lane);
   __syncthreads();
   // the A stages become the waves' 32 x 128 float32 slabs, B stage 0 the row-sum scratch
   static_assert(E * sizeof(bf16) == 32 * 128 * sizeof(float), "one A stage holds one slab");
   bf16* slab = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sa3;
-  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, reinterpret_cast<float*>(sb0)};
+  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, reinterpret_cast<float*>(sb0), bi};
   staged_epilogue<4, 4>(acc.c, epi, x, reinterpret_cast<float*>(slab));
   epi.finish(x);
 }
@@ -797,7 +807,7 @@ template <typename T, int LA, int LB, typename Epi>
 nc_status launch_gemm(const GemmShape& s, const Epi& epi, hipStream_t stream) {
   using Cfg = GemmTile<T>;
   int tiles_m = (s.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (s.N + Cfg::BN - 1) / Cfg::BN;
-  long blocks = (long)tiles_m * tiles_n * s.n_split;
+  long blocks = (long)tiles_m * tiles_n * s.n_split * s.batch;
   if (blocks <= 0) return NC_OK;
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((gemm_dma_kernel<LA, LB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,

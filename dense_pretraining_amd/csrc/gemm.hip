@@ -53,13 +53,29 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
 
 template <typename T>
 nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int N, int K, float alpha, float beta,
-                         hipStream_t st) {
+                         hipStream_t st, int batch, long x_batch, long w_batch, long y_batch) {
   GemmShape s{x, w, K, K, M, N, K, K, 1};
+  s.batch = batch;
+  s.a_batch = x_batch;
+  s.b_batch = w_batch;
   const double es = sizeof(T);
-  ProfScope prof(NC_NAME(T, "gemm_ns"), 2.0 * M * N * K,
-                 es * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
-  EpiAxpby<T> e{y, N, res, N, M, N, alpha, beta};
+  ProfScope prof(NC_NAME(T, "gemm_ns"), 2.0 * M * N * K * batch,
+                 es * batch * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
+  EpiAxpby<T> e{y, N, res, N, M, N, alpha, beta, y_batch, y_batch};
   return launch_gemm<T, kKc, kKc>(s, e, st);
+}
+
+template <typename T>
+nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch, long x_batch, long a_batch) {
+  // a[C,C] = x^T x for x [R,C]: both operands K-outer, the reduction over the R rows.
+  GemmShape s{x, x, C, C, C, C, R, R, 1};
+  s.batch = batch;
+  s.a_batch = x_batch;
+  s.b_batch = x_batch;
+  const double es = sizeof(T);
+  ProfScope prof(NC_NAME(T, "gemm_gram"), 2.0 * R * C * C * batch, es * batch * ((double)R * C + (double)C * C), st);
+  EpiAxpby<T> e{a, C, nullptr, C, C, C, 1.f, 0.f, a_batch, 0};
+  return launch_gemm<T, kKo, kKo>(s, e, st);
 }
 
 template <typename T>
@@ -137,7 +153,8 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
 #define NC_INST(T)                                                                                            \
   template nc_status gemm_xwt<T>(const T*, const T*, T*, const T*, int, int, int, bool, hipStream_t);        \
   template nc_status gemm_xwt_axpby<T>(const T*, const T*, T*, const T*, int, int, int, float, float,          \
-                                       hipStream_t);                                                          \
+                                       hipStream_t, int, long, long, long);                                   \
+  template nc_status gemm_gram<T>(const T*, T*, int, int, hipStream_t, int, long, long);                       \
   template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t, long);         \
   template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t,  \
                                 long);                                                                        \

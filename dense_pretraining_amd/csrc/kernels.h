@@ -31,10 +31,15 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
 // dx[M,K] = dy[M,N] W[N,K]; with act = max(u,0)^2 given, dx = (dy W) * 2 sqrt(act),
 // the input gradient of the ReLU^2 activation.
 // dy_panel: dy stored in column panels (stride dy_panel elements), else 0.
-// y[M,N] = alpha * x[M,K] w[N,K]^T + beta * res (res optional, [M,N]).
+// y[M,N] = alpha * x[M,K] w[N,K]^T + beta * res (res optional, [M,N], the
+// layout of y). batch independent products: problem b at x + b x_batch,
+// w + b w_batch and y, res + b y_batch.
 template <typename T>
 nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int N, int K, float alpha, float beta,
-                         hipStream_t st);
+                         hipStream_t st, int batch = 1, long x_batch = 0, long w_batch = 0, long y_batch = 0);
+// a[C,C] = x^T x for x [R,C] (the Gram matrix, in the storage type); batched as above.
+template <typename T>
+nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch = 1, long x_batch = 0, long a_batch = 0);
 template <typename T>
 nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
                    long dy_panel = 0);
@@ -153,12 +158,13 @@ nc_status opt_init(const T* params, float* master, float* s1, size_t n, float* s
 template <typename T>
 nc_status adamw_step(const float* g, float* w, float* m, float* v, T* p, size_t n, float lr, float beta1,
                      float beta2, float eps, float wd, int step, hipStream_t st);
-// One Muon step of the matrix w [R, C] (float32 master, p its stored copy)
-// with gradient g and momentum mom; work: muon_work_bytes(R, C, bf16) bytes.
+// One Muon step of L matrices w [R, C] (float32 master, p its stored copy)
+// with gradients g and momenta mom, matrix l at + l * ls elements of each;
+// work: muon_work_bytes(R, C, L, bf16) bytes.
 template <typename T>
-nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, float lr, float mu, int nesterov,
-                    float wd, void* work, size_t work_bytes, hipStream_t st);
-size_t muon_work_bytes(int R, int C, bool bf16_storage);
+nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, int L, long ls, float lr, float mu,
+                    int nesterov, float wd, void* work, size_t work_bytes, hipStream_t st);
+size_t muon_work_bytes(int R, int C, int L, bool bf16_storage);
 
 // ------------------------------------------------------------ embedding grad (embed_bwd.hip)
 struct EmbedSortBufs {

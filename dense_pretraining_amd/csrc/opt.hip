@@ -24,7 +24,7 @@
 namespace nc {
 namespace {
 
-constexpr int kNormParts = 1024;  // blocks of the momentum pass (partial sums of squares)
+constexpr int kNormParts = 256;  // blocks per matrix of the momentum pass (partial sums of squares)
 constexpr int kTile = 32;         // transposing tile of the layout kernels
 
 template <typename T>
@@ -66,9 +66,13 @@ __global__ void __launch_bounds__(256) adamw_kernel(const float* __restrict__ g,
 
 // Momentum pass: mom <- mu mom + g; the update U = g + mu mom (Nesterov) or mom;
 // part[block] = sum of U^2 over the block's elements (grid of kNormParts blocks).
+// Matrix blockIdx.y of a batch lies ls elements after the previous one.
 __global__ void __launch_bounds__(256) muon_mom_kernel(const float* __restrict__ g, float* __restrict__ mom, long n4,
-                                                       float mu, int nesterov, float* __restrict__ part) {
+                                                       long ls, float mu, int nesterov, float* __restrict__ part) {
   __shared__ float red[4];
+  g += blockIdx.y * ls;
+  mom += blockIdx.y * ls;
+  part += blockIdx.y * kNormParts;
   float acc = 0.f;
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
     const float4 gg = reinterpret_cast<const float4*>(g)[i];
@@ -100,13 +104,17 @@ __device__ __forceinline__ float inv_frobenius(const float* part, float* sh) {
 
 // X (tall layout, T) = U / |U|_F for U [R][C] (U recomputed from g and the new
 // momentum). transpose: X[c][r] = U[r][c]. One 32 x 32 tile per block.
+// Matrix blockIdx.z of a batch: g, mom at + z ls, its X at + z xs.
 template <typename T>
 __global__ void __launch_bounds__(256) muon_norm_kernel(const float* __restrict__ g, const float* __restrict__ mom,
-                                                        int R, int C, int transpose, float mu, int nesterov,
-                                                        const float* __restrict__ part, T* __restrict__ X) {
+                                                        long ls, int R, int C, int transpose, float mu, int nesterov,
+                                                        const float* __restrict__ part, T* __restrict__ X, long xs) {
   __shared__ float sh[4];
   __shared__ float tile[kTile][kTile + 1];
-  const float inv = inv_frobenius(part, sh);
+  g += blockIdx.z * ls;
+  mom += blockIdx.z * ls;
+  X += blockIdx.z * xs;
+  const float inv = inv_frobenius(part + blockIdx.z * kNormParts, sh);
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int j = ty; j < kTile; j += 8) {
@@ -130,22 +138,16 @@ __global__ void __launch_bounds__(256) muon_norm_kernel(const float* __restrict_
   }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) cast_f32_kernel(const float* __restrict__ a, T* __restrict__ b, long n4) {
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-    const float4 v = reinterpret_cast<const float4*>(a)[i];
-    const float f[4] = {v.x, v.y, v.z, v.w};
-    store4<T>(b + 4 * i, f);
-  }
-}
-
 // w[r][c] <- w[r][c] decay - step X (X in the tall layout, read transposed
 // when the matrix is wide); p = w in the storage type.
 template <typename T>
-__global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, T* __restrict__ p,
-                                                         const T* __restrict__ X, int R, int C, int transpose,
+__global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, T* __restrict__ p, long ls,
+                                                         const T* __restrict__ X, long xs, int R, int C, int transpose,
                                                          float decay, float step) {
   __shared__ float tile[kTile][kTile + 1];
+  w += blockIdx.z * ls;
+  p += blockIdx.z * ls;
+  X += blockIdx.z * xs;
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   if (transpose) {
@@ -195,71 +197,60 @@ nc_status adamw_step(const float* g, float* w, float* m, float* v, T* p, size_t 
   return NC_OK;
 }
 
-size_t muon_work_bytes(int R, int C, bool bf16_storage) {
-  const long Rt = R > C ? R : C, Ct = R > C ? C : R;
+size_t muon_work_bytes(int R, int C, int L, bool bf16_storage) {
+  const size_t Rt = R > C ? R : C, Ct = R > C ? C : R;
   const size_t es = bf16_storage ? 2 : 4;
-  const size_t part = gemm_dw_partial_elems((int)Rt, (int)Ct, (int)Ct);
-  return align_up(2 * (size_t)Rt * Ct * es, 256) + align_up(4 * (size_t)Ct * Ct, 256) +
-         align_up(2 * (size_t)Ct * Ct * es, 256) + align_up(4 * (part ? part : 1), 256) + align_up(4 * kNormParts, 256);
+  return align_up(2 * L * Rt * Ct * es, 256) + align_up(2 * L * Ct * Ct * es, 256) + align_up(4 * (size_t)L * kNormParts, 256);
 }
 
 template <typename T>
-nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, float lr, float mu, int nesterov,
-                    float wd, void* work, size_t work_bytes, hipStream_t st) {
-  if (((long)R * C) % 4 != 0 || R % 4 != 0 || C % 4 != 0) return NC_ERR_UNSUPPORTED;
-  if (work_bytes < muon_work_bytes(R, C, is_bf16<T>())) return NC_ERR_WORKSPACE;
+nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, int L, long ls, float lr, float mu,
+                    int nesterov, float wd, void* work, size_t work_bytes, hipStream_t st) {
+  if (((long)R * C) % 4 != 0 || R % 4 != 0 || C % 4 != 0 || L < 1 || L > 65535) return NC_ERR_UNSUPPORTED;
+  if (work_bytes < muon_work_bytes(R, C, L, is_bf16<T>())) return NC_ERR_WORKSPACE;
   const bool transpose = R < C;
   const int Rt = transpose ? C : R, Ct = transpose ? R : C;  // the tall form
+  const long xs = (long)Rt * Ct, as = (long)Ct * Ct;
   const size_t es = sizeof(T);
   char* q = static_cast<char*>(work);
   T* xa = reinterpret_cast<T*>(q);
-  T* xb = xa + (size_t)Rt * Ct;
-  q += align_up(2 * (size_t)Rt * Ct * es, 256);
-  float* A = reinterpret_cast<float*>(q);
-  q += align_up(4 * (size_t)Ct * Ct, 256);
+  T* xb = xa + L * xs;
+  q += align_up(2 * L * (size_t)xs * es, 256);
   T* Ab = reinterpret_cast<T*>(q);
-  T* Bb = Ab + (size_t)Ct * Ct;
-  q += align_up(2 * (size_t)Ct * Ct * es, 256);
-  const size_t part_elems = gemm_dw_partial_elems(Rt, Ct, Ct);
-  float* part = reinterpret_cast<float*>(q);
-  q += align_up(4 * (part_elems ? part_elems : 1), 256);
+  T* Bb = Ab + L * as;
+  q += align_up(2 * L * (size_t)as * es, 256);
   float* norm_part = reinterpret_cast<float*>(q);
 
   const long n4 = (long)R * C / 4;
   {
-    ProfScope prof("muon_momentum", 0, 12.0 * 4 * n4, st);
-    hipLaunchKernelGGL(muon_mom_kernel, dim3(kNormParts), dim3(256), 0, st, g, mom, n4, mu, nesterov, norm_part);
+    ProfScope prof("muon_momentum", 0, 12.0 * 4 * n4 * L, st);
+    hipLaunchKernelGGL(muon_mom_kernel, dim3(kNormParts, L), dim3(256), 0, st, g, mom, n4, ls, mu, nesterov,
+                       norm_part);
     NC_LAUNCH_CHECK("muon_momentum");
   }
-  const dim3 tiles((C + kTile - 1) / kTile, (R + kTile - 1) / kTile);
+  const dim3 tiles((C + kTile - 1) / kTile, (R + kTile - 1) / kTile, L);
   {
-    ProfScope prof("muon_normalize", 0, (8.0 + es) * 4 * n4, st);
-    hipLaunchKernelGGL((muon_norm_kernel<T>), tiles, dim3(256), 0, st, g, mom, R, C, transpose ? 1 : 0, mu, nesterov,
-                       norm_part, xa);
+    ProfScope prof("muon_normalize", 0, (8.0 + es) * 4 * n4 * L, st);
+    hipLaunchKernelGGL((muon_norm_kernel<T>), tiles, dim3(256), 0, st, g, mom, ls, R, C, transpose ? 1 : 0, mu,
+                       nesterov, norm_part, xa, xs);
     NC_LAUNCH_CHECK("muon_normalize");
   }
-  // the published coefficients (a, b, c) of the quintic map, five steps
+  // the published coefficients (a, b, c) of the quintic map, five steps, all L matrices at once
   const float a = 3.4445f, b = -4.7750f, c = 2.0315f;
   T* x = xa;
   T* xn = xb;
   for (int it = 0; it < 5; ++it) {
-    NC_TRY(gemm_dw<T>(x, x, A, Rt, Ct, Ct, 0, part, part_elems, st));  // A = X^T X
-    {
-      ProfScope prof("cast_f32", 0, (4.0 + es) * Ct * Ct, st);
-      hipLaunchKernelGGL((cast_f32_kernel<T>), dim3(grid_of((long)Ct * Ct / 4, 256, 4096)), dim3(256), 0, st, A, Ab,
-                         (long)Ct * Ct / 4);
-      NC_LAUNCH_CHECK("cast_f32");
-    }
-    NC_TRY(gemm_xwt_axpby<T>(Ab, Ab, Bb, Ab, Ct, Ct, Ct, c, b, st));  // B = c A A^T + b A
-    NC_TRY(gemm_xwt_axpby<T>(x, Bb, xn, x, Rt, Ct, Ct, 1.f, a, st));  // X' = X B^T + a X
+    NC_TRY(gemm_gram<T>(x, Ab, Rt, Ct, st, L, xs, as));                          // A = X^T X
+    NC_TRY(gemm_xwt_axpby<T>(Ab, Ab, Bb, Ab, Ct, Ct, Ct, c, b, st, L, as, as, as));  // B = c A A^T + b A
+    NC_TRY(gemm_xwt_axpby<T>(x, Bb, xn, x, Rt, Ct, Ct, 1.f, a, st, L, xs, as, xs));  // X' = X B^T + a X
     T* t = x;
     x = xn;
     xn = t;
   }
   const float scale = R > C ? std::sqrt((float)R / (float)C) : 1.f;
   {
-    ProfScope prof("muon_apply", 0, (8.0 + 2.0 * es) * 4 * n4, st);
-    hipLaunchKernelGGL((muon_apply_kernel<T>), tiles, dim3(256), 0, st, w, p, x, R, C, transpose ? 1 : 0,
+    ProfScope prof("muon_apply", 0, (8.0 + 2.0 * es) * 4 * n4 * L, st);
+    hipLaunchKernelGGL((muon_apply_kernel<T>), tiles, dim3(256), 0, st, w, p, ls, x, xs, R, C, transpose ? 1 : 0,
                        1.f - lr * wd, lr * scale);
     NC_LAUNCH_CHECK("muon_apply");
   }
@@ -270,8 +261,8 @@ nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, fl
   template nc_status opt_init<T>(const T*, float*, float*, size_t, float*, size_t, hipStream_t);                   \
   template nc_status adamw_step<T>(const float*, float*, float*, float*, T*, size_t, float, float, float, float,   \
                                    float, int, hipStream_t);                                                       \
-  template nc_status muon_step<T>(const float*, float*, float*, T*, int, int, float, float, int, float, void*,     \
-                                  size_t, hipStream_t);
+  template nc_status muon_step<T>(const float*, float*, float*, T*, int, int, int, long, float, float, int, float, \
+                                  void*, size_t, hipStream_t);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST
