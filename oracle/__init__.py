@@ -36,3 +36,4 @@ from .model import (  # noqa: F401
 )
 from . import infer  # noqa: F401  (greedy generation with a key/value cache)
 from . import optim  # noqa: F401  (the optimizer step: Muon and AdamW)
+from . import fp8  # noqa: F401  (FP8 E4M3 forward products)
