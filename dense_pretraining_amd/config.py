@@ -29,7 +29,9 @@ class Config:
     softcap: float = 15.0
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
-    dtype: str = "bf16"  # storage type of weights and activations: "bf16" or "f32"
+    # storage of weights and activations: "bf16", "f32" (check mode), or "bf16_fp8"
+    # (bf16 storage, the block's forward products in FP8 E4M3)
+    dtype: str = "bf16"
 
     @staticmethod
     def from_depth(depth, batch=32, seq_len=2048, vocab=65536, n_kv_head=1, dtype="bf16"):

@@ -27,11 +27,12 @@ struct Dims {
   float eps, cap, base;
   int dtype;
   size_t es;  // bytes per stored element
+  bool fp8;   // forward block products in FP8 E4M3 (bf16 storage)
 };
 
 nc_status make_dims(const nc_config* c, Dims* o, bool need_depth) {
   if (!c) return NC_ERR_INVALID_ARG;
-  if (c->dtype != NC_BF16 && c->dtype != NC_F32) return NC_ERR_UNSUPPORTED;
+  if (c->dtype != NC_BF16 && c->dtype != NC_F32 && c->dtype != NC_BF16_FP8) return NC_ERR_UNSUPPORTED;
   if (c->d_model <= 0 || c->n_head <= 0 || c->head_dim <= 0 || c->n_kv_head <= 0 || c->d_ff <= 0 || c->vocab <= 0 ||
       c->batch <= 0 || c->seq_len <= 0 || (need_depth && c->depth <= 0) || c->depth < 0)
     return NC_ERR_SHAPE;
@@ -65,7 +66,8 @@ nc_status make_dims(const nc_config* c, Dims* o, bool need_depth) {
   o->cap = c->softcap;
   o->base = c->rope_base;
   o->dtype = c->dtype;
-  o->es = c->dtype == NC_BF16 ? 2 : 4;
+  o->es = c->dtype == NC_F32 ? 4 : 2;
+  o->fp8 = c->dtype == NC_BF16_FP8;
   return NC_OK;
 }
 
@@ -186,6 +188,24 @@ EmbedScratch carve_embed_scratch(Carver& c, const Dims& m) {
   return s;
 }
 
+// The FP8 operand copies of the largest forward product (act [M, F] and W2
+// [d, F], or QKV's [QKV, d] weight), two scales and two amax words.
+Fp8Buf carve_fp8(Carver& c, const Dims& m) {
+  Fp8Buf b;
+  long kmax = m.d > m.HD ? m.d : m.HD;
+  kmax = kmax > m.F ? kmax : m.F;
+  size_t w = (size_t)m.QKV * m.d;
+  const size_t w2 = (size_t)m.d * m.F, w1 = (size_t)m.F * m.d, wo = (size_t)m.d * m.HD;
+  w = w > w2 ? w : w2;
+  w = w > w1 ? w : w1;
+  w = w > wo ? w : wo;
+  b.xq = c.take<uint8_t>((size_t)m.M * kmax);
+  b.wq = c.take<uint8_t>(w);
+  b.scale = c.take<float>(2);
+  b.amax = c.take<uint32_t>(2);
+  return b;
+}
+
 size_t block_saved_bytes(const Dims& m, bool table) {
   Carver c(nullptr);
   if (m.es == 2) carve_block_saved<bf16>(c, m, table);
@@ -212,6 +232,11 @@ size_t scratch_body_bytes(const Dims& m) {
   size_t r = a.used;
   if (b.used > r) r = b.used;
   if (e.used > r) r = e.used;
+  if (m.fp8) {
+    Carver f(nullptr);
+    carve_fp8(f, m);
+    if (f.used > r) r = f.used;
+  }
   return r;
 }
 
@@ -255,17 +280,24 @@ struct BlockW {
 
 template <typename T>
 nc_status block_fwd_t(const Dims& m, const BlockW<T>& w, const T* x, T* x_out, const BlockSaved<T>& s,
-                      const float* cs, const float* sn, hipStream_t st) {
+                      const float* cs, const float* sn, hipStream_t st, const Fp8Buf* f8 = nullptr) {
   const int M = (int)m.M;
+  // x[M,K] W[N,K]^T (+ res), FP8 products when the config asks for them
+  auto mm = [&](const T* a, const T* b, T* y, const T* res, int N, int K, bool relu_sq) -> nc_status {
+    if constexpr (sizeof(T) == 2) {
+      if (m.fp8) return f8 ? gemm_xwt_fp8(a, b, y, res, M, N, K, relu_sq, *f8, st) : NC_ERR_INVALID_ARG;
+    }
+    return gemm_xwt<T>(a, b, y, res, M, N, K, relu_sq, st);
+  };
   NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.h1, s.r1, M, m.d, m.eps, nullptr, st));
-  NC_TRY(gemm_xwt<T>(s.h1, w.wqkv, s.qkv, nullptr, M, m.QKV, m.d, false, st));
+  NC_TRY(mm(s.h1, w.wqkv, s.qkv, nullptr, m.QKV, m.d, false));
   NC_TRY(qknorm_rope_fwd<T>(s.qkv, m.QKV, s.qk, m.QK, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
   AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
   NC_TRY(attn_fwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, s.lse, st));
-  NC_TRY(gemm_xwt<T>(s.o, w.wo, s.x1, x, M, m.d, m.HD, false, st));
+  NC_TRY(mm(s.o, w.wo, s.x1, x, m.d, m.HD, false));
   NC_TRY(rmsnorm_fwd<T>(s.x1, nullptr, 0, s.h2, s.r2, M, m.d, m.eps, nullptr, st));
-  NC_TRY(gemm_xwt<T>(s.h2, w.w1, s.act, nullptr, M, m.F, m.d, true, st));
-  NC_TRY(gemm_xwt<T>(s.act, w.w2, x_out, s.x1, M, m.d, m.F, false, st));
+  NC_TRY(mm(s.h2, w.w1, s.act, nullptr, m.F, m.d, true));
+  NC_TRY(mm(s.act, w.w2, x_out, s.x1, m.d, m.F, false));
   return NC_OK;
 }
 
@@ -349,6 +381,8 @@ nc_status model_t(const Dims& m, const T* params, const int32_t* idx, const int3
   HeadScratch<T> hsc = carve_head_scratch<T>(c2, m);
   Carver c3(static_cast<char*>(ws) + kStatusBytes + body);
   EmbedScratch esc = carve_embed_scratch(c3, m);
+  Carver c4(static_cast<char*>(ws) + kStatusBytes + body);  // the forward only (before the head uses the area)
+  const Fp8Buf f8 = carve_fp8(c4, m);
 
   auto bw = [&](int l) {
     BlockW<T> w;
@@ -369,7 +403,7 @@ nc_status model_t(const Dims& m, const T* params, const int32_t* idx, const int3
 
   NC_TRY(rope_table(cs, sn, m.T, m.D, m.base, st));
   NC_TRY(rmsnorm_fwd<T>(params + off[0], idx, m.V, xs[0], r0, (int)m.M, m.d, m.eps, status, st));
-  for (int l = 0; l < m.L; ++l) NC_TRY(block_fwd_t<T>(m, bw(l), xs[l], xs[l + 1], sv[l], cs, sn, st));
+  for (int l = 0; l < m.L; ++l) NC_TRY(block_fwd_t<T>(m, bw(l), xs[l], xs[l + 1], sv[l], cs, sn, st, &f8));
   const T* wlm = params + off[1 + 4 * m.L];
   NC_TRY(head_fwd_t<T>(m, xs[m.L], wlm, tg, loss, hs, hsc, status, st));
   NC_TRY(head_bwd_t<T>(m, wlm, tg, hs, dloss, gx, grads + off[1 + 4 * m.L], acc, hsc, st));
@@ -444,6 +478,7 @@ InferBufs<T> carve_infer(void* ws, const Dims& m) {
 
 nc_status infer_dims(const nc_config* cfg, Dims* m) {
   NC_TRY(make_dims(cfg, m, true));
+  if (m->fp8) return NC_ERR_UNSUPPORTED;
   if (m->H / m->G > 32) return NC_ERR_UNSUPPORTED;
   return NC_OK;
 }
@@ -715,7 +750,10 @@ nc_status nc_block_fwd(const nc_config* cfg, const nc_block_params* w, const voi
     NC_TRY(rope_table(s.cs, s.sn, m.T, m.D, m.base, st));
     BlockW<bf16> bw{static_cast<const bf16*>(w->wqkv), static_cast<const bf16*>(w->wo),
                     static_cast<const bf16*>(w->w1), static_cast<const bf16*>(w->w2)};
-    return block_fwd_t<bf16>(m, bw, static_cast<const bf16*>(x_in), static_cast<bf16*>(x_out), s, s.cs, s.sn, st);
+    Carver cf(static_cast<char*>(scratch) + kStatusBytes);
+    const Fp8Buf f8 = carve_fp8(cf, m);
+    return block_fwd_t<bf16>(m, bw, static_cast<const bf16*>(x_in), static_cast<bf16*>(x_out), s, s.cs, s.sn, st,
+                             &f8);
   }
   BlockSaved<float> s = carve_block_saved<float>(c, m, true);
   NC_TRY(rope_table(s.cs, s.sn, m.T, m.D, m.base, st));

@@ -309,12 +309,18 @@ struct EpiStore {
   const T* res;  // optional residual, same layout as C
   long ldr;
   int M, N;
+  const float* scale = nullptr;  // FP8 products: the two operands' dequantisation scales, multiplied in first
   using Aux = Aux4<T>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
     return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
   }
   __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
     if (row >= M || col >= N) return;
+    if (scale) {
+      const float sc = scale[0] * scale[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= sc;
+    }
     if constexpr (ReluSqOut) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -668,6 +674,37 @@ struct DmaTile {
 #pragma unroll
       for (int j = 0; j < WTN; ++j) mfma32(acc.c[i][j], f.b[j], f.a[i]);
   }
+  // FP8 E4M3 operands stored as pairs in 16-bit elements: a stage's two
+  // halves together are 64 k of FP8, one 32x32x64 MFMA per sub-tile. A
+  // lane's 32 bytes are its 16 of the first half then its 16 of the second,
+  // the same for both operands (no block scales); each fragment is read straight
+  // into the 8 registers the MFMA takes.
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  struct Frags8 {
+    i32x8 a[WTM], b[WTN];
+  };
+  __device__ __forceinline__ static i32x8 cat32(const Frag<bf16>& lo, const Frag<bf16>& hi) {
+    const i32x4 x = __builtin_bit_cast(i32x4, lo.v), y = __builtin_bit_cast(i32x4, hi.v);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ static void load_f8(Frags8& f, const bf16* ta, const bf16* tb, int wm, int wn,
+                                                 int lane) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+      f.a[i] = cat32(OpA::frag(ta, wm + 32 * i, 0, lane), OpA::frag(ta, wm + 32 * i, 16, lane));
+#pragma unroll
+    for (int j = 0; j < WTN; ++j)
+      f.b[j] = cat32(OpB::frag(tb, wn + 32 * j, 0, lane), OpB::frag(tb, wn + 32 * j, 16, lane));
+  }
+  __device__ __forceinline__ static void mma_f8(TileAcc<bf16>& acc, const Frags8& f) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+        acc.c[i][j] =  // zero scale operands select the unscaled v_mfma_f32_32x32x64_f8f6f4 (AGPR accumulators)
+            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0, 0, 0, 0);
+  }
 };
 
 // One step of the ring, for tile t in stage S (its first half already in
@@ -755,7 +792,71 @@ __device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA&
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));
 }
 
-template <int LA, int LB, typename Epi>
+// The FP8 step: wait for tile t+1 and refill stage S (tile t's fragments,
+// both halves, are already in CUR); read tile t+1 into NXT while multiplying
+// tile t. The same one read and at most one load per multiply as the bf16
+// step, with half as many (twice as long) multiplies. The two fragment sets
+// trade places every step, so the main loop runs ten steps a trip (five
+// stages, two sets) and nothing is copied.
+#define NC_DMA_STEP_F8(t, SA, SB, NA, NB, CUR, NXT)         \
+  {                                                         \
+    ring_barrier<24>();                                     \
+    opa.issue(SA, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
+    opb.issue(SB, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
+    Tile::load_f8(NXT, NA, NB, wm, wn, lane);               \
+    Tile::mma_f8(acc, CUR);                                 \
+    interleave_reads_with_mfma<true>();                     \
+  }
+
+template <typename Tile>
+__device__ __forceinline__ void dma_ring_f8(TileAcc<bf16>& acc, typename Tile::OpA& opa, typename Tile::OpB& opb,
+                                            bf16* __restrict__ sa0, bf16* __restrict__ sa1, bf16* __restrict__ sa2,
+                                            bf16* __restrict__ sa3, bf16* __restrict__ sa4, bf16* __restrict__ sb0,
+                                            bf16* __restrict__ sb1, bf16* __restrict__ sb2, bf16* __restrict__ sb3,
+                                            bf16* __restrict__ sb4, int nk, int kbeg, int kend, int wave, int wm,
+                                            int wn, int lane) {
+  constexpr int BK = kDmaBK;
+  typename Tile::Frags8 F, G;
+  opa.issue(sa0, kbeg, kend, wave);
+  opb.issue(sb0, kbeg, kend, wave);
+  opa.issue(sa1, kbeg + BK, kend, wave);
+  opb.issue(sb1, kbeg + BK, kend, wave);
+  opa.issue(sa2, kbeg + 2 * BK, kend, wave);
+  opb.issue(sb2, kbeg + 2 * BK, kend, wave);
+  opa.issue(sa3, kbeg + 3 * BK, kend, wave);
+  opb.issue(sb3, kbeg + 3 * BK, kend, wave);
+  opa.issue(sa4, kbeg + 4 * BK, kend, wave);
+  opb.issue(sb4, kbeg + 4 * BK, kend, wave);
+  ring_barrier<32>();  // tile 0 has landed
+  Tile::load_f8(F, sa0, sb0, wm, wn, lane);
+  int kt = 0;
+  for (; kt + 10 <= nk; kt += 10) {
+    NC_DMA_STEP_F8(kt, sa0, sb0, sa1, sb1, F, G);
+    NC_DMA_STEP_F8(kt + 1, sa1, sb1, sa2, sb2, G, F);
+    NC_DMA_STEP_F8(kt + 2, sa2, sb2, sa3, sb3, F, G);
+    NC_DMA_STEP_F8(kt + 3, sa3, sb3, sa4, sb4, G, F);
+    NC_DMA_STEP_F8(kt + 4, sa4, sb4, sa0, sb0, F, G);
+    NC_DMA_STEP_F8(kt + 5, sa0, sb0, sa1, sb1, G, F);
+    NC_DMA_STEP_F8(kt + 6, sa1, sb1, sa2, sb2, F, G);
+    NC_DMA_STEP_F8(kt + 7, sa2, sb2, sa3, sb3, G, F);
+    NC_DMA_STEP_F8(kt + 8, sa3, sb3, sa4, sb4, F, G);
+    NC_DMA_STEP_F8(kt + 9, sa4, sb4, sa0, sb0, G, F);
+  }
+  // kt is a multiple of 10: tile kt sits in stage 0 with its fragments in F
+  if (kt < nk) NC_DMA_STEP_F8(kt, sa0, sb0, sa1, sb1, F, G);
+  if (kt + 1 < nk) NC_DMA_STEP_F8(kt + 1, sa1, sb1, sa2, sb2, G, F);
+  if (kt + 2 < nk) NC_DMA_STEP_F8(kt + 2, sa2, sb2, sa3, sb3, F, G);
+  if (kt + 3 < nk) NC_DMA_STEP_F8(kt + 3, sa3, sb3, sa4, sb4, G, F);
+  if (kt + 4 < nk) NC_DMA_STEP_F8(kt + 4, sa4, sb4, sa0, sb0, F, G);
+  if (kt + 5 < nk) NC_DMA_STEP_F8(kt + 5, sa0, sb0, sa1, sb1, G, F);
+  if (kt + 6 < nk) NC_DMA_STEP_F8(kt + 6, sa1, sb1, sa2, sb2, F, G);
+  if (kt + 7 < nk) NC_DMA_STEP_F8(kt + 7, sa2, sb2, sa3, sb3, G, F);
+  if (kt + 8 < nk) NC_DMA_STEP_F8(kt + 8, sa3, sb3, sa4, sb4, F, G);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));
+}
+#undef NC_DMA_STEP_F8
+
+template <int LA, int LB, typename Epi, bool F8 = false>
 __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) {
   constexpr int BM = 256, BN = 256, BK = kDmaBK;
   using Tile = DmaTile<LA, LB>;
@@ -788,8 +889,12 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   typename Tile::OpB opb;
   opa.init(static_cast<const bf16*>(s.A) + bi * s.a_batch, s.lda, m0, s.M, wave, lane, s.a_panel);
   opb.init(static_cast<const bf16*>(s.B) + bi * s.b_batch, s.ldb, n0, s.N, wave, lane, 0);
-  dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sa4, sb0, sb1, sb2, sb3, sb4, nk, kbeg, kend, wave, wm, wn,
-                 lane);
+  if constexpr (F8)
+    dma_ring_f8<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sa4, sb0, sb1, sb2, sb3, sb4, nk, kbeg, kend, wave, wm, wn,
+                      lane);
+  else
+    dma_ring<Tile>(acc, opa, opb, sa0, sa1, sa2, sa3, sa4, sb0, sb1, sb2, sb3, sb4, nk, kbeg, kend, wave, wm, wn,
+                   lane);
   __syncthreads();
   // the A stages become the waves' 32 x 128 float32 slabs, B stage 0 the row-sum scratch
   static_assert(E * sizeof(bf16) == 32 * 128 * sizeof(float), "one A stage holds one slab");
@@ -816,6 +921,18 @@ nc_status launch_gemm(const GemmShape& s, const Epi& epi, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_kernel<T, LA, LB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
                        epi);
   NC_LAUNCH_CHECK("gemm");
+  return NC_OK;
+}
+
+// FP8 E4M3 operands, both K-contiguous, each stored as 16-bit pairs: s.K,
+// s.lda, s.ldb count pairs.
+template <typename Epi>
+nc_status launch_gemm_f8(const GemmShape& s, const Epi& epi, hipStream_t stream) {
+  int tiles_m = (s.M + 255) / 256, tiles_n = (s.N + 255) / 256;
+  long blocks = (long)tiles_m * tiles_n * s.n_split * s.batch;
+  if (blocks <= 0) return NC_OK;
+  hipLaunchKernelGGL((gemm_dma_kernel<kKc, kKc, Epi, true>), dim3((unsigned)blocks), dim3(256), 0, stream, s, epi);
+  NC_LAUNCH_CHECK("gemm_f8");
   return NC_OK;
 }
 

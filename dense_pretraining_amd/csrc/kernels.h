@@ -150,6 +150,22 @@ template <typename T>
 nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const T* dO, const float* lse,
                    float* rowstat, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st);
 
+// ------------------------------------------------------------ FP8 forward products (fp8.hip, gemm.hip)
+// q = E4M3(x / s) over n elements (n % 8 == 0) with one scale s per tensor,
+// written to *scale; amax: one uint32 of scratch.
+template <typename T>
+nc_status quantize_fp8(const T* x, long n, uint8_t* q, float* scale, uint32_t* amax, hipStream_t st);
+// Scratch of the FP8 forward products: the operands' FP8 copies (xq: M * K
+// bytes, wq: N * K bytes for the largest product), two scales, two words.
+struct Fp8Buf {
+  uint8_t *xq, *wq;
+  float* scale;
+  uint32_t* amax;
+};
+// y[M,N] = act((x W^T) as FP8 E4M3 products) (+ res), bf16 storage; K % 16 == 0.
+nc_status gemm_xwt_fp8(const bf16* x, const bf16* w, bf16* y, const bf16* res, int M, int N, int K, bool relu_sq_out,
+                       const Fp8Buf& b, hipStream_t st);
+
 // ------------------------------------------------------------ optimizer (opt.hip)
 // master = widen(params), s1 = 0 (n elements), s2 = 0 (n2 elements).
 template <typename T>

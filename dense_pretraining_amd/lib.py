@@ -19,6 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnc.so")
 
 NC_OK = 0
+# storage modes of nc_config.dtype: bf16, float32 (check mode), bf16 with FP8 E4M3 forward block products
+_DTYPES = {"bf16": 0, "f32": 1, "bf16_fp8": 2}
 STATUS_NAMES = {
     0: "NC_OK", 1: "NC_ERR_INVALID_ARG", 2: "NC_ERR_SHAPE", 3: "NC_ERR_ALIGN", 4: "NC_ERR_WORKSPACE",
     5: "NC_ERR_UNSUPPORTED", 6: "NC_ERR_HIP", 7: "NC_ERR_DEVICE_DATA",
@@ -128,7 +130,7 @@ def load(path=LIB_PATH):
 def to_nc_config(cfg: Config) -> NcConfig:
     return NcConfig(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
                     cfg.batch, cfg.seq_len, cfg.softcap, cfg.rope_base, cfg.norm_eps,
-                    NC_BF16 if cfg.dtype == "bf16" else NC_F32)
+                    _DTYPES[cfg.dtype])
 
 
 def _check(code, where):
@@ -152,7 +154,8 @@ def _stream(stream):
 
 
 def torch_dtype(cfg: Config):
-    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    """Storage type of weights and activations."""
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
 
 
 # ------------------------------------------------------------------ queries

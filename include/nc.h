@@ -21,7 +21,16 @@
  *  - Storage type: cfg->dtype = NC_BF16 stores weights, activations and
  *    activation gradients as bfloat16 (round to nearest even); NC_F32 stores
  *    them as float (the check mode). Statistics, GEMM accumulation, softmax,
- *    loss and all weight gradients are float32 in both modes.
+ *    loss and all weight gradients are float32 in both modes. NC_BF16_FP8
+ *    stores as NC_BF16 and runs the four forward projections of every block
+ *    (QKV, O, W1, W2) as FP8 E4M3 products: each operand is rounded to E4M3
+ *    under one scale per tensor (its largest magnitude maps to 448), the
+ *    products accumulate in float32, and the result is scaled back. The page
+ *    on pomoai.com says nanochat's newest version trains with FP8 and gives no
+ *    recipe; this per-tensor, forward-only form is the plainest reading. The
+ *    backward is the NC_BF16 one on the same bf16 activations (the rounding
+ *    is treated as the identity). Inference (nc_prefill, nc_decode_step)
+ *    returns NC_ERR_UNSUPPORTED for it.
  *  - Layouts are row-major. Weights use the [out, in] layout of a linear
  *    layer. M = batch * seq_len tokens; token m is row b = m / seq_len,
  *    position t = m % seq_len. d = d_model, H = n_head, G = n_kv_head,
@@ -65,7 +74,7 @@ typedef enum nc_status {
   NC_ERR_DEVICE_DATA = 7  /* nc_read_status found a set device status bit */
 } nc_status;
 
-typedef enum nc_dtype { NC_BF16 = 0, NC_F32 = 1 } nc_dtype;
+typedef enum nc_dtype { NC_BF16 = 0, NC_F32 = 1, NC_BF16_FP8 = 2 } nc_dtype;
 
 /* Device status bits (see nc_read_status). */
 #define NC_STATUS_BAD_TOKEN 0x1u
