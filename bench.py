@@ -40,8 +40,12 @@ WORKLOADS = {
                            "32 x 2048 tokens, bf16, forward+backward"),
     "depth30": (C.DEPTH30, "depth-30 decoder (d 1920, 15x128 heads, 1 KV head, MLP 7680, vocab 65536), "
                            "16 x 2048 tokens, bf16, forward+backward"),
+    "depth20_fp8": (C.DEPTH20.with_(dtype="bf16_fp8"),
+                    "depth-20 decoder as above, 32 x 2048 tokens, bf16 storage with the four forward block "
+                    "products in FP8 E4M3 (per-tensor scales), forward+backward"),
 }
 PEAK_BF16 = C.MI355X_BF16_DENSE_PEAK
+PEAK_FP8 = C.MI355X_FP8_DENSE_PEAK
 PEAK_HBM = C.MI355X_HBM_PEAK
 
 
@@ -70,8 +74,9 @@ def roofline(table):
     name, r = next(iter(table.items()))
     if r["flops_per_launch"] > 0:
         ach = r["tflops"]
-        return name, dict(bound="mfma", achieved=round(ach, 2), peak=round(PEAK_BF16 / 1e12, 1), unit="TFLOP/s",
-                          frac=round(ach / (PEAK_BF16 / 1e12), 4), traffic=None,
+        peak = (PEAK_FP8 if name.endswith("_fp8") else PEAK_BF16) / 1e12  # a contraction against its own dtype
+        return name, dict(bound="mfma", achieved=round(ach, 2), peak=round(peak, 1), unit="TFLOP/s",
+                          frac=round(ach / peak, 4), traffic=None,
                           kernel=name, flops_per_launch=r["flops_per_launch"],
                           avg_launch_ms=round(r["ms_per_step"] / r["launches_per_step"], 4))
     ach = r["gbps"]
@@ -88,14 +93,12 @@ def measured_traffic(scope):
     import glob
     from dense_pretraining_amd.profiling import source_hash
 
-    h = None
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json"))):
         with open(f) as fh:
             rec = json.load(fh)
         if rec.get("scope") != scope:
             continue
-        h = h or source_hash()
-        if rec.get("source_sha256") == h:
+        if rec.get("source_sha256") == source_hash(rec.get("sources")):
             return rec["traffic_bytes_per_launch"]
     return None
 
@@ -348,7 +351,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["infer", "opt"], default="depth20",
-                    help="training step (depth20, depth30), KV-cache generation (infer) or the optimizer step (opt)")
+                    help="training step (depth20, depth30, depth20_fp8), KV-cache generation (infer) or the optimizer step (opt)")
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -375,7 +378,7 @@ def main():
     lib.load()
     t_gen = time.perf_counter()
     p = synth.init_params(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
-                          std=0.02, seed=0, dtype=cfg.dtype, out=np.float32)
+                          std=0.02, seed=0, dtype="f32" if cfg.dtype == "f32" else "bf16", out=np.float32)
     idx, tg = synth.zipf_tokens(cfg.vocab, cfg.batch, cfg.seq_len)
     params = torch.from_numpy(flat_params(p)).to("cuda", lib.torch_dtype(cfg))
     idx_d = torch.from_numpy(idx.reshape(-1)).cuda()
@@ -444,6 +447,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic: seeded Zipf(1.1) token ids, N(0, 0.02) weights",
         "config": {"workload": desc, "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none"},
+        # MFU against the bf16 peak in every mode (FP8 mode: the forward block products run at up to twice it)
         "mfu": round(tps * f_causal / PEAK_BF16, 4),
         "mfu_palm": round(tps * f_palm / PEAK_BF16, 4),
         "loss": round(float(loss.item()), 6),

@@ -86,4 +86,5 @@ def flops_per_token(cfg, convention="causal"):
 
 MI355X_BF16_DENSE_PEAK = 2.5166e15  # 256 CU x 2.4 GHz x 4096 flop/clk
 MI355X_FP32_MFMA_PEAK = 157.3e12
+MI355X_FP8_DENSE_PEAK = 5.0332e15  # twice the bf16 rate
 MI355X_HBM_PEAK = 8.0e12

@@ -12,7 +12,8 @@ Two jobs, both reading the CSV files rocprofv3 writes with
   counter is first scaled by what it reads for a plain device copy of known
   size in the same process (bench.py ``--copy-mib``), so that the figure is in
   the copy's bytes. The result goes to a JSON file that records a hash of the
-  kernel sources; bench.py reports the figure only while that hash matches.
+  files the kernel is built from; bench.py reports the figure only while that
+  hash matches.
 
 Usage (paths are those rocprofv3 wrote):
 
@@ -36,10 +37,14 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_hash() -> str:
-    """sha256 over the HIP sources and headers of the library, in name order."""
+def source_hash(names=None) -> str:
+    """sha256 over the named files of csrc/ (default: every HIP source and
+    header of the library), in name order."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h")))
+    if names:
+        files = sorted(os.path.join(PKG, "csrc", n) for n in names)
+    else:
+        files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h")))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -74,7 +79,8 @@ def stats_table(path, steps, kernel=None, bench_ms=None, top=25):
     out.append("| kernel | calls | total ms | avg us | % |")
     out.append("|---|---:|---:|---:|---:|")
     for name, calls, tot in recs[:top]:
-        out.append(f"| `{name}` | {calls} | {tot / 1e6:.2f} | {tot / calls / 1e3:.1f} | {100 * tot / total:.2f} |")
+        shown = name if len(name) <= 160 else name[:157] + "..."
+        out.append(f"| `{shown}` | {calls} | {tot / 1e6:.2f} | {tot / calls / 1e3:.1f} | {100 * tot / total:.2f} |")
     out.append("")
     out.append(f"Sum of all kernels: {total / 1e6:.1f} ms over {steps} steps = {total / 1e6 / steps:.1f} ms/step.")
     if kernel:
@@ -142,6 +148,8 @@ def main(argv=None):
     t.add_argument("--kernel", required=True, help="regex of the kernel symbol")
     t.add_argument("--scope", required=True, help="bench.py kernel name the figure belongs to")
     t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--sources", default="gemm.h,gemm.hip,common.h",
+                   help="comma-separated csrc/ files the kernel is built from; the figure is stale once they change")
     t.add_argument("--command", default="")
     t.add_argument("--out", required=True)
     a = ap.parse_args(argv)
@@ -163,7 +171,8 @@ def main(argv=None):
     f = scaled_counter(a.fetch, "FETCH_SIZE", a.kernel, copy_bytes)
     w = scaled_counter(a.write, "WRITE_SIZE", a.kernel, copy_bytes)
     res = dict(scope=a.scope, kernel_regex=a.kernel, traffic_bytes_per_launch=f["bytes_per_launch"] + w["bytes_per_launch"],
-               fetch=f, write=w, copy_bytes=copy_bytes, source_sha256=source_hash(), command=a.command)
+               fetch=f, write=w, copy_bytes=copy_bytes, sources=a.sources.split(","),
+               source_sha256=source_hash(a.sources.split(",")), command=a.command)
     with open(a.out, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res, indent=1))
