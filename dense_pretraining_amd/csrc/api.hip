@@ -188,21 +188,26 @@ EmbedScratch carve_embed_scratch(Carver& c, const Dims& m) {
   return s;
 }
 
-// The FP8 operand copies of the largest forward product (act [M, F] and W2
-// [d, F], or QKV's [QKV, d] weight), two scales and two amax words.
+// Elements of a block's four weight matrices, in FP8 slot order.
+void fp8_weight_sizes(const Dims& m, size_t* n) {
+  n[0] = (size_t)m.QKV * m.d;
+  n[1] = (size_t)m.d * m.HD;
+  n[2] = (size_t)m.F * m.d;
+  n[3] = (size_t)m.d * m.F;
+}
+
+// The codes of the largest activation operand (act [M, F] at most), the
+// block's four weight matrices' codes, and the per-tensor scales and maxima.
 Fp8Buf carve_fp8(Carver& c, const Dims& m) {
   Fp8Buf b;
   long kmax = m.d > m.HD ? m.d : m.HD;
   kmax = kmax > m.F ? kmax : m.F;
-  size_t w = (size_t)m.QKV * m.d;
-  const size_t w2 = (size_t)m.d * m.F, w1 = (size_t)m.F * m.d, wo = (size_t)m.d * m.HD;
-  w = w > w2 ? w : w2;
-  w = w > w1 ? w : w1;
-  w = w > wo ? w : wo;
+  size_t n[4];
+  fp8_weight_sizes(m, n);
   b.xq = c.take<uint8_t>((size_t)m.M * kmax);
-  b.wq = c.take<uint8_t>(w);
-  b.scale = c.take<float>(2);
-  b.amax = c.take<uint32_t>(2);
+  b.wq = c.take<uint8_t>(n[0] + n[1] + n[2] + n[3]);
+  b.scale = c.take<float>(kF8Slots);
+  b.amax = c.take<uint32_t>((size_t)kF8Slots * kAmaxWords);
   return b;
 }
 
@@ -278,26 +283,60 @@ struct BlockW {
   const T *wqkv, *wo, *w1, *w2;
 };
 
+// The block forward with the four projections as FP8 products (bf16 storage).
+// Each activation's maximum comes from the kernel that writes it; the
+// weights are quantised first, all four in one pass.
+nc_status block_fwd_fp8(const Dims& m, const BlockW<bf16>& w, const bf16* x, bf16* x_out, const BlockSaved<bf16>& s,
+                        const float* cs, const float* sn, const Fp8Buf& f, hipStream_t st) {
+  const int M = (int)m.M;
+  if (m.d % 16 || m.HD % 16 || m.F % 16) return NC_ERR_UNSUPPORTED;
+  size_t n[4];
+  fp8_weight_sizes(m, n);
+  Fp8Tab<bf16> wt{{w.wqkv, w.wo, w.w1, w.w2},
+                  {(long)n[0] / 8, (long)n[1] / 8, (long)n[2] / 8, (long)n[3] / 8},
+                  {f.wq, f.wq + n[0], f.wq + n[0] + n[1], f.wq + n[0] + n[1] + n[2]}};
+  auto amax = [&](int slot) { return f.amax + (size_t)slot * kAmaxWords; };
+  NC_TRY(fill_u32(f.amax, 0u, (size_t)kF8Slots * kAmaxWords, st));
+  NC_TRY(fp8_amax(wt, 4, amax(kF8Wqkv), st));
+  NC_TRY(fp8_quantize(wt, 4, amax(kF8Wqkv), f.scale + kF8Wqkv, st));
+  // one activation operand: its codes into xq (its maximum is already in amax(slot))
+  auto quant = [&](const bf16* a, long elems, int slot) -> nc_status {
+    Fp8Tab<bf16> t{{a}, {elems / 8}, {f.xq}};
+    return fp8_quantize(t, 1, amax(slot), f.scale + slot, st);
+  };
+  const float* sc = f.scale;
+  NC_TRY(rmsnorm_fwd<bf16>(x, nullptr, 0, s.h1, s.r1, M, m.d, m.eps, nullptr, st, amax(kF8H1)));
+  NC_TRY(quant(s.h1, m.M * m.d, kF8H1));
+  NC_TRY(gemm_fp8(f.xq, wt.q[0], sc + kF8H1, sc + kF8Wqkv, s.qkv, nullptr, M, m.QKV, m.d, false, nullptr, st));
+  NC_TRY(qknorm_rope_fwd<bf16>(s.qkv, m.QKV, s.qk, m.QK, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
+  AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
+  NC_TRY(attn_fwd<bf16>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, s.lse, st, amax(kF8O)));
+  NC_TRY(quant(s.o, m.M * m.HD, kF8O));
+  NC_TRY(gemm_fp8(f.xq, wt.q[1], sc + kF8O, sc + kF8Wo, s.x1, x, M, m.d, m.HD, false, nullptr, st));
+  NC_TRY(rmsnorm_fwd<bf16>(s.x1, nullptr, 0, s.h2, s.r2, M, m.d, m.eps, nullptr, st, amax(kF8H2)));
+  NC_TRY(quant(s.h2, m.M * m.d, kF8H2));
+  NC_TRY(gemm_fp8(f.xq, wt.q[2], sc + kF8H2, sc + kF8W1, s.act, nullptr, M, m.F, m.d, true, amax(kF8Act), st));
+  NC_TRY(quant(s.act, m.M * m.F, kF8Act));
+  NC_TRY(gemm_fp8(f.xq, wt.q[3], sc + kF8Act, sc + kF8W2, x_out, s.x1, M, m.d, m.F, false, nullptr, st));
+  return NC_OK;
+}
+
 template <typename T>
 nc_status block_fwd_t(const Dims& m, const BlockW<T>& w, const T* x, T* x_out, const BlockSaved<T>& s,
                       const float* cs, const float* sn, hipStream_t st, const Fp8Buf* f8 = nullptr) {
+  if constexpr (sizeof(T) == 2) {
+    if (m.fp8) return f8 ? block_fwd_fp8(m, w, x, x_out, s, cs, sn, *f8, st) : NC_ERR_INVALID_ARG;
+  }
   const int M = (int)m.M;
-  // x[M,K] W[N,K]^T (+ res), FP8 products when the config asks for them
-  auto mm = [&](const T* a, const T* b, T* y, const T* res, int N, int K, bool relu_sq) -> nc_status {
-    if constexpr (sizeof(T) == 2) {
-      if (m.fp8) return f8 ? gemm_xwt_fp8(a, b, y, res, M, N, K, relu_sq, *f8, st) : NC_ERR_INVALID_ARG;
-    }
-    return gemm_xwt<T>(a, b, y, res, M, N, K, relu_sq, st);
-  };
   NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.h1, s.r1, M, m.d, m.eps, nullptr, st));
-  NC_TRY(mm(s.h1, w.wqkv, s.qkv, nullptr, m.QKV, m.d, false));
+  NC_TRY(gemm_xwt<T>(s.h1, w.wqkv, s.qkv, nullptr, M, m.QKV, m.d, false, st));
   NC_TRY(qknorm_rope_fwd<T>(s.qkv, m.QKV, s.qk, m.QK, cs, sn, M, m.T, m.H + m.G, m.D, m.eps, st));
   AttnArgs a{m.B, m.T, m.H, m.G, m.D, m.QK, m.QKV, m.HD, m.QKV};
   NC_TRY(attn_fwd<T>(a, s.qk, s.qkv + (size_t)(m.H + m.G) * m.D, s.o, s.lse, st));
-  NC_TRY(mm(s.o, w.wo, s.x1, x, m.d, m.HD, false));
+  NC_TRY(gemm_xwt<T>(s.o, w.wo, s.x1, x, M, m.d, m.HD, false, st));
   NC_TRY(rmsnorm_fwd<T>(s.x1, nullptr, 0, s.h2, s.r2, M, m.d, m.eps, nullptr, st));
-  NC_TRY(mm(s.h2, w.w1, s.act, nullptr, m.F, m.d, true));
-  NC_TRY(mm(s.act, w.w2, x_out, s.x1, m.d, m.F, false));
+  NC_TRY(gemm_xwt<T>(s.h2, w.w1, s.act, nullptr, M, m.F, m.d, true, st));
+  NC_TRY(gemm_xwt<T>(s.act, w.w2, x_out, s.x1, M, m.d, m.F, false, st));
   return NC_OK;
 }
 

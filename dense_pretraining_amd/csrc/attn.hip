@@ -223,10 +223,12 @@ struct AttnGeom {
 };
 
 // ============================================================ forward
-template <typename T, int D>
+// With AMAX, the largest stored |o| goes into the striped maximum at amax (the
+// per-tensor scale of the FP8 output projection's operand).
+template <typename T, int D, bool AMAX>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* __restrict__ qk,
                                                           const T* __restrict__ vsrc, T* __restrict__ o,
-                                                          float* __restrict__ lse) {
+                                                          float* __restrict__ lse, uint32_t* amax) {
   using Kv = KvDma<T, D>;
   constexpr int BKV = Kv::BKV;
   __shared__ __align__(16) T ks0[Kv::TILE], vs0[Kv::TILE], ks1[Kv::TILE], vs1[Kv::TILE];
@@ -316,6 +318,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
   });
 
   lsum += __shfl_xor(lsum, 32, 64);
+  float om = 0.f;  // AMAX: largest stored |o| of the lane
   if (qok) {
     const float inv = 1.f / lsum;
     T* orow = o + (tok0 + tq) * g.ld_o + (long)hq * D;
@@ -325,10 +328,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
       for (int j = 0; j < 4; ++j) {
         T* dst = orow + 32 * dt + 8 * j + 4 * lh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(oacc[dt][4 * j + i] * inv);
+        for (int i = 0; i < 4; ++i) {
+          const float ov = oacc[dt][4 * j + i] * inv;
+          if constexpr (AMAX) om = fmaxf(om, fabsf(ov));
+          dst[i] = from_f32<T>(ov);
+        }
       }
     if (lh == 0) lse[(tok0 + tq) * g.H + hq] = (m0 + log2f(lsum)) / kLog2e;
   }
+  // an FP8 operand's per-tensor scale: the wave's largest stored magnitude
+  if constexpr (AMAX) amax_publish_wave(to_f32(from_f32<T>(om)), amax);
 }
 
 // ============================================================ decode: one query row per head
@@ -873,13 +882,19 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
 double causal_pairs(const AttnGeom& g) { return (double)g.B * g.H * g.T * (g.T + 1.0) / 2.0; }
 
 template <typename T, int D>
-nc_status attn_fwd_impl(const AttnGeom& g, const T* qk, const T* v, T* o, float* lse, hipStream_t st) {
+nc_status attn_fwd_impl(const AttnGeom& g, const T* qk, const T* v, T* o, float* lse, hipStream_t st,
+                        uint32_t* amax) {
   int nqb = (g.T * g.n_rep + 127) / 128;
   const double tok = (double)g.B * g.T, es = sizeof(T);
   // S = Q K^T and O = P V: 4 D flops per pair
   ProfScope prof(NC_NAME(T, "attn_fwd"), 4.0 * D * causal_pairs(g),
                  es * tok * D * (2.0 * g.H + 2.0 * g.G) + 4.0 * tok * g.H, st);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(nqb * g.G * g.B), dim3(256), 0, st, g, qk, v, o, lse);
+  if (amax)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), dim3(nqb * g.G * g.B), dim3(256), 0, st, g, qk, v, o, lse,
+                       amax);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), dim3(nqb * g.G * g.B), dim3(256), 0, st, g, qk, v, o, lse,
+                       amax);
   NC_LAUNCH_CHECK("attn_fwd");
   return NC_OK;
 }
@@ -953,10 +968,10 @@ AttnGeom make_geom(const AttnArgs& a) {
 }  // namespace
 
 template <typename T>
-nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse, hipStream_t st) {
+nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse, hipStream_t st, uint32_t* amax) {
   AttnGeom g = make_geom(a);
-  if (a.D == 128) return attn_fwd_impl<T, 128>(g, qk, v, o, lse, st);
-  if (a.D == 64) return attn_fwd_impl<T, 64>(g, qk, v, o, lse, st);
+  if (a.D == 128) return attn_fwd_impl<T, 128>(g, qk, v, o, lse, st, amax);
+  if (a.D == 64) return attn_fwd_impl<T, 64>(g, qk, v, o, lse, st, amax);
   return NC_ERR_UNSUPPORTED;
 }
 
@@ -986,8 +1001,9 @@ template nc_status attn_decode<bf16>(const bf16*, long, const bf16*, const bf16*
 template nc_status attn_decode<float>(const float*, long, const float*, const float*, int, int, int, int, int, int,
                                       float*, long, float*, float*, hipStream_t);
 
-template nc_status attn_fwd<bf16>(const AttnArgs&, const bf16*, const bf16*, bf16*, float*, hipStream_t);
-template nc_status attn_fwd<float>(const AttnArgs&, const float*, const float*, float*, float*, hipStream_t);
+template nc_status attn_fwd<bf16>(const AttnArgs&, const bf16*, const bf16*, bf16*, float*, hipStream_t, uint32_t*);
+template nc_status attn_fwd<float>(const AttnArgs&, const float*, const float*, float*, float*, hipStream_t,
+                                   uint32_t*);
 template nc_status attn_bwd<bf16>(const AttnArgs&, const bf16*, const bf16*, const bf16*, const bf16*, const float*,
                                   float*, bf16*, bf16*, bf16*, long, hipStream_t);
 template nc_status attn_bwd<float>(const AttnArgs&, const float*, const float*, const float*, const float*,

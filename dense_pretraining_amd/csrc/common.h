@@ -99,6 +99,36 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Running maximum magnitude of a tensor, kept as the bits of non-negative
+// floats: those order like the floats, so unsigned atomic maxima reach the
+// same words whatever the order of the calls. The maximum is spread over
+// kAmaxStripes words kAmaxStride words (128 bytes) apart; a block publishes
+// into the stripe of its index, so that thousands of blocks do not queue on
+// one address, and the reader takes the largest stripe. Callers pass the
+// maximum of the values they stored, in the storage type's rounding (which is
+// monotonic: the rounded maximum is the maximum of the rounded values).
+constexpr int kAmaxStripes = 64, kAmaxStride = 32;
+constexpr int kAmaxWords = kAmaxStripes * kAmaxStride;  // uint32 words per tensor
+__device__ __forceinline__ void amax_publish(uint32_t* amax, float m) {
+  atomicMax(amax + (blockIdx.x % kAmaxStripes) * kAmaxStride, __float_as_uint(m));
+}
+// Lane 0 of each wave publishes the wave's maximum; nothing waits for the atomic.
+__device__ __forceinline__ void amax_publish_wave(float m, uint32_t* amax) {
+  m = wave_max(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) amax_publish(amax, m);
+}
+// The tensor's maximum, read by a whole wave (lane i reads stripe i).
+__device__ __forceinline__ float amax_read(const uint32_t* amax) {
+  static_assert(kAmaxStripes == kWave, "one stripe per lane");
+  return wave_max(__uint_as_float(amax[(threadIdx.x & (kWave - 1)) * kAmaxStride]));
+}
+
 __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bits) {
   if (status) atomicOr(status, bits);
 }

@@ -227,12 +227,20 @@ struct EpiCtx {
 // writes and reads (lane-dependent addresses it cannot tell apart) in program
 // order, so no fence is needed between the two phases.
 
+// Epilogues that can report the largest stored magnitude (kTracksMax).
+template <typename Epi, typename = void>
+struct EpiTracksMax { static constexpr bool value = false; };
+template <typename Epi>
+struct EpiTracksMax<Epi, std::void_t<decltype(Epi::kTracksMax)>> { static constexpr bool value = Epi::kTracksMax; };
+
 template <int WTM, int WTN, typename Epi>
 __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi& epi, const EpiCtx& x,
                                                 float* slab) {
   constexpr int NCH = 8 * WTN;  // 16-byte chunks per slab row
+  constexpr bool kMax = EpiTracksMax<Epi>::value;
   const int lane = x.lane, lr = lane & 31, h = lane >> 5;
   const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
+  float tmax = 0.f;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
     // the slab's other inputs (residual, activation) are fetched first, in
@@ -264,9 +272,11 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
         const float4 q = *reinterpret_cast<const float4*>(slab + 4 * (rr * NCH + (cc ^ (rr & 15))));
         float v[4] = {q.x, q.y, q.z, q.w};
         epi.post(x, r0 + 32 * i + rr, c0 + 4 * cc, v, aux[it][k]);
+        if constexpr (kMax) epi.track(tmax, r0 + 32 * i + rr, c0 + 4 * cc, v);
       }
     }
   }
+  if constexpr (kMax) epi.publish(tmax);
 }
 
 // Four values of a second [M,N] input in the storage type, fetched ahead.
@@ -300,8 +310,9 @@ struct NoAux {};
   __device__ __forceinline__ void finish(const EpiCtx&) const {}
 
 // C = act(acc) (+ residual), act = identity or the ReLU^2 activation
-// max(x, 0)^2. Output in the storage type.
-template <typename T, bool ReluSqOut = false>
+// max(x, 0)^2. Output in the storage type. With TrackMax, the largest stored
+// |C| goes into the striped maximum at amax (an FP8 operand's scale).
+template <typename T, bool ReluSqOut = false, bool TrackMax = false>
 struct EpiStore {
   NC_EPI_NO_ROW_WORK
   T* C;
@@ -309,15 +320,18 @@ struct EpiStore {
   const T* res;  // optional residual, same layout as C
   long ldr;
   int M, N;
-  const float* scale = nullptr;  // FP8 products: the two operands' dequantisation scales, multiplied in first
+  const float* sa = nullptr;  // FP8 products: the two operands' dequantisation scales, multiplied in first
+  const float* sb = nullptr;
+  uint32_t* amax = nullptr;   // TrackMax: the striped maximum
+  static constexpr bool kTracksMax = TrackMax;
   using Aux = Aux4<T>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
     return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
   }
   __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
     if (row >= M || col >= N) return;
-    if (scale) {
-      const float sc = scale[0] * scale[1];
+    if (sa) {
+      const float sc = *sa * *sb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] *= sc;
     }
@@ -336,6 +350,11 @@ struct EpiStore {
     }
     store4<T>(C + (long)row * ldc + col, v);
   }
+  // after post (v holds the stored values before rounding)
+  __device__ __forceinline__ void track(float& t, int row, int col, const float* v) const {
+    if (row < M && col < N) t = fmaxf(t, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  __device__ __forceinline__ void publish(float t) const { amax_publish_wave(to_f32(from_f32<T>(t)), amax); }
 };
 
 // y = alpha * acc + beta * res (res optional), stored in T: the steps of the

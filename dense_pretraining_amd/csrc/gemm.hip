@@ -65,23 +65,32 @@ nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int 
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
-nc_status gemm_xwt_fp8(const bf16* x, const bf16* w, bf16* y, const bf16* res, int M, int N, int K, bool relu_sq_out,
-                       const Fp8Buf& b, hipStream_t st) {
-  if (K % 16 != 0) return NC_ERR_UNSUPPORTED;
-  NC_TRY(quantize_fp8<bf16>(x, (long)M * K, b.xq, b.scale, b.amax, st));
-  NC_TRY(quantize_fp8<bf16>(w, (long)N * K, b.wq, b.scale + 1, b.amax + 1, st));
+nc_status gemm_fp8(const uint8_t* xq, const uint8_t* wq, const float* sx, const float* sw, bf16* y, const bf16* res,
+                   int M, int N, int K, bool relu_sq_out, uint32_t* amax_out, hipStream_t st) {
+  if (K % 16 != 0 || !sx || !sw) return NC_ERR_UNSUPPORTED;
   // the FP8 matrices seen as rows of K / 2 sixteen-bit pairs
   const int K2 = K / 2;
-  GemmShape s{b.xq, b.wq, K2, K2, M, N, K2, K2, 1};
+  GemmShape s{xq, wq, K2, K2, M, N, K2, K2, 1};
   ProfScope prof(relu_sq_out ? "gemm_fwd_relusq_fp8" : "gemm_fwd_fp8", 2.0 * M * N * K,
                  (double)M * K + (double)N * K + 2.0 * M * N * (res ? 2 : 1), st);
+  // the ReLU^2 output is the next product's FP8 operand: its maximum is taken here
+  if (relu_sq_out && amax_out) {
+    EpiStore<bf16, true, true> e{y, N, res, N, M, N};
+    e.sa = sx;
+    e.sb = sw;
+    e.amax = amax_out;
+    return launch_gemm_f8(s, e, st);
+  }
+  if (amax_out) return NC_ERR_UNSUPPORTED;
   if (relu_sq_out) {
     EpiStore<bf16, true> e{y, N, res, N, M, N};
-    e.scale = b.scale;
+    e.sa = sx;
+    e.sb = sw;
     return launch_gemm_f8(s, e, st);
   }
   EpiStore<bf16> e{y, N, res, N, M, N};
-  e.scale = b.scale;
+  e.sa = sx;
+  e.sb = sw;
   return launch_gemm_f8(s, e, st);
 }
 

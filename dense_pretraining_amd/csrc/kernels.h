@@ -82,9 +82,11 @@ nc_status argmax_cand(const float2* cand, int M, int ntn, int32_t* out, hipStrea
 nc_status fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 nc_status fill_f32(float* p, float v, size_t n, hipStream_t st);
 // y = x / sqrt(mean(x^2)+eps) per row, r = the scale; with idx, row m reads x[idx[m]].
+// With amax (not with idx): the stored |y| into the striped maximum at amax
+// (kAmaxWords words, cleared by the caller).
 template <typename T>
 nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int M, int d, float eps,
-                      uint32_t* status, hipStream_t st);
+                      uint32_t* status, hipStream_t st, uint32_t* amax = nullptr);
 // dx = (res) + r (dy - y mean(dy y)); output T or float.
 template <typename T, typename TO>
 nc_status rmsnorm_bwd(const T* dy, const T* y, const float* r, const T* res, TO* dx, int M, int d, hipStream_t st);
@@ -142,8 +144,11 @@ struct AttnArgs {
   long ld_o;   // row stride of o and dO
   long ld_dq;  // row stride of dq
 };
+// o = causal softmax(q k^T / sqrt(D)) v per query head, lse per (row, head).
+// With amax: the stored |o| into the striped maximum at amax.
 template <typename T>
-nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse, hipStream_t st);
+nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse, hipStream_t st,
+                   uint32_t* amax = nullptr);
 template <typename T>
 // rowstat: scratch of 2 * B * T * H floats, the per-row (lse log2 e, Delta)
 // pairs the dQ pass hands to the dK/dV pass.
@@ -151,20 +156,41 @@ nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const
                    float* rowstat, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st);
 
 // ------------------------------------------------------------ FP8 forward products (fp8.hip, gemm.hip)
-// q = E4M3(x / s) over n elements (n % 8 == 0) with one scale s per tensor,
-// written to *scale; amax: one uint32 of scratch.
+// Up to kFp8TabMax tensors handled by one launch: x[k] holds 8 * n8[k]
+// elements, q[k] receives their E4M3 codes.
+constexpr int kFp8TabMax = 4;
 template <typename T>
-nc_status quantize_fp8(const T* x, long n, uint8_t* q, float* scale, uint32_t* amax, hipStream_t st);
-// Scratch of the FP8 forward products: the operands' FP8 copies (xq: M * K
-// bytes, wq: N * K bytes for the largest product), two scales, two words.
+struct Fp8Tab {
+  const T* x[kFp8TabMax];
+  long n8[kFp8TabMax];
+  uint8_t* q[kFp8TabMax];
+};
+// Tensor k's maximum |x[k]| into amax + k * kAmaxWords (striped float bits,
+// see common.h; the caller clears the words).
+template <typename T>
+nc_status fp8_amax(const Fp8Tab<T>& t, int count, uint32_t* amax, hipStream_t st);
+// q[k] = E4M3(clip(x[k] * 448 / a, +-448)), scale[k] = a / 448 with a the maximum
+// held at amax + k * kAmaxWords
+// (1 and 1 when a = 0): one read of x, one write of the codes.
+template <typename T>
+nc_status fp8_quantize(const Fp8Tab<T>& t, int count, const uint32_t* amax, float* scale, hipStream_t st);
+
+// Per-tensor words of one block's FP8 products, in this order.
+enum Fp8Slot { kF8H1, kF8O, kF8H2, kF8Act, kF8Wqkv, kF8Wo, kF8W1, kF8W2, kF8Slots };
+// Scratch of the FP8 forward products: the current activation operand's codes
+// (xq: M * largest K bytes), the block's four weight matrices' codes packed
+// in slot order (wq), kF8Slots scales, and kF8Slots striped maxima of
+// kAmaxWords words each.
 struct Fp8Buf {
   uint8_t *xq, *wq;
   float* scale;
   uint32_t* amax;
 };
-// y[M,N] = act((x W^T) as FP8 E4M3 products) (+ res), bf16 storage; K % 16 == 0.
-nc_status gemm_xwt_fp8(const bf16* x, const bf16* w, bf16* y, const bf16* res, int M, int N, int K, bool relu_sq_out,
-                       const Fp8Buf& b, hipStream_t st);
+// y[M,N] = act((xq wq^T) * sx * sw) (+ res) from E4M3 codes (xq [M,K], wq [N,K]),
+// bf16 storage; K % 16 == 0. With amax_out: the stored |y| into the striped
+// maximum at amax_out.
+nc_status gemm_fp8(const uint8_t* xq, const uint8_t* wq, const float* sx, const float* sw, bf16* y, const bf16* res,
+                   int M, int N, int K, bool relu_sq_out, uint32_t* amax_out, hipStream_t st);
 
 // ------------------------------------------------------------ optimizer (opt.hip)
 // master = widen(params), s1 = 0 (n elements), s2 = 0 (n2 elements).

@@ -27,14 +27,14 @@ __global__ void fill_f32_kernel(float* p, float v, size_t n) {
 // ------------------------------------------------------------ RMSNorm
 // N(v) = v / sqrt(mean(v^2) + eps) (no gain: the architecture list on vpshk.cn
 // gives RMSNorm without learnable parameters). With GATHER, row m is the
-// embedding row idx[m] (the norm that follows the token embedding).
-template <typename T, bool GATHER>
-__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const T* __restrict__ x, const int32_t* __restrict__ idx,
-                                                          int V, T* __restrict__ y, float* __restrict__ r, int M,
-                                                          int d, float eps, uint32_t* status) {
+// embedding row idx[m] (the norm that follows the token embedding). One wave
+// per row; returns the lane's largest stored |y| when AMAX.
+template <typename T, bool GATHER, bool AMAX>
+__device__ __forceinline__ float rmsnorm_fwd_row(const T* __restrict__ x, const int32_t* __restrict__ idx, int V,
+                                                 T* __restrict__ y, float* __restrict__ r, int row, int d, float eps,
+                                                 uint32_t* status) {
   constexpr int VE = Vec<T>::n, MAXV = max_vecs<T>();
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= M) return;
+  const int lane = threadIdx.x & 63;
   long src_row = row;
   bool zero = false;
   if constexpr (GATHER) {
@@ -65,16 +65,39 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const T* __restrict__ 
   ss = wave_sum(ss);
   const float rr = 1.f / sqrtf(ss / (float)d + eps);
   T* dst = y + (long)row * d;
+  float m = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXV; ++c) {
     int vi = lane + 64 * c;
     if (vi < nv) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) v[c][e] *= rr;
+      for (int e = 0; e < VE; ++e) {
+        v[c][e] *= rr;
+        if constexpr (AMAX) m = fmaxf(m, fabsf(v[c][e]));
+      }
       store16<T>(dst + vi * VE, v[c]);
     }
   }
   if (lane == 0) r[row] = rr;
+  return m;
+}
+
+// Four rows per block. With AMAX the block's largest stored magnitude goes
+// into *amax (the per-tensor scale of an FP8 operand).
+template <typename T, bool GATHER, bool AMAX = false>
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const T* __restrict__ x, const int32_t* __restrict__ idx,
+                                                          int V, T* __restrict__ y, float* __restrict__ r, int M,
+                                                          int d, float eps, uint32_t* status, uint32_t* amax) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  float m = 0.f;
+  if (row < M) m = rmsnorm_fwd_row<T, GATHER, AMAX>(x, idx, V, y, r, row, d, eps, status);
+  if constexpr (AMAX) {
+    __shared__ float red[4];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = to_f32(from_f32<T>(m));
+    __syncthreads();
+    if (threadIdx.x == 0) amax_publish(amax, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  }
 }
 
 // dx = res + r (dy - y mean(dy y)), written in terms of the output y.
@@ -367,14 +390,20 @@ nc_status fill_f32(float* p, float v, size_t n, hipStream_t st) {
 
 template <typename T>
 nc_status rmsnorm_fwd(const T* x, const int32_t* idx, int V, T* y, float* r, int M, int d, float eps, uint32_t* status,
-                      hipStream_t st) {
+                      hipStream_t st, uint32_t* amax) {
   dim3 grid((M + 3) / 4);
   ProfScope prof(idx ? NC_NAME(T, "embed_gather_rmsnorm") : NC_NAME(T, "rmsnorm_fwd"), 0,
                  2.0 * sizeof(T) * M * d + 4.0 * M + (idx ? 4.0 * M : 0.0), st);
+  if (idx && amax) return NC_ERR_UNSUPPORTED;
   if (idx)
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, true>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status);
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, true>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status,
+                       amax);
+  else if (amax)
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, false, true>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps,
+                       status, amax);
   else
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, false>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status);
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, false>), grid, dim3(256), 0, st, x, idx, V, y, r, M, d, eps, status,
+                       amax);
   NC_LAUNCH_CHECK("rmsnorm_fwd");
   return NC_OK;
 }
@@ -468,7 +497,7 @@ nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, 
 
 #define NC_INST(T)                                                                                                  \
   template nc_status rmsnorm_fwd<T>(const T*, const int32_t*, int, T*, float*, int, int, float, uint32_t*,         \
-                                    hipStream_t);                                                                   \
+                                    hipStream_t, uint32_t*);                                                        \
   template nc_status rmsnorm_bwd<T, T>(const T*, const T*, const float*, const T*, T*, int, int, hipStream_t);     \
   template nc_status qknorm_rope_fwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
                                         float, hipStream_t, int);                                                   \

@@ -33,7 +33,10 @@ def test_traffic_scaled_by_copy(tmp_path):
     assert rec["fetch"]["factor"] == 2.0 and rec["write"]["factor"] == 1.0
     # mean fetch 200 KiB x 2 + mean write 20 KiB x 1
     assert rec["traffic_bytes_per_launch"] == (200 * 2 + 20) * 1024
-    assert rec["source_sha256"] == profiling.source_hash()
+    # the record is tied to the GEMM's own source files, not to the rest of the library
+    assert rec["sources"] == ["gemm.h", "gemm.hip", "common.h"]
+    assert rec["source_sha256"] == profiling.source_hash(rec["sources"])
+    assert rec["source_sha256"] != profiling.source_hash(["gemm.h", "gemm.hip", "common.h", "attn.hip"])
 
 
 def test_stats_table(tmp_path):
