@@ -25,6 +25,8 @@
 // walk, so that tiles sharing operand rows share an L2.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace nc {
@@ -220,7 +222,19 @@ struct EpiCtx {
   int lane, wave;
   float* red;     // LDS scratch beside the slabs (2 * BM floats)
   int batch;      // problem index of a batched launch
+  float scale = 1.f;  // FP8 products: the operands' scale product, read once per tile
 };
+
+// The dequantisation scale product of an FP8 epilogue (members sa, sb), 1 otherwise.
+template <typename Epi, typename = void>
+struct EpiScaled { static constexpr bool value = false; };
+template <typename Epi>
+struct EpiScaled<Epi, std::void_t<decltype(Epi::sa)>> { static constexpr bool value = true; };
+template <typename Epi>
+__device__ __forceinline__ float epi_scale(const Epi& e) {
+  if constexpr (EpiScaled<Epi>::value) return e.sa ? *e.sa * *e.sb : 1.f;
+  else return 1.f;
+}
 
 
 // A wave's LDS instructions execute in order, and the compiler keeps the slab
@@ -328,12 +342,11 @@ struct EpiStore {
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
     return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
   }
-  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
+  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
     if (row >= M || col >= N) return;
     if (sa) {
-      const float sc = *sa * *sb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] *= sc;
+      for (int e = 0; e < 4; ++e) v[e] *= x.scale;
     }
     if constexpr (ReluSqOut) {
 #pragma unroll
@@ -918,7 +931,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   // the A stages become the waves' 32 x 128 float32 slabs, B stage 0 the row-sum scratch
   static_assert(E * sizeof(bf16) == 32 * 128 * sizeof(float), "one A stage holds one slab");
   bf16* slab = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sa3;
-  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, reinterpret_cast<float*>(sb0), bi};
+  const EpiCtx x{m0, n0, wm, wn, z, lane, wave, reinterpret_cast<float*>(sb0), bi, epi_scale(epi)};
   staged_epilogue<4, 4>(acc.c, epi, x, reinterpret_cast<float*>(slab));
   epi.finish(x);
 }
