@@ -252,6 +252,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
                                                 float* slab) {
   constexpr int NCH = 8 * WTN;  // 16-byte chunks per slab row
   constexpr bool kMax = EpiTracksMax<Epi>::value;
+  constexpr int kReadBatch = (kMax || !std::is_empty<typename Epi::RowState>::value) ? 4 : 8;
   const int lane = x.lane, lr = lane & 31, h = lane >> 5;
   const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
   float tmax = 0.f;
@@ -277,16 +278,31 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
         *reinterpret_cast<float4*>(slab + 4 * (lr * NCH + (cc ^ (lr & 15)))) = make_float4(v[0], v[1], v[2], v[3]);
       }
     epi.row_end(rs, x, i);
+    // a batch of the slab's reads first, then its stores: the reads overlap
+    // and are waited for together, instead of one read, one wait, one store
+    // at a time (half batches where the epilogue's own registers are many)
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rr = 4 * it + (lane >> 4);
+    for (int b0 = 0; b0 < 8; b0 += kReadBatch) {
+      float4 q[kReadBatch][NCH / 16];
 #pragma unroll
-      for (int k = 0; k < NCH / 16; ++k) {
-        const int cc = (lane & 15) + 16 * k;
-        const float4 q = *reinterpret_cast<const float4*>(slab + 4 * (rr * NCH + (cc ^ (rr & 15))));
-        float v[4] = {q.x, q.y, q.z, q.w};
-        epi.post(x, r0 + 32 * i + rr, c0 + 4 * cc, v, aux[it][k]);
-        if constexpr (kMax) epi.track(tmax, r0 + 32 * i + rr, c0 + 4 * cc, v);
+      for (int ib = 0; ib < kReadBatch; ++ib) {
+        const int rr = 4 * (b0 + ib) + (lane >> 4);
+#pragma unroll
+        for (int k = 0; k < NCH / 16; ++k) {
+          const int cc = (lane & 15) + 16 * k;
+          q[ib][k] = *reinterpret_cast<const float4*>(slab + 4 * (rr * NCH + (cc ^ (rr & 15))));
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < kReadBatch; ++ib) {
+        const int it = b0 + ib, rr = 4 * it + (lane >> 4);
+#pragma unroll
+        for (int k = 0; k < NCH / 16; ++k) {
+          const int cc = (lane & 15) + 16 * k;
+          float v[4] = {q[ib][k].x, q[ib][k].y, q[ib][k].z, q[ib][k].w};
+          epi.post(x, r0 + 32 * i + rr, c0 + 4 * cc, v, aux[it][k]);
+          if constexpr (kMax) epi.track(tmax, r0 + 32 * i + rr, c0 + 4 * cc, v);
+        }
       }
     }
   }
@@ -315,6 +331,40 @@ __device__ __forceinline__ void aux_get(const Aux4<T>& a, float* v) {
 }
 struct NoAux {};
 
+// Branch-free epilogue I/O. A buffer resource starts at the tile origin; an
+// element outside the matrix gets an offset past the record, which the
+// hardware drops on a store and reads as zero on a load. With no branch per
+// element, the slab reads and stores of a row are scheduled together instead
+// of one read, one wait, one store at a time.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* base, long ld, const EpiCtx& x) {
+  return dma_rsrc(base + (long)x.m0 * ld + x.n0);
+}
+template <typename T>
+__device__ __forceinline__ int tile_off(const EpiCtx& x, int row, int col, long ld, int M, int N) {
+  return (int)(row < M && col < N ? (unsigned)(((long)(row - x.m0) * ld + (col - x.n0)) * (long)sizeof(T)) : kDmaOOB);
+}
+typedef int epi_v2i __attribute__((ext_vector_type(2)));
+typedef int epi_v4i __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ void tile_store4(__amdgpu_buffer_rsrc_t rs, int off, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 o;
+    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(epi_v2i, o), rs, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(epi_v4i, make_float4(v[0], v[1], v[2], v[3])), rs, off,
+                                           0, 0);
+  }
+}
+template <typename T>
+__device__ __forceinline__ Aux4<T> tile_load4(__amdgpu_buffer_rsrc_t rs, int off) {
+  Aux4<T> a;
+  if constexpr (sizeof(T) == 2) a.u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+  else a.u = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  return a;
+}
+
 // Hooks of an epilogue with no per-row state and no phase-1 work.
 #define NC_EPI_NO_ROW_WORK                                                          \
   struct RowState {};                                                               \
@@ -325,8 +375,12 @@ struct NoAux {};
 
 // C = act(acc) (+ residual), act = identity or the ReLU^2 activation
 // max(x, 0)^2. Output in the storage type. With TrackMax, the largest stored
-// |C| goes into the striped maximum at amax (an FP8 operand's scale).
-template <typename T, bool ReluSqOut = false, bool TrackMax = false>
+// |C| goes into the striped maximum at amax (an FP8 operand's scale). The
+// residual is a compile-time choice (HasRes): a residual load waited for after
+// the slab's first store makes the compiler drain every store in flight (one
+// counter covers loads and stores, and it cannot assume they retire in
+// order), so an epilogue without one must carry no loads at all.
+template <typename T, bool ReluSqOut = false, bool TrackMax = false, bool HasRes = false>
 struct EpiStore {
   NC_EPI_NO_ROW_WORK
   T* C;
@@ -338,16 +392,15 @@ struct EpiStore {
   const float* sb = nullptr;
   uint32_t* amax = nullptr;   // TrackMax: the striped maximum
   static constexpr bool kTracksMax = TrackMax;
-  using Aux = Aux4<T>;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
-    return aux_load<T>(res + (long)row * ldr + col, res != nullptr && row < M && col < N);
+  using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
+  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
+    if constexpr (HasRes) return tile_load4<T>(tile_rsrc(res, ldr, x), tile_off<T>(x, row, col, ldr, M, N));
+    else return Aux{};
   }
   __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
-    if (row >= M || col >= N) return;
-    if (sa) {
+    // x.scale is exactly 1 without FP8 operands (a multiply, not a branch per call)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] *= x.scale;
-    }
+    for (int e = 0; e < 4; ++e) v[e] *= x.scale;
     if constexpr (ReluSqOut) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -355,24 +408,25 @@ struct EpiStore {
         v[e] = r * r;
       }
     }
-    if (res) {
+    if constexpr (HasRes) {
       float r[4];
       aux_get<T>(a, r);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += r[e];
     }
-    store4<T>(C + (long)row * ldc + col, v);
+    tile_store4<T>(tile_rsrc(C, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
   }
   // after post (v holds the stored values before rounding)
   __device__ __forceinline__ void track(float& t, int row, int col, const float* v) const {
-    if (row < M && col < N) t = fmaxf(t, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    const float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    t = row < M && col < N ? fmaxf(t, m) : t;
   }
   __device__ __forceinline__ void publish(float t) const { amax_publish_wave(to_f32(from_f32<T>(t)), amax); }
 };
 
-// y = alpha * acc + beta * res (res optional), stored in T: the steps of the
+// y = alpha * acc + beta * res (res a compile-time choice), stored in T: the steps of the
 // Newton-Schulz iteration (B = c (A A^T) + b A, X' = (X B^T) + a X).
-template <typename T>
+template <typename T, bool HasRes = true>
 struct EpiAxpby {
   NC_EPI_NO_ROW_WORK
   T* C;
@@ -382,17 +436,23 @@ struct EpiAxpby {
   int M, N;
   float alpha, beta;
   long c_batch, r_batch;  // per-problem strides of C and res in a batched launch
-  using Aux = Aux4<T>;
+  using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
-    return aux_load<T>(res + x.batch * r_batch + (long)row * ldr + col, res != nullptr && row < M && col < N);
+    if constexpr (HasRes)
+      return tile_load4<T>(tile_rsrc(res + x.batch * r_batch, ldr, x), tile_off<T>(x, row, col, ldr, M, N));
+    else return Aux{};
   }
   __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
-    if (row >= M || col >= N) return;
-    float r[4] = {0.f, 0.f, 0.f, 0.f};
-    if (res) aux_get<T>(a, r);
+    if constexpr (HasRes) {
+      float r[4];
+      aux_get<T>(a, r);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = alpha * v[e] + beta * r[e];
-    store4<T>(C + x.batch * c_batch + (long)row * ldc + col, v);
+      for (int e = 0; e < 4; ++e) v[e] = alpha * v[e] + beta * r[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] *= alpha;
+    }
+    tile_store4<T>(tile_rsrc(C + x.batch * c_batch, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
   }
 };
 
@@ -407,16 +467,15 @@ struct EpiDReluSq {
   long lda;
   int M, N;
   using Aux = Aux4<T>;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int row, int col) const {
-    return aux_load<T>(act + (long)row * lda + col, row < M && col < N);
+  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
+    return tile_load4<T>(tile_rsrc(act, lda, x), tile_off<T>(x, row, col, lda, M, N));
   }
-  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux& a) const {
-    if (row >= M || col >= N) return;
+  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
     float av[4];
     aux_get<T>(a, av);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= 2.f * __builtin_sqrtf(av[e]);
-    store4<T>(C + (long)row * ldc + col, v);
+    tile_store4<T>(tile_rsrc(C, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
   }
 };
 
@@ -432,14 +491,15 @@ struct EpiF32 {
   using Aux = NoAux;
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
-    if (row >= M || col >= N) return;
-    float* p = C + (long)x.z * split_stride + (long)row * ldc + col;
-    float4 o = make_float4(v[0], v[1], v[2], v[3]);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(C + (long)x.z * split_stride, ldc, x);
+    const int off = tile_off<float>(x, row, col, ldc, M, N);
     if (accumulate) {
-      const float4 q = *reinterpret_cast<const float4*>(p);
-      o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+      float q[4];
+      aux_get<float>(tile_load4<float>(rs, off), q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += q[e];
     }
-    *reinterpret_cast<float4*>(p) = o;
+    tile_store4<float>(rs, off, v);
   }
 };
 

@@ -36,6 +36,25 @@ size_t gemm_dw_partial_elems(int M, int N, int K) {
   return s > 1 ? (size_t)s * N * K : 0;
 }
 
+// Builds the store epilogue for y (ld N) with or without the residual and
+// hands it to launch.
+template <typename T, bool Relu, bool Track, typename Launch>
+nc_status with_store_epi(T* y, const T* res, int M, int N, const float* sa, const float* sb, uint32_t* amax,
+                         Launch&& launch) {
+  if (res) {
+    EpiStore<T, Relu, Track, true> e{y, N, res, N, M, N};
+    e.sa = sa;
+    e.sb = sb;
+    e.amax = amax;
+    return launch(e);
+  }
+  EpiStore<T, Relu, Track, false> e{y, N, nullptr, 0, M, N};
+  e.sa = sa;
+  e.sb = sb;
+  e.amax = amax;
+  return launch(e);
+}
+
 template <typename T>
 nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_out,
                    hipStream_t st) {
@@ -43,12 +62,9 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
   const double es = sizeof(T);
   ProfScope prof(relu_sq_out ? NC_NAME(T, "gemm_fwd_relusq") : NC_NAME(T, "gemm_fwd"), 2.0 * M * N * K,
                  es * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
-  if (relu_sq_out) {
-    EpiStore<T, true> e{y, N, res, N, M, N};
-    return launch_gemm<T, kKc, kKc>(s, e, st);
-  }
-  EpiStore<T> e{y, N, res, N, M, N};
-  return launch_gemm<T, kKc, kKc>(s, e, st);
+  auto launch = [&](const auto& e) { return launch_gemm<T, kKc, kKc>(s, e, st); };
+  if (relu_sq_out) return with_store_epi<T, true, false>(y, res, M, N, nullptr, nullptr, nullptr, launch);
+  return with_store_epi<T, false, false>(y, res, M, N, nullptr, nullptr, nullptr, launch);
 }
 
 template <typename T>
@@ -61,7 +77,11 @@ nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int 
   const double es = sizeof(T);
   ProfScope prof(NC_NAME(T, "gemm_ns"), 2.0 * M * N * K * batch,
                  es * batch * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
-  EpiAxpby<T> e{y, N, res, N, M, N, alpha, beta, y_batch, y_batch};
+  if (!res) {
+    EpiAxpby<T, false> e{y, N, nullptr, N, M, N, alpha, 0.f, y_batch, 0};
+    return launch_gemm<T, kKc, kKc>(s, e, st);
+  }
+  EpiAxpby<T, true> e{y, N, res, N, M, N, alpha, beta, y_batch, y_batch};
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
@@ -74,24 +94,17 @@ nc_status gemm_fp8(const uint8_t* xq, const uint8_t* wq, const float* sx, const 
   ProfScope prof(relu_sq_out ? "gemm_fwd_relusq_fp8" : "gemm_fwd_fp8", 2.0 * M * N * K,
                  (double)M * K + (double)N * K + 2.0 * M * N * (res ? 2 : 1), st);
   // the ReLU^2 output is the next product's FP8 operand: its maximum is taken here
-  if (relu_sq_out && amax_out) {
-    EpiStore<bf16, true, true> e{y, N, res, N, M, N};
+  auto launch = [&](const auto& e) { return launch_gemm_f8(s, e, st); };
+  if (amax_out) {
+    if (!relu_sq_out || res) return NC_ERR_UNSUPPORTED;
+    EpiStore<bf16, true, true> e{y, N, nullptr, 0, M, N};
     e.sa = sx;
     e.sb = sw;
     e.amax = amax_out;
-    return launch_gemm_f8(s, e, st);
+    return launch(e);
   }
-  if (amax_out) return NC_ERR_UNSUPPORTED;
-  if (relu_sq_out) {
-    EpiStore<bf16, true> e{y, N, res, N, M, N};
-    e.sa = sx;
-    e.sb = sw;
-    return launch_gemm_f8(s, e, st);
-  }
-  EpiStore<bf16> e{y, N, res, N, M, N};
-  e.sa = sx;
-  e.sb = sw;
-  return launch_gemm_f8(s, e, st);
+  if (relu_sq_out) return with_store_epi<bf16, true, false>(y, res, M, N, sx, sw, nullptr, launch);
+  return with_store_epi<bf16, false, false>(y, res, M, N, sx, sw, nullptr, launch);
 }
 
 template <typename T>
@@ -103,7 +116,7 @@ nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch, l
   s.b_batch = x_batch;
   const double es = sizeof(T);
   ProfScope prof(NC_NAME(T, "gemm_gram"), 2.0 * R * C * C * batch, es * batch * ((double)R * C + (double)C * C), st);
-  EpiAxpby<T> e{a, C, nullptr, C, C, C, 1.f, 0.f, a_batch, 0};
+  EpiAxpby<T, false> e{a, C, nullptr, C, C, C, 1.f, 0.f, a_batch, 0};
   return launch_gemm<T, kKo, kKo>(s, e, st);
 }
 
