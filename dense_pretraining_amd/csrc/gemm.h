@@ -256,6 +256,10 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
   const int lane = x.lane, lr = lane & 31, h = lane >> 5;
   const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
   float tmax = 0.f;
+  // every row's state first: whatever it loads is in flight before the first store
+  typename Epi::RowState rs[WTM];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) epi.row_begin(rs[i], r0 + 32 * i + lr);
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
     // the slab's other inputs (residual, activation) are fetched first, in
@@ -266,18 +270,16 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
 #pragma unroll
       for (int k = 0; k < NCH / 16; ++k)
         aux[it][k] = epi.load_aux(x, r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k));
-    typename Epi::RowState rs;
-    epi.row_begin(rs, r0 + 32 * i + lr);
 #pragma unroll
     for (int j = 0; j < WTN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float v[4] = {c[i][j][4 * g], c[i][j][4 * g + 1], c[i][j][4 * g + 2], c[i][j][4 * g + 3]};
         const int cc = 8 * j + 2 * g + h;
-        epi.pre(rs, r0 + 32 * i + lr, c0 + 4 * cc, v);
+        epi.pre(rs[i], r0 + 32 * i + lr, c0 + 4 * cc, v);
         *reinterpret_cast<float4*>(slab + 4 * (lr * NCH + (cc ^ (lr & 15)))) = make_float4(v[0], v[1], v[2], v[3]);
       }
-    epi.row_end(rs, x, i);
+    epi.row_end(rs[i], x, i);
     // a batch of the slab's reads first, then its stores: the reads overlap
     // and are waited for together, instead of one read, one wait, one store
     // at a time (half batches where the epilogue's own registers are many)
@@ -525,8 +527,11 @@ struct EpiSoftcap {
   };
   __device__ __forceinline__ void row_begin(RowState& rs, int row) const {
     rs.sum = 0.f;
-    rs.tgt = row < M ? targets[row] : -1;
+    const int t = targets[row < M ? row : M - 1];
+    rs.tgt = row < M ? t : -1;
   }
+  // branch-free: out-of-range columns add nothing, and the target's logit is
+  // stored through an offset past the record unless this run of 4 holds it
   __device__ __forceinline__ void pre(RowState& rs, int row, int col, float* v) const {
     const float k2 = 2.8853900817779268f / cap;  // 2 log2(e) / c
     const float lg = 1.4426950408889634f;
@@ -535,12 +540,17 @@ struct EpiSoftcap {
       const float t = __builtin_amdgcn_exp2f(v[e] * k2);
       v[e] = cap - 2.f * cap * __builtin_amdgcn_rcpf(t + 1.f);
     }
-    if (row < M && col < N) {
+    const bool in = row < M && col < N;
+    float s4 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rs.sum += __builtin_amdgcn_exp2f(v[e] * lg);
-      const unsigned d = (unsigned)(rs.tgt - col);
-      if (d < 4u) zt[row] = d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
-    }
+    for (int e = 0; e < 4; ++e) s4 += __builtin_amdgcn_exp2f(v[e] * lg);
+    rs.sum += in ? s4 : 0.f;
+    const unsigned d = (unsigned)(rs.tgt - col);
+    // |z'| <= c: the 0/1 weights pick one value exactly, with no branch
+    const float vt = v[0] * (float)(d == 0u) + v[1] * (float)(d == 1u) + v[2] * (float)(d == 2u) +
+                     v[3] * (float)(d == 3u);
+    const int off = in && d < 4u ? row * (int)sizeof(float) : (int)kDmaOOB;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, vt), dma_rsrc(zt), off, 0, 0);
   }
   __device__ __forceinline__ void row_end(RowState& rs, const EpiCtx& x, int i) const {
     // the other half of this row's columns sits in lane ^ 32
@@ -549,8 +559,15 @@ struct EpiSoftcap {
   }
   using Aux = NoAux;
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
-  __device__ __forceinline__ void post(const EpiCtx&, int row, int col, float* v, const Aux&) const {
-    if (row < M && col < N) store4<T>(Z + (long)(col / kPanel) * zpanel + (long)row * kPanel + col % kPanel, v);
+  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
+    // the tile's panels from its origin: panel (col - n0) / kPanel, row (row - m0)
+    const __amdgpu_buffer_rsrc_t rs = dma_rsrc(Z + (long)(x.n0 / kPanel) * zpanel + (long)x.m0 * kPanel);
+    const int dc = col - x.n0;
+    const int off = row < M && col < N
+                        ? (int)((((long)(dc / kPanel) * zpanel + (long)(row - x.m0) * kPanel + dc % kPanel)) *
+                                (long)sizeof(T))
+                        : (int)kDmaOOB;
+    tile_store4<T>(rs, off, v);
   }
   __device__ __forceinline__ void finish(const EpiCtx& x) const {
     __syncthreads();

@@ -36,6 +36,13 @@ size_t gemm_dw_partial_elems(int M, int N, int K) {
   return s > 1 ? (size_t)s * N * K : 0;
 }
 
+// The epilogues address a 256 x 256 tile through 32-bit byte offsets from its
+// origin (the unembedding: its 8 column panels of M rows each), which must
+// stay inside one buffer record.
+bool tile_span_ok(long row_stride_elems, size_t es) {
+  return row_stride_elems >= 0 && 256L * row_stride_elems * (long)es < (long)kDmaRecords;
+}
+
 // Builds the store epilogue for y (ld N) with or without the residual and
 // hands it to launch.
 template <typename T, bool Relu, bool Track, typename Launch>
@@ -58,6 +65,7 @@ nc_status with_store_epi(T* y, const T* res, int M, int N, const float* sa, cons
 template <typename T>
 nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int K, bool relu_sq_out,
                    hipStream_t st) {
+  if (!tile_span_ok(N, sizeof(T))) return NC_ERR_UNSUPPORTED;
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   const double es = sizeof(T);
   ProfScope prof(relu_sq_out ? NC_NAME(T, "gemm_fwd_relusq") : NC_NAME(T, "gemm_fwd"), 2.0 * M * N * K,
@@ -70,6 +78,7 @@ nc_status gemm_xwt(const T* x, const T* w, T* y, const T* res, int M, int N, int
 template <typename T>
 nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int N, int K, float alpha, float beta,
                          hipStream_t st, int batch, long x_batch, long w_batch, long y_batch) {
+  if (!tile_span_ok(N, sizeof(T))) return NC_ERR_UNSUPPORTED;
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   s.batch = batch;
   s.a_batch = x_batch;
@@ -87,7 +96,7 @@ nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int 
 
 nc_status gemm_fp8(const uint8_t* xq, const uint8_t* wq, const float* sx, const float* sw, bf16* y, const bf16* res,
                    int M, int N, int K, bool relu_sq_out, uint32_t* amax_out, hipStream_t st) {
-  if (K % 16 != 0 || !sx || !sw) return NC_ERR_UNSUPPORTED;
+  if (K % 16 != 0 || !sx || !sw || !tile_span_ok(N, sizeof(bf16))) return NC_ERR_UNSUPPORTED;
   // the FP8 matrices seen as rows of K / 2 sixteen-bit pairs
   const int K2 = K / 2;
   GemmShape s{xq, wq, K2, K2, M, N, K2, K2, 1};
@@ -109,6 +118,7 @@ nc_status gemm_fp8(const uint8_t* xq, const uint8_t* wq, const float* sx, const 
 
 template <typename T>
 nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch, long x_batch, long a_batch) {
+  if (!tile_span_ok(C, sizeof(T))) return NC_ERR_UNSUPPORTED;
   // a[C,C] = x^T x for x [R,C]: both operands K-outer, the reduction over the R rows.
   GemmShape s{x, x, C, C, C, C, R, R, 1};
   s.batch = batch;
@@ -123,6 +133,7 @@ nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch, l
 template <typename T>
 nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
                    long dy_panel) {
+  if (!tile_span_ok(K, sizeof(T))) return NC_ERR_UNSUPPORTED;
   // C[M,K] = A[M,N] * B where B(n=k_out, k=n_in) = W[n_in][k_out]: K-outer.
   GemmShape s{dy, w, N, K, M, K, N, N, 1};
   s.a_panel = dy_panel;
@@ -140,6 +151,7 @@ nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, i
 template <typename T>
 nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int accumulate, float* partial,
                   size_t partial_elems, hipStream_t st, long dy_panel) {
+  if (!tile_span_ok(K, sizeof(float))) return NC_ERR_UNSUPPORTED;
   int nsplit, kper;
   dw_split(M, N, K, GemmTile<T>::BK, GemmTile<T>::BM, nsplit, kper);
   // C[N,K] = sum_m dy[m][n] x[m][k]: both operands K-outer (token axis is the reduction).
@@ -183,6 +195,7 @@ int lmhead_tiles(int N, bool bf16_storage) {
 template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
                       float* part, float* zt, hipStream_t st) {
+  if (!tile_span_ok(M, sizeof(T)) || (long)M * (long)sizeof(float) >= (long)kDmaRecords) return NC_ERR_UNSUPPORTED;
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
                  sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
