@@ -842,16 +842,20 @@ struct DmaTile {
   }
 
 // Schedule the code since the last scheduling barrier as one fragment read
-// (and, after a ring barrier, one of the 8 tile loads) after each multiply
-// (16 multiplies, at most 16 reads), then fence it off: a wave never stops
-// issuing multiplies to push a burst of loads through the address unit.
+// after each multiply (16 multiplies, at most 16 reads) and, after a ring
+// barrier, one of the 8 tile loads after every other multiply, then fence it
+// off: a wave never stops issuing multiplies to push a burst of loads through
+// the address unit.
 template <bool WithLoads>
 __device__ __forceinline__ void interleave_reads_with_mfma() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    if (WithLoads && i < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one tile load
+    // the 8 tile loads go after every other multiply: in a burst they overrun
+    // the CU's texture-address queue, and a wave stalled on a load issues no
+    // multiply (the queue is full for about a fifth of the cycles even so)
+    if (WithLoads && (i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one tile load
   }
   __builtin_amdgcn_sched_barrier(0);
 }
