@@ -816,36 +816,10 @@ struct DmaTile {
   }
 };
 
-// One step of the ring, for tile t in stage S (its first half already in
-// registers, f0): read the second half (f1) while multiplying f0; wait until
-// tile t+1 has landed and every wave is done with stage S; refill S with
-// tile t+4; read the first half of tile t+1 (next stage N) while multiplying
-// f1. No multiply waits for a fragment read issued just before it, and with
-// one wavefront per SIMD that is what keeps the matrix core busy. Each stage
-// is its own LDS array so that the compiler can tell the DMA writes from the
-// reads. Loads past the end of K read zeros, so every step is the same and
-// the main loop (four steps per trip, fixed stage names) has no branch.
-// The scheduler is told to put one read after each multiply: the reads of a
-// half stay ahead of the multiplies that need them (it would otherwise pull
-// those forward), and no more than a few reads are ever waited on at once.
-#define NC_DMA_STEP(t, SA, SB, NA, NB)                      \
-  {                                                         \
-    Tile::load(f1, SA, SB, 16, wm, wn, lane);               \
-    Tile::mma(acc, f0);                                     \
-    interleave_reads_with_mfma<false>();                    \
-    ring_barrier<24>();                                     \
-    opa.issue(SA, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
-    opb.issue(SB, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
-    Tile::load(f0, NA, NB, 0, wm, wn, lane);                \
-    Tile::mma(acc, f1);                                     \
-    interleave_reads_with_mfma<true>();                     \
-  }
-
-// Schedule the code since the last scheduling barrier as one fragment read
-// after each multiply (16 multiplies, at most 16 reads) and, after a ring
-// barrier, one of the 8 tile loads after every other multiply, then fence it
-// off: a wave never stops issuing multiplies to push a burst of loads through
-// the address unit.
+// The FP8 step's schedule: one fragment read after each multiply (16
+// multiplies, at most 16 reads) and one of the 8 tile loads after every other
+// multiply, then a fence: a wave never stops issuing multiplies to push a
+// burst of loads through the address unit.
 template <bool WithLoads>
 __device__ __forceinline__ void interleave_reads_with_mfma() {
 #pragma unroll
@@ -860,6 +834,33 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The scheduler is told to put one fragment read after every other multiply
+// and one tile load after every fourth: the reads of a set stay ahead of the
+// multiplies that need them (it would otherwise pull those forward), and a
+// burst of loads would overrun the CU's texture-address queue, stalling the
+// wave's multiplies behind it.
+template <bool WithLoads>
+__device__ __forceinline__ void interleave_full() {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if ((i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    if (WithLoads && (i & 3) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one tile load
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+#define NC_DMA_STEP_FULL(t, SA, SB, NA, NB, CUR, NXT)       \
+  {                                                         \
+    ring_barrier<24>();                                     \
+    opa.issue(SA, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
+    opb.issue(SB, kbeg + ((t) + 5) * kDmaBK, kend, wave);   \
+    Tile::load(NXT.h0, NA, NB, 0, wm, wn, lane);            \
+    Tile::load(NXT.h1, NA, NB, 16, wm, wn, lane);           \
+    Tile::mma(acc, CUR.h0);                                 \
+    Tile::mma(acc, CUR.h1);                                 \
+    interleave_full<true>();                                \
+  }
+
 // The whole ring in one inlined function whose stage arrays are __restrict__
 // parameters: every LDS access inside then carries alias-scope information,
 // which lets the compiler see that the reads of one stage do not depend on
@@ -867,15 +868,25 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
 // Five 32 KB stages fill the 160 KB of LDS: tiles t+1 .. t+4 are in flight
 // while tile t is multiplied (about 2 us of lookahead at the clock the
 // matrix cores sustain), enough to ride out the operand fetches that miss L2.
+// Each step waits for tile t+1 and for every wave to be done with tile t's
+// stage (its fragments are all in registers by then), refills that stage with
+// tile t+5, and reads all of tile t+1 into the second fragment set while
+// multiplying tile t: no multiply waits for a read issued just before it, and
+// with one wavefront per SIMD that is what keeps the matrix core busy. The two
+// sets trade places every step, so the main loop runs ten steps a trip (five
+// stages, two sets) with fixed stage names and no branch, and nothing is
+// copied. Loads past the end of K read zeros, so every step is the same.
 template <typename Tile>
 __device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA& opa, typename Tile::OpB& opb,
-                                         bf16* __restrict__ sa0, bf16* __restrict__ sa1, bf16* __restrict__ sa2,
-                                         bf16* __restrict__ sa3, bf16* __restrict__ sa4, bf16* __restrict__ sb0,
-                                         bf16* __restrict__ sb1, bf16* __restrict__ sb2, bf16* __restrict__ sb3,
-                                         bf16* __restrict__ sb4, int nk, int kbeg, int kend, int wave, int wm, int wn,
-                                         int lane) {
+                                              bf16* __restrict__ sa0, bf16* __restrict__ sa1, bf16* __restrict__ sa2,
+                                              bf16* __restrict__ sa3, bf16* __restrict__ sa4, bf16* __restrict__ sb0,
+                                              bf16* __restrict__ sb1, bf16* __restrict__ sb2, bf16* __restrict__ sb3,
+                                              bf16* __restrict__ sb4, int nk, int kbeg, int kend, int wave, int wm,
+                                              int wn, int lane) {
   constexpr int BK = kDmaBK;
-  typename Tile::Frags f0, f1;
+  struct Full {
+    typename Tile::Frags h0, h1;
+  } F, G;
   opa.issue(sa0, kbeg, kend, wave);
   opb.issue(sb0, kbeg, kend, wave);
   opa.issue(sa1, kbeg + BK, kend, wave);
@@ -887,30 +898,40 @@ __device__ __forceinline__ void dma_ring(TileAcc<bf16>& acc, typename Tile::OpA&
   opa.issue(sa4, kbeg + 4 * BK, kend, wave);
   opb.issue(sb4, kbeg + 4 * BK, kend, wave);
   ring_barrier<32>();  // tile 0 has landed
-  Tile::load(f0, sa0, sb0, 0, wm, wn, lane);
+  Tile::load(F.h0, sa0, sb0, 0, wm, wn, lane);
+  Tile::load(F.h1, sa0, sb0, 16, wm, wn, lane);
   int kt = 0;
-  for (; kt + 5 <= nk; kt += 5) {
-    NC_DMA_STEP(kt, sa0, sb0, sa1, sb1);
-    NC_DMA_STEP(kt + 1, sa1, sb1, sa2, sb2);
-    NC_DMA_STEP(kt + 2, sa2, sb2, sa3, sb3);
-    NC_DMA_STEP(kt + 3, sa3, sb3, sa4, sb4);
-    NC_DMA_STEP(kt + 4, sa4, sb4, sa0, sb0);
+  for (; kt + 10 <= nk; kt += 10) {
+    NC_DMA_STEP_FULL(kt, sa0, sb0, sa1, sb1, F, G);
+    NC_DMA_STEP_FULL(kt + 1, sa1, sb1, sa2, sb2, G, F);
+    NC_DMA_STEP_FULL(kt + 2, sa2, sb2, sa3, sb3, F, G);
+    NC_DMA_STEP_FULL(kt + 3, sa3, sb3, sa4, sb4, G, F);
+    NC_DMA_STEP_FULL(kt + 4, sa4, sb4, sa0, sb0, F, G);
+    NC_DMA_STEP_FULL(kt + 5, sa0, sb0, sa1, sb1, G, F);
+    NC_DMA_STEP_FULL(kt + 6, sa1, sb1, sa2, sb2, F, G);
+    NC_DMA_STEP_FULL(kt + 7, sa2, sb2, sa3, sb3, G, F);
+    NC_DMA_STEP_FULL(kt + 8, sa3, sb3, sa4, sb4, F, G);
+    NC_DMA_STEP_FULL(kt + 9, sa4, sb4, sa0, sb0, G, F);
   }
-  // kt is a multiple of 5, so tile kt sits in stage 0
-  if (kt < nk) NC_DMA_STEP(kt, sa0, sb0, sa1, sb1);
-  if (kt + 1 < nk) NC_DMA_STEP(kt + 1, sa1, sb1, sa2, sb2);
-  if (kt + 2 < nk) NC_DMA_STEP(kt + 2, sa2, sb2, sa3, sb3);
-  if (kt + 3 < nk) NC_DMA_STEP(kt + 3, sa3, sb3, sa4, sb4);
-  // the refills past the end are still landing in the stages the epilogue reuses
+  // kt is a multiple of 10: tile kt sits in stage 0 with its fragments in F
+  if (kt < nk) NC_DMA_STEP_FULL(kt, sa0, sb0, sa1, sb1, F, G);
+  if (kt + 1 < nk) NC_DMA_STEP_FULL(kt + 1, sa1, sb1, sa2, sb2, G, F);
+  if (kt + 2 < nk) NC_DMA_STEP_FULL(kt + 2, sa2, sb2, sa3, sb3, F, G);
+  if (kt + 3 < nk) NC_DMA_STEP_FULL(kt + 3, sa3, sb3, sa4, sb4, G, F);
+  if (kt + 4 < nk) NC_DMA_STEP_FULL(kt + 4, sa4, sb4, sa0, sb0, F, G);
+  if (kt + 5 < nk) NC_DMA_STEP_FULL(kt + 5, sa0, sb0, sa1, sb1, G, F);
+  if (kt + 6 < nk) NC_DMA_STEP_FULL(kt + 6, sa1, sb1, sa2, sb2, F, G);
+  if (kt + 7 < nk) NC_DMA_STEP_FULL(kt + 7, sa2, sb2, sa3, sb3, G, F);
+  if (kt + 8 < nk) NC_DMA_STEP_FULL(kt + 8, sa3, sb3, sa4, sb4, F, G);
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));
 }
+#undef NC_DMA_STEP_FULL
 
-// The FP8 step: wait for tile t+1 and refill stage S (tile t's fragments,
-// both halves, are already in CUR); read tile t+1 into NXT while multiplying
-// tile t. The same one read and at most one load per multiply as the bf16
-// step, with half as many (twice as long) multiplies. The two fragment sets
-// trade places every step, so the main loop runs ten steps a trip (five
-// stages, two sets) and nothing is copied.
+// The FP8 step has the bf16 step's shape: wait for tile t+1 and refill
+// stage S (tile t's fragments, both halves, are already in CUR); read tile
+// t+1 into NXT while multiplying tile t. Its 16 multiplies are each as long
+// as two bf16 ones, so it places one fragment read after each multiply and
+// one tile load after every other (interleave_reads_with_mfma).
 #define NC_DMA_STEP_F8(t, SA, SB, NA, NB, CUR, NXT)         \
   {                                                         \
     ring_barrier<24>();                                     \
@@ -1016,7 +1037,6 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   staged_epilogue<4, 4>(acc.c, epi, x, reinterpret_cast<float*>(slab));
   epi.finish(x);
 }
-#undef NC_DMA_STEP
 
 
 // ---------------------------------------------------------------- launcher
