@@ -233,3 +233,33 @@ def test_single_token_sequences():
         scale = np.max(np.abs(b["wv"]))
         assert np.max(np.abs(a["wq"])) <= 1e-5 * scale
         assert np.max(np.abs(a["wk"])) <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "bf16_fp8"])
+def test_block_writes_stay_inside_outputs(dt):
+    """The ragged block (M = 300 rows, d = 192: both edges of the 256 x 256
+    tiles cut) writes x_out and dx_in only inside their [M, d] views: the
+    epilogues' out-of-range lanes store through offsets the hardware drops, so
+    a padding of sentinel rows after each view must come back untouched."""
+    cfg = _cfg("ragged", dt).with_(depth=1)
+    p = params(cfg.with_(dtype="f32" if dt == "f32" else "bf16"), fan_in=True)
+    w = p["layers"][0]
+    M, d, pad = cfg.tokens, cfg.d_model, 64
+    x_np, dy_np = synth.block_inputs(cfg.batch, cfg.seq_len, d, dtype="f32" if dt == "f32" else "bf16")
+    sz = lib.query_sizes(cfg)
+    saved = lib.alloc_bytes(sz.block_saved)
+    scratch = lib.new_scratch(cfg)
+    wd = {k: dev(v, cfg) for k, v in pack_block(w).items()}
+    x = dev(x_np.reshape(M, d), cfg)
+    sentinel = -12345.0
+    out_buf = torch.full((M + pad, d), sentinel, dtype=x.dtype, device="cuda")
+    dx_buf = torch.full((M + pad, d), sentinel, dtype=x.dtype, device="cuda")
+    lib.block_fwd(cfg, wd, x, out_buf[:M], saved, scratch)
+    dy = dev(dy_np.reshape(M, d), cfg)
+    gd = {k: torch.empty(v.shape, dtype=torch.float32, device="cuda") for k, v in wd.items()}
+    lib.block_bwd(cfg, wd, x, saved, dy, dx_buf[:M], gd, scratch)
+    torch.cuda.synchronize()
+    assert lib.read_status(scratch) == 0
+    for name, buf in (("x_out", out_buf), ("dx_in", dx_buf)):
+        assert bool(torch.all(buf[M:] == sentinel)), f"{name}: rows past the output were written"
+        assert bool(torch.all(torch.isfinite(buf[:M]))) and not bool(torch.any(buf[:M] == sentinel)), name
