@@ -32,7 +32,11 @@ namespace {
 
 constexpr int kSkBN = 32;       // output columns per block
 constexpr int kSkKC = 64;       // k per wave step (four 16-wide MFMA steps)
-constexpr int kSkTarget = 256;  // blocks aimed for when splitting K
+// Blocks aimed for when splitting K. Half the CUs: a decode step at depth 20
+// (64 rows) ran 10 % faster than with 256 (W1 no longer splits, so it needs
+// no finishing pass; Wo and W2 take 4 splits instead of 7); 64 and 512 were
+// slower, 128 to 160 a plateau.
+constexpr int kSkTarget = 128;
 constexpr int kSkFin = 8;       // partials loaded at once by the finishing kernel
 
 struct SkinnyArgs {
