@@ -362,8 +362,9 @@ def main():
     a = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU data-parallel path is not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}): the library's "
+              "data-parallel step on several GPUs (one process per GPU, one gradient all-reduce) is not "
+              "implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -110,14 +110,16 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const T* __restrict__ 
   if (row >= M) return;
   const long off = (long)row * d;
   const int nv = d / VE;
-  float g[MAXV][VE], yy[MAXV][VE];
+  float g[MAXV][VE], yy[MAXV][VE], rs[MAXV][VE];
   float dot = 0.f;
+  // all three inputs in flight before the row sum (the residual was loaded after it)
 #pragma unroll
   for (int c = 0; c < MAXV; ++c) {
     int vi = lane + 64 * c;
     if (vi < nv) {
       load16<T>(dy + off + vi * VE, g[c]);
       load16<T>(y + off + vi * VE, yy[c]);
+      if (res) load16<T>(res + off + vi * VE, rs[c]);
 #pragma unroll
       for (int e = 0; e < VE; ++e) dot += g[c][e] * yy[c][e];
     }
@@ -132,10 +134,8 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const T* __restrict__ 
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[e] = rr * (g[c][e] - yy[c][e] * dot);
       if (res) {
-        float rs[VE];
-        load16<T>(res + off + vi * VE, rs);
 #pragma unroll
-        for (int e = 0; e < VE; ++e) o[e] += rs[e];
+        for (int e = 0; e < VE; ++e) o[e] += rs[c][e];
       }
       if constexpr (sizeof(TO) == sizeof(T)) {
         store16<TO>(dx + off + vi * VE, o);
@@ -327,6 +327,14 @@ __global__ void __launch_bounds__(256) xent_final_kernel(const float* __restrict
 // dz = (softmax(z') - onehot(y)) * dloss / Nv * (1 - (z'/c)^2), in place, over
 // the column-panel layout of the logits: block (x, p) covers rows
 // [x * ROWS, (x+1) * ROWS) of panel p, each thread one 16-byte piece.
+// A thread takes one 16-byte piece of a row in each of kXentPanels
+// consecutive panels: the row's target and LSE are read once, and the
+// pieces' loads are all in flight together.
+#ifndef NC_XENT_PANELS
+#define NC_XENT_PANELS 8
+#endif
+constexpr int kXentPanels = NC_XENT_PANELS;
+
 template <typename T>
 __global__ void __launch_bounds__(256) xent_dz_kernel(T* __restrict__ z, int M, int V, const float* __restrict__ lse,
                                                       const int32_t* __restrict__ tg, const int* __restrict__ nvp,
@@ -334,35 +342,52 @@ __global__ void __launch_bounds__(256) xent_dz_kernel(T* __restrict__ z, int M, 
   constexpr int VE = Vec<T>::n;
   constexpr int PER_ROW = kPanel / VE;  // pieces per panel row
   constexpr int ROWS = 256 / PER_ROW;
-  const int p = blockIdx.y;
+  const int p0 = blockIdx.y * kXentPanels;
   const int m = blockIdx.x * ROWS + threadIdx.x / PER_ROW;
-  const int v0 = p * kPanel + (threadIdx.x % PER_ROW) * VE;
-  if (m >= M || v0 >= V) return;  // V % VE == 0: a piece is wholly inside or outside
+  const int c0 = (threadIdx.x % PER_ROW) * VE;  // column inside a panel
+  if (m >= M) return;
   const int y = tg[m];
   const bool valid = y >= 0 && y < V;
   const float gsc = valid ? dloss / (float)*nvp : 0.f;
   const float l = lse[m];
-  T* q = z + (long)p * M * kPanel + (long)m * kPanel + (v0 % kPanel);
-  float v[VE];
-  load16<T>(q, v);
+  float v[kXentPanels][VE];
 #pragma unroll
-  for (int e = 0; e < VE; ++e) {
-    float pr = __expf(v[e] - l);
-    if (v0 + e == y) pr -= 1.f;
-    const float zc = v[e] * inv_cap;
-    v[e] = pr * gsc * (1.f - zc * zc);
+  for (int i = 0; i < kXentPanels; ++i) {
+    const int v0 = (p0 + i) * kPanel + c0;  // V % VE == 0: a piece is wholly inside or outside
+    if (v0 < V) load16<T>(z + (long)(p0 + i) * M * kPanel + (long)m * kPanel + c0, v[i]);
   }
-  store16<T>(q, v);
+#pragma unroll
+  for (int i = 0; i < kXentPanels; ++i) {
+    const int v0 = (p0 + i) * kPanel + c0;
+    if (v0 >= V) continue;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      float pr = __expf(v[i][e] - l);
+      if (v0 + e == y) pr -= 1.f;
+      const float zc = v[i][e] * inv_cap;
+      v[i][e] = pr * gsc * (1.f - zc * zc);
+    }
+    store16<T>(z + (long)(p0 + i) * M * kPanel + (long)m * kPanel + c0, v[i]);
+  }
 }
 
+// Sums the splits' partial tiles in split order (deterministic). All of a
+// thread's partial loads are issued before the first add (a loop over a
+// runtime count would wait for each before issuing the next).
+constexpr int kMaxSplits = 16;
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int nsplit, size_t n4,
                                                             float* __restrict__ out, int accumulate) {
   for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    float4 p[kMaxSplits];
+#pragma unroll
+    for (int zz = 0; zz < kMaxSplits; ++zz)
+      if (zz < nsplit) p[zz] = reinterpret_cast<const float4*>(part + (size_t)zz * n4 * 4)[i];
     float4 a = accumulate ? reinterpret_cast<const float4*>(out)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int zz = 0; zz < nsplit; ++zz) {
-      float4 p = reinterpret_cast<const float4*>(part + (size_t)zz * n4 * 4)[i];
-      a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
-    }
+#pragma unroll
+    for (int zz = 0; zz < kMaxSplits; ++zz)
+      if (zz < nsplit) {
+        a.x += p[zz].x; a.y += p[zz].y; a.z += p[zz].z; a.w += p[zz].w;
+      }
     reinterpret_cast<float4*>(out)[i] = a;
   }
 }
@@ -479,7 +504,8 @@ template <typename T>
 nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, const int* nv, float dloss, float cap,
                   hipStream_t st) {
   constexpr int ROWS = 256 / (kPanel / Vec<T>::n);
-  dim3 grid((M + ROWS - 1) / ROWS, (V + kPanel - 1) / kPanel);
+  const int panels = (V + kPanel - 1) / kPanel;
+  dim3 grid((M + ROWS - 1) / ROWS, (panels + kXentPanels - 1) / kXentPanels);
   ProfScope prof(NC_NAME(T, "xent_dz"), 0, 2.0 * sizeof(T) * M * V + 12.0 * M, st);
   hipLaunchKernelGGL((xent_dz_kernel<T>), grid, dim3(256), 0, st, z, M, V, lse, targets, nv, dloss, 1.f / cap);
   NC_LAUNCH_CHECK("xent_dz");
@@ -487,6 +513,7 @@ nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, 
 }
 
 nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st) {
+  if (nsplit < 1 || nsplit > kMaxSplits) return NC_ERR_UNSUPPORTED;
   size_t n4 = n / 4;
   ProfScope prof("splitk_reduce", 0, 4.0 * n * (nsplit + (accumulate ? 2 : 1)), st);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st, partial, nsplit, n4, out,
