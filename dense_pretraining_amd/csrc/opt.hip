@@ -102,13 +102,49 @@ __device__ __forceinline__ float inv_frobenius(const float* part, float* sh) {
   return 1.f / (sqrtf(sh[0] + sh[1] + sh[2] + sh[3]) + 1e-7f);
 }
 
-// X (tall layout, T) = U / |U|_F for U [R][C] (U recomputed from g and the new
-// momentum). transpose: X[c][r] = U[r][c]. One 32 x 32 tile per block.
-// Matrix blockIdx.z of a batch: g, mom at + z ls, its X at + z xs.
+// X = U / |U|_F, U [R][C] recomputed from g and the new momentum, when X keeps
+// U's layout (a tall or square matrix): groups of 4 elements, two per thread
+// and trip, 256 groups apart (each load instruction of a wave stays contiguous).
+// Matrix blockIdx.y of a batch: g, mom at + y ls, its X at + y xs.
 template <typename T>
-__global__ void __launch_bounds__(256) muon_norm_kernel(const float* __restrict__ g, const float* __restrict__ mom,
-                                                        long ls, int R, int C, int transpose, float mu, int nesterov,
-                                                        const float* __restrict__ part, T* __restrict__ X, long xs) {
+__global__ void __launch_bounds__(256) muon_norm_flat_kernel(const float* __restrict__ g,
+                                                             const float* __restrict__ mom, long ls, long n4, float mu,
+                                                             int nesterov, const float* __restrict__ part,
+                                                             T* __restrict__ X, long xs) {
+  __shared__ float sh[4];
+  g += blockIdx.y * ls;
+  mom += blockIdx.y * ls;
+  X += blockIdx.y * xs;
+  const float inv = inv_frobenius(part + blockIdx.y * kNormParts, sh);
+  for (long i0 = (long)blockIdx.x * 512 + threadIdx.x; i0 < n4; i0 += (long)gridDim.x * 512) {
+    float4 gs[2], ms[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long i = i0 + 256 * u < n4 ? i0 + 256 * u : i0;
+      gs[u] = reinterpret_cast<const float4*>(g)[i];
+      ms[u] = reinterpret_cast<const float4*>(mom)[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long i = i0 + 256 * u;
+      if (i >= n4) break;
+      const float gv[4] = {gs[u].x, gs[u].y, gs[u].z, gs[u].w}, mv[4] = {ms[u].x, ms[u].y, ms[u].z, ms[u].w};
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (nesterov ? gv[e] + mu * mv[e] : mv[e]) * inv;
+      store4<T>(X + 4 * i, v);
+    }
+  }
+}
+
+// The same for a wide matrix, whose X is the transpose: X[c][r] = U[r][c] / |U|_F,
+// through a 32 x 32 LDS tile, 4 elements per access (R % 4 == C % 4 == 0).
+// Matrix blockIdx.z of a batch.
+template <typename T>
+__global__ void __launch_bounds__(256) muon_norm_tr_kernel(const float* __restrict__ g, const float* __restrict__ mom,
+                                                           long ls, int R, int C, float mu, int nesterov,
+                                                           const float* __restrict__ part, T* __restrict__ X,
+                                                           long xs) {
   __shared__ float sh[4];
   __shared__ float tile[kTile][kTile + 1];
   g += blockIdx.z * ls;
@@ -116,56 +152,91 @@ __global__ void __launch_bounds__(256) muon_norm_kernel(const float* __restrict_
   X += blockIdx.z * xs;
   const float inv = inv_frobenius(part + blockIdx.z * kNormParts, sh);
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int j = ty; j < kTile; j += 8) {
-    const int r = r0 + j, c = c0 + tx;
-    float u = 0.f;
+  const int ty = threadIdx.x >> 3, tx = threadIdx.x & 7;  // 32 rows x 8 groups of 4 columns
+  {
+    const int r = r0 + ty, c = c0 + 4 * tx;
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
     if (r < R && c < C) {
       const long i = (long)r * C + c;
-      u = nesterov ? g[i] + mu * mom[i] : mom[i];
+      const float4 gg = *reinterpret_cast<const float4*>(g + i), mm = *reinterpret_cast<const float4*>(mom + i);
+      const float gv[4] = {gg.x, gg.y, gg.z, gg.w}, mv[4] = {mm.x, mm.y, mm.z, mm.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = nesterov ? gv[e] + mu * mv[e] : mv[e];
     }
-    if (!transpose) {
-      if (r < R && c < C) X[(long)r * C + c] = from_f32<T>(u * inv);
-    } else {
-      tile[j][tx] = u * inv;
-    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[ty][4 * tx + e] = u[e] * inv;
   }
-  if (!transpose) return;
   __syncthreads();
-  for (int j = ty; j < kTile; j += 8) {  // X [C][R]: row c0 + j, column r0 + tx
-    const int c = c0 + j, r = r0 + tx;
-    if (r < R && c < C) X[(long)c * R + r] = from_f32<T>(tile[tx][j]);
+  {  // X [C][R]: row c0 + ty, columns r0 + 4 tx .. + 3
+    const int c = c0 + ty, r = r0 + 4 * tx;
+    if (r < R && c < C) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[4 * tx + e][ty];
+      store4<T>(X + (long)c * R + r, v);
+    }
   }
 }
 
-// w[r][c] <- w[r][c] decay - step X (X in the tall layout, read transposed
-// when the matrix is wide); p = w in the storage type.
+// w <- w decay - step X, p = w in the storage type, when X keeps w's layout:
+// groups of 4, two per thread and trip, 256 groups apart.
 template <typename T>
-__global__ void __launch_bounds__(256) muon_apply_kernel(float* __restrict__ w, T* __restrict__ p, long ls,
-                                                         const T* __restrict__ X, long xs, int R, int C, int transpose,
-                                                         float decay, float step) {
+__global__ void __launch_bounds__(256) muon_apply_flat_kernel(float* __restrict__ w, T* __restrict__ p, long ls,
+                                                              const T* __restrict__ X, long xs, long n4, float decay,
+                                                              float step) {
+  w += blockIdx.y * ls;
+  p += blockIdx.y * ls;
+  X += blockIdx.y * xs;
+  for (long i0 = (long)blockIdx.x * 512 + threadIdx.x; i0 < n4; i0 += (long)gridDim.x * 512) {
+    float4 ws[2];
+    float x[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long i = i0 + 256 * u < n4 ? i0 + 256 * u : i0;
+      ws[u] = reinterpret_cast<const float4*>(w)[i];
+      load4<T>(X + 4 * i, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long i = i0 + 256 * u;
+      if (i >= n4) break;
+      float nw[4] = {ws[u].x, ws[u].y, ws[u].z, ws[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nw[e] = nw[e] * decay - step * x[u][e];
+      reinterpret_cast<float4*>(w)[i] = make_float4(nw[0], nw[1], nw[2], nw[3]);
+      store4<T>(p + 4 * i, nw);
+    }
+  }
+}
+
+// The same for a wide matrix: X [C][R] read transposed through a 32 x 32 tile.
+template <typename T>
+__global__ void __launch_bounds__(256) muon_apply_tr_kernel(float* __restrict__ w, T* __restrict__ p, long ls,
+                                                            const T* __restrict__ X, long xs, int R, int C,
+                                                            float decay, float step) {
   __shared__ float tile[kTile][kTile + 1];
   w += blockIdx.z * ls;
   p += blockIdx.z * ls;
   X += blockIdx.z * xs;
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  if (transpose) {
-    for (int j = ty; j < kTile; j += 8) {  // X [C][R]: row c0 + j, column r0 + tx
-      const int c = c0 + j, r = r0 + tx;
-      tile[j][tx] = (r < R && c < C) ? to_f32(X[(long)c * R + r]) : 0.f;
-    }
-    __syncthreads();
+  const int ty = threadIdx.x >> 3, tx = threadIdx.x & 7;
+  {  // X row c0 + ty, columns r0 + 4 tx .. + 3
+    const int c = c0 + ty, r = r0 + 4 * tx;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < R && c < C) load4<T>(X + (long)c * R + r, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[4 * tx + e][ty] = v[e];
   }
-  for (int j = ty; j < kTile; j += 8) {
-    const int r = r0 + j, c = c0 + tx;
-    if (r >= R || c >= C) continue;
-    const long i = (long)r * C + c;
-    const float x = transpose ? tile[tx][j] : to_f32(X[i]);
-    const float nw = w[i] * decay - step * x;
-    w[i] = nw;
-    p[i] = from_f32<T>(nw);
-  }
+  __syncthreads();
+  const int r = r0 + ty, c = c0 + 4 * tx;
+  if (r >= R || c >= C) return;
+  const long i = (long)r * C + c;
+  const float4 ww = *reinterpret_cast<const float4*>(w + i);
+  float nw[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) nw[e] = nw[e] * decay - step * tile[ty][4 * tx + e];
+  *reinterpret_cast<float4*>(w + i) = make_float4(nw[0], nw[1], nw[2], nw[3]);
+  store4<T>(p + i, nw);
 }
 
 unsigned grid_of(long n, long per_block, unsigned cap) {
@@ -206,7 +277,11 @@ size_t muon_work_bytes(int R, int C, int L, bool bf16_storage) {
 template <typename T>
 nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, int L, long ls, float lr, float mu,
                     int nesterov, float wd, void* work, size_t work_bytes, hipStream_t st) {
-  if (((long)R * C) % 4 != 0 || R % 4 != 0 || C % 4 != 0 || L < 1 || L > 65535) return NC_ERR_UNSUPPORTED;
+  // 16-byte accesses: R % 4 == C % 4 == 0, and every matrix of the batch starts 32-byte aligned
+  auto al = [](const void* v) { return reinterpret_cast<uintptr_t>(v) % 32 == 0; };
+  if (R % 4 != 0 || C % 4 != 0 || L < 1 || L > 65535 || ls % 8 != 0 || !al(g) || !al(mom) || !al(w) ||
+      reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return NC_ERR_UNSUPPORTED;
   if (work_bytes < muon_work_bytes(R, C, L, is_bf16<T>())) return NC_ERR_WORKSPACE;
   const bool transpose = R < C;
   const int Rt = transpose ? C : R, Ct = transpose ? R : C;  // the tall form
@@ -229,10 +304,15 @@ nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, in
     NC_LAUNCH_CHECK("muon_momentum");
   }
   const dim3 tiles((C + kTile - 1) / kTile, (R + kTile - 1) / kTile, L);
+  const dim3 flat(grid_of(n4, 512, 4096), L);
   {
     ProfScope prof("muon_normalize", 0, (8.0 + es) * 4 * n4 * L, st);
-    hipLaunchKernelGGL((muon_norm_kernel<T>), tiles, dim3(256), 0, st, g, mom, ls, R, C, transpose ? 1 : 0, mu,
-                       nesterov, norm_part, xa, xs);
+    if (transpose)
+      hipLaunchKernelGGL((muon_norm_tr_kernel<T>), tiles, dim3(256), 0, st, g, mom, ls, R, C, mu, nesterov, norm_part,
+                         xa, xs);
+    else
+      hipLaunchKernelGGL((muon_norm_flat_kernel<T>), flat, dim3(256), 0, st, g, mom, ls, n4, mu, nesterov, norm_part,
+                         xa, xs);
     NC_LAUNCH_CHECK("muon_normalize");
   }
   // the published coefficients (a, b, c) of the quintic map, five steps, all L matrices at once
@@ -250,8 +330,12 @@ nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, in
   const float scale = R > C ? std::sqrt((float)R / (float)C) : 1.f;
   {
     ProfScope prof("muon_apply", 0, (8.0 + 2.0 * es) * 4 * n4 * L, st);
-    hipLaunchKernelGGL((muon_apply_kernel<T>), tiles, dim3(256), 0, st, w, p, ls, x, xs, R, C, transpose ? 1 : 0,
-                       1.f - lr * wd, lr * scale);
+    if (transpose)
+      hipLaunchKernelGGL((muon_apply_tr_kernel<T>), tiles, dim3(256), 0, st, w, p, ls, x, xs, R, C, 1.f - lr * wd,
+                         lr * scale);
+    else
+      hipLaunchKernelGGL((muon_apply_flat_kernel<T>), flat, dim3(256), 0, st, w, p, ls, x, xs, n4, 1.f - lr * wd,
+                         lr * scale);
     NC_LAUNCH_CHECK("muon_apply");
   }
   return NC_OK;
