@@ -143,7 +143,7 @@ BlockScratch<T> carve_block_scratch(Carver& c, const Dims& m) {
 template <typename T>
 struct HeadSaved {
   T *xf, *z;
-  float *rf, *lse, *zt;
+  float *rf, *lse;
   int* nv;
 };
 template <typename T>
@@ -153,7 +153,6 @@ HeadSaved<T> carve_head_saved(Carver& c, const Dims& m) {
   s.rf = c.take<float>(m.M);
   s.z = c.take<T>(logit_elems(m.M, m.V));  // column panels of kPanel
   s.lse = c.take<float>(m.M);
-  s.zt = c.take<float>(m.M);
   s.nv = c.take<int>(1);
   return s;
 }
@@ -372,9 +371,9 @@ nc_status head_fwd_t(const Dims& m, const T* x, const T* wlm, const int32_t* tg,
                      const HeadScratch<T>& c, uint32_t* status, hipStream_t st) {
   const int M = (int)m.M;
   NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.xf, s.rf, M, m.d, m.eps, nullptr, st));
-  NC_TRY(gemm_lmhead<T>(s.xf, wlm, s.z, M, m.V, m.d, m.cap, tg, c.part, s.zt, st));
-  NC_TRY(xent_loss(c.part, lmhead_tiles(m.V, m.es == 2), s.zt, tg, M, m.V, s.lse, nullptr, c.block_sums, c.block_counts, loss,
-                   s.nv, status, st));
+  NC_TRY(gemm_lmhead<T>(s.xf, wlm, s.z, M, m.V, m.d, m.cap, c.part, st));
+  NC_TRY(xent_loss<T>(c.part, lmhead_tiles(m.V, m.es == 2), s.xf, wlm, m.d, m.cap, tg, M, m.V, s.lse, c.block_sums,
+                      c.block_counts, loss, s.nv, status, st));
   return NC_OK;
 }
 

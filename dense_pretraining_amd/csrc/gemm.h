@@ -513,25 +513,18 @@ struct EpiF32 {
 // hardware exp2 and reciprocal: c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
 template <typename T, int BM, int BN>
 struct EpiSoftcap {
-  T* Z;         // [M, N] in column panels of kPanel
-  long zpanel;  // panel stride (elements): M * kPanel
+  T* Z;        // [M, N] in column panels of kPanel
+  int zpanel;  // panel stride (elements): M * kPanel
   float cap;
-  const int32_t* targets;
   float* part;
-  float* zt;
   int n_tiles;
   int M, N;
   struct RowState {
     float sum;
-    int tgt;
   };
-  __device__ __forceinline__ void row_begin(RowState& rs, int row) const {
-    rs.sum = 0.f;
-    const int t = targets[row < M ? row : M - 1];
-    rs.tgt = row < M ? t : -1;
-  }
-  // branch-free: out-of-range columns add nothing, and the target's logit is
-  // stored through an offset past the record unless this run of 4 holds it
+  __device__ __forceinline__ void row_begin(RowState& rs, int) const { rs.sum = 0.f; }
+  // z' = c - 2c / (2^(2 log2(e) z / c) + 1) = c tanh(z / c); out-of-range
+  // columns add nothing to the row's sum of exp(z')
   __device__ __forceinline__ void pre(RowState& rs, int row, int col, float* v) const {
     const float k2 = 2.8853900817779268f / cap;  // 2 log2(e) / c
     const float lg = 1.4426950408889634f;
@@ -540,17 +533,10 @@ struct EpiSoftcap {
       const float t = __builtin_amdgcn_exp2f(v[e] * k2);
       v[e] = cap - 2.f * cap * __builtin_amdgcn_rcpf(t + 1.f);
     }
-    const bool in = row < M && col < N;
     float s4 = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) s4 += __builtin_amdgcn_exp2f(v[e] * lg);
-    rs.sum += in ? s4 : 0.f;
-    const unsigned d = (unsigned)(rs.tgt - col);
-    // |z'| <= c: the 0/1 weights pick one value exactly, with no branch
-    const float vt = v[0] * (float)(d == 0u) + v[1] * (float)(d == 1u) + v[2] * (float)(d == 2u) +
-                     v[3] * (float)(d == 3u);
-    const int off = in && d < 4u ? row * (int)sizeof(float) : (int)kDmaOOB;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, vt), dma_rsrc(zt), off, 0, 0);
+    rs.sum += row < M && col < N ? s4 : 0.f;
   }
   __device__ __forceinline__ void row_end(RowState& rs, const EpiCtx& x, int i) const {
     // the other half of this row's columns sits in lane ^ 32
@@ -562,12 +548,9 @@ struct EpiSoftcap {
   __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
     // the tile's panels from its origin: panel (col - n0) / kPanel, row (row - m0)
     const __amdgpu_buffer_rsrc_t rs = dma_rsrc(Z + (long)(x.n0 / kPanel) * zpanel + (long)x.m0 * kPanel);
-    const int dc = col - x.n0;
-    const int off = row < M && col < N
-                        ? (int)((((long)(dc / kPanel) * zpanel + (long)(row - x.m0) * kPanel + dc % kPanel)) *
-                                (long)sizeof(T))
-                        : (int)kDmaOOB;
-    tile_store4<T>(rs, off, v);
+    const unsigned dc = (unsigned)(col - x.n0), dr = (unsigned)(row - x.m0);
+    const unsigned o = ((dc / kPanel) * (unsigned)zpanel + dr * kPanel + dc % kPanel) * (unsigned)sizeof(T);
+    tile_store4<T>(rs, row < M && col < N ? (int)o : (int)kDmaOOB, v);
   }
   __device__ __forceinline__ void finish(const EpiCtx& x) const {
     __syncthreads();

@@ -193,15 +193,15 @@ int lmhead_tiles(int N, bool bf16_storage) {
 }
 
 template <typename T>
-nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
-                      float* part, float* zt, hipStream_t st) {
-  if (!tile_span_ok(M, sizeof(T)) || (long)M * (long)sizeof(float) >= (long)kDmaRecords) return NC_ERR_UNSUPPORTED;
+nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st) {
+  // a tile's 8 column panels of M * kPanel elements are addressed with 32-bit offsets
+  if (!tile_span_ok(M, sizeof(T)) || (long)M * kPanel * 8 * (long)sizeof(T) >= (long)kDmaRecords)
+    return NC_ERR_UNSUPPORTED;
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
                  sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
                  st);
-  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, (long)M * kPanel, cap, targets, part, zt, lmhead_tiles(N, is_bf16<T>()),
-                                                   M, N};
+  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, M * kPanel, cap, part, lmhead_tiles(N, is_bf16<T>()), M, N};
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
@@ -213,8 +213,7 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t, long);         \
   template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t,  \
                                 long);                                                                        \
-  template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, const int32_t*, float*,     \
-                                    float*, hipStream_t);
+  template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, float*, hipStream_t);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST

@@ -50,10 +50,9 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int a
                   size_t partial_elems, hipStream_t st, long dy_panel = 0);
 size_t gemm_dw_partial_elems(int M, int N, int K);
 // Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N] in column panels;
-// part[M, lmhead_tiles(N)] = per-tile sums of exp(z); zt[m] = z[m][targets[m]].
+// part[M, lmhead_tiles(N)] = per-tile sums of exp(z).
 template <typename T>
-nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, const int32_t* targets,
-                      float* part, float* zt, hipStream_t st);
+nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st);
 int lmhead_tiles(int N, bool bf16_storage);
 
 // ------------------------------------------------------------ few-row products (skinny.hip)
@@ -104,10 +103,13 @@ template <typename T>
 nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float* cs, const float* sn, int M, int T_,
                           int nheads, int D, float eps, hipStream_t st);
 // Cross-entropy: lse[m] = log(sum of part[m][:]); loss = mean over valid
-// targets of lse - zt; nv = count of valid targets; writes loss and status.
-nc_status xent_loss(const float* part, int ntiles, const float* zt, const int32_t* targets, int M, int V, float* lse,
-                    float* row_loss, float* block_sums, int* block_counts, float* loss, int* nv, uint32_t* status,
-                    hipStream_t st);
+// targets of lse - z_t, with the target's logit z_t = c tanh(x[m] . w[t] / c)
+// recomputed from the unembedding's input x [M, d] and weight w [V, d];
+// nv = count of valid targets; writes loss and status.
+template <typename T>
+nc_status xent_loss(const float* part, int ntiles, const T* x, const T* w, int d, float cap, const int32_t* targets,
+                    int M, int V, float* lse, float* block_sums, int* block_counts, float* loss, int* nv,
+                    uint32_t* status, hipStream_t st);
 size_t xent_loss_blocks(int M);
 // In place: z <- (exp(z - lse) - onehot) * dloss/nv * (1 - (z/c)^2) on valid rows, 0 elsewhere.
 template <typename T>

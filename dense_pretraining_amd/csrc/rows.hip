@@ -253,12 +253,16 @@ __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(const T* __restric
 // ------------------------------------------------------------ cross-entropy
 // Next-token cross-entropy over the softcapped logits (imeisheng.com section
 // "预训练"; softcap from the architecture list). Per row: lse = log(sum of the
-// unembedding epilogue's per-tile exp sums); loss term lse - z'[target].
+// unembedding epilogue's per-tile exp sums); loss term lse - z'[target], the
+// target's logit recomputed here as one float32 dot product of the row's
+// input with the target's weight row (the epilogue then has no per-element
+// target test).
+template <typename T>
 __global__ void __launch_bounds__(256) xent_rows_kernel(const float* __restrict__ part, int ntiles,
-                                                        const float* __restrict__ zt, const int32_t* __restrict__ tg,
-                                                        int M, int V, float* __restrict__ lse,
-                                                        float* __restrict__ block_sums, int* __restrict__ block_counts,
-                                                        uint32_t* status) {
+                                                        const T* __restrict__ x, const T* __restrict__ w, int d,
+                                                        float cap, const int32_t* __restrict__ tg, int M, int V,
+                                                        float* __restrict__ lse, float* __restrict__ block_sums,
+                                                        int* __restrict__ block_counts, uint32_t* status) {
   __shared__ float ws[4];
   __shared__ int wc[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -278,7 +282,17 @@ __global__ void __launch_bounds__(256) xent_rows_kernel(const float* __restrict_
     }
     if (lane == 0) lse[m] = l;
     if (y >= 0) {
-      acc += l - zt[m];
+      constexpr int n = Vec<T>::n;
+      float dot = 0.f;
+      for (int c = n * lane; c < d; c += 64 * n) {
+        float a[n], b[n];
+        load16<T>(x + (long)m * d + c, a);
+        load16<T>(w + (long)y * d + c, b);
+#pragma unroll
+        for (int e = 0; e < n; ++e) dot += a[e] * b[e];
+      }
+      dot = wave_sum(dot);
+      acc += l - cap * tanhf(dot / cap);
       cnt += 1;
     }
   }
@@ -484,14 +498,15 @@ nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float
 
 size_t xent_loss_blocks(int M) { return (size_t)(M + 31) / 32; }
 
-nc_status xent_loss(const float* part, int ntiles, const float* zt, const int32_t* targets, int M, int V, float* lse,
-                    float* row_loss, float* block_sums, int* block_counts, float* loss, int* nv, uint32_t* status,
-                    hipStream_t st) {
-  (void)row_loss;
+template <typename T>
+nc_status xent_loss(const float* part, int ntiles, const T* x, const T* w, int d, float cap, const int32_t* targets,
+                    int M, int V, float* lse, float* block_sums, int* block_counts, float* loss, int* nv,
+                    uint32_t* status, hipStream_t st) {
+  if (d % Vec<T>::n != 0) return NC_ERR_UNSUPPORTED;
   int nb = (int)xent_loss_blocks(M);
-  ProfScope prof("xent_loss", 0, 4.0 * M * ntiles + 16.0 * M, st);
-  hipLaunchKernelGGL(xent_rows_kernel, dim3(nb), dim3(256), 0, st, part, ntiles, zt, targets, M, V, lse, block_sums,
-                     block_counts, status);
+  ProfScope prof("xent_loss", 0, 4.0 * M * ntiles + 12.0 * M + 2.0 * sizeof(T) * M * d, st);
+  hipLaunchKernelGGL((xent_rows_kernel<T>), dim3(nb), dim3(256), 0, st, part, ntiles, x, w, d, cap, targets, M, V,
+                     lse, block_sums, block_counts, status);
   NC_LAUNCH_CHECK("xent_rows");
   hipLaunchKernelGGL(xent_final_kernel, dim3(1), dim3(256), 0, st, block_sums, block_counts, nb, loss, nv, status);
   NC_LAUNCH_CHECK("xent_final");
@@ -528,7 +543,9 @@ nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, 
                                         float, hipStream_t, int);                                                   \
   template nc_status qknorm_rope_bwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
                                         float, hipStream_t);                                                        \
-  template nc_status xent_dz<T>(T*, int, int, const float*, const int32_t*, const int*, float, float, hipStream_t);
+  template nc_status xent_dz<T>(T*, int, int, const float*, const int32_t*, const int*, float, float, hipStream_t); \
+  template nc_status xent_loss<T>(const float*, int, const T*, const T*, int, float, const int32_t*, int, int,      \
+                                  float*, float*, int*, float*, int*, uint32_t*, hipStream_t);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST
