@@ -508,9 +508,9 @@ struct EpiF32 {
 // Unembedding epilogue: z' = c tanh(z / c) (the logit softcap of the
 // architecture list), stored in the storage type; per row, the sum of
 // exp(z') over this tile's BN columns goes to part[row * n_tiles + tile]
-// (|z'| <= c, so no running maximum is needed in float32); the float32 z'
-// of the target column goes to zt[row]. The tanh and exponentials use the
-// hardware exp2 and reciprocal: c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
+// (|z'| <= c, so no running maximum is needed in float32). The tanh and
+// exponentials use the hardware exp2 and reciprocal:
+// c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
 template <typename T, int BM, int BN>
 struct EpiSoftcap {
   T* Z;        // [M, N] in column panels of kPanel
