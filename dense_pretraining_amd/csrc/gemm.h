@@ -516,6 +516,7 @@ struct EpiSoftcap {
   T* Z;        // [M, N] in column panels of kPanel
   int zpanel;  // panel stride (elements): M * kPanel
   float cap;
+  float k2;  // 2 log2(e) / c, computed by the host
   float* part;
   int n_tiles;
   int M, N;
@@ -526,7 +527,6 @@ struct EpiSoftcap {
   // z' = c - 2c / (2^(2 log2(e) z / c) + 1) = c tanh(z / c); out-of-range
   // columns add nothing to the row's sum of exp(z')
   __device__ __forceinline__ void pre(RowState& rs, int row, int col, float* v) const {
-    const float k2 = 2.8853900817779268f / cap;  // 2 log2(e) / c
     const float lg = 1.4426950408889634f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

@@ -201,7 +201,8 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
                  sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
                  st);
-  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, M * kPanel, cap, part, lmhead_tiles(N, is_bf16<T>()), M, N};
+  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, M * kPanel, cap, (float)(2.8853900817779268 / cap), part,
+                                                   lmhead_tiles(N, is_bf16<T>()), M, N};
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
