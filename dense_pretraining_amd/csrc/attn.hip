@@ -40,6 +40,18 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // exp2f needs its denormal rescaling.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A buffer descriptor from an address the caller knows to be the same in
+// every lane. A descriptor the compiler cannot prove uniform sits in vector
+// registers, and every buffer instruction using it is wrapped in a loop over
+// the distinct values (readfirstlane, compare, exec mask); taking the address
+// through readfirstlane keeps it in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc_uniform(const void* base) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return dma_rsrc(reinterpret_cast<const void*>(((unsigned long long)hi << 32) | lo));
+}
+
 // r / n for 0 <= r < 2^24 without an integer division.
 struct DivN {
   int n;
@@ -179,7 +191,8 @@ struct KvDma {
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
       const unsigned o = key0 + row[i] < T_ ? off[i] : kDmaOOB;
-      __amdgpu_buffer_rsrc_t rs = dma_rsrc(isv[i] ? vbase + key0 * ldv : kbase + key0 * ldk);
+      // K or V by the wave's instruction index: the same in every lane
+      __amdgpu_buffer_rsrc_t rs = dma_rsrc_uniform(isv[i] ? vbase + key0 * ldv : kbase + key0 * ldk);
       T* dst = (isv[i] ? sv : sk) + blk[i] * 64 * VE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, o, 0, 0, 0);
     }
