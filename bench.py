@@ -11,8 +11,9 @@ with fp32 accumulation -- one GPU's share of the pretraining step the
 imeisheng.com page ("预训练") describes.
 
 Prints one JSON line: tokens/s, MFU, the dominant kernel's roofline (its
-launches timed with HIP events inside the timed region) and the fp64 CPU
-oracle's throughput on a bounded sample of the same workload.
+launches timed with HIP events inside the timed region, the only events
+there), the per-kernel table (from untimed steps with every launch timed)
+and the fp64 CPU oracle's throughput on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -355,7 +356,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="do not record per-kernel HIP events in the timed region")
+                    help="no per-kernel HIP events: no kernel table, no roofline")
+    ap.add_argument("--table-steps", type=int, default=2,
+                    help="untimed steps after the warmup whose every launch is timed by HIP events (the kernel "
+                         "table); the timed steps then time the dominant kernel only")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, copy this many MiB device to device once (a plain copy kernel "
                          "of known size that calibrates the HBM byte counters of a profiling run)")
@@ -404,7 +408,22 @@ def main():
     if st:
         print(f"# device status bits set: {st:#x}", file=sys.stderr)
 
+    # Per-kernel table from a few untimed steps with every launch bracketed by
+    # events; the timed steps then carry events around the dominant kernel
+    # only (its roofline figure is measured live), since two event records
+    # per launch of all ~500 launches would add about 1 % to the step.
     timing = not a.no_kernel_timing
+    table = dominant = None
+    if timing:
+        lib.profile_only(None)
+        lib.profile_enable(True)
+        for _ in range(a.table_steps):
+            step()
+        torch.cuda.synchronize()
+        lib.profile_enable(False)
+        table = kernel_table(lib.profile_summary(), a.table_steps)
+        dominant = next(iter(table))
+        lib.profile_only(dominant)
     torch.cuda.synchronize()
     if timing:
         lib.profile_enable(True)
@@ -419,6 +438,8 @@ def main():
     wall = time.perf_counter() - t0
     if timing:
         lib.profile_enable(False)
+        live = kernel_table(lib.profile_summary(), a.steps)
+        lib.profile_only(None)
     ms = e0.elapsed_time(e1) / a.steps
     print(f"# timed {a.steps} steps: {ms:.2f} ms/step (wall {wall / a.steps * 1e3:.2f})", file=sys.stderr,
           flush=True)
@@ -454,8 +475,7 @@ def main():
         "loss": round(float(loss.item()), 6),
     }
     if timing:
-        table = kernel_table(lib.profile_summary(), a.steps)
-        name, rl = roofline(table)
+        name, rl = roofline(live)
         tb = measured_traffic(name)
         rl["traffic"] = None if tb is None else round(tb)
         out["roofline"] = rl

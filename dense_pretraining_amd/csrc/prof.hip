@@ -1,7 +1,7 @@
-// Kernel timing: while enabled, each launch of the library is bracketed by two
-// HIP events on its stream and recorded with its algorithmic work (model
-// FLOPs and the minimum bytes the kernel must move). Disabled, a scope costs
-// one relaxed load of a flag.
+// Kernel timing: while enabled, each launch of the library (or of one kernel
+// class only) is bracketed by two HIP events on its stream and recorded with
+// its algorithmic work (model FLOPs and the minimum bytes the kernel must
+// move). Disabled, a scope costs one relaxed load of a flag.
 #include <atomic>
 #include <cstdio>
 #include <cstring>
@@ -27,6 +27,7 @@ struct Prof {
   std::mutex mu;
   std::vector<Rec> recs;
   std::vector<hipEvent_t> events;  // 2 per record, reused across enables
+  std::string only;                // record only this kernel class (empty: all)
 };
 
 Prof& prof() {
@@ -40,6 +41,7 @@ ProfScope::ProfScope(const char* name, double flops, double bytes, hipStream_t s
   Prof& p = prof();
   if (!p.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> g(p.mu);
+  if (!p.only.empty() && p.only != name) return;
   int i = (int)p.recs.size();
   while ((int)p.events.size() < 2 * (i + 1)) {
     hipEvent_t e;
@@ -69,6 +71,13 @@ nc_status nc_profile_enable(int on) {
   std::lock_guard<std::mutex> g(p.mu);
   if (on) p.recs.clear();
   p.on.store(on != 0);
+  return NC_OK;
+}
+
+nc_status nc_profile_only(const char* kernel_class) {
+  Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.only = kernel_class ? kernel_class : "";
   return NC_OK;
 }
 

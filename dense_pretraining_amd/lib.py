@@ -35,7 +35,7 @@ EXPORTED = [
     "nc_query_sizes", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
     "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_opt_query_sizes",
-    "nc_opt_init", "nc_opt_step", "nc_profile_enable", "nc_profile_summary",
+    "nc_opt_init", "nc_opt_step", "nc_profile_enable", "nc_profile_only", "nc_profile_summary",
 ]
 
 
@@ -117,6 +117,7 @@ def load(path=LIB_PATH):
         "nc_opt_init": ([cfgp, P, P, P], I),
         "nc_opt_step": ([cfgp, C.POINTER(NcOptHparams), P, P, P, P, S, P], I),
         "nc_profile_enable": ([I], I),
+        "nc_profile_only": ([C.c_char_p], I),
         "nc_profile_summary": ([C.c_char_p, S, C.POINTER(S)], I),
     }
     for name, (args, res) in sig.items():
@@ -266,6 +267,11 @@ def model_loss_and_grad(cfg, params, idx, targets, loss, grads, workspace, dloss
 
 def profile_enable(on=True):
     _check(load().nc_profile_enable(int(on)), "nc_profile_enable")
+
+
+def profile_only(kernel_class=None):
+    """Record only the launches of one kernel class (None: all of them)."""
+    _check(load().nc_profile_only(kernel_class.encode() if kernel_class else None), "nc_profile_only")
 
 
 def profile_summary():

@@ -298,6 +298,13 @@ nc_status nc_opt_step(const nc_config* cfg, const nc_opt_hparams* hp, void* para
  * device buffer is allocated. Recording costs two event records per launch. */
 nc_status nc_profile_enable(int on);
 
+/* Restricts the recording to the launches of one kernel class, named as in the
+ * summary below (a host string, copied); NULL or "" records every launch
+ * again. Timing one kernel costs two event records per launch of that kernel
+ * only, so a timed run of the whole step can carry it. Takes effect for
+ * launches issued after the call. */
+nc_status nc_profile_only(const char* kernel_class);
+
 /* Waits for the recorded events and writes, into buf (host, buf_len bytes), a
  * JSON object {"kernel": {"launches": n, "ms": t, "flops": f, "bytes": b}, ...}
  * summed per kernel. *written (host) receives the bytes needed including the

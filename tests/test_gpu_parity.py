@@ -263,3 +263,36 @@ def test_block_writes_stay_inside_outputs(dt):
     for name, buf in (("x_out", out_buf), ("dx_in", dx_buf)):
         assert bool(torch.all(buf[M:] == sentinel)), f"{name}: rows past the output were written"
         assert bool(torch.all(torch.isfinite(buf[:M]))) and not bool(torch.any(buf[:M] == sentinel)), name
+
+
+def test_profile_records_every_launch_or_one_class():
+    """Kernel timing: with every launch recorded, one block forward holds the
+    attention forward and the GEMMs; restricted to one class, only that
+    class's launches are recorded, with the same count."""
+    cfg = _cfg("ragged", "bf16").with_(depth=1)
+    p = params(cfg, fan_in=True)
+    wd = {k: dev(v, cfg) for k, v in pack_block(p["layers"][0]).items()}
+    x_np, _ = synth.block_inputs(cfg.batch, cfg.seq_len, cfg.d_model, dtype="bf16")
+    x = dev(x_np.reshape(cfg.tokens, cfg.d_model), cfg)
+    out = torch.empty_like(x)
+    saved = lib.alloc_bytes(lib.query_sizes(cfg).block_saved)
+    scratch = lib.new_scratch(cfg)
+    try:
+        lib.profile_only(None)
+        lib.profile_enable(True)
+        lib.block_fwd(cfg, wd, x, out, saved, scratch)
+        lib.profile_enable(False)
+        every = lib.profile_summary()
+        lib.profile_only("attn_fwd_bf16")
+        lib.profile_enable(True)
+        lib.block_fwd(cfg, wd, x, out, saved, scratch)
+        lib.block_fwd(cfg, wd, x, out, saved, scratch)
+        lib.profile_enable(False)
+        one = lib.profile_summary()
+    finally:
+        lib.profile_enable(False)
+        lib.profile_only(None)
+    assert "attn_fwd_bf16" in every and len(every) > 3
+    assert list(one) == ["attn_fwd_bf16"]
+    assert one["attn_fwd_bf16"]["launches"] == 2 * every["attn_fwd_bf16"]["launches"]
+    assert one["attn_fwd_bf16"]["ms"] > 0
