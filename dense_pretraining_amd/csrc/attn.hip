@@ -652,21 +652,47 @@ struct DkdvCtx {
   // per load instruction of this wave: tile row, chunk column offset, operand
   int lrow[Sh::NPW], lcol[Sh::NPW], lblk[Sh::NPW];
   bool ldo[Sh::NPW];
+  // and, for the tile the next issue() loads: the row, its head index within
+  // the KV group (h in [0, n_rep)) and its byte offset. Tiles are issued in
+  // order, each BQ rows below the last, so these advance by a subtraction and
+  // a borrow instead of a division per load.
+  int nr[Sh::NPW], nh[Sh::NPW], noff[Sh::NPW];
+  int dr, dstep[Sh::NPW], wrap[Sh::NPW];
 
   __device__ __forceinline__ int row0(int s) const { return r_start + Sh::BQ * (ntiles - 1 - s); }
 
-  // Loads of the tile processed at step s into one ring stage.
-  __device__ __forceinline__ void issue(int s, T* __restrict__ sq, T* __restrict__ sd, float* __restrict__ ss) const {
+  // The state for step 0, once (n_rep, hbase, lrow, lcol, ldo, ld_* set).
+  __device__ __forceinline__ void init_rows() {
+    const int dq = Sh::BQ / n_rep;
+    dr = Sh::BQ - dq * n_rep;
+#pragma unroll
+    for (int i = 0; i < Sh::NPW; ++i) {
+      const long ld = ldo[i] ? ld_o : ld_qk;
+      const int r = row0(0) + lrow[i];
+      const int t = dvn.q(r);  // rows up to nrows + BQ: inside the divider's range
+      nr[i] = r;
+      nh[i] = r - t * n_rep;
+      noff[i] = (int)((t * ld + (long)(hbase + nh[i]) * D + lcol[i]) * (long)sizeof(T));
+      dstep[i] = (int)(((long)dq * ld + (long)dr * D) * (long)sizeof(T));
+      wrap[i] = (int)(((long)n_rep * D - ld) * (long)sizeof(T));
+    }
+  }
+
+  // Loads of the tile processed at step s into one ring stage; steps are
+  // issued in order 0, 1, 2, ...
+  __device__ __forceinline__ void issue(int s, T* __restrict__ sq, T* __restrict__ sd, float* __restrict__ ss) {
     const int rq0 = row0(s);
     const bool live = s < ntiles;
 #pragma unroll
     for (int i = 0; i < Sh::NPW; ++i) {
-      const int r = rq0 + lrow[i];
-      unsigned off = kDmaOOB;
-      if (live && r < nrows) {
-        const int t = dvn.q(r), h = hbase + (r - t * n_rep);
-        off = (unsigned)((((long)t * (ldo[i] ? ld_o : ld_qk)) + (long)h * D + lcol[i]) * (long)sizeof(T));
-      }
+      const unsigned off = (live && nr[i] < nrows) ? (unsigned)noff[i] : kDmaOOB;
+      // the same load of the next tile: BQ rows up = dq positions and dr heads, with a borrow
+      nr[i] -= Sh::BQ;
+      nh[i] -= dr;
+      noff[i] -= dstep[i];
+      const bool borrow = nh[i] < 0;
+      nh[i] += borrow ? n_rep : 0;
+      noff[i] += borrow ? wrap[i] : 0;
       T* dst = (ldo[i] ? sd : sq) + lblk[i] * 64 * Sh::VE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ldo[i] ? rd : rq, (lds_void*)dst, 16, off, 0, 0, 0);
     }
@@ -798,7 +824,7 @@ __device__ __forceinline__ void dkdv_tile_ds(const DkdvCtx<T, D>& c, int s, int 
   }
 
 template <int ROLE, typename T, int D>
-__device__ __forceinline__ void dkdv_ring(const DkdvCtx<T, D>& c, f32x16* acc, const F8<T>* kv, F8<T>* pb,
+__device__ __forceinline__ void dkdv_ring(DkdvCtx<T, D>& c, f32x16* acc, const F8<T>* kv, F8<T>* pb,
                                           float c1, T* __restrict__ q0, T* __restrict__ q1, T* __restrict__ q2,
                                           T* __restrict__ q3, T* __restrict__ d0, T* __restrict__ d1,
                                           T* __restrict__ d2, T* __restrict__ d3, float* __restrict__ t0,
@@ -884,6 +910,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
     c.lrow[i] = row;
     c.lcol[i] = (pc ^ Swz<T, D>::f(row)) * Sh::VE;
   }
+  c.init_rows();
 
   // own 32 keys: K (P side) or V (dS side) as B operands, 8 consecutive d per lane
   const int key = c.kw0 + l32;
