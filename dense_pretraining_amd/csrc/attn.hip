@@ -574,9 +574,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          int key = kb + crow(v, lh);
-          float p = fast_exp2(sacc[v] * c1 - lse2);
-          ds[v] = (qok && key <= tq) ? p * (pacc[v] - dlt) : 0.f;
+          // a 0/1 factor, not a select: the compiler would put the exponential
+          // under a branch per element (every score is bounded, so the
+          // masked products are finite)
+          const int key = kb + crow(v, lh);
+          const float p = fast_exp2(sacc[v] * c1 - lse2);
+          ds[v] = p * (pacc[v] - dlt) * (float)(qok && key <= tq);
         }
       }
 #pragma unroll
