@@ -47,8 +47,9 @@ nc_status make_dims(const nc_config* c, Dims* o, bool need_depth) {
       (long)c->vocab * c->d_model > 0x7fffffffL || M * c->d_ff > 0x7fffffffL || M * qkv > 0x7fffffffL)
     return NC_ERR_UNSUPPORTED;
   // a weight-gradient tile of the unembedding spans 8 logit panels of M * kPanel
-  // elements, addressed with 32-bit byte offsets
-  if (M * kPanel * 8 * 2 > 0x7fffffffL) return NC_ERR_UNSUPPORTED;
+  // elements, addressed with 32-bit byte offsets; the unembedding epilogue
+  // multiplies the panel stride in 24 bits
+  if (M * kPanel * 8 * 2 > 0x7fffffffL || M * kPanel >= (1L << 24)) return NC_ERR_UNSUPPORTED;
   o->M = M;
   o->B = c->batch;
   o->T = c->seq_len;

@@ -344,7 +344,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* base, long 
 }
 template <typename T>
 __device__ __forceinline__ int tile_off(const EpiCtx& x, int row, int col, long ld, int M, int N) {
-  return (int)(row < M && col < N ? (unsigned)(((long)(row - x.m0) * ld + (col - x.n0)) * (long)sizeof(T)) : kDmaOOB);
+  // row - m0 < 256 and 256 ld es < 2^31 (checked by every launcher): both
+  // factors fit 24 bits, so the full-rate 24-bit multiply gives the product
+  const unsigned r = __umul24((unsigned)(row - x.m0), (unsigned)ld);
+  return (int)(row < M && col < N ? (r + (unsigned)(col - x.n0)) * (unsigned)sizeof(T) : kDmaOOB);
 }
 typedef int epi_v2i __attribute__((ext_vector_type(2)));
 typedef int epi_v4i __attribute__((ext_vector_type(4)));
@@ -549,7 +552,8 @@ struct EpiSoftcap {
     // the tile's panels from its origin: panel (col - n0) / kPanel, row (row - m0)
     const __amdgpu_buffer_rsrc_t rs = dma_rsrc(Z + (long)(x.n0 / kPanel) * zpanel + (long)x.m0 * kPanel);
     const unsigned dc = (unsigned)(col - x.n0), dr = (unsigned)(row - x.m0);
-    const unsigned o = ((dc / kPanel) * (unsigned)zpanel + dr * kPanel + dc % kPanel) * (unsigned)sizeof(T);
+    // panel index < 8 and zpanel < 2^24 (checked by the launcher): a 24-bit multiply
+    const unsigned o = (__umul24(dc / kPanel, (unsigned)zpanel) + dr * kPanel + dc % kPanel) * (unsigned)sizeof(T);
     tile_store4<T>(rs, row < M && col < N ? (int)o : (int)kDmaOOB, v);
   }
   __device__ __forceinline__ void finish(const EpiCtx& x) const {

@@ -194,8 +194,10 @@ int lmhead_tiles(int N, bool bf16_storage) {
 
 template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st) {
-  // a tile's 8 column panels of M * kPanel elements are addressed with 32-bit offsets
-  if (!tile_span_ok(M, sizeof(T)) || (long)M * kPanel * 8 * (long)sizeof(T) >= (long)kDmaRecords)
+  // a tile's 8 column panels of M * kPanel elements are addressed with 32-bit
+  // offsets, the panel stride through a 24-bit multiply
+  if (!tile_span_ok(M, sizeof(T)) || (long)M * kPanel * 8 * (long)sizeof(T) >= (long)kDmaRecords ||
+      (long)M * kPanel >= (1L << 24))
     return NC_ERR_UNSUPPORTED;
   GemmShape s{x, w, K, K, M, N, K, K, 1};
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,

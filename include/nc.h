@@ -120,7 +120,8 @@ const char* nc_last_hip_error(void);
 /* Checks a configuration. NC_ERR_SHAPE: a non-positive size, H % G != 0,
  * d/H/F/V not matching. NC_ERR_UNSUPPORTED: head_dim not 64 or 128, d_model
  * or d_ff not a multiple of 64, vocab not a multiple of 8, more than
- * 2^31 - 1 elements in any tensor, dtype unknown. */
+ * 2^31 - 1 elements in any tensor, 2^19 or more tokens (batch * seq_len),
+ * dtype unknown. */
 nc_status nc_validate(const nc_config* cfg);
 
 /* Host outputs. offsets[0] = Wte [V,d]; for layer l (0-based)

@@ -52,6 +52,7 @@ def test_named_configs_validate(cfg):
     (dict(d_ff=100), 5),
     (dict(softcap=0.0), 2),
     (dict(depth=0), 2),
+    (dict(batch=256, seq_len=2048), 5),     # 2^19 tokens: the logit panel stride exceeds 24 bits
 ])
 def test_bad_configs_rejected(change, code):
     assert lib.validate(cfgmod.TINY.with_(**change)) == code
