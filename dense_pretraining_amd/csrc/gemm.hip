@@ -182,11 +182,6 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int a
   return splitk_reduce(partial, nsplit, (size_t)N * K, dw, accumulate, st);
 }
 
-namespace {
-// Splits of the reduction for a few-row product: enough workgroups to keep
-// every compute unit streaming W (at most 16 splits, at least 2 k-tiles each).
-}  // namespace
-
 int lmhead_tiles(int N, bool bf16_storage) {
   const int bn = bf16_storage ? GemmTile<bf16>::BN : GemmTile<float>::BN;
   return (N + bn - 1) / bn;
