@@ -40,6 +40,25 @@ __global__ void __launch_bounds__(256) opt_init_kernel(const T* __restrict__ p, 
 
 // AdamW on n4 groups of 4: m, v updated in place, w <- w (1 - lr wd) - lr m_hat / (sqrt(v_hat) + eps),
 // p = w in the storage type. c1, c2 = 1 / (1 - beta^t).
+// The optimizer's results (master weights, moments, stored parameters) are
+// read again only at the next step: stored non-temporal.
+typedef float opt_v4f __attribute__((ext_vector_type(4)));
+typedef unsigned opt_v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_f4_stream(float* p, float a, float b, float c, float d) {
+  const opt_v4f v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<opt_v4f*>(p));
+}
+template <typename T>
+__device__ __forceinline__ void store4_stream(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 o;
+    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+    __builtin_nontemporal_store(__builtin_bit_cast(opt_v2u, o), reinterpret_cast<opt_v2u*>(p));
+  } else {
+    store_f4_stream(p, v[0], v[1], v[2], v[3]);
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) adamw_kernel(const float* __restrict__ g, float* __restrict__ w,
                                                     float* __restrict__ m, float* __restrict__ v, T* __restrict__ p,
@@ -57,10 +76,10 @@ __global__ void __launch_bounds__(256) adamw_kernel(const float* __restrict__ g,
       va[e] = b2 * va[e] + (1.f - b2) * ga[e] * ga[e];
       wa[e] = wa[e] * decay - lr * (ma[e] * c1) / (sqrtf(va[e] * c2) + eps);
     }
-    reinterpret_cast<float4*>(w)[i] = make_float4(wa[0], wa[1], wa[2], wa[3]);
-    reinterpret_cast<float4*>(m)[i] = make_float4(ma[0], ma[1], ma[2], ma[3]);
-    reinterpret_cast<float4*>(v)[i] = make_float4(va[0], va[1], va[2], va[3]);
-    store4<T>(p + 4 * i, wa);
+    store_f4_stream(w + 4 * i, wa[0], wa[1], wa[2], wa[3]);
+    store_f4_stream(m + 4 * i, ma[0], ma[1], ma[2], ma[3]);
+    store_f4_stream(v + 4 * i, va[0], va[1], va[2], va[3]);
+    store4_stream<T>(p + 4 * i, wa);
   }
 }
 
@@ -203,8 +222,8 @@ __global__ void __launch_bounds__(256) muon_apply_flat_kernel(float* __restrict_
       float nw[4] = {ws[u].x, ws[u].y, ws[u].z, ws[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) nw[e] = nw[e] * decay - step * x[u][e];
-      reinterpret_cast<float4*>(w)[i] = make_float4(nw[0], nw[1], nw[2], nw[3]);
-      store4<T>(p + 4 * i, nw);
+      store_f4_stream(w + 4 * i, nw[0], nw[1], nw[2], nw[3]);
+      store4_stream<T>(p + 4 * i, nw);
     }
   }
 }
@@ -235,8 +254,8 @@ __global__ void __launch_bounds__(256) muon_apply_tr_kernel(float* __restrict__ 
   float nw[4] = {ww.x, ww.y, ww.z, ww.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) nw[e] = nw[e] * decay - step * tile[ty][4 * tx + e];
-  *reinterpret_cast<float4*>(w + i) = make_float4(nw[0], nw[1], nw[2], nw[3]);
-  store4<T>(p + i, nw);
+  store_f4_stream(w + i, nw[0], nw[1], nw[2], nw[3]);
+  store4_stream<T>(p + i, nw);
 }
 
 unsigned grid_of(long n, long per_block, unsigned cap) {
