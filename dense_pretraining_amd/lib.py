@@ -36,6 +36,7 @@ EXPORTED = [
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
     "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_opt_query_sizes",
     "nc_opt_init", "nc_opt_step", "nc_profile_enable", "nc_profile_only", "nc_profile_summary",
+    "nc_gemm_scratch_size", "nc_gemm",
 ]
 
 
@@ -77,6 +78,17 @@ class NcOptHparams(C.Structure):
                 ("eps", C.c_float), ("wd_matrix", C.c_float), ("wd_adam", C.c_float), ("step", C.c_int32)]
 
 
+class NcGemmArgs(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("dtype", C.c_int32), ("M", C.c_int32), ("N", C.c_int32), ("K", C.c_int32),
+                ("a", C.c_void_p), ("b", C.c_void_p), ("aux", C.c_void_p), ("y", C.c_void_p), ("yf", C.c_void_p),
+                ("a_panels", C.c_int32), ("accumulate", C.c_int32), ("alpha", C.c_float), ("beta", C.c_float),
+                ("softcap", C.c_float)]
+
+
+# nc_gemm_kind
+GEMM_KINDS = {"xwt": 0, "xwt_relusq": 1, "dyw": 2, "dyw_drelusq": 3, "dw": 4, "softcap": 5, "axpby": 6, "gram": 7}
+
+
 class NcOptSizes(C.Structure):
     _fields_ = [("state", C.c_size_t), ("workspace", C.c_size_t)]
 
@@ -116,6 +128,8 @@ def load(path=LIB_PATH):
         "nc_opt_query_sizes": ([cfgp, C.POINTER(NcOptSizes)], I),
         "nc_opt_init": ([cfgp, P, P, P], I),
         "nc_opt_step": ([cfgp, C.POINTER(NcOptHparams), P, P, P, P, S, P], I),
+        "nc_gemm_scratch_size": ([C.POINTER(NcGemmArgs), C.POINTER(S)], I),
+        "nc_gemm": ([C.POINTER(NcGemmArgs), P, S, P], I),
         "nc_profile_enable": ([I], I),
         "nc_profile_only": ([C.c_char_p], I),
         "nc_profile_summary": ([C.c_char_p, S, C.POINTER(S)], I),
@@ -261,6 +275,26 @@ def model_loss_and_grad(cfg, params, idx, targets, loss, grads, workspace, dloss
                                          float(dloss), int(accumulate), _p(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream)),
            "nc_model_loss_and_grad")
+
+
+# ------------------------------------------------------------------ products
+
+def gemm_args(kind, dtype, M, N, K, a, b=None, y=None, yf=None, aux=None, a_panels=False, accumulate=False,
+              alpha=1.0, beta=0.0, softcap=0.0) -> NcGemmArgs:
+    """nc_gemm_args for one product (kind: a key of GEMM_KINDS; dtype 'bf16' or 'f32')."""
+    return NcGemmArgs(GEMM_KINDS[kind], _DTYPES[dtype], int(M), int(N), int(K), _p(a), _p(b), _p(aux), _p(y),
+                      _p(yf), int(bool(a_panels)), int(bool(accumulate)), float(alpha), float(beta), float(softcap))
+
+
+def gemm_scratch_size(args: NcGemmArgs) -> int:
+    n = C.c_size_t()
+    _check(load().nc_gemm_scratch_size(C.byref(args), C.byref(n)), "nc_gemm_scratch_size")
+    return n.value
+
+
+def gemm(args: NcGemmArgs, scratch=None, stream=None):
+    nbytes = scratch.numel() * scratch.element_size() if scratch is not None else 0
+    _check(load().nc_gemm(C.byref(args), _p(scratch), nbytes, _stream(stream)), "nc_gemm")
 
 
 # ------------------------------------------------------------------ tracing

@@ -206,6 +206,61 @@ nc_status nc_model_loss_and_grad(const nc_config* cfg, const void* params, const
                                  int accumulate, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* ---------------------------------------------------------------- products */
+
+/* One linear-layer product of the step, run by the same kernel and epilogue
+ * that nc_block_*, nc_lmhead_* and nc_opt_step launch for it (the bias-free
+ * linears and the untied unembedding with its logit softcap of the
+ * architecture list on vpshk.cn; the Newton-Schulz steps of the optimizer
+ * below). It lets a caller run, time or check one product in isolation.
+ * Operands are row-major in the storage dtype (NC_BF16 or NC_F32), float32
+ * accumulation; bf16 outputs are rounded to nearest even once. */
+typedef enum nc_gemm_kind {
+  NC_GEMM_XWT = 0,         /* y[M,N] = a[M,K] b[N,K]^T, plus aux[M,N] when aux != NULL (the QKV,
+                              O and W2 forward products; aux is the residual stream) */
+  NC_GEMM_XWT_RELUSQ = 1,  /* y[M,N] = max(a b^T, 0)^2 (the MLP's first product and its ReLU^2) */
+  NC_GEMM_DYW = 2,         /* y[M,K] = a[M,N] b[N,K] (an input gradient: dy times the weight) */
+  NC_GEMM_DYW_DRELUSQ = 3, /* y[M,K] = (a b) * 2 sqrt(aux[M,K]) with aux = max(u,0)^2 as the MLP
+                              forward stored it: the gradient through ReLU^2 */
+  NC_GEMM_DW = 4,          /* yf[N,K] = a[M,N]^T b[M,K] in float32, or yf += when accumulate != 0
+                              (a weight gradient, the reduction over the M tokens; split over M
+                              when that fills the GPU, partials in scratch, summed in a fixed order) */
+  NC_GEMM_SOFTCAP = 5,     /* z = a b^T, y = c tanh(z / c) with c = softcap, stored in column
+                              panels of 32: element (m, n) at (n/32)*32M + 32m + n%32 (y holds
+                              M * ceil(N/32)*32 elements); yf[M, ceil(N/256)] (bf16) or
+                              [M, ceil(N/128)] (f32) receives, per row and 256- (128-) column
+                              tile, the float32 sum of exp(y) before rounding */
+  NC_GEMM_AXPBY = 6,       /* y[M,N] = alpha a b^T, plus beta aux[M,N] when aux != NULL */
+  NC_GEMM_GRAM = 7         /* y[K,K] = a[M,K]^T a (b and N unused) */
+} nc_gemm_kind;
+
+typedef struct nc_gemm_args {
+  int32_t kind;       /* nc_gemm_kind */
+  int32_t dtype;      /* NC_BF16 or NC_F32: storage type of a, b, aux and y */
+  int32_t M, N, K;    /* M >= 1 (any), N and K multiples of 8 */
+  const void* a;      /* device */
+  const void* b;      /* device */
+  const void* aux;    /* device, see the kinds; NULL otherwise */
+  void* y;            /* device output in the storage type (not NC_GEMM_DW) */
+  float* yf;          /* device float32 output (NC_GEMM_DW, NC_GEMM_SOFTCAP) */
+  int32_t a_panels;   /* NC_GEMM_DYW / NC_GEMM_DW: a [M,N] is stored in the column panels
+                         NC_GEMM_SOFTCAP writes (as the head's backward reads its dz) */
+  int32_t accumulate; /* NC_GEMM_DW */
+  float alpha, beta;  /* NC_GEMM_AXPBY */
+  float softcap;      /* NC_GEMM_SOFTCAP, > 0 */
+} nc_gemm_args;
+
+/* Scratch bytes nc_gemm needs for args (0 unless a split NC_GEMM_DW). */
+nc_status nc_gemm_scratch_size(const nc_gemm_args* args /* host */, size_t* bytes /* host */);
+
+/* Runs the product on `stream`. Checks (before any launch): NC_ERR_INVALID_ARG
+ * for an unknown kind or a missing pointer, NC_ERR_SHAPE for a non-positive
+ * size, NC_ERR_UNSUPPORTED for N or K not a multiple of 8 or a tensor over
+ * 2^31 - 1 elements, NC_ERR_ALIGN for a pointer not 16-byte aligned,
+ * NC_ERR_WORKSPACE when scratch is smaller than nc_gemm_scratch_size. Outputs
+ * must not alias inputs. */
+nc_status nc_gemm(const nc_gemm_args* args /* host */, void* scratch, size_t scratch_bytes, void* stream);
+
 /* ---------------------------------------------------------------- inference */
 
 /* Greedy generation with a key/value cache: a prefill pass over the prompts,

@@ -3,10 +3,17 @@ benchmark times, checked against the oracle on what it can compute row by row.
 
 Batch rows are independent in the forward pass, and the backward pass of a
 row with zero upstream gradient (or only ignored targets) is exactly zero. So
-a full-size run whose upstream gradient / valid targets sit in one batch row
-b must give weight gradients equal to the oracle's on row b alone, dx rows
-that are exactly zero elsewhere, and (causality) a loss over the first T'
-positions of row b that the oracle reproduces from those T' tokens."""
+a full-size run whose upstream gradient / valid targets sit in a few batch
+rows must give weight gradients equal to the oracle's on those rows alone, dx
+rows that are exactly zero elsewhere, and (causality) a loss over the first
+T' positions of those rows that the oracle reproduces from those T' tokens.
+
+The rows are chosen far apart (the first few and the last few of the batch),
+so that every weight gradient's reduction over the tokens, split into 5 to
+10 ranges summed in a fixed order, adds non-zero partials from at least two
+different ranges.
+
+Every tensor's error is printed (run with -s to see them), worst first."""
 
 import numpy as np
 import pytest
@@ -20,18 +27,23 @@ from gpu_util import TOL, ModelRun, assert_close, dev, host, ocfg, pack_block, s
 pytestmark = pytest.mark.gpu
 
 
-def test_block_full_shape_one_row_gradient():
+def _report(tag, errs):
+    worst = sorted(errs.items(), key=lambda kv: -kv[1])
+    print(f"{tag}: " + ", ".join(f"{k} {v:.3e}" for k, v in worst), flush=True)
+
+
+def test_block_full_shape_two_row_gradient():
     cfg = BLOCK_D20  # B=32, T=2048, d=1280, 10 x 128 heads, 1 KV head, MLP 5120, bf16
     tol = TOL["bf16"]
     M, d, T = cfg.tokens, cfg.d_model, cfg.seq_len
-    b = 5
+    rows = [5, 30]  # token ranges 1 and 7 of dWqkv's 8, 1 and 9 of dWo's 10, 0 and 4 of dW1's 5
     p = synth.init_params(1, d, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab, dtype="bf16",
                           fan_in_std=True, out=np.float32)
     w = p["layers"][0]
     rng_x, rng_dy = np.random.default_rng(3), np.random.default_rng(4)
     x_np = synth.normal((cfg.batch, T, d), 1.0, rng_x, "bf16", np.float32)
     dy_np = np.zeros_like(x_np)
-    dy_np[b] = synth.normal((T, d), 1.0, rng_dy, "bf16", np.float32)
+    dy_np[rows] = synth.normal((len(rows), T, d), 1.0, rng_dy, "bf16", np.float32)
 
     sz = lib.query_sizes(cfg)
     saved = lib.alloc_bytes(sz.block_saved)
@@ -46,59 +58,78 @@ def test_block_full_shape_one_row_gradient():
     lib.block_bwd(cfg, wd, x, saved, dy, dx, gd, scratch)
     torch.cuda.synchronize()
 
-    oc = ocfg(cfg.with_(batch=1))
-    for row in (b, cfg.batch - 1):
-        x_ref, cache = oracle.block_fwd(oc, w, x_np[row:row + 1].astype(np.float64))
-        assert_close(host(x_out.view(cfg.batch, T, d)[row]), x_ref[0], tol["act"], f"x_out[{row}]")
-        if row == b:
-            dx_ref, g_ref = oracle.block_bwd(oc, w, x_np[b:b + 1].astype(np.float64),
-                                             dy_np[b:b + 1].astype(np.float64), cache)
+    print("oracle ...", flush=True)
+    oc = ocfg(cfg.with_(batch=len(rows)))
+    x_ref, cache = oracle.block_fwd(oc, w, x_np[rows].astype(np.float64))
+    dx_ref, g_ref = oracle.block_bwd(oc, w, x_np[rows].astype(np.float64), dy_np[rows].astype(np.float64), cache)
+    errs = {}
+    xo = x_out.view(cfg.batch, T, d)
+    for i, row in enumerate(rows):
+        errs[f"x_out[{row}]"] = assert_close(host(xo[row]), x_ref[i], tol["act"], f"x_out[{row}]")
+    oc1 = ocfg(cfg.with_(batch=1))
+    x_last, _ = oracle.block_fwd(oc1, w, x_np[-1:].astype(np.float64))
+    errs["x_out[31]"] = assert_close(host(xo[cfg.batch - 1]), x_last[0], tol["act"], "x_out[31]")
     dxv = dx.view(cfg.batch, T, d)
-    assert_close(host(dxv[b]), dx_ref[0], tol["grad"], "dx_in[b]")
-    others = torch.cat([dxv[:b], dxv[b + 1:]])
-    assert torch.count_nonzero(others).item() == 0
+    for i, row in enumerate(rows):
+        errs[f"dx_in[{row}]"] = assert_close(host(dxv[row]), dx_ref[i], tol["grad"], f"dx_in[{row}]")
+    keep = torch.ones(cfg.batch, dtype=torch.bool, device="cuda")
+    keep[rows] = False
+    assert torch.count_nonzero(dxv[keep]).item() == 0
     gq, gk, gv = unpack_qkv(host(gd["wqkv"]), cfg)
-    assert_close(gq, g_ref["wq"], tol["grad"], "dWq")
-    assert_close(gk, g_ref["wk"], tol["grad"], "dWk")
-    assert_close(gv, g_ref["wv"], tol["grad"], "dWv")
+    errs["dWq"] = assert_close(gq, g_ref["wq"], tol["grad"], "dWq")
+    errs["dWk"] = assert_close(gk, g_ref["wk"], tol["grad"], "dWk")
+    errs["dWv"] = assert_close(gv, g_ref["wv"], tol["grad"], "dWv")
     for k in ("wo", "w1", "w2"):
-        assert_close(host(gd[k]), g_ref[k], tol["grad"], f"dW{k[1:]}")
+        errs[f"dW{k[1:]}"] = assert_close(host(gd[k]), g_ref[k], tol["grad"], f"dW{k[1:]}")
+    _report("block d20", errs)
 
 
-def _one_row_model(cfg, b, t_valid):
-    """Full-size run with valid targets only on positions < t_valid of row b;
-    returns the GPU run and the oracle's loss/grads on that prefix."""
+def _rows_model(cfg, rows, t_valid):
+    """Full-size run with valid targets only on positions < t_valid of the
+    given rows; returns the GPU run and the oracle's loss/grads on those
+    prefixes."""
     p = synth.init_params(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
                           std=0.02, dtype=cfg.dtype, out=np.float32)
     idx, tg = synth.zipf_tokens(cfg.vocab, cfg.batch, cfg.seq_len)
     tg_masked = np.full_like(tg, -1)
-    tg_masked[b, :t_valid] = tg[b, :t_valid]
+    tg_masked[rows, :t_valid] = tg[rows, :t_valid]
+    print(f"GPU step, rows {rows} ...", flush=True)
     run = ModelRun(cfg, p, idx, tg_masked)
     loss = run.run()
     assert run.status() == 0
-    oc = ocfg(cfg.with_(batch=1, seq_len=t_valid))
-    loss_ref, g_ref = oracle.model_loss_and_grad(oc, p, idx[b:b + 1, :t_valid], tg[b:b + 1, :t_valid])
+    print("oracle ...", flush=True)
+    oc = ocfg(cfg.with_(batch=len(rows), seq_len=t_valid))
+    loss_ref, g_ref = oracle.model_loss_and_grad(oc, p, idx[rows, :t_valid], tg[rows, :t_valid])
     return run, loss, loss_ref, g_ref
 
 
-def _compare_model(cfg, run, loss, loss_ref, g_ref):
+def _compare_model(cfg, run, loss, loss_ref, g_ref, tag):
+    """Checks every tensor, prints each one's error (worst first) and the
+    worst per layer, and returns the largest error and its tensor."""
     tol = TOL[cfg.dtype]
-    assert abs(loss - loss_ref) <= tol["loss"] * abs(loss_ref), (loss, loss_ref)
     g = split_grads(cfg, run.grads.cpu().numpy())
-    assert_close(g["wte"], g_ref["wte"], tol["grad"], "dWte")
-    assert_close(g["wlm"], g_ref["wlm"], tol["grad"], "dWlm")
-    worst = 0.0
+    errs = {"loss": abs(loss - loss_ref) / abs(loss_ref)}
+    errs["dWte"] = assert_close(g["wte"], g_ref["wte"], tol["grad"], "dWte")
+    errs["dWlm"] = assert_close(g["wlm"], g_ref["wlm"], tol["grad"], "dWlm")
+    per_layer = []
     for l, (a, r) in enumerate(zip(g["layers"], g_ref["layers"])):
-        for k in a:
-            worst = max(worst, assert_close(a[k], r[k], tol["grad"], f"d{k}[{l}]"))
-    return worst
+        le = {f"d{k}[{l}]": assert_close(a[k], r[k], tol["grad"], f"d{k}[{l}]") for k in a}
+        errs.update(le)
+        per_layer.append(max(le.values()))
+    assert errs["loss"] <= tol["loss"], (loss, loss_ref)
+    _report(f"{tag} loss {loss:.6f} oracle {loss_ref:.6f}", errs)
+    print(f"{tag} worst per layer: " + " ".join(f"{e:.2e}" for e in per_layer), flush=True)
+    name = max((k for k in errs if k != "loss"), key=lambda k: errs[k])
+    return errs[name], name
 
 
 def test_model_depth20_full_shape():
     cfg = DEPTH20  # 20 layers, B=32 x T=2048, vocab 65536, bf16
-    run, loss, loss_ref, g_ref = _one_row_model(cfg, b=17, t_valid=cfg.seq_len)
-    worst = _compare_model(cfg, run, loss, loss_ref, g_ref)
-    print(f"depth20 loss {loss:.6f} oracle {loss_ref:.6f} worst layer grad err {worst:.3e}")
+    # rows 1 and 30 (first 1024 positions each): token ranges 0 and 7 of dWqkv's 8,
+    # 0 and 9 of dWo's 10, 0 and 4 of dW1's 5
+    run, loss, loss_ref, g_ref = _rows_model(cfg, rows=[1, 30], t_valid=1024)
+    worst, name = _compare_model(cfg, run, loss, loss_ref, g_ref, "depth20")
+    print(f"depth20 worst gradient error {worst:.3e} ({name})")
     # bitwise determinism of the full step
     g1 = run.grads.clone()
     assert run.run() == loss and torch.equal(run.grads, g1)
@@ -106,6 +137,7 @@ def test_model_depth20_full_shape():
 
 def test_model_depth30_full_shape():
     cfg = DEPTH30  # 30 layers, d 1920, 15 x 128 heads, B=16 x T=2048, vocab 65536, bf16
-    run, loss, loss_ref, g_ref = _one_row_model(cfg, b=3, t_valid=512)
-    worst = _compare_model(cfg, run, loss, loss_ref, g_ref)
-    print(f"depth30 loss {loss:.6f} oracle {loss_ref:.6f} worst layer grad err {worst:.3e}")
+    # rows 3 and 12 (first 256 positions each): token ranges 1 and 5 of dWqkv's 7
+    run, loss, loss_ref, g_ref = _rows_model(cfg, rows=[3, 12], t_valid=256)
+    worst, name = _compare_model(cfg, run, loss, loss_ref, g_ref, "depth30")
+    print(f"depth30 worst gradient error {worst:.3e} ({name})")

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import infer
 from dense_pretraining_amd import lib, synth
 from dense_pretraining_amd.config import Config
@@ -168,3 +169,70 @@ def test_long_cache_multi_tile_chunks():
     p = _params(cfg, seed=5)
     prompt, _ = synth.zipf_tokens(cfg.vocab, cfg.batch, 389)
     _run_and_check(cfg, p, prompt, n_steps=4, seed_note="long cache")
+
+
+@pytest.mark.parametrize("pairing", ["adjacent", "far"])
+def test_greedy_ties_go_to_the_lowest_id(pairing):
+    """Exact ties: unembedding rows shared by two ids give both ids bitwise
+    equal logits, so every greedy choice is a tie between twins and must be
+    the lower id (the stated reading for an argmax tie). "adjacent": ids 2i
+    and 2i + 1 (the same 32-column tile of the logit kernel), so every token
+    must be even; "far": ids i and i + V/2 (different tiles, decided by the
+    cross-tile reduction), so every token must be below V/2."""
+    cfg = SHAPES["mqa_d64_bf16"]
+    p = _params(cfg, seed=6)
+    V = cfg.vocab
+    w = p["wlm"]
+    if pairing == "adjacent":
+        w[1::2] = w[0::2]
+    else:
+        w[V // 2:] = w[: V // 2]
+    prompt, _ = synth.zipf_tokens(cfg.vocab, cfg.batch, 9)
+    g, toks = _run_and_check(cfg, p, prompt, n_steps=8, seed_note=f"ties {pairing}")
+    if pairing == "adjacent":
+        assert np.all(toks % 2 == 0), toks
+    else:
+        assert np.all(toks < V // 2), toks
+
+
+def test_depth20_generation_benchmark_shape_sampled():
+    """The inference benchmark's shape: 64 sequences, a 1024-token prompt, then
+    decode steps up to position 1279 (cache capacity 1280). Sequence 0 is
+    checked against the oracle in one forward pass over its 1279 positions
+    (the prompt and the GPU's own tokens): every one of its 256 greedy tokens
+    against the oracle's logits at that position, and its cache rows in
+    layers 0 and 19 (positions 0 .. 1023 written by the prefill, 1024 .. 1278
+    by the decode steps). Full recomputation equals cached decoding in exact
+    arithmetic (pinned in the oracle's own tests)."""
+    n_prompt, n_steps = 1024, 256
+    cfg = Config(depth=20, d_model=1280, n_head=10, head_dim=128, n_kv_head=1, d_ff=5120, vocab=65536, batch=64,
+                 seq_len=n_prompt + n_steps, dtype="bf16")
+    p = synth.init_params(cfg.depth, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.n_kv_head, cfg.d_ff, cfg.vocab,
+                          std=0.02, seed=0, dtype="bf16", out=np.float32)
+    rng = np.random.default_rng(11)
+    p["wlm"] = synth.round_to(rng.standard_normal(p["wlm"].shape) * (2.5 / np.sqrt(cfg.d_model)), "bf16",
+                              out=np.float32)
+    prompt, _ = synth.zipf_tokens(cfg.vocab, cfg.batch, n_prompt)
+    g = Gen(cfg, p)
+    # positions 1024 .. 1278 are decoded: the last step appends position 1278 and
+    # picks the token for 1279, the capacity's last position
+    print("GPU prefill and decode ...", flush=True)
+    toks = g.run(prompt, n_steps - 1)
+    assert lib.read_status(g.ws) == 0
+    print("oracle forward over 1279 positions ...", flush=True)
+    oc = ocfg(cfg.with_(batch=1, seq_len=n_prompt + n_steps - 1))
+    seq = np.concatenate([prompt[:1], toks[:1, :-1]], axis=1)  # [1, 1279]
+    x, _ = oracle.embed_fwd(oc, seq, p["wte"])
+    ks, vs = [], []
+    for w in p["layers"]:
+        x, c = oracle.block_fwd(oc, w, x)
+        ks.append(c["kr"])
+        vs.append(c["v"])
+    z = infer.softcap_logits(oc, x[0, n_prompt - 1:, :], p["wlm"])  # positions 1023 .. 1278: [256, V]
+    for s in range(n_steps):
+        _check_valid(z[s:s + 1], toks[:1, s], MARGIN["bf16"], f"depth20 token after position {n_prompt - 1 + s}")
+    gc = g.cache_np()
+    n = n_prompt + n_steps - 1
+    for l in (0, 19):
+        assert_close(gc[l, 0, :1, :n], ks[l], TOL["bf16"]["act"], f"K cache layer {l}")
+        assert_close(gc[l, 1, :1, :n], vs[l], TOL["bf16"]["act"], f"V cache layer {l}")
