@@ -178,12 +178,10 @@ HeadScratch<T> carve_head_scratch(Carver& c, const Dims& m) {
 }
 
 struct EmbedScratch {
-  float* de;
   void* sort;
 };
 EmbedScratch carve_embed_scratch(Carver& c, const Dims& m) {
   EmbedScratch s;
-  s.de = c.take<float>(m.M * m.d);
   s.sort = c.take<char>(embed_sort_bytes((int)m.M, m.V, m.d));
   return s;
 }
@@ -393,8 +391,7 @@ template <typename T>
 nc_status embed_bwd_t(const Dims& m, const int32_t* idx, const T* x0, const float* r0, const T* dx0, float* dwte,
                       int acc, const EmbedScratch& c, hipStream_t st) {
   const int M = (int)m.M;
-  NC_TRY((rmsnorm_bwd<T, float>(dx0, x0, r0, nullptr, c.de, M, m.d, st)));
-  return embed_scatter(idx, c.de, dwte, M, m.V, m.d, acc, embed_sort_carve(c.sort, M, m.V, m.d), st);
+  return embed_bwd<T>(idx, x0, r0, dx0, dwte, M, m.V, m.d, acc, embed_sort_carve(c.sort, M, m.V, m.d), st);
 }
 
 template <typename T>

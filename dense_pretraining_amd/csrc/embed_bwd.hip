@@ -1,6 +1,11 @@
 // Deterministic embedding-gradient scatter: dWte[v] = sum of de[m] over the
 // positions m with idx[m] = v (the untied token embedding of the architecture
-// list on vpshk.cn; its gradient is a sum of rows, one per occurrence).
+// list on vpshk.cn; its gradient is a sum of rows, one per occurrence), where
+// de = N_bwd(dx0) is the backward of the parameter-free norm that follows the
+// embedding: de = r (dx0 - x0 mean(dx0 x0)). The norm backward is folded into
+// the sums: a first pass keeps two numbers per token (a = r and
+// b = r mean(dx0 x0)), and the window sums form de = a dx0 - b x0 from the
+// stored rows as they read them, so de never reaches memory.
 //
 // No floating-point atomics: the positions are first sorted by (id, m) with a
 // counting sort whose within-id ranks are computed exactly (chunk histograms,
@@ -109,49 +114,105 @@ __global__ void __launch_bounds__(256) eb_place_kernel(const int32_t* __restrict
   }
 }
 
-// Window sums. Thread t owns float4 column groups t, t+256, ...
-__global__ void __launch_bounds__(256) eb_window_kernel(const float* __restrict__ de, int d,
+// Per token, the coefficients of the norm backward: coef[m] = (r, r mean(dx x)),
+// so that de[m] = r dx - (r mean(dx x)) x. One wavefront per token.
+template <typename T>
+__global__ void __launch_bounds__(256) eb_coef_kernel(const T* __restrict__ dx, const T* __restrict__ x,
+                                                      const float* __restrict__ r, int M, int d,
+                                                      float2* __restrict__ coef) {
+  constexpr int VE = Vec<T>::n;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= M) return;  // whole waves leave together
+  const long off = (long)m * d;
+  float dot = 0.f;
+  for (int c = VE * lane; c < d; c += 64 * VE) {
+    float a[VE], b[VE];
+    load16<T>(dx + off + c, a);
+    load16<T>(x + off + c, b);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) dot += a[e] * b[e];
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) {
+    const float rr = r[m];
+    coef[m] = make_float2(rr, rr * dot / (float)d);
+  }
+}
+
+// Window sums of de = a dx - b x over the sorted positions. Thread t owns the
+// VE consecutive columns of 16-byte group t (d <= 256 VE); a window's
+// positions, ids and coefficients are staged in LDS first, and the rows of
+// kBatch positions are loaded before any of them is added.
+constexpr int kBatch = 4;
+template <typename T>
+__global__ void __launch_bounds__(256) eb_window_kernel(const T* __restrict__ dx, const T* __restrict__ x,
+                                                        const float2* __restrict__ coef, int d,
                                                         const int* __restrict__ seg, const int* __restrict__ perm,
                                                         const int* __restrict__ sid, int V, float* __restrict__ dwte,
                                                         float* __restrict__ spill) {
+  constexpr int VE = Vec<T>::n;
+  __shared__ int spos[kWin], sids[kWin];
+  __shared__ float2 scoef[kWin];
   const int w = blockIdx.x;
   const int nvalid = seg[V];
   const int p0 = w * kWin;
   if (p0 >= nvalid) return;
-  const int p1 = min(p0 + kWin, nvalid);
-  const int d4 = d / 4;
-  for (int c4 = threadIdx.x; c4 < d4; c4 += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int cur = sid[p0];
-    for (int p = p0; p < p1; ++p) {
-      const int v = sid[p];
-      if (v != cur) {
-        // flush run of `cur` (it ended inside the window)
-        const int s = seg[cur], e = seg[cur + 1];
-        if (s >= p0 && e <= p1) {
-          float4* o = reinterpret_cast<float4*>(dwte + (long)cur * d) + c4;
-          float4 x = *o;
-          x.x += acc.x; x.y += acc.y; x.z += acc.z; x.w += acc.w;
-          *o = x;
-        } else {
-          reinterpret_cast<float4*>(spill + (long)(2 * w + (s <= p0 ? 0 : 1)) * d)[c4] = acc;
-        }
-        cur = v;
-        acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      const float4 x = reinterpret_cast<const float4*>(de + (long)perm[p] * d)[c4];
-      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  const int n = min(kWin, nvalid - p0);
+  if (threadIdx.x < n) {
+    const int m = perm[p0 + threadIdx.x];
+    spos[threadIdx.x] = m;
+    sids[threadIdx.x] = sid[p0 + threadIdx.x];
+    scoef[threadIdx.x] = coef[m];
+  }
+  __syncthreads();
+  const int c = VE * threadIdx.x;  // first column of this thread's group
+  const bool on = c < d;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  int cur = sids[0];
+  // adds acc to dwte[cur] when its run lies inside the window, else to the
+  // window's spill slot (0: the run started before the window, 1: after)
+  auto flush = [&](int v) {
+    const int s0 = seg[v], e0 = seg[v + 1];
+    float* o = (s0 >= p0 && e0 <= p0 + n) ? dwte + (long)v * d + c
+                                          : spill + (long)(2 * w + (s0 <= p0 ? 0 : 1)) * d + c;
+    const bool add = s0 >= p0 && e0 <= p0 + n;
+#pragma unroll
+    for (int q = 0; q < VE; q += 4) {
+      float4 y = add ? *reinterpret_cast<const float4*>(o + q) : make_float4(0.f, 0.f, 0.f, 0.f);
+      y.x += acc[q]; y.y += acc[q + 1]; y.z += acc[q + 2]; y.w += acc[q + 3];
+      *reinterpret_cast<float4*>(o + q) = y;
     }
-    const int s = seg[cur], e = seg[cur + 1];
-    if (s >= p0 && e <= p1) {
-      float4* o = reinterpret_cast<float4*>(dwte + (long)cur * d) + c4;
-      float4 x = *o;
-      x.x += acc.x; x.y += acc.y; x.z += acc.z; x.w += acc.w;
-      *o = x;
-    } else {
-      reinterpret_cast<float4*>(spill + (long)(2 * w + (s <= p0 ? 0 : 1)) * d)[c4] = acc;
+  };
+  for (int b0 = 0; b0 < n; b0 += kBatch) {
+    float gx[kBatch][VE], xx[kBatch][VE];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (on && b0 + i < n) {
+        const long ro = (long)spos[b0 + i] * d + c;
+        load16<T>(dx + ro, gx[i]);
+        load16<T>(x + ro, xx[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (b0 + i >= n) break;
+      const int v = sids[b0 + i];
+      if (v != cur) {
+        if (on) flush(cur);
+        cur = v;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+      }
+      const float2 k = scoef[b0 + i];
+      if (on) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] += k.x * gx[i][e] - k.y * xx[i][e];
+      }
     }
   }
+  if (on) flush(cur);
 }
 
 // Segments spanning windows: block w owns the segment whose first crossed
@@ -191,44 +252,58 @@ size_t embed_sort_bytes(int M, int V, int d) {
   b += align_up(nch * V * sizeof(int), 256);
   b += align_up((size_t)(V + 1) * sizeof(int), 256);
   b += 2 * align_up((size_t)M * sizeof(int), 256);
+  b += align_up((size_t)M * sizeof(float2), 256);
   b += align_up(nwin * 2 * d * sizeof(float), 256);
   return b;
 }
 
 EmbedSortBufs embed_sort_carve(void* base, int M, int V, int d) {
   size_t nch = (size_t)(M + kChunk - 1) / kChunk;
-  size_t nwin = (size_t)(M + kWin - 1) / kWin;
   char* p = static_cast<char*>(base);
   EmbedSortBufs b;
   b.hist = reinterpret_cast<int*>(p); p += align_up(nch * V * sizeof(int), 256);
   b.seg = reinterpret_cast<int*>(p); p += align_up((size_t)(V + 1) * sizeof(int), 256);
   b.perm = reinterpret_cast<int*>(p); p += align_up((size_t)M * sizeof(int), 256);
   b.sid = reinterpret_cast<int*>(p); p += align_up((size_t)M * sizeof(int), 256);
+  b.coef = reinterpret_cast<float2*>(p); p += align_up((size_t)M * sizeof(float2), 256);
   b.spill = reinterpret_cast<float*>(p);
   return b;
 }
 
-nc_status embed_scatter(const int32_t* idx, const float* de, float* dwte, int M, int V, int d, int accumulate,
-                        const EmbedSortBufs& b, hipStream_t st) {
+template <typename T>
+nc_status embed_bwd(const int32_t* idx, const T* x0, const float* r0, const T* dx0, float* dwte, int M, int V, int d,
+                    int accumulate, const EmbedSortBufs& b, hipStream_t st) {
+  if (d % Vec<T>::n != 0 || d > 256 * Vec<T>::n) return NC_ERR_UNSUPPORTED;
   const int nch = (M + kChunk - 1) / kChunk;
   const int nwin = (M + kWin - 1) / kWin;
   NC_TRY(fill_u32(reinterpret_cast<uint32_t*>(b.hist), 0u, (size_t)nch * V, st));
   if (!accumulate) NC_TRY(fill_f32(dwte, 0.f, (size_t)V * d, st));
+  const double es = sizeof(T);
   {
-  ProfScope prof("embed_sort", 0, 4.0 * M * 5 + 8.0 * nch * V, st);
-  hipLaunchKernelGGL(eb_hist_kernel, dim3((M + 255) / 256), dim3(256), 0, st, idx, M, V, b.hist);
-  NC_LAUNCH_CHECK("eb_hist");
-  hipLaunchKernelGGL(eb_colscan_kernel, dim3((V + 255) / 256), dim3(256), 0, st, b.hist, nch, V, b.seg);
-  NC_LAUNCH_CHECK("eb_colscan");
-  hipLaunchKernelGGL(eb_scan_kernel, dim3(1), dim3(1024), 0, st, b.seg, V);
-  NC_LAUNCH_CHECK("eb_scan");
-  hipLaunchKernelGGL(eb_place_kernel, dim3(nch), dim3(256), 0, st, idx, M, V, b.hist, b.seg, b.perm, b.sid);
-  NC_LAUNCH_CHECK("eb_place");
+    // the norm backward's per-token coefficients: dx0 and x0 read once
+    ProfScope prof(NC_NAME(T, "embed_norm_coef"), 0, 2.0 * es * M * d + 12.0 * M, st);
+    hipLaunchKernelGGL((eb_coef_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, dx0, x0, r0, M, d, b.coef);
+    NC_LAUNCH_CHECK("eb_coef");
   }
   {
-  ProfScope prof("embed_window_sum", 0, 4.0 * M * d + 8.0 * M + 4.0 * (double)d * M, st);
-  hipLaunchKernelGGL(eb_window_kernel, dim3(nwin), dim3(256), 0, st, de, d, b.seg, b.perm, b.sid, V, dwte, b.spill);
-  NC_LAUNCH_CHECK("eb_window");
+    ProfScope prof("embed_sort", 0, 4.0 * M * 5 + 8.0 * nch * V, st);
+    hipLaunchKernelGGL(eb_hist_kernel, dim3((M + 255) / 256), dim3(256), 0, st, idx, M, V, b.hist);
+    NC_LAUNCH_CHECK("eb_hist");
+    hipLaunchKernelGGL(eb_colscan_kernel, dim3((V + 255) / 256), dim3(256), 0, st, b.hist, nch, V, b.seg);
+    NC_LAUNCH_CHECK("eb_colscan");
+    hipLaunchKernelGGL(eb_scan_kernel, dim3(1), dim3(1024), 0, st, b.seg, V);
+    NC_LAUNCH_CHECK("eb_scan");
+    hipLaunchKernelGGL(eb_place_kernel, dim3(nch), dim3(256), 0, st, idx, M, V, b.hist, b.seg, b.perm, b.sid);
+    NC_LAUNCH_CHECK("eb_place");
+  }
+  {
+    // counted: dx0 and x0 rows once, positions, ids and coefficients. The
+    // read-modify-write of the distinct ids' dWte rows (unknown to the host)
+    // and the spill slots are left out, so the rate is a lower bound.
+    ProfScope prof(NC_NAME(T, "embed_window_sum"), 0, 2.0 * es * M * d + 16.0 * M, st);
+    hipLaunchKernelGGL((eb_window_kernel<T>), dim3(nwin), dim3(256), 0, st, dx0, x0, b.coef, d, b.seg, b.perm,
+                       b.sid, V, dwte, b.spill);
+    NC_LAUNCH_CHECK("eb_window");
   }
   if (nwin > 1) {
     ProfScope prof("embed_fixup", 0, 0, st);
@@ -237,5 +312,10 @@ nc_status embed_scatter(const int32_t* idx, const float* de, float* dwte, int M,
   }
   return NC_OK;
 }
+
+template nc_status embed_bwd<bf16>(const int32_t*, const bf16*, const float*, const bf16*, float*, int, int, int, int,
+                                   const EmbedSortBufs&, hipStream_t);
+template nc_status embed_bwd<float>(const int32_t*, const float*, const float*, const float*, float*, int, int, int,
+                                    int, const EmbedSortBufs&, hipStream_t);
 
 }  // namespace nc

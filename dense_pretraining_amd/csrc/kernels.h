@@ -216,12 +216,16 @@ struct EmbedSortBufs {
   int* seg;       // [V + 1] segment starts (exclusive scan of counts)
   int* perm;      // [M] token positions sorted by (id, position)
   int* sid;       // [M] ids in sorted order
+  float2* coef;   // [M] the norm backward's (r, r mean(dx0 x0)) per token
   float* spill;   // [n_windows * 2 * d]
 };
 size_t embed_sort_bytes(int M, int V, int d);
 EmbedSortBufs embed_sort_carve(void* base, int M, int V, int d);
-// dwte[v] (+)= sum over m with idx[m] = v of de[m]; de float [M,d].
-nc_status embed_scatter(const int32_t* idx, const float* de, float* dwte, int M, int V, int d, int accumulate,
-                        const EmbedSortBufs& b, hipStream_t st);
+// dwte[v] (+)= sum over m with idx[m] = v of de[m], de = N_bwd(dx0) the
+// backward of x0 = N(Wte[idx]) (x0 and r0 as the forward stored them), formed
+// on the fly. d <= 256 * 16 / sizeof(T).
+template <typename T>
+nc_status embed_bwd(const int32_t* idx, const T* x0, const float* r0, const T* dx0, float* dwte, int M, int V, int d,
+                    int accumulate, const EmbedSortBufs& b, hipStream_t st);
 
 }  // namespace nc

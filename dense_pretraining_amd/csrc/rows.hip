@@ -549,7 +549,5 @@ nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, 
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST
-template nc_status rmsnorm_bwd<bf16, float>(const bf16*, const bf16*, const float*, const bf16*, float*, int, int,
-                                            hipStream_t);
 
 }  // namespace nc

@@ -149,9 +149,13 @@ nc_status nc_embed_fwd(const nc_config* cfg, const int32_t* idx, const void* wte
                        float* r0, void* scratch, void* stream);
 
 /* Backward of nc_embed_fwd: de = N_bwd(dx0) = r0 * (dx0 - x0 * mean(dx0 * x0)),
- * dWte[v] = sum over m with idx[m] = v of de[m], summed in increasing m for
- * every v (deterministic). dwte float [V,d]: overwritten, or added to when
- * accumulate != 0 (rows of ids absent from idx are then left unchanged). */
+ * dWte[v] = sum over m with idx[m] = v of de[m], in a fixed order: the
+ * positions sorted by (id, m) are cut into windows of 64; inside a window a
+ * run of equal ids is summed in increasing m, and an id whose run crosses
+ * windows adds its per-window partial sums in window order. The result is
+ * bitwise deterministic for fixed inputs. dwte float [V,d]: overwritten, or
+ * added to when accumulate != 0 (rows of ids absent from idx are then left
+ * unchanged). */
 nc_status nc_embed_bwd(const nc_config* cfg, const int32_t* idx, const void* x0, const float* r0,
                        const void* dx0, float* dwte, int accumulate, void* scratch, void* stream);
 
