@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnc.so")
-SOURCES = ["api.hip", "gemm.hip", "rows.hip", "attn.hip", "embed_bwd.hip", "infer.hip", "skinny.hip", "opt.hip", "fp8.hip", "prof.hip", "products.hip"]
+SOURCES = ["api.hip", "gemm.hip", "rows.hip", "attn.hip", "embed_bwd.hip", "infer.hip", "skinny.hip", "opt.hip", "fp8.hip", "prof.hip", "products.hip", "noalloc.hip"]
 HEADERS = ["common.h", "frag.h", "gemm.h", "kernels.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

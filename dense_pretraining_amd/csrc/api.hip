@@ -512,6 +512,42 @@ InferBufs<T> carve_infer(void* ws, const Dims& m) {
   return b;
 }
 
+// The decode step's buffers alone, carved from base with nothing before them:
+// the rotation row of the step's position, one row per sequence of each
+// activation, the attention partials, the few-row products' split partials
+// and the logit maxima (the decode part of carve_infer, without the status
+// word and the prompt pass).
+template <typename T>
+InferBufs<T> carve_decode(void* base, const Dims& m) {
+  InferBufs<T> b{};
+  Carver cd(base);
+  const long B = m.B;
+  b.cs = cd.take<float>((size_t)m.D / 2);
+  b.sn = cd.take<float>((size_t)m.D / 2);
+  b.x = cd.take<T>(B * m.d);
+  b.qk = cd.take<T>(B * m.QK);
+  b.o = cd.take<T>(B * m.HD);
+  b.x1 = cd.take<T>(B * m.d);
+  b.act = cd.take<T>(B * m.F);
+  b.r = cd.take<float>(B);
+  const int nch = attn_decode_chunks(m.T);
+  b.po = cd.take<float>((size_t)B * nch * m.H * m.D);
+  b.pl = cd.take<float>((size_t)B * nch * m.H);
+  // split partials: the QKV product always writes them (qkv_finish sums them),
+  // the others only when their reduction is split
+  size_t pe = skinny_part_elems((int)B, m.QKV, m.d);
+  const int shapes[4][2] = {{m.d, m.HD}, {m.F, m.d}, {m.d, m.F}, {m.V, m.d}};
+  for (auto& nk : shapes) {
+    const size_t e = skinny_plan((int)B, nk[0], nk[1]).nsplit > 1 ? skinny_part_elems((int)B, nk[0], nk[1]) : 0;
+    pe = e > pe ? e : pe;
+  }
+  b.part = cd.take<float>(pe);
+  b.part_elems = pe;
+  b.cand = cd.take<float2>((size_t)B * skinny_col_tiles(m.V));
+  b.bytes = cd.used;
+  return b;
+}
+
 nc_status infer_dims(const nc_config* cfg, Dims* m) {
   NC_TRY(make_dims(cfg, m, true));
   if (m->fp8) return NC_ERR_UNSUPPORTED;
@@ -570,13 +606,13 @@ nc_status prefill_t(const Dims& m, const T* params, const int32_t* idx, int n_pr
                        next_tok, st);
 }
 
+// One decode step on the buffers b (carve_infer or carve_decode); bad token
+// ids set bits of *status when status is not null.
 template <typename T>
 nc_status decode_t(const Dims& m, const T* params, const int32_t* tok, int pos, void* cache, int32_t* next_tok,
-                   void* ws, hipStream_t st) {
+                   const InferBufs<T>& b, uint32_t* status, hipStream_t st) {
   std::vector<size_t> off(2 + 4 * (size_t)m.L);
   param_offsets(m, off.data());
-  uint32_t* status = static_cast<uint32_t*>(ws);
-  const InferBufs<T> b = carve_infer<T>(ws, m);
   const int B = m.B;
   NC_TRY(rope_table(b.cs, b.sn, 1, m.D, m.base, st, pos));  // the one row of position pos
   const int qkv_split = skinny_plan(B, m.QKV, m.d).nsplit;
@@ -664,6 +700,32 @@ nc_status opt_step_t(const Dims& m, const nc_opt_hparams& h, T* params, const fl
 }
 
 }  // namespace
+
+// The decode step on one caller-supplied buffer holding only its own scratch
+// (carve_decode), for the allocation-free entry point: checks the arguments
+// like nc_decode_step and reports the bytes needed in *need. With buf NULL it
+// stops there (a query: nothing touches the device); otherwise it launches
+// only when buf holds that many bytes.
+nc_status decode_step_on(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
+                         int32_t* next_tok, uint32_t* status, void* buf, size_t buf_bytes, size_t* need,
+                         hipStream_t st) {
+  Dims m;
+  NC_TRY(infer_dims(cfg, &m));
+  if (!params || !tok || !cache || !next_tok || !need) return NC_ERR_INVALID_ARG;
+  if (pos < 1 || pos >= m.T) return NC_ERR_SHAPE;
+  if (!aligned(params) || !aligned(tok) || !aligned(cache) || !aligned(next_tok) || !aligned(buf) ||
+      (status && (reinterpret_cast<uintptr_t>(status) & 3u)))
+    return NC_ERR_ALIGN;
+  *need = m.es == 2 ? carve_decode<bf16>(nullptr, m).bytes : carve_decode<float>(nullptr, m).bytes;
+  if (!buf) return NC_OK;
+  if (buf_bytes < *need) return NC_ERR_WORKSPACE;
+  if (m.es == 2)
+    return decode_t<bf16>(m, static_cast<const bf16*>(params), tok, pos, cache, next_tok, carve_decode<bf16>(buf, m),
+                          status, st);
+  return decode_t<float>(m, static_cast<const float*>(params), tok, pos, cache, next_tok, carve_decode<float>(buf, m),
+                         status, st);
+}
+
 }  // namespace nc
 
 using namespace nc;
@@ -912,10 +974,12 @@ nc_status nc_decode_step(const nc_config* cfg, const void* params, const int32_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (m.es == 2) {
     if (workspace_bytes < carve_infer<bf16>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
-    return decode_t<bf16>(m, static_cast<const bf16*>(params), tok, pos, cache, next_tok, workspace, st);
+    return decode_t<bf16>(m, static_cast<const bf16*>(params), tok, pos, cache, next_tok,
+                          carve_infer<bf16>(workspace, m), static_cast<uint32_t*>(workspace), st);
   }
   if (workspace_bytes < carve_infer<float>(nullptr, m).bytes) return NC_ERR_WORKSPACE;
-  return decode_t<float>(m, static_cast<const float*>(params), tok, pos, cache, next_tok, workspace, st);
+  return decode_t<float>(m, static_cast<const float*>(params), tok, pos, cache, next_tok,
+                         carve_infer<float>(workspace, m), static_cast<uint32_t*>(workspace), st);
 }
 
 nc_status nc_opt_query_sizes(const nc_config* cfg, nc_opt_sizes* out) {

@@ -119,6 +119,12 @@ nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, 
 nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st);
 
 // ------------------------------------------------------------ inference (infer.hip)
+// One decode step (nc_decode_step's kernels) on a caller buffer holding only
+// the step's own scratch (api.hip); *need receives the bytes it takes, and
+// nothing is launched when buf_bytes is smaller (NC_ERR_WORKSPACE).
+nc_status decode_step_on(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
+                         int32_t* next_tok, uint32_t* status, void* buf, size_t buf_bytes, size_t* need,
+                         hipStream_t st);
 // cache[b][pos0 + t] <- rows b * Tsrc + t of k and v (G*D columns each).
 template <typename T>
 nc_status kv_store(const T* k, long ldk, const T* v, long ldv, T* ck, T* cv, int B, int Tsrc, int pos0, int cap,

@@ -36,7 +36,7 @@ EXPORTED = [
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
     "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_opt_query_sizes",
     "nc_opt_init", "nc_opt_step", "nc_profile_enable", "nc_profile_only", "nc_profile_summary",
-    "nc_gemm_scratch_size", "nc_gemm",
+    "nc_gemm_scratch_size", "nc_gemm", "nc_decode_step_noalloc",
 ]
 
 
@@ -125,6 +125,7 @@ def load(path=LIB_PATH):
         "nc_infer_query_sizes": ([cfgp, C.POINTER(NcInferSizes)], I),
         "nc_prefill": ([cfgp, P, P, I, P, P, P, S, P], I),
         "nc_decode_step": ([cfgp, P, P, I, P, P, P, S, P], I),
+        "nc_decode_step_noalloc": ([cfgp, P, P, I, P, P, P, P], I),
         "nc_opt_query_sizes": ([cfgp, C.POINTER(NcOptSizes)], I),
         "nc_opt_init": ([cfgp, P, P, P], I),
         "nc_opt_step": ([cfgp, C.POINTER(NcOptHparams), P, P, P, P, S, P], I),
@@ -340,6 +341,14 @@ def decode_step(cfg, params, tok, pos, cache, next_tok, workspace, stream=None):
     _check(load().nc_decode_step(C.byref(c), _p(params), _p(tok), int(pos), _p(cache), _p(next_tok),
                                  _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "nc_decode_step")
+
+
+def decode_step_noalloc(cfg, params, tok, pos, cache, next_tok, status=None, stream=None):
+    """nc_decode_step with the library's static scratch (no workspace);
+    status: an optional device uint32 tensor the bad-token bit is OR-ed into."""
+    c = to_nc_config(cfg)
+    _check(load().nc_decode_step_noalloc(C.byref(c), _p(params), _p(tok), int(pos), _p(cache), _p(next_tok),
+                                         _p(status), _stream(stream)), "nc_decode_step_noalloc")
 
 
 # ------------------------------------------------------------------ optimizer

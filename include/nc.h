@@ -302,6 +302,24 @@ nc_status nc_prefill(const nc_config* cfg, const void* params, const int32_t* id
 nc_status nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
                          int32_t* next_tok, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The decode step for callers that cannot allocate device memory or hand
+ * over a workspace (code under graph capture, tight serving loops): the same
+ * kernels as nc_decode_step, with their scratch in a static device array of
+ * NC_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds from the
+ * library's load to the end of the process. It calls no allocating routine.
+ * The scratch holds one row per sequence of every activation, the attention
+ * partials (batch * ceil(seq_len / 64) * n_head * (head_dim + 1) floats) and
+ * the logit maxima: about 10 MB at 64 sequences of the depth-20 shape with a
+ * 1280-position cache. Arguments as nc_decode_step; status (device, may be
+ * NULL) receives NC_STATUS_BAD_TOKEN (OR-ed in) for a token id outside
+ * [0, vocab). NC_ERR_WORKSPACE (before any launch) when the configuration
+ * needs more scratch than the array holds. Every call on one GPU shares that
+ * GPU's array and leaves its contents behind: calls that overlap on one GPU
+ * (two streams, two threads) race and must be serialised by the caller. */
+#define NC_NOALLOC_SCRATCH_BYTES (32u << 20)
+nc_status nc_decode_step_noalloc(const nc_config* cfg, const void* params, const int32_t* tok, int pos, void* cache,
+                                 int32_t* next_tok, uint32_t* status, void* stream);
+
 /* ---------------------------------------------------------------- optimizer
  * The optimizer step (the page on vpshk.cn, Q&A section "卡帕西亲自揭秘背后技术",
  * names Muon + AdamW; imeisheng.com, section "预训练": Muon for the matrices,
