@@ -104,23 +104,72 @@ def measured_traffic(scope):
     return None
 
 
-def cpu_baseline(cfg, p, idx, tg, tokens):
-    """The fp64 oracle, untuned, on one sequence of `tokens` positions of the
-    same model (all blocks, full vocabulary): tokens per second."""
-    import oracle
+def host_info():
+    """The host's CPU model (lscpu), its usable cores and the BLAS library
+    NumPy calls, for the cpu_baseline record."""
+    import subprocess
     from threadpoolctl import threadpool_info
 
-    T = min(tokens, cfg.seq_len)
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for line in fh:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            model = "unknown"
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '?')})"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    return dict(cpu=model, nproc=len(os.sched_getaffinity(0)), blas=", ".join(blas) or "unknown")
+
+
+def _oracle_time(cfg, p, idx, tg, T, threads=None):
+    """Wall time of the oracle's forward+backward over row 0's first T tokens."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     oc = oracle.Cfg(depth=cfg.depth, d_model=cfg.d_model, n_head=cfg.n_head, head_dim=cfg.head_dim,
                     n_kv_head=cfg.n_kv_head, d_ff=cfg.d_ff, vocab=cfg.vocab, batch=1, seq_len=T,
                     softcap=cfg.softcap, rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
-    t0 = time.perf_counter()
-    oracle.model_loss_and_grad(oc, p, idx[:1, :T], tg[:1, :T])
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return dict(value=round(T / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"fp64 NumPy oracle, forward+backward of the same {cfg.depth}-layer model over one "
-                       f"sequence of {T} tokens (full vocabulary), {dt:.1f} s wall on {threads} BLAS threads")
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        oracle.model_loss_and_grad(oc, p, idx[:1, :T], tg[:1, :T])
+        dt = time.perf_counter() - t0
+    return dt, int(used)
+
+
+def cpu_baseline(cfg, p, idx, tg, tokens, tokens_1t):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload: one
+    of the batch's rows (T tokens, all blocks, the full vocabulary) on every
+    host core the BLAS library uses, and a shorter row on one thread. Every
+    cost of the oracle is linear in the number of rows at a fixed T, so the
+    full batch takes `batch` times the first sample's time."""
+    info = host_info()
+    T = min(tokens, cfg.seq_len)
+    dt, used = _oracle_time(cfg, p, idx, tg, T)
+    rec = dict(value=round(T / dt, 2), unit="tokens/s", cores=used, kind="oracle",
+               sample=f"fp64 NumPy oracle, forward+backward of the same {cfg.depth}-layer model over one of the "
+                      f"batch's {cfg.batch} rows ({T} tokens, full vocabulary): {dt:.1f} s wall on {used} BLAS "
+                      f"threads",
+               full_batch_s_extrapolated=round(dt * cfg.batch * cfg.seq_len / T, 1) if T == cfg.seq_len else None,
+               **info)
+    if tokens_1t > 0:
+        T1 = min(tokens_1t, cfg.seq_len)
+        dt1, _ = _oracle_time(cfg, p, idx, tg, T1, threads=1)
+        rec["single_thread"] = dict(value=round(T1 / dt1, 2), unit="tokens/s", cores=1,
+                                    sample=f"one row of {T1} tokens on 1 thread: {dt1:.1f} s wall")
+    return rec
 
 
 def decode_bytes(cfg, n):
@@ -364,8 +413,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["infer", "opt"], default="depth20",
                     help="training step (depth20, depth30, depth20_fp8), KV-cache generation (infer) or the optimizer step (opt)")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
-                    help="sequence length of the oracle sample for cpu_baseline (0 skips it)")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="sequence length of the oracle sample for cpu_baseline, one row on every core (0 skips "
+                         "the CPU baseline)")
+    ap.add_argument("--cpu-tokens-1t", type=int, default=256,
+                    help="sequence length of the single-thread oracle sample (0 skips it)")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="no per-kernel HIP events: no kernel table, no roofline")
     ap.add_argument("--table-steps", type=int, default=2,
@@ -438,15 +490,18 @@ def main():
     torch.cuda.synchronize()
     if timing:
         lib.profile_enable(True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # one event at every step boundary (on the stream the library launches on):
+    # the per-step median, minimum and maximum beside the timed region's mean
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(a.steps):
+    ev[0].record()
+    for i in range(a.steps):
         step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    e0, e1 = ev[0], ev[-1]
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps))
     if timing:
         lib.profile_enable(False)
         live = kernel_table(lib.profile_summary(), a.steps)
@@ -484,6 +539,8 @@ def main():
         "mfu": round(tps * f_causal / PEAK_BF16, 4),
         "mfu_palm": round(tps * f_palm / PEAK_BF16, 4),
         "loss": round(float(loss.item()), 6),
+        "step_ms": {"median": round(float(np.median(per_step)), 3), "min": round(per_step[0], 3),
+                    "max": round(per_step[-1], 3)},
     }
     if timing:
         name, rl = roofline(live)
@@ -496,7 +553,7 @@ def main():
         out["kernel_ms_sum"] = round(sum(v["ms_per_step"] for v in table.values()), 3)
     if a.cpu_tokens > 0:
         print("# timing the CPU oracle sample ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, p, idx, tg, a.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, p, idx, tg, a.cpu_tokens, a.cpu_tokens_1t)
     print(json.dumps(out), flush=True)
 
 
