@@ -19,7 +19,12 @@ nc_status gemm_args_ok(const nc_gemm_args* a) {
   // 16-byte operand chunks: every row length and every K-outer row count a multiple of 8
   if (a->K % 8 != 0 || (a->kind != NC_GEMM_GRAM && a->N % 8 != 0)) return NC_ERR_UNSUPPORTED;
   const long M = a->M, N = a->kind == NC_GEMM_GRAM ? a->K : a->N, K = a->K;
-  if (M * N > 0x7fffffffL || M * K > 0x7fffffffL || N * K > 0x7fffffffL) return NC_ERR_UNSUPPORTED;
+  // the [M, N] logits of the softcap product and a panelled a (the logit
+  // gradient) are addressed per 32-column panel, as the unembedding does
+  const bool panel_mn = a->kind == NC_GEMM_SOFTCAP || a->a_panels;
+  if ((!panel_mn && M * N > 0x7fffffffL) || M * K > 0x7fffffffL || N * K > 0x7fffffffL) return NC_ERR_UNSUPPORTED;
+  if (a->kind == NC_GEMM_SOFTCAP && (M * kPanel * 8 * 2 > 0x7fffffffL || M * kPanel >= (1L << 24)))
+    return NC_ERR_UNSUPPORTED;
   if (a->a_panels && a->kind != NC_GEMM_DYW && a->kind != NC_GEMM_DW) return NC_ERR_INVALID_ARG;
   if (a->a_panels && (M * kPanel * 8 * 4 > 0x7fffffffL || M * kPanel >= (1L << 24))) return NC_ERR_UNSUPPORTED;
   const bool want_y = a->kind != NC_GEMM_DW;
