@@ -643,7 +643,9 @@ struct DkdvShape {
   static_assert((2 * NQI) % WAVES == 0, "tile loads split evenly over the waves");
 };
 
-template <typename T, int D>
+// UP: the query tiles run from the key block's diagonal upwards, else from
+// the last row down.
+template <typename T, int D, bool UP = false>
 struct DkdvCtx {
   using Sh = DkdvShape<T, D>;
   int nrows, r_start, ntiles, T_, kw0, lane, wave, kw;
@@ -662,7 +664,7 @@ struct DkdvCtx {
   int nr[Sh::NPW], nh[Sh::NPW], noff[Sh::NPW];
   int dr, dstep[Sh::NPW], wrap[Sh::NPW];
 
-  __device__ __forceinline__ int row0(int s) const { return r_start + Sh::BQ * (ntiles - 1 - s); }
+  __device__ __forceinline__ int row0(int s) const { return r_start + Sh::BQ * (UP ? s : ntiles - 1 - s); }
 
   // The state for step 0, once (n_rep, hbase, lrow, lcol, ldo, ld_* set).
   __device__ __forceinline__ void init_rows() {
@@ -689,13 +691,23 @@ struct DkdvCtx {
 #pragma unroll
     for (int i = 0; i < Sh::NPW; ++i) {
       const unsigned off = (live && nr[i] < nrows) ? (unsigned)noff[i] : kDmaOOB;
-      // the same load of the next tile: BQ rows up = dq positions and dr heads, with a borrow
-      nr[i] -= Sh::BQ;
-      nh[i] -= dr;
-      noff[i] -= dstep[i];
-      const bool borrow = nh[i] < 0;
-      nh[i] += borrow ? n_rep : 0;
-      noff[i] += borrow ? wrap[i] : 0;
+      // the same load of the next tile, BQ rows = dq positions and dr heads away:
+      // down with a borrow, or up with a carry
+      if constexpr (UP) {
+        nr[i] += Sh::BQ;
+        nh[i] += dr;
+        noff[i] += dstep[i];
+        const bool carry = nh[i] >= n_rep;
+        nh[i] -= carry ? n_rep : 0;
+        noff[i] -= carry ? wrap[i] : 0;
+      } else {
+        nr[i] -= Sh::BQ;
+        nh[i] -= dr;
+        noff[i] -= dstep[i];
+        const bool borrow = nh[i] < 0;
+        nh[i] += borrow ? n_rep : 0;
+        noff[i] += borrow ? wrap[i] : 0;
+      }
       T* dst = (ldo[i] ? sd : sq) + lblk[i] * 64 * Sh::VE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ldo[i] ? rd : rq, (lds_void*)dst, 16, off, 0, 0, 0);
     }
@@ -720,8 +732,8 @@ struct DkdvCtx {
 };
 
 // P side of sub-tile u (32 rows) of step s: S = Q K^T, P, hand P over, dV += P^T dO.
-template <typename T, int D>
-__device__ __forceinline__ void dkdv_tile_p(const DkdvCtx<T, D>& c, int s, int u, const T* __restrict__ sq,
+template <typename T, int D, typename Ctx>
+__device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T* __restrict__ sq,
                                             const T* __restrict__ sdo, const float* __restrict__ st, F8<T>* pb,
                                             f32x16* acc, const F8<T>* kf, float c1) {
   if (c.skip(s, u)) return;
@@ -768,8 +780,8 @@ __device__ __forceinline__ void dkdv_tile_p(const DkdvCtx<T, D>& c, int s, int u
 }
 
 // dS side of sub-tile u of step s: dP = dO V^T, dS = P (dP - Delta), dK += dS^T Q.
-template <typename T, int D>
-__device__ __forceinline__ void dkdv_tile_ds(const DkdvCtx<T, D>& c, int s, int u, const T* __restrict__ sq,
+template <typename T, int D, typename Ctx>
+__device__ __forceinline__ void dkdv_tile_ds(const Ctx& c, int s, int u, const T* __restrict__ sq,
                                              const T* __restrict__ sdo, const float* __restrict__ st,
                                              const F8<T>* pb, f32x16* acc, const F8<T>* vf) {
   if (c.skip(s, u)) return;
@@ -826,8 +838,8 @@ __device__ __forceinline__ void dkdv_tile_ds(const DkdvCtx<T, D>& c, int s, int 
     }                                                                                                      \
   }
 
-template <int ROLE, typename T, int D>
-__device__ __forceinline__ void dkdv_ring(DkdvCtx<T, D>& c, f32x16* acc, const F8<T>* kv, F8<T>* pb,
+template <int ROLE, typename T, int D, typename Ctx>
+__device__ __forceinline__ void dkdv_ring(Ctx& c, f32x16* acc, const F8<T>* kv, F8<T>* pb,
                                           float c1, T* __restrict__ q0, T* __restrict__ q1, T* __restrict__ q2,
                                           T* __restrict__ q3, T* __restrict__ d0, T* __restrict__ d1,
                                           T* __restrict__ d2, T* __restrict__ d3, float* __restrict__ t0,
@@ -862,29 +874,21 @@ __device__ __forceinline__ void dkdv_ring(DkdvCtx<T, D>& c, f32x16* acc, const F
 }
 #undef NC_DKDV_STEP
 
-template <typename T, int D>
-__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const T* __restrict__ qk,
-                                                               const T* __restrict__ vsrc, const T* __restrict__ dO,
-                                                               const float2* __restrict__ rowstat,
-                                                               T* __restrict__ dk, T* __restrict__ dv, long ld_dkv) {
+// One key block of the dK/dV pass (kblk), its query tiles walked down or up.
+template <typename T, int D, bool UP>
+__device__ __forceinline__ void dkdv_part(const AttnGeom& g, const T* __restrict__ qk, const T* __restrict__ vsrc,
+                                          const T* __restrict__ dO, const float2* __restrict__ rowstat,
+                                          T* __restrict__ dk, T* __restrict__ dv, long ld_dkv, int kblk, int kvh, int b,
+                                          long tok0, int role, int lane, int lh, int l32, int wave, float c1,
+                                          T* __restrict__ q0, T* __restrict__ q1, T* __restrict__ q2,
+                                          T* __restrict__ q3, T* __restrict__ d0, T* __restrict__ d1,
+                                          T* __restrict__ d2, T* __restrict__ d3, float* __restrict__ t0,
+                                          float* __restrict__ t1, float* __restrict__ t2, float* __restrict__ t3,
+                                          F8<T>* pb) {
   using Sh = DkdvShape<T, D>;
-  __shared__ __align__(16) T q0[Sh::TILE], q1[Sh::TILE], q2[Sh::TILE], q3[Sh::STAGES == 4 ? Sh::TILE : 1];
-  __shared__ __align__(16) T d0[Sh::TILE], d1[Sh::TILE], d2[Sh::TILE], d3[Sh::STAGES == 4 ? Sh::TILE : 1];
-  __shared__ __align__(16) float t0[64 * Sh::NSUB * Sh::WAVES], t1[64 * Sh::NSUB * Sh::WAVES],
-      t2[64 * Sh::NSUB * Sh::WAVES], t3[Sh::STAGES == 4 ? 64 * Sh::NSUB * Sh::WAVES : 1];
-  // P hand-over: [parity][sub-tile][key group][half][lane]
-  __shared__ __align__(16) F8<T> pb[2 * 512 * Sh::NSUB];
-
-  const int tid = threadIdx.x, lane = tid & 63, lh = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets and buffer resources
-  const int per = g.G * g.B;
-  const int kblk = (int)(blockIdx.x / per);  // key block 0 sees every query row: first
-  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
-  const long tok0 = (long)b * g.T;
   const int kb0 = kblk * 128;
-  const int role = wave >> 2;
 
-  DkdvCtx<T, D> c;
+  DkdvCtx<T, D, UP> c;
   c.lane = lane;
   c.wave = wave;
   c.kw = wave & 3;
@@ -927,7 +931,6 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-  const float c1 = kLog2e / sqrtf((float)D);
 
   if (role == 0) dkdv_ring<0, T, D>(c, acc, kv, pb, c1, q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3);
   else dkdv_ring<1, T, D>(c, acc, kv, pb, c1, q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3);
@@ -940,6 +943,50 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const
 #pragma unroll
       for (int v = 0; v < 16; ++v) out[32 * dti + crow(v, lh)] = from_f32<T>(acc[dti][v] * sc);
   }
+  // every wave is done with the ring and the hand-over buffers before the
+  // next key block's loads overwrite them
+  __syncthreads();
+}
+
+// Block p of a (sequence, KV head) takes two key blocks, p and nkb - 1 - p:
+// their causal work adds up to the same for every p, so the grid of
+// ceil(nkb / 2) blocks per sequence has no tail. The first key block walks
+// the query tiles from the last row down, the second from its diagonal up.
+// All first parts of a sequence start together on the last row; the second
+// parts start at different times but one key block (20 tiles at 10 heads)
+// lower for every tile they start earlier, so they too reach every row
+// together. Either way a tile of Q and dO is fetched once and read from L2
+// by every key block of its sequence (the blocks of one sequence share an
+// XCD: workgroups go round-robin over the 8 XCDs and the sequence index is
+// the block index modulo the (sequence, head) count).
+template <typename T, int D>
+__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_kernel(AttnGeom g, const T* __restrict__ qk,
+                                                               const T* __restrict__ vsrc, const T* __restrict__ dO,
+                                                               const float2* __restrict__ rowstat,
+                                                               T* __restrict__ dk, T* __restrict__ dv, long ld_dkv) {
+  using Sh = DkdvShape<T, D>;
+  __shared__ __align__(16) T q0[Sh::TILE], q1[Sh::TILE], q2[Sh::TILE], q3[Sh::STAGES == 4 ? Sh::TILE : 1];
+  __shared__ __align__(16) T d0[Sh::TILE], d1[Sh::TILE], d2[Sh::TILE], d3[Sh::STAGES == 4 ? Sh::TILE : 1];
+  __shared__ __align__(16) float t0[64 * Sh::NSUB * Sh::WAVES], t1[64 * Sh::NSUB * Sh::WAVES],
+      t2[64 * Sh::NSUB * Sh::WAVES], t3[Sh::STAGES == 4 ? 64 * Sh::NSUB * Sh::WAVES : 1];
+  // P hand-over: [parity][sub-tile][key group][half][lane]
+  __shared__ __align__(16) F8<T> pb[2 * 512 * Sh::NSUB];
+
+  const int tid = threadIdx.x, lane = tid & 63, lh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets and buffer resources
+  const int per = g.G * g.B;
+  const int nkb = (g.T + 127) / 128;
+  const int pair = (int)(blockIdx.x / per);
+  const int kvh = blockIdx.x % per % g.G, b = blockIdx.x % per / g.G;
+  const long tok0 = (long)b * g.T;
+  const int role = wave >> 2;
+  const float c1 = kLog2e / sqrtf((float)D);
+
+  dkdv_part<T, D, false>(g, qk, vsrc, dO, rowstat, dk, dv, ld_dkv, pair, kvh, b, tok0, role, lane, lh, l32, wave, c1,
+                         q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3, pb);
+  if (nkb - 1 - pair != pair)  // the middle key block of an odd count: one part
+    dkdv_part<T, D, true>(g, qk, vsrc, dO, rowstat, dk, dv, ld_dkv, nkb - 1 - pair, kvh, b, tok0, role, lane, lh, l32,
+                          wave, c1, q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3, pb);
 }
 
 // Unmasked (query, key) pairs of causal attention over all heads and rows.
@@ -984,8 +1031,8 @@ nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, 
   // recompute S and dP, then dV = P^T dO and dK = dS^T Q: 8 D flops per pair
   ProfScope prof(NC_NAME(T, "attn_bwd_dkdv"), 8.0 * D * causal_pairs(g),
                  es * tok * D * (2.0 * g.H + 4.0 * g.G) + 8.0 * tok * g.H, st);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(nkb * g.G * g.B), dim3(512), 0, st, g, qk, v, dO, rs, dk,
-                     dv, ld_dkv);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3((nkb + 1) / 2 * g.G * g.B), dim3(512), 0, st, g, qk, v, dO,
+                     rs, dk, dv, ld_dkv);
   NC_LAUNCH_CHECK("attn_bwd_dkdv");
   return NC_OK;
 }
