@@ -39,7 +39,19 @@ __global__ void __launch_bounds__(256) eb_colscan_kernel(int* __restrict__ hist,
   int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   int run = 0;
-  for (int c = 0; c < nchunks; ++c) {
+  // eight chunks' loads in flight at a time (a rolled loop would wait for each)
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    int h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = hist[(long)(c + j) * V + v];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hist[(long)(c + j) * V + v] = run;
+      run += h[j];
+    }
+  }
+  for (; c < nchunks; ++c) {
     long i = (long)c * V + v;
     int h = hist[i];
     hist[i] = run;
@@ -49,11 +61,43 @@ __global__ void __launch_bounds__(256) eb_colscan_kernel(int* __restrict__ hist,
 }
 
 // Exclusive scan of seg[0..V) in place, seg[V] = total (one block of 1024).
+// Thread t owns the contiguous slice [t per, t per + per); with per <= 64 (a
+// multiple of 4) the slice is held in registers, read and written four at a time.
+constexpr int kScanPer = 64;
 __global__ void __launch_bounds__(1024) eb_scan_kernel(int* __restrict__ seg, int V) {
   __shared__ int sums[1024];
   const int t = threadIdx.x;
   const int per = (V + 1023) / 1024;
   const int b = t * per, e = min(V, b + per);
+  if (per <= kScanPer && per % 4 == 0 && V % 4 == 0) {
+    int4 x[kScanPer / 4];
+#pragma unroll
+    for (int j = 0; j < kScanPer / 4; ++j)
+      x[j] = b + 4 * j < e ? reinterpret_cast<const int4*>(seg + b)[j] : make_int4(0, 0, 0, 0);
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer / 4; ++j) s += (x[j].x + x[j].y) + (x[j].z + x[j].w);
+    sums[t] = s;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      int y = (t >= off) ? sums[t - off] : 0;
+      __syncthreads();
+      sums[t] += y;
+      __syncthreads();
+    }
+    int run = (t > 0) ? sums[t - 1] : 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer / 4; ++j) {
+      int4 o;
+      o.x = run; run += x[j].x;
+      o.y = run; run += x[j].y;
+      o.z = run; run += x[j].z;
+      o.w = run; run += x[j].w;
+      if (b + 4 * j < e) reinterpret_cast<int4*>(seg + b)[j] = o;
+    }
+    if (t == 1023) seg[V] = sums[1023];
+    return;
+  }
   int s = 0;
   for (int i = b; i < e; ++i) s += seg[i];
   sums[t] = s;
@@ -120,17 +164,26 @@ template <typename T>
 __global__ void __launch_bounds__(256) eb_coef_kernel(const T* __restrict__ dx, const T* __restrict__ x,
                                                       const float* __restrict__ r, int M, int d,
                                                       float2* __restrict__ coef) {
-  constexpr int VE = Vec<T>::n;
+  constexpr int VE = Vec<T>::n, MAXV = 2048 / VE / 64;  // d <= 2048
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (m >= M) return;  // whole waves leave together
   const long off = (long)m * d;
-  float dot = 0.f;
-  for (int c = VE * lane; c < d; c += 64 * VE) {
-    float a[VE], b[VE];
-    load16<T>(dx + off + c, a);
-    load16<T>(x + off + c, b);
+  float a[MAXV][VE], b[MAXV][VE];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) dot += a[e] * b[e];
+  for (int c = 0; c < MAXV; ++c) {  // every load in flight before the first product
+    const int col = VE * (lane + 64 * c);
+    if (col < d) {
+      load16<T>(dx + off + col, a[c]);
+      load16<T>(x + off + col, b[c]);
+    }
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXV; ++c) {
+    if (VE * (lane + 64 * c) < d) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) dot += a[c][e] * b[c][e];
+    }
   }
   dot = wave_sum(dot);
   if (lane == 0) {
@@ -143,7 +196,7 @@ __global__ void __launch_bounds__(256) eb_coef_kernel(const T* __restrict__ dx, 
 // VE consecutive columns of 16-byte group t (d <= 256 VE); a window's
 // positions, ids and coefficients are staged in LDS first, and the rows of
 // kBatch positions are loaded before any of them is added.
-constexpr int kBatch = 4;
+constexpr int kBatch = 8;
 template <typename T>
 __global__ void __launch_bounds__(256) eb_window_kernel(const T* __restrict__ dx, const T* __restrict__ x,
                                                         const float2* __restrict__ coef, int d,
@@ -229,9 +282,24 @@ __global__ void __launch_bounds__(256) eb_fixup_kernel(int d, const int* __restr
   const int s = seg[v], e = seg[v + 1];
   if (s / kWin + 1 != w) return;
   const int d4 = d / 4;
+  const int w0 = s / kWin, w1 = (e - 1) / kWin;
   for (int c4 = threadIdx.x; c4 < d4; c4 += 256) {
     float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int ww = s / kWin; ww <= (e - 1) / kWin; ++ww) {
+    // eight windows' partials loaded before they are added (in window order)
+    int ww = w0;
+    for (; ww + 8 <= w1 + 1; ww += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int slot = (s <= (ww + j) * kWin) ? 0 : 1;
+        x[j] = reinterpret_cast<const float4*>(spill + (long)(2 * (ww + j) + slot) * d)[c4];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tot.x += x[j].x; tot.y += x[j].y; tot.z += x[j].z; tot.w += x[j].w;
+      }
+    }
+    for (; ww <= w1; ++ww) {
       const int slot = (s <= ww * kWin) ? 0 : 1;
       const float4 x = reinterpret_cast<const float4*>(spill + (long)(2 * ww + slot) * d)[c4];
       tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
