@@ -3,9 +3,9 @@
 // list on vpshk.cn; its gradient is a sum of rows, one per occurrence), where
 // de = N_bwd(dx0) is the backward of the parameter-free norm that follows the
 // embedding: de = r (dx0 - x0 mean(dx0 x0)). The norm backward is folded into
-// the sums: a first pass keeps two numbers per token (a = r and
-// b = r mean(dx0 x0)), and the window sums form de = a dx0 - b x0 from the
-// stored rows as they read them, so de never reaches memory.
+// the window sums: they read each sorted position's dx0 and x0 rows once, take
+// the row's dot product dx0 . x0 over the block, and add de = r dx0 - b x0
+// (b = r mean(dx0 x0)) to the run, so de never reaches memory.
 //
 // No floating-point atomics: the positions are first sorted by (id, m) with a
 // counting sort whose within-id ranks are computed exactly (chunk histograms,
@@ -158,114 +158,133 @@ __global__ void __launch_bounds__(256) eb_place_kernel(const int32_t* __restrict
   }
 }
 
-// Per token, the coefficients of the norm backward: coef[m] = (r, r mean(dx x)),
-// so that de[m] = r dx - (r mean(dx x)) x. One wavefront per token.
+// 16 bytes of T as float values.
 template <typename T>
-__global__ void __launch_bounds__(256) eb_coef_kernel(const T* __restrict__ dx, const T* __restrict__ x,
-                                                      const float* __restrict__ r, int M, int d,
-                                                      float2* __restrict__ coef) {
-  constexpr int VE = Vec<T>::n, MAXV = 2048 / VE / 64;  // d <= 2048
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M) return;  // whole waves leave together
-  const long off = (long)m * d;
-  float a[MAXV][VE], b[MAXV][VE];
+__device__ __forceinline__ void unpack16(const uint4& u, float* out) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int c = 0; c < MAXV; ++c) {  // every load in flight before the first product
-    const int col = VE * (lane + 64 * c);
-    if (col < d) {
-      load16<T>(dx + off + col, a[c]);
-      load16<T>(x + off + col, b[c]);
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
-  }
-  float dot = 0.f;
-#pragma unroll
-  for (int c = 0; c < MAXV; ++c) {
-    if (VE * (lane + 64 * c) < d) {
-#pragma unroll
-      for (int e = 0; e < VE; ++e) dot += a[c][e] * b[c][e];
-    }
-  }
-  dot = wave_sum(dot);
-  if (lane == 0) {
-    const float rr = r[m];
-    coef[m] = make_float2(rr, rr * dot / (float)d);
+  } else {
+    out[0] = __uint_as_float(u.x); out[1] = __uint_as_float(u.y);
+    out[2] = __uint_as_float(u.z); out[3] = __uint_as_float(u.w);
   }
 }
 
-// Window sums of de = a dx - b x over the sorted positions. Thread t owns the
-// VE consecutive columns of 16-byte group t (d <= 256 VE); a window's
-// positions, ids and coefficients are staged in LDS first, and the rows of
-// kBatch positions are loaded before any of them is added.
-constexpr int kBatch = 8;
+// Window sums of de = r dx - (r mean(dx x)) x over the sorted positions.
+// Thread t owns the VE consecutive columns of 16-byte group t (d <= 256 VE).
+// A window's positions, ids and norm scales r are staged in LDS first, with
+// whether its first run began before the window and its last run goes on
+// past it. The rows of kBatch positions are in flight while the previous
+// batch is summed; their dot products dx . x are summed per wave and then
+// over the four waves in order (double-buffered, one barrier per batch), and
+// each position's de is added to its run. A run inside the window goes to
+// its dWte row, stored outright over the zero-filled row unless accumulating;
+// a run crossing an edge goes to the window's spill slot (0: the window's
+// first run, 1: its last).
+constexpr int kBatch = 4;
 template <typename T>
 __global__ void __launch_bounds__(256) eb_window_kernel(const T* __restrict__ dx, const T* __restrict__ x,
-                                                        const float2* __restrict__ coef, int d,
+                                                        const float* __restrict__ r, int d,
                                                         const int* __restrict__ seg, const int* __restrict__ perm,
-                                                        const int* __restrict__ sid, int V, float* __restrict__ dwte,
-                                                        float* __restrict__ spill) {
+                                                        const int* __restrict__ sid, int V, int accumulate,
+                                                        float* __restrict__ dwte, float* __restrict__ spill) {
   constexpr int VE = Vec<T>::n;
   __shared__ int spos[kWin], sids[kWin];
-  __shared__ float2 scoef[kWin];
+  __shared__ float sr[kWin];
+  __shared__ float red[2][4][kBatch];
+  __shared__ int cont[2];  // first run began before the window, last run goes on past it
   const int w = blockIdx.x;
   const int nvalid = seg[V];
   const int p0 = w * kWin;
-  if (p0 >= nvalid) return;
+  if (p0 >= nvalid) return;  // the whole block leaves together
   const int n = min(kWin, nvalid - p0);
   if (threadIdx.x < n) {
     const int m = perm[p0 + threadIdx.x];
     spos[threadIdx.x] = m;
     sids[threadIdx.x] = sid[p0 + threadIdx.x];
-    scoef[threadIdx.x] = coef[m];
+    sr[threadIdx.x] = r[m];
   }
+  if (threadIdx.x == 64) cont[0] = p0 > 0 && sid[p0 - 1] == sid[p0];
+  if (threadIdx.x == 65) cont[1] = p0 + n < nvalid && sid[p0 + n] == sid[p0 + n - 1];
   __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = VE * threadIdx.x;  // first column of this thread's group
   const bool on = c < d;
-  float acc[VE];
-#pragma unroll
-  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-  int cur = sids[0];
-  // adds acc to dwte[cur] when its run lies inside the window, else to the
-  // window's spill slot (0: the run started before the window, 1: after)
-  auto flush = [&](int v) {
-    const int s0 = seg[v], e0 = seg[v + 1];
-    float* o = (s0 >= p0 && e0 <= p0 + n) ? dwte + (long)v * d + c
-                                          : spill + (long)(2 * w + (s0 <= p0 ? 0 : 1)) * d + c;
-    const bool add = s0 >= p0 && e0 <= p0 + n;
+  const float inv_d = 1.f / (float)d;
+  const int v_first = sids[0], v_last = sids[n - 1];
+  const bool c_first = cont[0], c_last = cont[1];
+  auto flush = [&](int v, const float* a) {
+    const bool inside = !((v == v_first && c_first) || (v == v_last && c_last));
+    float* o = inside ? dwte + (long)v * d + c : spill + (long)(2 * w + (v == v_first ? 0 : 1)) * d + c;
+    const bool add = inside && accumulate;
 #pragma unroll
     for (int q = 0; q < VE; q += 4) {
       float4 y = add ? *reinterpret_cast<const float4*>(o + q) : make_float4(0.f, 0.f, 0.f, 0.f);
-      y.x += acc[q]; y.y += acc[q + 1]; y.z += acc[q + 2]; y.w += acc[q + 3];
+      y.x += a[q]; y.y += a[q + 1]; y.z += a[q + 2]; y.w += a[q + 3];
       *reinterpret_cast<float4*>(o + q) = y;
     }
   };
-  for (int b0 = 0; b0 < n; b0 += kBatch) {
-    float gx[kBatch][VE], xx[kBatch][VE];
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  int cur = v_first;
+  uint4 nd[kBatch], nx[kBatch];  // the next batch's chunks, in flight
+  auto fetch = [&](int b0) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
+      nd[i] = nx[i] = make_uint4(0u, 0u, 0u, 0u);
       if (on && b0 + i < n) {
         const long ro = (long)spos[b0 + i] * d + c;
-        load16<T>(dx + ro, gx[i]);
-        load16<T>(x + ro, xx[i]);
+        nd[i] = *reinterpret_cast<const uint4*>(dx + ro);
+        nx[i] = *reinterpret_cast<const uint4*>(x + ro);
       }
     }
+  };
+  fetch(0);
+  int par = 0;
+  for (int b0 = 0; b0 < n; b0 += kBatch, par ^= 1) {
+    float gx[kBatch][VE], xx[kBatch][VE], dot[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      unpack16<T>(nd[i], gx[i]);
+      unpack16<T>(nx[i], xx[i]);
+    }
+    if (b0 + kBatch < n) fetch(b0 + kBatch);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) t += gx[i][e] * xx[i][e];
+      dot[i] = wave_sum(t);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) red[par][wv][i] = dot[i];
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       if (b0 + i >= n) break;
       const int v = sids[b0 + i];
       if (v != cur) {
-        if (on) flush(cur);
+        if (on) flush(cur, acc);
         cur = v;
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[e] = 0.f;
       }
-      const float2 k = scoef[b0 + i];
+      const float tot = red[par][0][i] + red[par][1][i] + red[par][2][i] + red[par][3][i];
+      const float ka = sr[b0 + i], kb = ka * tot * inv_d;
       if (on) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] += k.x * gx[i][e] - k.y * xx[i][e];
+        for (int e = 0; e < VE; ++e) acc[e] += ka * gx[i][e] - kb * xx[i][e];
       }
     }
   }
-  if (on) flush(cur);
+  if (on) flush(cur, acc);
 }
 
 // Segments spanning windows: block w owns the segment whose first crossed
@@ -320,7 +339,6 @@ size_t embed_sort_bytes(int M, int V, int d) {
   b += align_up(nch * V * sizeof(int), 256);
   b += align_up((size_t)(V + 1) * sizeof(int), 256);
   b += 2 * align_up((size_t)M * sizeof(int), 256);
-  b += align_up((size_t)M * sizeof(float2), 256);
   b += align_up(nwin * 2 * d * sizeof(float), 256);
   return b;
 }
@@ -333,7 +351,6 @@ EmbedSortBufs embed_sort_carve(void* base, int M, int V, int d) {
   b.seg = reinterpret_cast<int*>(p); p += align_up((size_t)(V + 1) * sizeof(int), 256);
   b.perm = reinterpret_cast<int*>(p); p += align_up((size_t)M * sizeof(int), 256);
   b.sid = reinterpret_cast<int*>(p); p += align_up((size_t)M * sizeof(int), 256);
-  b.coef = reinterpret_cast<float2*>(p); p += align_up((size_t)M * sizeof(float2), 256);
   b.spill = reinterpret_cast<float*>(p);
   return b;
 }
@@ -348,12 +365,6 @@ nc_status embed_bwd(const int32_t* idx, const T* x0, const float* r0, const T* d
   if (!accumulate) NC_TRY(fill_f32(dwte, 0.f, (size_t)V * d, st));
   const double es = sizeof(T);
   {
-    // the norm backward's per-token coefficients: dx0 and x0 read once
-    ProfScope prof(NC_NAME(T, "embed_norm_coef"), 0, 2.0 * es * M * d + 12.0 * M, st);
-    hipLaunchKernelGGL((eb_coef_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, dx0, x0, r0, M, d, b.coef);
-    NC_LAUNCH_CHECK("eb_coef");
-  }
-  {
     ProfScope prof("embed_sort", 0, 4.0 * M * 5 + 8.0 * nch * V, st);
     hipLaunchKernelGGL(eb_hist_kernel, dim3((M + 255) / 256), dim3(256), 0, st, idx, M, V, b.hist);
     NC_LAUNCH_CHECK("eb_hist");
@@ -365,12 +376,12 @@ nc_status embed_bwd(const int32_t* idx, const T* x0, const float* r0, const T* d
     NC_LAUNCH_CHECK("eb_place");
   }
   {
-    // counted: dx0 and x0 rows once, positions, ids and coefficients. The
-    // read-modify-write of the distinct ids' dWte rows (unknown to the host)
-    // and the spill slots are left out, so the rate is a lower bound.
-    ProfScope prof(NC_NAME(T, "embed_window_sum"), 0, 2.0 * es * M * d + 16.0 * M, st);
-    hipLaunchKernelGGL((eb_window_kernel<T>), dim3(nwin), dim3(256), 0, st, dx0, x0, b.coef, d, b.seg, b.perm,
-                       b.sid, V, dwte, b.spill);
+    // counted: dx0 and x0 rows once, r, positions and ids. The distinct ids'
+    // dWte rows and the spill slots it writes are unknown to the host and
+    // left out, so the rate is a lower bound.
+    ProfScope prof(NC_NAME(T, "embed_window_sum"), 0, 2.0 * es * M * d + 12.0 * M, st);
+    hipLaunchKernelGGL((eb_window_kernel<T>), dim3(nwin), dim3(256), 0, st, dx0, x0, r0, d, b.seg, b.perm, b.sid,
+                       V, accumulate, dwte, b.spill);
     NC_LAUNCH_CHECK("eb_window");
   }
   if (nwin > 1) {

@@ -222,7 +222,6 @@ struct EmbedSortBufs {
   int* seg;       // [V + 1] segment starts (exclusive scan of counts)
   int* perm;      // [M] token positions sorted by (id, position)
   int* sid;       // [M] ids in sorted order
-  float2* coef;   // [M] the norm backward's (r, r mean(dx0 x0)) per token
   float* spill;   // [n_windows * 2 * d]
 };
 size_t embed_sort_bytes(int M, int V, int d);
