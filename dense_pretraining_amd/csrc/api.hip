@@ -781,6 +781,16 @@ nc_status nc_query_sizes(const nc_config* cfg, nc_sizes* s) {
   return NC_OK;
 }
 
+nc_status nc_workspace_size(const nc_config* cfg, size_t* model_bytes, size_t* block_saved_bytes,
+                            size_t* scratch_bytes) {
+  nc_sizes s;
+  NC_TRY(nc_query_sizes(cfg, &s));
+  if (model_bytes) *model_bytes = s.model_workspace;
+  if (block_saved_bytes) *block_saved_bytes = s.block_saved;
+  if (scratch_bytes) *scratch_bytes = s.scratch;
+  return NC_OK;
+}
+
 nc_status nc_read_status(const void* scratch, uint32_t* flags, void* stream) {
   if (!scratch || !flags) return NC_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);

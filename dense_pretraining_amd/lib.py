@@ -32,7 +32,7 @@ STATUS_NO_TARGETS = 0x8
 
 EXPORTED = [
     "nc_abi_version", "nc_status_str", "nc_last_hip_error", "nc_validate", "nc_param_layout",
-    "nc_query_sizes", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
+    "nc_query_sizes", "nc_workspace_size", "nc_read_status", "nc_clear_status", "nc_embed_fwd", "nc_embed_bwd",
     "nc_block_fwd", "nc_block_bwd", "nc_lmhead_softcap_xent_fwd", "nc_lmhead_softcap_xent_bwd",
     "nc_model_loss_and_grad", "nc_infer_query_sizes", "nc_prefill", "nc_decode_step", "nc_opt_query_sizes",
     "nc_opt_init", "nc_opt_step", "nc_profile_enable", "nc_profile_only", "nc_profile_summary",
@@ -113,6 +113,7 @@ def load(path=LIB_PATH):
         "nc_validate": ([cfgp], I),
         "nc_param_layout": ([cfgp, C.POINTER(S), S, C.POINTER(S)], I),
         "nc_query_sizes": ([cfgp, C.POINTER(NcSizes)], I),
+        "nc_workspace_size": ([cfgp, C.POINTER(S), C.POINTER(S), C.POINTER(S)], I),
         "nc_read_status": ([P, C.POINTER(C.c_uint32), P], I),
         "nc_clear_status": ([P, P], I),
         "nc_embed_fwd": ([cfgp, P, P, P, P, P, P], I),
@@ -186,6 +187,14 @@ def query_sizes(cfg: Config) -> NcSizes:
     s = NcSizes()
     _check(load().nc_query_sizes(C.byref(c), C.byref(s)), "nc_query_sizes")
     return s
+
+
+def workspace_size(cfg: Config):
+    """(model workspace, one block's saved, scratch) bytes."""
+    c = to_nc_config(cfg)
+    out = [C.c_size_t() for _ in range(3)]
+    _check(load().nc_workspace_size(C.byref(c), *[C.byref(o) for o in out]), "nc_workspace_size")
+    return tuple(o.value for o in out)
 
 
 def param_layout(cfg: Config):

@@ -132,6 +132,13 @@ nc_status nc_param_layout(const nc_config* cfg, size_t* offsets, size_t n_offset
 
 nc_status nc_query_sizes(const nc_config* cfg, nc_sizes* sizes /* host */);
 
+/* The same sizes in three host outputs, any of which may be NULL:
+ * model_bytes = the `workspace` of nc_model_loss_and_grad, block_saved_bytes
+ * = one block's `saved`, scratch_bytes = the `scratch` of the per-function
+ * entry points. Errors as nc_validate. */
+nc_status nc_workspace_size(const nc_config* cfg, size_t* model_bytes, size_t* block_saved_bytes,
+                            size_t* scratch_bytes);
+
 /* Copies the status word from the start of `scratch` (or a model workspace)
  * to *flags (host) after synchronising `stream`. Returns NC_OK when no bit is
  * set, NC_ERR_DEVICE_DATA otherwise. */

@@ -80,6 +80,17 @@ def test_sizes_grow_with_batch():
     assert b.model_workspace < 100e9
 
 
+def test_workspace_size_agrees_with_query_sizes():
+    for cfg in (cfgmod.TINY, cfgmod.DEPTH20):
+        s = lib.query_sizes(cfg)
+        assert lib.workspace_size(cfg) == (s.model_workspace, s.block_saved, s.scratch)
+    L = lib.load()
+    c = lib.to_nc_config(cfgmod.TINY)
+    assert L.nc_workspace_size(C.byref(c), None, None, None) == 0
+    bad = lib.to_nc_config(cfgmod.TINY.with_(head_dim=96))
+    assert L.nc_workspace_size(C.byref(bad), None, None, None) != 0
+
+
 def _fake(addr):
     return C.c_void_p(addr)
 
