@@ -159,7 +159,7 @@ CLASSES = [
     ("xent_dz", r"xent_dz_kernel"),
     ("xent_loss", r"xent_rows_kernel|xent_final_kernel"),
     ("splitk_reduce", r"splitk_reduce_kernel"),
-    ("embed_bwd (sort, coefficients, window sums)", r"eb_\w+_kernel"),
+    ("embed_bwd (sort, window sums with the norm backward, fixup)", r"eb_\w+_kernel"),
     ("fills", r"fill_u32_kernel|fill_f32_kernel"),
 ]
 NUM_CUS, SIMDS_PER_CU, XCDS = 256, 4, 8

@@ -137,7 +137,7 @@ def test_model_depth20_full_shape():
 
 def test_model_depth30_full_shape():
     cfg = DEPTH30  # 30 layers, d 1920, 15 x 128 heads, B=16 x T=2048, vocab 65536, bf16
-    # rows 3 and 12 (first 256 positions each): token ranges 1 and 5 of dWqkv's 7
-    run, loss, loss_ref, g_ref = _rows_model(cfg, rows=[3, 12], t_valid=256)
+    # rows 3 and 12 (first 1024 positions each): token ranges 1 and 5 of dWqkv's 7
+    run, loss, loss_ref, g_ref = _rows_model(cfg, rows=[3, 12], t_valid=1024)
     worst, name = _compare_model(cfg, run, loss, loss_ref, g_ref, "depth30")
     print(f"depth30 worst gradient error {worst:.3e} ({name})")
