@@ -748,7 +748,6 @@ __device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T*
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) mma32(sacc, swz_row8<T, D>(sq, l32, 16 * k + 8 * lh), kf[k]);
   const float* sw = st + 64 * (Sh::NSUB * c.wave + u);
-  const bool full = c.full(s, u);
   const int rq0 = c.row0(s) + 32 * u, key = c.kw0 + l32;
   float p[16];
 #pragma unroll
@@ -758,14 +757,21 @@ __device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T*
     const float4 b = *reinterpret_cast<const float4*>(sw + 2 * q0 + 4);
     const float la[4] = {a.x, a.z, b.x, b.z};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float pv = fast_exp2(sacc[4 * j + i] * c1 - la[i]);
-      if (!full) {
-        const int r = rq0 + q0 + i;
-        pv = (c.kok & (r < c.nrows) & (key <= c.dvn.q(r))) ? pv : 0.f;
+    for (int i = 0; i < 4; ++i) p[4 * j + i] = fast_exp2(sacc[4 * j + i] * c1 - la[i]);
+  }
+  // Sub-tiles on the diagonal or at the end: row rq0 + q is unmasked for this
+  // lane's key iff key <= (rq0 + q) / n_rep, i.e. q >= key n_rep - rq0, and
+  // rq0 + q < nrows. A 0/1 factor after the exponentials (a select there
+  // became a branch around each exponential), under a branch uniform per wave.
+  if (!c.full(s, u)) {
+    const int lo = c.kok ? key * c.n_rep - rq0 : 0x3fffffff, hi = c.nrows - rq0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = 8 * j + 4 * lh + i;
+        p[4 * j + i] *= (float)((q >= lo) & (q < hi));
       }
-      p[4 * j + i] = pv;
-    }
   }
   const F8<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
   pb[(2 * c.kw) * 64 + lane] = pf0;
