@@ -538,8 +538,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
   dsum += __shfl_xor(dsum, 32, 64);
   const float dlt = dsum;
   const float lse2 = qok ? lse[qi] * kLog2e : 0.f;
-  // (lse log2 e, Delta) of each flattened row, in row order, for the dK/dV pass
-  if (qok && lh == 0) rowstat[((long)b * g.G + kvh) * nrows + rq] = make_float2(lse2, dlt);
+  // (lse log2 e, -Delta) of each flattened row, in row order, for the dK/dV
+  // pass (which starts its dP accumulators at -Delta)
+  if (qok && lh == 0) rowstat[((long)b * g.G + kvh) * nrows + rq] = make_float2(lse2, -dlt);
   const float c1 = kLog2e / sqrtf((float)D);
 
   Kv dma;
@@ -619,7 +620,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnGeom g, const T
 // 3-stage LDS ring of Q and dO tiles filled by direct-to-LDS loads
 // (XOR-swizzled 16-byte chunks: conflict-free for the row reads of S and dP
 // and for the transposing reads of dV and dK), each wave also staging its
-// own copy of the tiles' (lse log2 e, Delta) pairs. Tiles run from the last
+// own copy of the tiles' (lse log2 e, -Delta) pairs. Tiles run from the last
 // query row down, so that all key blocks of a sequence start on the same rows
 // and share them in L2.
 
@@ -711,10 +712,12 @@ struct DkdvCtx {
       T* dst = (ldo[i] ? sd : sq) + lblk[i] * 64 * Sh::VE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ldo[i] ? rd : rq, (lds_void*)dst, 16, off, 0, 0, 0);
     }
+    // per 32-row sub-tile: lanes 0-31 take the rows' lse2, lanes 32-63 their
+    // -Delta, so each lands as 32 consecutive floats
 #pragma unroll
     for (int u = 0; u < Sh::NSUB; ++u) {
-      const int e = 2 * rq0 + 64 * u + lane;  // float index into this tile's (lse2, Delta) pairs
-      const unsigned soff = (live && e < 2 * nrows) ? (unsigned)e * 4u : kDmaOOB;
+      const int row = rq0 + 32 * u + (lane & 31);
+      const unsigned soff = (live && row < nrows) ? (unsigned)(2 * row + (lane >> 5)) * 4u : kDmaOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(ss + 64 * (Sh::NSUB * wave + u)), 4, soff, 0, 0, 0);
     }
   }
@@ -732,11 +735,17 @@ struct DkdvCtx {
 };
 
 // P side of sub-tile u (32 rows) of step s: S = Q K^T, P, hand P over, dV += P^T dO.
+// Row rq0 + q is unmasked for this lane's key iff key <= (rq0 + q) / n_rep,
+// i.e. q >= key n_rep - rq0, and rq0 + q < nrows: one unsigned range test per
+// element after the exponentials, on every sub-tile. (A select before the
+// exponentials became a branch around each of them; the test under a branch
+// taken only on the diagonal was turned into selects on every sub-tile
+// anyway, and an unmasked copy of the body as a block of its own pushed the
+// kernel past its registers.)
 template <typename T, int D, typename Ctx>
-__device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T* __restrict__ sq,
-                                            const T* __restrict__ sdo, const float* __restrict__ st, F8<T>* pb,
-                                            f32x16* acc, const F8<T>* kf, float c1) {
-  if (c.skip(s, u)) return;
+__device__ __forceinline__ void dkdv_tile_p_body(const Ctx& c, int s, int u, const T* __restrict__ sq,
+                                                 const T* __restrict__ sdo, const float* __restrict__ st, F8<T>* pb,
+                                                 f32x16* acc, const F8<T>* kf, float c1) {
   using Sh = DkdvShape<T, D>;
   sq += 32 * D * u;  // rows 32 u .. of the tile: the same swizzle (it repeats every 16 rows)
   sdo += 32 * D * u;
@@ -748,29 +757,24 @@ __device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T*
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) mma32(sacc, swz_row8<T, D>(sq, l32, 16 * k + 8 * lh), kf[k]);
   const float* sw = st + 64 * (Sh::NSUB * c.wave + u);
-  const int rq0 = c.row0(s) + 32 * u, key = c.kw0 + l32;
   float p[16];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int q0 = 8 * j + 4 * lh;
-    const float4 a = *reinterpret_cast<const float4*>(sw + 2 * q0);
-    const float4 b = *reinterpret_cast<const float4*>(sw + 2 * q0 + 4);
-    const float la[4] = {a.x, a.z, b.x, b.z};
+    const float4 a = *reinterpret_cast<const float4*>(sw + 8 * j + 4 * lh);  // lse2 of the rows
+    const float la[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[4 * j + i] = fast_exp2(sacc[4 * j + i] * c1 - la[i]);
   }
-  // Sub-tiles on the diagonal or at the end: row rq0 + q is unmasked for this
-  // lane's key iff key <= (rq0 + q) / n_rep, i.e. q >= key n_rep - rq0, and
-  // rq0 + q < nrows. A 0/1 factor after the exponentials (a select there
-  // became a branch around each exponential), under a branch uniform per wave.
-  if (!c.full(s, u)) {
-    const int lo = c.kok ? key * c.n_rep - rq0 : 0x3fffffff, hi = c.nrows - rq0;
+  {
+    const int rq0 = c.row0(s) + 32 * u, key = c.kw0 + l32;
+    const int lo = c.kok ? key * c.n_rep - rq0 : 0x3fffffff;  // q >= lo and q < nrows - rq0
+    const unsigned span = (unsigned)max(0, c.nrows - rq0 - lo);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = 8 * j + 4 * lh + i;
-        p[4 * j + i] *= (float)((q >= lo) & (q < hi));
+        p[4 * j + i] = (unsigned)(q - lo) < span ? p[4 * j + i] : 0.f;
       }
   }
   const F8<T> pf0 = pack8<T>(p), pf1 = pack8<T>(p + 8);
@@ -785,6 +789,14 @@ __device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T*
   }
 }
 
+template <typename T, int D, typename Ctx>
+__device__ __forceinline__ void dkdv_tile_p(const Ctx& c, int s, int u, const T* __restrict__ sq,
+                                            const T* __restrict__ sdo, const float* __restrict__ st, F8<T>* pb,
+                                            f32x16* acc, const F8<T>* kf, float c1) {
+  if (c.skip(s, u)) return;
+  dkdv_tile_p_body<T, D>(c, s, u, sq, sdo, st, pb, acc, kf, c1);
+}
+
 // dS side of sub-tile u of step s: dP = dO V^T, dS = P (dP - Delta), dK += dS^T Q.
 template <typename T, int D, typename Ctx>
 __device__ __forceinline__ void dkdv_tile_ds(const Ctx& c, int s, int u, const T* __restrict__ sq,
@@ -796,27 +808,23 @@ __device__ __forceinline__ void dkdv_tile_ds(const Ctx& c, int s, int u, const T
   sdo += 32 * D * u;
   pb += 512 * u;
   const int lane = c.lane, lh = lane >> 5, l32 = lane & 31, g16 = (lane >> 4) & 1;
+  // dP - Delta: the accumulators start at the rows' -Delta
+  const float* sw = st + 64 * (Sh::NSUB * c.wave + u);
   f32x16 pacc;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) pacc[v] = 0.f;
+  for (int j = 0; j < 4; ++j) {
+    const float4 a = *reinterpret_cast<const float4*>(sw + 32 + 8 * j + 4 * lh);
+    pacc[4 * j] = a.x;
+    pacc[4 * j + 1] = a.y;
+    pacc[4 * j + 2] = a.z;
+    pacc[4 * j + 3] = a.w;
+  }
 #pragma unroll
   for (int k = 0; k < D / 16; ++k) mma32(pacc, swz_row8<T, D>(sdo, l32, 16 * k + 8 * lh), vf[k]);
-  const float* sw = st + 64 * (Sh::NSUB * c.wave + u);
   const F8<T> pf0 = pb[(2 * c.kw) * 64 + lane], pf1 = pb[(2 * c.kw + 1) * 64 + lane];
   float ds[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q0 = 8 * j + 4 * lh;
-    const float4 a = *reinterpret_cast<const float4*>(sw + 2 * q0);
-    const float4 b = *reinterpret_cast<const float4*>(sw + 2 * q0 + 4);
-    const float da[4] = {a.y, a.w, b.y, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = 4 * j + i;
-      const float pv = to_f32((v < 8 ? pf0 : pf1).v[v & 7]);
-      ds[v] = pv * (pacc[v] - da[i]);
-    }
-  }
+  for (int v = 0; v < 16; ++v) ds[v] = to_f32((v < 8 ? pf0 : pf1).v[v & 7]) * pacc[v];
   const F8<T> sf0 = pack8<T>(ds), sf1 = pack8<T>(ds + 8);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {

@@ -158,7 +158,7 @@ template <typename T>
 nc_status attn_fwd(const AttnArgs& a, const T* qk, const T* v, T* o, float* lse, hipStream_t st,
                    uint32_t* amax = nullptr);
 template <typename T>
-// rowstat: scratch of 2 * B * T * H floats, the per-row (lse log2 e, Delta)
+// rowstat: scratch of 2 * B * T * H floats, the per-row (lse log2 e, -Delta)
 // pairs the dQ pass hands to the dK/dV pass.
 nc_status attn_bwd(const AttnArgs& a, const T* qk, const T* v, const T* o, const T* dO, const float* lse,
                    float* rowstat, T* dq, T* dk, T* dv, long ld_dkv, hipStream_t st);
