@@ -1026,7 +1026,9 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   __shared__ __align__(1024) bf16 sb0[E], sb1[E], sb2[E], sb3[E], sb4[E];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane: uniform, so every LDS destination
+  // of the direct-to-LDS loads (M0) is formed in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (s.M + BM - 1) / BM, tiles_n = (s.N + BN - 1) / BN;
   int tm, tn, z;
   gemm_tile_coords(tiles_m, tiles_n, tm, tn, z);
