@@ -249,7 +249,9 @@ struct EpiTracksMax { static constexpr bool value = false; };
 template <typename Epi>
 struct EpiTracksMax<Epi, std::void_t<decltype(Epi::kTracksMax)>> { static constexpr bool value = Epi::kTracksMax; };
 
-template <int WTM, int WTN, typename Epi>
+// Scaled: multiply the accumulators by x.scale first (FP8 products only; a
+// multiply per element costs about a microsecond of a tile's epilogue).
+template <int WTM, int WTN, typename Epi, bool Scaled = false>
 __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi& epi, const EpiCtx& x,
                                                 float* slab) {
   constexpr int NCH = 8 * WTN;  // 16-byte chunks per slab row
@@ -277,6 +279,10 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float v[4] = {c[i][j][4 * g], c[i][j][4 * g + 1], c[i][j][4 * g + 2], c[i][j][4 * g + 3]};
+        if constexpr (Scaled) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= x.scale;
+        }
         const int cc = 8 * j + 2 * g + h;
         epi.pre(rs[i], r0 + 32 * i + lr, c0 + 4 * cc, v);
         *reinterpret_cast<float4*>(slab + 4 * (lr * NCH + (cc ^ (lr & 15)))) = make_float4(v[0], v[1], v[2], v[3]);
@@ -409,10 +415,8 @@ struct EpiStore {
     if constexpr (HasRes) return tile_load4<T>(tile_rsrc(res, ldr, x), tile_off<T>(x, row, col, ldr, M, N));
     else return Aux{};
   }
+  // (an FP8 product's scale is applied to the accumulators before phase 1)
   __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
-    // x.scale is exactly 1 without FP8 operands (a multiply, not a branch per call)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] *= x.scale;
     if constexpr (ReluSqOut) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1063,7 +1067,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(GemmShape s, Epi epi) 
   static_assert(E * sizeof(bf16) == 32 * 128 * sizeof(float), "one A stage holds one slab");
   bf16* slab = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sa3;
   const EpiCtx x{m0, n0, wm, wn, z, lane, wave, reinterpret_cast<float*>(sb0), bi, epi_scale(epi)};
-  staged_epilogue<4, 4>(acc.c, epi, x, reinterpret_cast<float*>(slab));
+  staged_epilogue<4, 4, Epi, F8>(acc.c, epi, x, reinterpret_cast<float*>(slab));
   epi.finish(x);
 }
 

@@ -126,7 +126,7 @@ def test_opt_step_is_deterministic():
 
 def test_depth20_opt_step_sampled():
     """One step of the depth-20 model (502M parameters, bf16) on seeded
-    gradients; checked: every matrix shape of layers 0 and 19 (Wq square, Wk
+    gradients; checked: every matrix of layers 0 and 19 (Wq and Wo square, Wk
     and Wv wide 128 x 1280, W1 tall 5120 x 1280, W2 wide 1280 x 5120) against
     the oracle's Muon, and 512 rows of each of Wte and Wlm against AdamW."""
     cfg = DEPTH20
@@ -148,8 +148,8 @@ def test_depth20_opt_step_sampled():
     HD, GD = cfg.n_head * cfg.head_dim, cfg.n_kv_head * cfg.head_dim
     for l in (0, 19):
         q = offs[1 + 4 * l]
-        mats = dict(wq=(q, HD, d), wk=(q + HD * d, GD, d), wv=(q + (HD + GD) * d, GD, d), w1=(offs[3 + 4 * l], F, d),
-                    w2=(offs[4 + 4 * l], d, F))
+        mats = dict(wq=(q, HD, d), wk=(q + HD * d, GD, d), wv=(q + (HD + GD) * d, GD, d), wo=(offs[2 + 4 * l], d, HD),
+                    w1=(offs[3 + 4 * l], F, d), w2=(offs[4 + 4 * l], d, F))
         for k, (o, R, C) in mats.items():
             W = host(w0[o:o + R * C]).reshape(R, C)
             G = host(grads[o:o + R * C]).reshape(R, C)
