@@ -114,6 +114,39 @@ __device__ __forceinline__ F8<T> swz_tr8(const T* t, int ka, int kb, int c0, int
   return f;
 }
 
+// A bf16 tile read only through the transposing read (V in the forward and
+// decode): 16-byte chunk c of row r sits at chunk slot
+// 4 NC (r/4) + 16 (c/4) + 4 (r%4) + c%4. The 4 rows x 4 chunks one transposing
+// read covers per 32 lanes then fill one 256-byte bank line, and the lane's
+// fragments for different rows and column groups differ by constant offsets
+// (one address register instead of one per fragment).
+template <int D>
+struct SwzT {
+  static constexpr int NC = D / 8;
+  static_assert(NC % 4 == 0, "whole 4-chunk groups");
+  // inverse of the slot map: the row and chunk stored at slot u
+  __device__ __forceinline__ static int row(int u) { return 4 * (u / (4 * NC)) + ((u >> 2) & 3); }
+  __device__ __forceinline__ static int chunk(int u) { return 4 * ((u % (4 * NC)) >> 4) + (u & 3); }
+};
+// Fragment X[ka .. ka+3 | kb .. kb+3][32 dt + 16 ((lane/16)%2) + lane % 16]
+// of a tile in the SwzT layout (ka, kb multiples of 4); float tiles keep the
+// Swz layout.
+template <typename T, int D>
+__device__ __forceinline__ F8<T> vtr8(const T* t, int ka, int kb, int dt, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const int j = lane & 15;
+    const int lp = 32 * (j >> 2) + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<T*>(t + D * ka + 128 * dt + lp));
+    v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<T*>(t + D * kb + 128 * dt + lp));
+    uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    F8<T> f;
+    f.v = __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
+    return f;
+  } else {
+    return swz_tr8<T, D>(t, ka, kb, 32 * dt + 16 * ((lane >> 4) & 1), lane);
+  }
+}
+
 // ------------------------------------------------------------ tile staging
 // Row-major tile [ROWS][D] -> LDS in the swizzled layout above, staged
 // through registers; the row addresses come from a function (nullptr = zero row).
@@ -152,8 +185,9 @@ struct RowTile {
 // K and V tiles of 64 keys streamed straight into LDS (buffer_load ... lds),
 // in the swizzled layout, through a 2-stage ring: tile t+1 loads while tile
 // t is used, and no registers hold data in flight. Keys at or past T read as
-// zeros. NW waves share the loads of a tile.
-template <typename T, int D, int NW = 4>
+// zeros. NW waves share the loads of a tile. With VT, a bf16 V tile lands in
+// the SwzT layout (for kernels that read V only through the transposing read).
+template <typename T, int D, int NW = 4, bool VT = false>
 struct KvDma {
   static constexpr int BKV = 64;
   static constexpr int VE = 16 / sizeof(T);
@@ -181,8 +215,14 @@ struct KvDma {
       isv[i] = ins >= NI;
       blk[i] = ins % NI;
       const int u = 64 * blk[i] + lane;  // chunk slot inside the tile
-      row[i] = u / Swz<T, D>::NC;
-      const int col = ((u % Swz<T, D>::NC) ^ Swz<T, D>::f(row[i])) * VE;
+      int col;
+      if (VT && sizeof(T) == 2 && isv[i]) {
+        row[i] = SwzT<D>::row(u);
+        col = SwzT<D>::chunk(u) * VE;
+      } else {
+        row[i] = u / Swz<T, D>::NC;
+        col = ((u % Swz<T, D>::NC) ^ Swz<T, D>::f(row[i])) * VE;
+      }
       off[i] = (unsigned)(((long)row[i] * (isv[i] ? ldv : ldk) + col) * (long)sizeof(T));
     }
   }
@@ -203,8 +243,8 @@ struct KvDma {
 // are separate LDS arrays passed as __restrict__ parameters of this inlined
 // function, so the compiler can tell one stage's loads from the other
 // stage's reads.
-template <typename T, int D, int NW, typename Body>
-__device__ __forceinline__ void kv_ring(const KvDma<T, D, NW>& dma, int nkt, T* __restrict__ k0, T* __restrict__ v0,
+template <typename T, int D, int NW, bool VT, typename Body>
+__device__ __forceinline__ void kv_ring(const KvDma<T, D, NW, VT>& dma, int nkt, T* __restrict__ k0, T* __restrict__ v0,
                                         T* __restrict__ k1, T* __restrict__ v1, Body&& body) {
   dma.issue(0, k0, v0);
   int kt = 0;
@@ -235,6 +275,20 @@ struct AttnGeom {
   float inv_rep;
 };
 
+// Scheduling pattern for NM matrix products, each with RD of their LDS
+// operand reads, spread over the vector work of the same block: two reads
+// ahead, then one product, its reads and six vector instructions at a time.
+template <int NM, int RD>
+__device__ __forceinline__ void fwd_overlap() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);  // LDS reads ahead
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if (i + 2 < NM) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+  }
+}
+
 // ============================================================ forward
 // With AMAX, the largest stored |o| goes into the striped maximum at amax (the
 // per-tensor scale of the FP8 output projection's operand).
@@ -242,13 +296,12 @@ template <typename T, int D, bool AMAX>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* __restrict__ qk,
                                                           const T* __restrict__ vsrc, T* __restrict__ o,
                                                           float* __restrict__ lse, uint32_t* amax) {
-  using Kv = KvDma<T, D>;
+  using Kv = KvDma<T, D, 4, true>;
   constexpr int BKV = Kv::BKV;
   __shared__ __align__(16) T ks0[Kv::TILE], vs0[Kv::TILE], ks1[Kv::TILE], vs1[Kv::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, lh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g16 = (lane >> 4) & 1;
   const int nrows = g.T * g.n_rep;
   const int nqb = (nrows + 127) / 128;
   const int per = g.G * g.B;
@@ -289,6 +342,54 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
   const float m0 = sqrtf((float)D) * kLog2e;  // fixed shift: |s| <= sqrt(D)
 
   kv_ring<T, D>(dma, nkt, ks0, vs0, ks1, vs1, [&](int kt, const T* sk, const T* sv) {
+    if (wfull && kt * BKV + BKV - 1 <= t_wmin) {
+      // Whole tile below the diagonal for every row of the wave: a straight
+      // block in which the second sub-tile's score products run on the matrix
+      // cores while the first sub-tile's exponentials run on the vector unit,
+      // then the first sub-tile's P V products while the second's run.
+      f32x16 sa, sb;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sa[v] = sb[v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) mma32(sa, swz_row8<T, D>(sk, l32, 16 * s + 8 * lh), qf[s]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) mma32(sb, swz_row8<T, D>(sk, 32 + l32, 16 * s + 8 * lh), qf[s]);
+      float pa[16], pb[16];
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        pa[v] = fast_exp2(sa[v] * c1 - m0);
+        la += pa[v];
+      }
+      F8<T> pfa[2] = {pack8<T>(pa), pack8<T>(pa + 8)};
+      fwd_overlap<D / 16, 1>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k0 = 16 * kk + 4 * lh;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          mma32(oacc[dt], vtr8<T, D>(sv, k0, k0 + 8, dt, lane), pfa[kk]);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        pb[v] = fast_exp2(sb[v] * c1 - m0);
+        lb += pb[v];
+      }
+      F8<T> pfb[2] = {pack8<T>(pb), pack8<T>(pb + 8)};
+      fwd_overlap<D / 16, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k0 = 32 + 16 * kk + 4 * lh;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          mma32(oacc[dt], vtr8<T, D>(sv, k0, k0 + 8, dt, lane), pfb[kk]);
+      }
+      lsum += la + lb;
+      return;
+    }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int kb = kt * BKV + 32 * sub;
@@ -323,8 +424,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnGeom g, const T* _
         const int k0 = 32 * sub + 16 * kk + 4 * lh;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          F8<T> vf = swz_tr8<T, D>(sv, k0, k0 + 8, 32 * dt + 16 * g16, lane);
-          mma32(oacc[dt], vf, pf);
+          mma32(oacc[dt], vtr8<T, D>(sv, k0, k0 + 8, dt, lane), pf);
         }
       }
     }
@@ -364,14 +464,13 @@ template <typename T, int D, int NST>
 __global__ void __launch_bounds__(128) attn_decode_kernel(const T* __restrict__ q, long ldq, const T* __restrict__ ck,
                                                           const T* __restrict__ cv, int H, int G, int n, int cap,
                                                           int kch, float* __restrict__ po, float* __restrict__ pl) {
-  using Kv = KvDma<T, D, 2>;
+  using Kv = KvDma<T, D, 2, true>;
   constexpr int BKV = Kv::BKV;
   __shared__ __align__(16) T ks0[Kv::TILE], vs0[Kv::TILE];
   __shared__ __align__(16) T ks1[NST > 1 ? Kv::TILE : 8], vs1[NST > 1 ? Kv::TILE : 8];
 
   const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g16 = (lane >> 4) & 1;
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nrep = H / G;
   const int k_begin = c * kch;
@@ -418,7 +517,7 @@ __global__ void __launch_bounds__(128) attn_decode_kernel(const T* __restrict__ 
       const F8<T> pf = pack8<T>(p + 8 * kk);
       const int k0 = 32 * wave + 16 * kk + 4 * lh;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma32(oacc[dt], swz_tr8<T, D>(sv, k0, k0 + 8, 32 * dt + 16 * g16, lane), pf);
+      for (int dt = 0; dt < D / 32; ++dt) mma32(oacc[dt], vtr8<T, D>(sv, k0, k0 + 8, dt, lane), pf);
     }
   };
 
