@@ -3,6 +3,8 @@
 // forward/backward, the softcapped cross-entropy reductions, split-K sums and
 // fills. One wavefront owns one row, the row stays in registers, and the row
 // statistics are reduced with cross-lane shuffles in a fixed order.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -383,25 +385,35 @@ __global__ void __launch_bounds__(256) xent_dz_kernel(T* __restrict__ z, int M, 
   }
 }
 
-// Sums the splits' partial tiles in split order (deterministic). All of a
-// thread's partial loads are issued before the first add (a loop over a
-// runtime count would wait for each before issuing the next).
+// Sums the splits' partial tiles in split order (deterministic). The split
+// count is a template parameter, so all of a thread's partial loads are issued
+// before the first add with no per-split test; one 16-byte piece per thread.
 constexpr int kMaxSplits = 16;
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int nsplit, size_t n4,
+template <int NS>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, size_t n4,
                                                             float* __restrict__ out, int accumulate) {
-  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    float4 p[kMaxSplits];
+  const size_t i = blockIdx.x * (size_t)256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 p[NS];
 #pragma unroll
-    for (int zz = 0; zz < kMaxSplits; ++zz)
-      if (zz < nsplit) p[zz] = reinterpret_cast<const float4*>(part + (size_t)zz * n4 * 4)[i];
-    float4 a = accumulate ? reinterpret_cast<const float4*>(out)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int zz = 0; zz < NS; ++zz) p[zz] = reinterpret_cast<const float4*>(part + (size_t)zz * n4 * 4)[i];
+  float4 a = accumulate ? reinterpret_cast<const float4*>(out)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int zz = 0; zz < kMaxSplits; ++zz)
-      if (zz < nsplit) {
-        a.x += p[zz].x; a.y += p[zz].y; a.z += p[zz].z; a.w += p[zz].w;
-      }
-    reinterpret_cast<float4*>(out)[i] = a;
+  for (int zz = 0; zz < NS; ++zz) {
+    a.x += p[zz].x; a.y += p[zz].y; a.z += p[zz].z; a.w += p[zz].w;
   }
+  reinterpret_cast<float4*>(out)[i] = a;
+}
+
+template <int NS>
+void launch_splitk(const float* part, size_t n4, float* out, int accumulate, hipStream_t st) {
+  hipLaunchKernelGGL(splitk_reduce_kernel<NS>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, n4, out,
+                     accumulate);
+}
+template <int... NS>
+bool launch_splitk_n(int nsplit, const float* part, size_t n4, float* out, int accumulate, hipStream_t st,
+                     std::integer_sequence<int, NS...>) {
+  return ((nsplit == NS + 1 ? (launch_splitk<NS + 1>(part, n4, out, accumulate, st), true) : false) || ...);
 }
 
 unsigned grid_for(size_t n, size_t per_block) {
@@ -526,11 +538,13 @@ nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, 
 }
 
 nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st) {
-  if (nsplit < 1 || nsplit > kMaxSplits) return NC_ERR_UNSUPPORTED;
+  if (nsplit < 1 || nsplit > kMaxSplits || n % 4 != 0) return NC_ERR_UNSUPPORTED;
   size_t n4 = n / 4;
+  // one piece per thread: the grid's x dimension bounds the element count
+  if ((n4 + 255) / 256 > 0x7fffffffULL) return NC_ERR_UNSUPPORTED;
+  if (n4 == 0) return NC_OK;
   ProfScope prof("splitk_reduce", 0, 4.0 * n * (nsplit + (accumulate ? 2 : 1)), st);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, st, partial, nsplit, n4, out,
-                     accumulate);
+  launch_splitk_n(nsplit, partial, n4, out, accumulate, st, std::make_integer_sequence<int, kMaxSplits>{});
   NC_LAUNCH_CHECK("splitk_reduce");
   return NC_OK;
 }
