@@ -143,8 +143,8 @@ BlockScratch<T> carve_block_scratch(Carver& c, const Dims& m) {
 
 template <typename T>
 struct HeadSaved {
-  T *xf, *z;
-  float *rf, *lse;
+  T *xf, *z;  // z: what the softcap epilogue stores per logit (see head_fwd_t)
+  float *rf, *lse, *zt;
   int* nv;
 };
 template <typename T>
@@ -154,15 +154,16 @@ HeadSaved<T> carve_head_saved(Carver& c, const Dims& m) {
   s.rf = c.take<float>(m.M);
   s.z = c.take<T>(logit_elems(m.M, m.V));  // column panels of kPanel
   s.lse = c.take<float>(m.M);
+  s.zt = c.take<float>(m.M);
   s.nv = c.take<int>(1);
   return s;
 }
 
 template <typename T>
 struct HeadScratch {
-  float *part, *block_sums, *partial;
+  float *part, *block_sums, *partial, *q;
   int* block_counts;
-  T* dxf;
+  T *dxf, *xs;
   size_t partial_elems;
 };
 template <typename T>
@@ -171,7 +172,9 @@ HeadScratch<T> carve_head_scratch(Carver& c, const Dims& m) {
   s.part = c.take<float>(m.M * lmhead_tiles(m.V, m.es == 2));
   s.block_sums = c.take<float>(xent_loss_blocks((int)m.M));
   s.block_counts = c.take<int>(xent_loss_blocks((int)m.M));
+  s.q = c.take<float>(m.M);
   s.dxf = c.take<T>(m.M * m.d);
+  s.xs = c.take<T>(m.M * m.d);
   s.partial_elems = gemm_dw_partial_elems((int)m.M, m.V, m.d);
   s.partial = c.take<float>(s.partial_elems ? s.partial_elems : 1);
   return s;
@@ -370,9 +373,11 @@ nc_status head_fwd_t(const Dims& m, const T* x, const T* wlm, const int32_t* tg,
                      const HeadScratch<T>& c, uint32_t* status, hipStream_t st) {
   const int M = (int)m.M;
   NC_TRY(rmsnorm_fwd<T>(x, nullptr, 0, s.xf, s.rf, M, m.d, m.eps, nullptr, st));
-  NC_TRY(gemm_lmhead<T>(s.xf, wlm, s.z, M, m.V, m.d, m.cap, c.part, st));
+  // the logits are not stored: per logit, u = exp(z' - c) (1 - (z'/c)^2), and
+  // per row the sums of exp(z' - c), so lse = c + log(sum)
+  NC_TRY(gemm_lmhead<T>(s.xf, wlm, s.z, M, m.V, m.d, m.cap, c.part, st, true));
   NC_TRY(xent_loss<T>(c.part, lmhead_tiles(m.V, m.es == 2), s.xf, wlm, m.d, m.cap, tg, M, m.V, s.lse, c.block_sums,
-                      c.block_counts, loss, s.nv, status, st));
+                      c.block_counts, loss, s.nv, status, st, m.cap, s.zt));
   return NC_OK;
 }
 
@@ -380,9 +385,12 @@ template <typename T>
 nc_status head_bwd_t(const Dims& m, const T* wlm, const int32_t* tg, const HeadSaved<T>& s, float dloss, T* dx,
                      float* dwlm, int acc, const HeadScratch<T>& c, hipStream_t st) {
   const int M = (int)m.M;
-  NC_TRY(xent_dz<T>(s.z, M, m.V, s.lse, tg, s.nv, dloss, m.cap, st));
-  NC_TRY(gemm_dyw<T>(s.z, wlm, c.dxf, nullptr, M, m.V, m.d, st, (long)M * kPanel));
-  NC_TRY(gemm_dw<T>(s.z, s.xf, dwlm, M, m.V, m.d, acc, c.partial, c.partial_elems, st, (long)M * kPanel));
+  // dz = diag(q) u' (u' = u with each row's target element corrected): the
+  // row factor q goes into the input-grad product's epilogue and, as xs =
+  // diag(q) xf, into the weight-grad product's operand
+  NC_TRY(xent_grad_prep<T>(s.z, M, m.V, s.lse, s.zt, tg, s.nv, dloss, m.cap, s.xf, m.d, c.xs, c.q, st));
+  NC_TRY(gemm_dyw_scaled<T>(s.z, wlm, c.dxf, c.q, M, m.V, m.d, st, (long)M * kPanel));
+  NC_TRY(gemm_dw<T>(s.z, c.xs, dwlm, M, m.V, m.d, acc, c.partial, c.partial_elems, st, (long)M * kPanel));
   NC_TRY(rmsnorm_bwd<T, T>(c.dxf, s.xf, s.rf, nullptr, dx, M, m.d, st));
   return NC_OK;
 }

@@ -444,6 +444,32 @@ struct EpiStore {
   __device__ __forceinline__ void publish(float t) const { amax_publish_wave(to_f32(from_f32<T>(t)), amax); }
 };
 
+// C = q[row] acc in the storage type: the unembedding's input-grad product,
+// whose rows carry the softmax normaliser and the loss scale as one factor.
+// The factors are loaded for every row of the wave before its first store.
+template <typename T>
+struct EpiRowScale {
+  T* C;
+  long ldc;
+  const float* q;
+  int M, N;
+  struct RowState {
+    float q;
+  };
+  __device__ __forceinline__ void row_begin(RowState& rs, int row) const { rs.q = row < M ? q[row] : 0.f; }
+  __device__ __forceinline__ void pre(RowState& rs, int, int, float* v) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= rs.q;
+  }
+  __device__ __forceinline__ void row_end(RowState&, const EpiCtx&, int) const {}
+  __device__ __forceinline__ void finish(const EpiCtx&) const {}
+  using Aux = NoAux;
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
+  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
+    tile_store4<T>(tile_rsrc(C, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
+  }
+};
+
 // y = alpha * acc + beta * res (res a compile-time choice), stored in T: the steps of the
 // Newton-Schulz iteration (B = c (A A^T) + b A, X' = (X B^T) + a X).
 template <typename T, bool HasRes = true>
@@ -532,7 +558,14 @@ struct EpiF32 {
 // (|z'| <= c, so no running maximum is needed in float32). The tanh and
 // exponentials use the hardware exp2 and reciprocal:
 // c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
-template <typename T, int BM, int BN>
+// With Grad (the training step's head) the tile stores instead what the
+// softcapped cross-entropy's gradient needs from each logit,
+// u = exp(z' - c) (1 - (z'/c)^2), and the row sums are of exp(z' - c): then
+// dz = dloss / Nv / S (u - onehot(target) S (1 - (z'_target/c)^2)), S the
+// row's sum, so the backward never passes over the [M, V] matrix again
+// (one element a row is corrected, 1/S goes into the products as a row
+// scale), and the factor 1 - (z'/c)^2 comes from float32 z', not its rounding.
+template <typename T, int BM, int BN, bool Grad = false>
 struct EpiSoftcap {
   T* Z;        // [M, N] in column panels of kPanel
   int zpanel;  // panel stride (elements): M * kPanel
@@ -541,6 +574,8 @@ struct EpiSoftcap {
   float* part;
   int n_tiles;
   int M, N;
+  float inv_cap = 0.f;  // Grad: 1 / c
+  float cap_lg = 0.f;   // Grad: c log2(e)
   struct RowState {
     float sum;
   };
@@ -555,8 +590,18 @@ struct EpiSoftcap {
       v[e] = cap - 2.f * cap * __builtin_amdgcn_rcpf(t + 1.f);
     }
     float s4 = 0.f;
+    if constexpr (Grad) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s4 += __builtin_amdgcn_exp2f(v[e] * lg);
+      for (int e = 0; e < 4; ++e) {
+        const float ex = __builtin_amdgcn_exp2f(v[e] * lg - cap_lg);  // exp(z' - c) <= 1
+        const float w = v[e] * inv_cap;
+        s4 += ex;
+        v[e] = ex * (1.f - w * w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s4 += __builtin_amdgcn_exp2f(v[e] * lg);
+    }
     rs.sum += row < M && col < N ? s4 : 0.f;
   }
   __device__ __forceinline__ void row_end(RowState& rs, const EpiCtx& x, int i) const {

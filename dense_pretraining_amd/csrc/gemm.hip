@@ -149,6 +149,19 @@ nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, i
 }
 
 template <typename T>
+nc_status gemm_dyw_scaled(const T* dy, const T* w, T* dx, const float* q, int M, int N, int K, hipStream_t st,
+                          long dy_panel) {
+  if (!tile_span_ok(K, sizeof(T)) || !q) return NC_ERR_UNSUPPORTED;
+  GemmShape s{dy, w, N, K, M, K, N, N, 1};
+  s.a_panel = dy_panel;
+  const double es = sizeof(T);
+  ProfScope prof(NC_NAME(T, "gemm_dx"), 2.0 * M * N * K, es * ((double)M * N + (double)N * K + (double)M * K) + 4.0 * M,
+                 st);
+  EpiRowScale<T> e{dx, K, q, M, K};
+  return launch_gemm<T, kKc, kKo>(s, e, st);
+}
+
+template <typename T>
 nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int accumulate, float* partial,
                   size_t partial_elems, hipStream_t st, long dy_panel) {
   if (!tile_span_ok(K, sizeof(float))) return NC_ERR_UNSUPPORTED;
@@ -188,7 +201,8 @@ int lmhead_tiles(int N, bool bf16_storage) {
 }
 
 template <typename T>
-nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st) {
+nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st,
+                      bool grad) {
   // a tile's 8 column panels of M * kPanel elements are addressed with 32-bit
   // offsets, the panel stride through a 24-bit multiply
   if (!tile_span_ok(M, sizeof(T)) || (long)M * kPanel * 8 * (long)sizeof(T) >= (long)kDmaRecords ||
@@ -198,8 +212,15 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   ProfScope prof(NC_NAME(T, "gemm_lmhead_softcap"), 2.0 * M * N * K,
                  sizeof(T) * ((double)M * K + (double)N * K + (double)M * N) + 4.0 * M * lmhead_tiles(N, is_bf16<T>()),
                  st);
-  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, M * kPanel, cap, (float)(2.8853900817779268 / cap), part,
-                                                   lmhead_tiles(N, is_bf16<T>()), M, N};
+  const float k2 = (float)(2.8853900817779268 / cap);
+  if (grad) {
+    EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN, true> e{z, M * kPanel, cap, k2, part, lmhead_tiles(N, is_bf16<T>()),
+                                                         M, N};
+    e.inv_cap = 1.f / cap;
+    e.cap_lg = (float)(cap * 1.4426950408889634);
+    return launch_gemm<T, kKc, kKc>(s, e, st);
+  }
+  EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, M * kPanel, cap, k2, part, lmhead_tiles(N, is_bf16<T>()), M, N};
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
@@ -211,7 +232,8 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   template nc_status gemm_dyw<T>(const T*, const T*, T*, const T*, int, int, int, hipStream_t, long);         \
   template nc_status gemm_dw<T>(const T*, const T*, float*, int, int, int, int, float*, size_t, hipStream_t,  \
                                 long);                                                                        \
-  template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, float*, hipStream_t);
+  template nc_status gemm_dyw_scaled<T>(const T*, const T*, T*, const float*, int, int, int, hipStream_t, long); \
+  template nc_status gemm_lmhead<T>(const T*, const T*, T*, int, int, int, float, float*, hipStream_t, bool);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST

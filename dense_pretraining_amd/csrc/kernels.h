@@ -43,6 +43,10 @@ nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch = 
 template <typename T>
 nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, int K, hipStream_t st,
                    long dy_panel = 0);
+// dx[M,K] = diag(q) dy[M,N] W[N,K]: the unembedding's input gradient, q one factor per row.
+template <typename T>
+nc_status gemm_dyw_scaled(const T* dy, const T* w, T* dx, const float* q, int M, int N, int K, hipStream_t st,
+                          long dy_panel = 0);
 // dW[N,K] (+)= dy[M,N]^T x[M,K] (float32), split over M when that helps fill
 // the GPU (partials in `partial`, summed in a fixed order).
 template <typename T>
@@ -50,9 +54,11 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int a
                   size_t partial_elems, hipStream_t st, long dy_panel = 0);
 size_t gemm_dw_partial_elems(int M, int N, int K);
 // Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N] in column panels;
-// part[M, lmhead_tiles(N)] = per-tile sums of exp(z).
+// part[M, lmhead_tiles(N)] = per-tile sums of exp(z). With grad: u = exp(z - c) (1 - (z/c)^2)
+// is stored instead and the sums are of exp(z - c).
 template <typename T>
-nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st);
+nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st,
+                      bool grad = false);
 int lmhead_tiles(int N, bool bf16_storage);
 
 // ------------------------------------------------------------ few-row products (skinny.hip)
@@ -102,19 +108,23 @@ nc_status qknorm_rope_fwd(const T* qkv, long ld_in, T* qk, long ld_out, const fl
 template <typename T>
 nc_status qknorm_rope_bwd(const T* qkv, long ld_in, T* g, long ld_g, const float* cs, const float* sn, int M, int T_,
                           int nheads, int D, float eps, hipStream_t st);
-// Cross-entropy: lse[m] = log(sum of part[m][:]); loss = mean over valid
-// targets of lse - z_t, with the target's logit z_t = c tanh(x[m] . w[t] / c)
-// recomputed from the unembedding's input x [M, d] and weight w [V, d];
-// nv = count of valid targets; writes loss and status.
+// Cross-entropy: lse[m] = shift + log(sum of part[m][:]) (the sums taken of
+// exp(z - shift)); loss = mean over valid targets of lse - z_t, with the
+// target's logit z_t = c tanh(x[m] . w[t] / c) recomputed from the
+// unembedding's input x [M, d] and weight w [V, d] (also written to zt[m]
+// when zt is given); nv = count of valid targets; writes loss and status.
 template <typename T>
 nc_status xent_loss(const float* part, int ntiles, const T* x, const T* w, int d, float cap, const int32_t* targets,
                     int M, int V, float* lse, float* block_sums, int* block_counts, float* loss, int* nv,
-                    uint32_t* status, hipStream_t st);
+                    uint32_t* status, hipStream_t st, float shift = 0.f, float* zt = nullptr);
 size_t xent_loss_blocks(int M);
-// In place: z <- (exp(z - lse) - onehot) * dloss/nv * (1 - (z/c)^2) on valid rows, 0 elsewhere.
+// The backward's pass over the rows (not the logits) when the head stored
+// u = exp(z - c) (1 - (z/c)^2): u[m][t] -= S (1 - (zt/c)^2) at each row's target,
+// S = exp(lse - c); q[m] = dloss / nv / S on rows with a target, 0 elsewhere;
+// xs = diag(q) xf. Then dz = diag(q) u.
 template <typename T>
-nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, const int* nv, float dloss, float cap,
-                  hipStream_t st);
+nc_status xent_grad_prep(T* u, int M, int V, const float* lse, const float* zt, const int32_t* targets, const int* nv,
+                         float dloss, float cap, const T* xf, int d, T* xs, float* q, hipStream_t st);
 // out (+)= sum_z partial[z] (fixed order) for float arrays of n elements.
 nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, int accumulate, hipStream_t st);
 

@@ -264,7 +264,8 @@ __global__ void __launch_bounds__(256) xent_rows_kernel(const float* __restrict_
                                                         const T* __restrict__ x, const T* __restrict__ w, int d,
                                                         float cap, const int32_t* __restrict__ tg, int M, int V,
                                                         float* __restrict__ lse, float* __restrict__ block_sums,
-                                                        int* __restrict__ block_counts, uint32_t* status) {
+                                                        int* __restrict__ block_counts, uint32_t* status, float shift,
+                                                        float* __restrict__ zt) {
   __shared__ float ws[4];
   __shared__ int wc[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -276,13 +277,14 @@ __global__ void __launch_bounds__(256) xent_rows_kernel(const float* __restrict_
     float s = 0.f;
     for (int t = lane; t < ntiles; t += 64) s += part[(long)m * ntiles + t];
     s = wave_sum(s);
-    const float l = logf(s);
+    const float l = shift + logf(s);
     int y = tg[m];
     if (y < -1 || y >= V) {
       if (lane == 0) set_status(status, kStatusBadTarget);
       y = -1;
     }
     if (lane == 0) lse[m] = l;
+    if (zt && y < 0 && lane == 0) zt[m] = 0.f;
     if (y >= 0) {
       constexpr int n = Vec<T>::n;
       float dot = 0.f;
@@ -294,7 +296,9 @@ __global__ void __launch_bounds__(256) xent_rows_kernel(const float* __restrict_
         for (int e = 0; e < n; ++e) dot += a[e] * b[e];
       }
       dot = wave_sum(dot);
-      acc += l - cap * tanhf(dot / cap);
+      const float zy = cap * tanhf(dot / cap);
+      if (zt && lane == 0) zt[m] = zy;
+      acc += l - zy;
       cnt += 1;
     }
   }
@@ -340,48 +344,45 @@ __global__ void __launch_bounds__(256) xent_final_kernel(const float* __restrict
   }
 }
 
-// dz = (softmax(z') - onehot(y)) * dloss / Nv * (1 - (z'/c)^2), in place, over
-// the column-panel layout of the logits: block (x, p) covers rows
-// [x * ROWS, (x+1) * ROWS) of panel p, each thread one 16-byte piece.
-// A thread takes one 16-byte piece of a row in each of kXentPanels
-// consecutive panels: the row's target and LSE are read once per two pieces,
-// and both pieces' loads are in flight together (measured: 1, 2, 4, 8 panels
-// at 68, 70, 67, 64 % of HBM peak).
-constexpr int kXentPanels = 2;
-
+// The softcapped cross-entropy's backward over rows (the logits are not read
+// again): the unembedding stored u = exp(z' - c) (1 - (z'/c)^2) per logit, so
+// dz[m][v] = g / S (u[m][v] - [v = y] S (1 - (z'_y/c)^2)) with g = dloss / Nv
+// and S = exp(lse - c) the row's sum of exp(z' - c) (imeisheng.com section
+// "预训练" for the loss; the softcap from the architecture list). One wave a
+// row: lane 0 corrects the target's element of u (in the column-panel layout)
+// and writes q = g / S; the wave writes xs = q xf, the weight-gradient
+// product's row-scaled operand. Rows without a target get q = 0.
 template <typename T>
-__global__ void __launch_bounds__(256) xent_dz_kernel(T* __restrict__ z, int M, int V, const float* __restrict__ lse,
-                                                      const int32_t* __restrict__ tg, const int* __restrict__ nvp,
-                                                      float dloss, float inv_cap) {
+__global__ void __launch_bounds__(256) xent_grad_prep_kernel(T* __restrict__ u, int M, int V,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ zt,
+                                                             const int32_t* __restrict__ tg,
+                                                             const int* __restrict__ nvp, float dloss, float cap,
+                                                             const T* __restrict__ xf, int d, T* __restrict__ xs,
+                                                             float* __restrict__ q) {
   constexpr int VE = Vec<T>::n;
-  constexpr int PER_ROW = kPanel / VE;  // pieces per panel row
-  constexpr int ROWS = 256 / PER_ROW;
-  const int p0 = blockIdx.y * kXentPanels;
-  const int m = blockIdx.x * ROWS + threadIdx.x / PER_ROW;
-  const int c0 = (threadIdx.x % PER_ROW) * VE;  // column inside a panel
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (m >= M) return;
   const int y = tg[m];
-  const bool valid = y >= 0 && y < V;
-  const float gsc = valid ? dloss / (float)*nvp : 0.f;
-  const float l = lse[m];
-  float v[kXentPanels][VE];
-#pragma unroll
-  for (int i = 0; i < kXentPanels; ++i) {
-    const int v0 = (p0 + i) * kPanel + c0;  // V % VE == 0: a piece is wholly inside or outside
-    if (v0 < V) load16<T>(z + (long)(p0 + i) * M * kPanel + (long)m * kPanel + c0, v[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < kXentPanels; ++i) {
-    const int v0 = (p0 + i) * kPanel + c0;
-    if (v0 >= V) continue;
-#pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      float pr = __expf(v[i][e] - l);
-      if (v0 + e == y) pr -= 1.f;
-      const float zc = v[i][e] * inv_cap;
-      v[i][e] = pr * gsc * (1.f - zc * zc);
+  const int nv = *nvp;
+  const bool valid = y >= 0 && y < V && nv > 0;
+  const float S = expf(lse[m] - cap);
+  const float qm = valid ? dloss / (float)nv / S : 0.f;
+  if (lane == 0) {
+    q[m] = qm;
+    if (valid) {
+      T* p = u + (long)(y / kPanel) * M * kPanel + (long)m * kPanel + y % kPanel;
+      const float w = zt[m] / cap;
+      *p = from_f32<T>(to_f32(*p) - S * (1.f - w * w));
     }
-    store16<T>(z + (long)(p0 + i) * M * kPanel + (long)m * kPanel + c0, v[i]);
+  }
+  const long off = (long)m * d;
+  for (int c = VE * lane; c < d; c += 64 * VE) {
+    float a[VE];
+    load16<T>(xf + off + c, a);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) a[e] *= qm;
+    store16<T>(xs + off + c, a);
   }
 }
 
@@ -513,12 +514,12 @@ size_t xent_loss_blocks(int M) { return (size_t)(M + 31) / 32; }
 template <typename T>
 nc_status xent_loss(const float* part, int ntiles, const T* x, const T* w, int d, float cap, const int32_t* targets,
                     int M, int V, float* lse, float* block_sums, int* block_counts, float* loss, int* nv,
-                    uint32_t* status, hipStream_t st) {
+                    uint32_t* status, hipStream_t st, float shift, float* zt) {
   if (d % Vec<T>::n != 0) return NC_ERR_UNSUPPORTED;
   int nb = (int)xent_loss_blocks(M);
   ProfScope prof("xent_loss", 0, 4.0 * M * ntiles + 12.0 * M + 2.0 * sizeof(T) * M * d, st);
   hipLaunchKernelGGL((xent_rows_kernel<T>), dim3(nb), dim3(256), 0, st, part, ntiles, x, w, d, cap, targets, M, V,
-                     lse, block_sums, block_counts, status);
+                     lse, block_sums, block_counts, status, shift, zt);
   NC_LAUNCH_CHECK("xent_rows");
   hipLaunchKernelGGL(xent_final_kernel, dim3(1), dim3(256), 0, st, block_sums, block_counts, nb, loss, nv, status);
   NC_LAUNCH_CHECK("xent_final");
@@ -526,14 +527,14 @@ nc_status xent_loss(const float* part, int ntiles, const T* x, const T* w, int d
 }
 
 template <typename T>
-nc_status xent_dz(T* z, int M, int V, const float* lse, const int32_t* targets, const int* nv, float dloss, float cap,
-                  hipStream_t st) {
-  constexpr int ROWS = 256 / (kPanel / Vec<T>::n);
-  const int panels = (V + kPanel - 1) / kPanel;
-  dim3 grid((M + ROWS - 1) / ROWS, (panels + kXentPanels - 1) / kXentPanels);
-  ProfScope prof(NC_NAME(T, "xent_dz"), 0, 2.0 * sizeof(T) * M * V + 12.0 * M, st);
-  hipLaunchKernelGGL((xent_dz_kernel<T>), grid, dim3(256), 0, st, z, M, V, lse, targets, nv, dloss, 1.f / cap);
-  NC_LAUNCH_CHECK("xent_dz");
+nc_status xent_grad_prep(T* u, int M, int V, const float* lse, const float* zt, const int32_t* targets, const int* nv,
+                         float dloss, float cap, const T* xf, int d, T* xs, float* q, hipStream_t st) {
+  if (d % Vec<T>::n != 0) return NC_ERR_UNSUPPORTED;
+  // rows' x read and scaled x written; the target corrections and per-row words
+  ProfScope prof(NC_NAME(T, "xent_grad_prep"), 0, 2.0 * sizeof(T) * M * d + 20.0 * M, st);
+  hipLaunchKernelGGL((xent_grad_prep_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, st, u, M, V, lse, zt, targets, nv,
+                     dloss, cap, xf, d, xs, q);
+  NC_LAUNCH_CHECK("xent_grad_prep");
   return NC_OK;
 }
 
@@ -557,9 +558,10 @@ nc_status splitk_reduce(const float* partial, int nsplit, size_t n, float* out, 
                                         float, hipStream_t, int);                                                   \
   template nc_status qknorm_rope_bwd<T>(const T*, long, T*, long, const float*, const float*, int, int, int, int,   \
                                         float, hipStream_t);                                                        \
-  template nc_status xent_dz<T>(T*, int, int, const float*, const int32_t*, const int*, float, float, hipStream_t); \
+  template nc_status xent_grad_prep<T>(T*, int, int, const float*, const float*, const int32_t*, const int*, float, \
+                                       float, const T*, int, T*, float*, hipStream_t);                                 \
   template nc_status xent_loss<T>(const float*, int, const T*, const T*, int, float, const int32_t*, int, int,      \
-                                  float*, float*, int*, float*, int*, uint32_t*, hipStream_t);
+                                  float*, float*, int*, float*, int*, uint32_t*, hipStream_t, float, float*);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST

@@ -156,7 +156,7 @@ CLASSES = [
     ("rmsnorm_fwd", r"rmsnorm_fwd_kernel"),
     ("qknorm_rope_bwd", r"qknorm_rope_bwd_kernel"),
     ("qknorm_rope_fwd", r"qknorm_rope_fwd_kernel"),
-    ("xent_dz", r"xent_dz_kernel"),
+    ("xent_grad_prep", r"xent_grad_prep_kernel"),
     ("xent_loss", r"xent_rows_kernel|xent_final_kernel"),
     ("splitk_reduce", r"splitk_reduce_kernel"),
     ("embed_bwd (sort, window sums with the norm backward, fixup)", r"eb_\w+_kernel"),

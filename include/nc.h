@@ -189,16 +189,20 @@ nc_status nc_block_bwd(const nc_config* cfg, const nc_block_params* w, const voi
  * xf = N(x); z = xf Wlm^T; z' = c tanh(z/c);
  * loss = mean over m with targets[m] != -1 of logsumexp(z'[m]) - z'[m][targets[m]].
  * x [M,d]; wlm [V,d]; loss: one float (device, out). saved [lmhead_saved bytes]
- * keeps xf, the logits z' (storage dtype, [M,V]) and the row log-sum-exps. */
+ * keeps xf, per logit u = exp(z' - c) (1 - (z'/c)^2) (storage dtype, [M,V]; the
+ * logits themselves are not kept), the row log-sum-exps and the targets'
+ * softcapped logits. */
 nc_status nc_lmhead_softcap_xent_fwd(const nc_config* cfg, const void* x, const void* wlm,
                                      const int32_t* targets, float* loss, void* saved,
                                      void* scratch, void* stream);
 
 /* Backward of the above scaled by dloss: dz = (softmax(z') - onehot(target))
  * * dloss / Nv * (1 - (z'/c)^2) on valid rows (0 on ignored rows);
- * dWlm = dz^T xf; dx = N_bwd(dz Wlm). The logits in `saved` are overwritten
- * by dz, so call it once per forward. dx [M,d] (out); dwlm float [V,d]
- * (written, or added to when accumulate != 0). */
+ * dWlm = dz^T xf; dx = N_bwd(dz Wlm). dz is never formed: with S the row's
+ * sum of exp(z' - c), dz = dloss / Nv / S (u - onehot(target) S (1 - (z'_t/c)^2)),
+ * the target's element of u in `saved` is corrected in place (call it once
+ * per forward) and the row factor goes into both products. dx [M,d] (out);
+ * dwlm float [V,d] (written, or added to when accumulate != 0). */
 nc_status nc_lmhead_softcap_xent_bwd(const nc_config* cfg, const void* x, const void* wlm,
                                      const int32_t* targets, void* saved, float dloss, void* dx,
                                      float* dwlm, int accumulate, void* scratch, void* stream);
