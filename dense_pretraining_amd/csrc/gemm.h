@@ -560,11 +560,13 @@ struct EpiF32 {
 // c tanh(x/c) = c - 2c / (2^(x 2 log2(e)/c) + 1).
 // With Grad (the training step's head) the tile stores instead what the
 // softcapped cross-entropy's gradient needs from each logit,
-// u = exp(z' - c) (1 - (z'/c)^2), and the row sums are of exp(z' - c): then
-// dz = dloss / Nv / S (u - onehot(target) S (1 - (z'_target/c)^2)), S the
-// row's sum, so the backward never passes over the [M, V] matrix again
-// (one element a row is corrected, 1/S goes into the products as a row
-// scale), and the factor 1 - (z'/c)^2 comes from float32 z', not its rounding.
+// u = exp(z' - c) (1 - (z'/c)^2) / 4, and the row sums are of exp(z' - c):
+// then dz = 4 dloss / Nv / S (u - onehot(target) S (1 - (z'_target/c)^2) / 4),
+// S the row's sum, so the backward never passes over the [M, V] matrix again
+// (one element a row is corrected, 4/S goes into the products as a row
+// scale). With r = 1 / (2^(2 log2(e) z / c) + 1): z' - c = -2c r and
+// (1 - (z'/c)^2) / 4 = r (1 - r), so z' itself is never formed, and the factor
+// comes from float32 r rather than a rounded z' (which cancels near |z'| = c).
 template <typename T, int BM, int BN, bool Grad = false>
 struct EpiSoftcap {
   T* Z;        // [M, N] in column panels of kPanel
@@ -574,8 +576,7 @@ struct EpiSoftcap {
   float* part;
   int n_tiles;
   int M, N;
-  float inv_cap = 0.f;  // Grad: 1 / c
-  float cap_lg = 0.f;   // Grad: c log2(e)
+  float kc = 0.f;  // Grad: -2 c log2(e)
   struct RowState {
     float sum;
   };
@@ -584,21 +585,21 @@ struct EpiSoftcap {
   // columns add nothing to the row's sum of exp(z')
   __device__ __forceinline__ void pre(RowState& rs, int row, int col, float* v) const {
     const float lg = 1.4426950408889634f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float t = __builtin_amdgcn_exp2f(v[e] * k2);
-      v[e] = cap - 2.f * cap * __builtin_amdgcn_rcpf(t + 1.f);
-    }
     float s4 = 0.f;
     if constexpr (Grad) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float ex = __builtin_amdgcn_exp2f(v[e] * lg - cap_lg);  // exp(z' - c) <= 1
-        const float w = v[e] * inv_cap;
+        const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(v[e] * k2) + 1.f);
+        const float ex = __builtin_amdgcn_exp2f(r * kc);  // exp(z' - c) <= 1
         s4 += ex;
-        v[e] = ex * (1.f - w * w);
+        v[e] = ex * (r - r * r);
       }
     } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = __builtin_amdgcn_exp2f(v[e] * k2);
+        v[e] = cap - 2.f * cap * __builtin_amdgcn_rcpf(t + 1.f);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) s4 += __builtin_amdgcn_exp2f(v[e] * lg);
     }

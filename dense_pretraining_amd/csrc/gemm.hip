@@ -216,8 +216,7 @@ nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float c
   if (grad) {
     EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN, true> e{z, M * kPanel, cap, k2, part, lmhead_tiles(N, is_bf16<T>()),
                                                          M, N};
-    e.inv_cap = 1.f / cap;
-    e.cap_lg = (float)(cap * 1.4426950408889634);
+    e.kc = (float)(-2.0 * cap * 1.4426950408889634);
     return launch_gemm<T, kKc, kKc>(s, e, st);
   }
   EpiSoftcap<T, GemmTile<T>::BM, GemmTile<T>::BN> e{z, M * kPanel, cap, k2, part, lmhead_tiles(N, is_bf16<T>()), M, N};

@@ -54,7 +54,7 @@ nc_status gemm_dw(const T* dy, const T* x, float* dw, int M, int N, int K, int a
                   size_t partial_elems, hipStream_t st, long dy_panel = 0);
 size_t gemm_dw_partial_elems(int M, int N, int K);
 // Unembedding with the softcap epilogue: z = c tanh((x W^T)/c) stored [M,N] in column panels;
-// part[M, lmhead_tiles(N)] = per-tile sums of exp(z). With grad: u = exp(z - c) (1 - (z/c)^2)
+// part[M, lmhead_tiles(N)] = per-tile sums of exp(z). With grad: u = exp(z - c) (1 - (z/c)^2) / 4
 // is stored instead and the sums are of exp(z - c).
 template <typename T>
 nc_status gemm_lmhead(const T* x, const T* w, T* z, int M, int N, int K, float cap, float* part, hipStream_t st,
@@ -119,9 +119,9 @@ nc_status xent_loss(const float* part, int ntiles, const T* x, const T* w, int d
                     uint32_t* status, hipStream_t st, float shift = 0.f, float* zt = nullptr);
 size_t xent_loss_blocks(int M);
 // The backward's pass over the rows (not the logits) when the head stored
-// u = exp(z - c) (1 - (z/c)^2): u[m][t] -= S (1 - (zt/c)^2) at each row's target,
-// S = exp(lse - c); q[m] = dloss / nv / S on rows with a target, 0 elsewhere;
-// xs = diag(q) xf. Then dz = diag(q) u.
+// u = exp(z - c) (1 - (z/c)^2) / 4: u[m][t] -= S (1 - (zt/c)^2) / 4 at each
+// row's target, S = exp(lse - c); q[m] = 4 dloss / nv / S on rows with a
+// target, 0 elsewhere; xs = diag(q) xf. Then dz = diag(q) u.
 template <typename T>
 nc_status xent_grad_prep(T* u, int M, int V, const float* lse, const float* zt, const int32_t* targets, const int* nv,
                          float dloss, float cap, const T* xf, int d, T* xs, float* q, hipStream_t st);

@@ -345,13 +345,14 @@ __global__ void __launch_bounds__(256) xent_final_kernel(const float* __restrict
 }
 
 // The softcapped cross-entropy's backward over rows (the logits are not read
-// again): the unembedding stored u = exp(z' - c) (1 - (z'/c)^2) per logit, so
-// dz[m][v] = g / S (u[m][v] - [v = y] S (1 - (z'_y/c)^2)) with g = dloss / Nv
-// and S = exp(lse - c) the row's sum of exp(z' - c) (imeisheng.com section
-// "预训练" for the loss; the softcap from the architecture list). One wave a
-// row: lane 0 corrects the target's element of u (in the column-panel layout)
-// and writes q = g / S; the wave writes xs = q xf, the weight-gradient
-// product's row-scaled operand. Rows without a target get q = 0.
+// again): the unembedding stored u = exp(z' - c) (1 - (z'/c)^2) / 4 per logit,
+// so dz[m][v] = 4 g / S (u[m][v] - [v = y] S (1 - (z'_y/c)^2) / 4) with
+// g = dloss / Nv and S = exp(lse - c) the row's sum of exp(z' - c)
+// (imeisheng.com section "预训练" for the loss; the softcap from the
+// architecture list). One wave a row: lane 0 corrects the target's element of
+// u (in the column-panel layout) and writes q = 4 g / S; the wave writes
+// xs = q xf, the weight-gradient product's row-scaled operand. Rows without a
+// target get q = 0.
 template <typename T>
 __global__ void __launch_bounds__(256) xent_grad_prep_kernel(T* __restrict__ u, int M, int V,
                                                              const float* __restrict__ lse,
@@ -367,13 +368,13 @@ __global__ void __launch_bounds__(256) xent_grad_prep_kernel(T* __restrict__ u, 
   const int nv = *nvp;
   const bool valid = y >= 0 && y < V && nv > 0;
   const float S = expf(lse[m] - cap);
-  const float qm = valid ? dloss / (float)nv / S : 0.f;
+  const float qm = valid ? 4.f * dloss / (float)nv / S : 0.f;
   if (lane == 0) {
     q[m] = qm;
     if (valid) {
       T* p = u + (long)(y / kPanel) * M * kPanel + (long)m * kPanel + y % kPanel;
       const float w = zt[m] / cap;
-      *p = from_f32<T>(to_f32(*p) - S * (1.f - w * w));
+      *p = from_f32<T>(to_f32(*p) - 0.25f * S * (1.f - w * w));
     }
   }
   const long off = (long)m * d;

@@ -189,7 +189,7 @@ nc_status nc_block_bwd(const nc_config* cfg, const nc_block_params* w, const voi
  * xf = N(x); z = xf Wlm^T; z' = c tanh(z/c);
  * loss = mean over m with targets[m] != -1 of logsumexp(z'[m]) - z'[m][targets[m]].
  * x [M,d]; wlm [V,d]; loss: one float (device, out). saved [lmhead_saved bytes]
- * keeps xf, per logit u = exp(z' - c) (1 - (z'/c)^2) (storage dtype, [M,V]; the
+ * keeps xf, per logit u = exp(z' - c) (1 - (z'/c)^2) / 4 (storage dtype, [M,V]; the
  * logits themselves are not kept), the row log-sum-exps and the targets'
  * softcapped logits. */
 nc_status nc_lmhead_softcap_xent_fwd(const nc_config* cfg, const void* x, const void* wlm,
