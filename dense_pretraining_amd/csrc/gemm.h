@@ -231,6 +231,13 @@ struct EpiCtx {
   float scale = 1.f;  // FP8 products: the operands' scale product, read once per tile
 };
 
+// A store-phase group of 4 values: its row and first column, and the parts
+// of them that are the same in every lane (ru rows and cu columns past the
+// lane's first group).
+struct EpiPos {
+  int row, col, ru, cu;
+};
+
 // The dequantisation scale product of an FP8 epilogue (members sa, sb), 1 otherwise.
 template <typename Epi, typename = void>
 struct EpiScaled { static constexpr bool value = false; };
@@ -277,7 +284,8 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
     for (int it = 0; it < 8; ++it)
 #pragma unroll
       for (int k = 0; k < NCH / 16; ++k)
-        aux[it][k] = epi.load_aux(x, r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k));
+        aux[it][k] = epi.load_aux(x, EpiPos{r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k),
+                                            32 * i + 4 * it, 64 * k});
 #pragma unroll
     for (int j = 0; j < WTN; ++j)
 #pragma unroll
@@ -314,7 +322,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
         for (int k = 0; k < NCH / 16; ++k) {
           const int cc = (lane & 15) + 16 * k;
           float v[4] = {q[ib][k].x, q[ib][k].y, q[ib][k].z, q[ib][k].w};
-          epi.post(x, r0 + 32 * i + rr, c0 + 4 * cc, v, aux[it][k]);
+          epi.post(x, EpiPos{r0 + 32 * i + rr, c0 + 4 * cc, 32 * i + 4 * it, 64 * k}, v, aux[it][k]);
           if constexpr (kMax) epi.track(tmax, r0 + 32 * i + rr, c0 + 4 * cc, v);
         }
       }
@@ -345,21 +353,27 @@ __device__ __forceinline__ void aux_get(const Aux4<T>& a, float* v) {
 }
 struct NoAux {};
 
-// Branch-free epilogue I/O. A buffer resource starts at the tile origin; an
-// element outside the matrix gets an offset past the record, which the
-// hardware drops on a store and reads as zero on a load. With no branch per
-// element, the slab reads and stores of a row are scheduled together instead
-// of one read, one wait, one store at a time.
+// Branch-free epilogue I/O. A buffer resource starts at the tile origin and
+// its record ends at the matrix's last row, so a row at or past M is out of
+// the record with no test per element: the hardware drops such stores and
+// reads such loads as zero. A column at or past N gets an offset past the
+// record. With no branch per element, the slab reads and stores of a row are
+// scheduled together instead of one read, one wait, one store at a time (and
+// leaving the row test to the record takes about 110 vector instructions per
+// thread and tile out of the store phase).
 template <typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* base, long ld, const EpiCtx& x) {
-  return dma_rsrc(base + (long)x.m0 * ld + x.n0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc_m(const T* base, long ld, const EpiCtx& x, int M) {
+  const long rem = (long)(M - x.m0) * ld * (long)sizeof(T);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base + (long)x.m0 * ld + x.n0), (short)0,
+                                           (int)(rem < (long)kDmaRecords ? rem : (long)kDmaRecords), 0x00020000);
 }
+// Byte offset of a store-phase group from the tile origin: row - m0 < 256
+// and 256 ld es < 2^31 (checked by every launcher), so both factors fit 24
+// bits and the full-rate 24-bit multiply gives the product.
 template <typename T>
-__device__ __forceinline__ int tile_off(const EpiCtx& x, int row, int col, long ld, int M, int N) {
-  // row - m0 < 256 and 256 ld es < 2^31 (checked by every launcher): both
-  // factors fit 24 bits, so the full-rate 24-bit multiply gives the product
-  const unsigned r = __umul24((unsigned)(row - x.m0), (unsigned)ld);
-  return (int)(row < M && col < N ? (r + (unsigned)(col - x.n0)) * (unsigned)sizeof(T) : kDmaOOB);
+__device__ __forceinline__ int tile_off(const EpiCtx& x, const EpiPos& p, long ld, int N) {
+  const unsigned r = __umul24((unsigned)(p.row - x.m0), (unsigned)ld);
+  return (int)(p.col < N ? (r + (unsigned)(p.col - x.n0)) * (unsigned)sizeof(T) : kDmaOOB);
 }
 typedef int epi_v2i __attribute__((ext_vector_type(2)));
 typedef int epi_v4i __attribute__((ext_vector_type(4)));
@@ -415,12 +429,12 @@ struct EpiStore {
   uint32_t* amax = nullptr;   // TrackMax: the striped maximum
   static constexpr bool kTracksMax = TrackMax;
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
-    if constexpr (HasRes) return tile_load4<T>(tile_rsrc(res, ldr, x), tile_off<T>(x, row, col, ldr, M, N));
+  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
+    if constexpr (HasRes) return tile_load4<T>(tile_rsrc_m(res, ldr, x, M), tile_off<T>(x, p, ldr, N));
     else return Aux{};
   }
   // (an FP8 product's scale is applied to the accumulators before phase 1)
-  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
     if constexpr (ReluSqOut) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -434,7 +448,7 @@ struct EpiStore {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += r[e];
     }
-    tile_store4<T>(tile_rsrc(C, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
+    tile_store4<T>(tile_rsrc_m(C, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
   }
   // after post (v holds the stored values before rounding)
   __device__ __forceinline__ void track(float& t, int row, int col, const float* v) const {
@@ -464,9 +478,9 @@ struct EpiRowScale {
   __device__ __forceinline__ void row_end(RowState&, const EpiCtx&, int) const {}
   __device__ __forceinline__ void finish(const EpiCtx&) const {}
   using Aux = NoAux;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
-  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
-    tile_store4<T>(tile_rsrc(C, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
+    tile_store4<T>(tile_rsrc_m(C, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
   }
 };
 
@@ -483,12 +497,12 @@ struct EpiAxpby {
   float alpha, beta;
   long c_batch, r_batch;  // per-problem strides of C and res in a batched launch
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
+  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
     if constexpr (HasRes)
-      return tile_load4<T>(tile_rsrc(res + x.batch * r_batch, ldr, x), tile_off<T>(x, row, col, ldr, M, N));
+      return tile_load4<T>(tile_rsrc_m(res + x.batch * r_batch, ldr, x, M), tile_off<T>(x, p, ldr, N));
     else return Aux{};
   }
-  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
     if constexpr (HasRes) {
       float r[4];
       aux_get<T>(a, r);
@@ -498,7 +512,7 @@ struct EpiAxpby {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] *= alpha;
     }
-    tile_store4<T>(tile_rsrc(C + x.batch * c_batch, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
+    tile_store4<T>(tile_rsrc_m(C + x.batch * c_batch, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
   }
 };
 
@@ -513,18 +527,18 @@ struct EpiDReluSq {
   long lda;
   int M, N;
   using Aux = Aux4<T>;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, int row, int col) const {
-    return tile_load4<T>(tile_rsrc(act, lda, x), tile_off<T>(x, row, col, lda, M, N));
+  __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
+    return tile_load4<T>(tile_rsrc_m(act, lda, x, M), tile_off<T>(x, p, lda, N));
   }
   // The square root is the bare hardware instruction (within 1 ulp): the
   // correctly rounded library form is about 17 vector instructions, which for
   // 256 elements a thread per tile cost several microseconds of every tile.
-  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux& a) const {
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
     float av[4];
     aux_get<T>(a, av);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= 2.f * __builtin_amdgcn_sqrtf(av[e]);
-    tile_store4<T>(tile_rsrc(C, ldc, x), tile_off<T>(x, row, col, ldc, M, N), v);
+    tile_store4<T>(tile_rsrc_m(C, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
   }
 };
 
@@ -538,10 +552,10 @@ struct EpiF32 {
   int accumulate;
   int M, N;
   using Aux = NoAux;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
-  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(C + (long)x.z * split_stride, ldc, x);
-    const int off = tile_off<float>(x, row, col, ldc, M, N);
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc_m(C + (long)x.z * split_stride, ldc, x, M);
+    const int off = tile_off<float>(x, p, ldc, N);
     if (accumulate) {
       float q[4];
       aux_get<float>(tile_load4<float>(rs, off), q);
@@ -611,8 +625,9 @@ struct EpiSoftcap {
     if (x.lane < 32) x.red[(x.wn ? BM : 0) + x.wm + 32 * i + x.lane] = s2;
   }
   using Aux = NoAux;
-  __device__ __forceinline__ Aux load_aux(const EpiCtx&, int, int) const { return Aux{}; }
-  __device__ __forceinline__ void post(const EpiCtx& x, int row, int col, float* v, const Aux&) const {
+  __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
+    const int row = p.row, col = p.col;
     // the tile's panels from its origin: panel (col - n0) / kPanel, row (row - m0)
     const __amdgpu_buffer_rsrc_t rs = dma_rsrc(Z + (long)(x.n0 / kPanel) * zpanel + (long)x.m0 * kPanel);
     const unsigned dc = (unsigned)(col - x.n0), dr = (unsigned)(row - x.m0);
