@@ -436,9 +436,11 @@ struct EpiStore {
   // (an FP8 product's scale is applied to the accumulators before phase 1)
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
     if constexpr (ReluSqOut) {
+      // max(v, 0) as one median of three (fmaxf adds a canonicalising max per
+      // element: 256 more vector instructions per thread and tile)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float r = fmaxf(v[e], 0.f);
+        const float r = __builtin_amdgcn_fmed3f(v[e], 0.f, 3.402823466e38f);
         v[e] = r * r;
       }
     }

@@ -125,7 +125,7 @@ __device__ __forceinline__ void skinny_epilogue(const SkinnyArgs& a, int nt, int
       for (int e = 0; e < 4; ++e) {
         o[e] = v[c + e] * rs;
         if constexpr (EPI == kSkinnyReluSq) {
-          const float q = fmaxf(o[e], 0.f);
+          const float q = __builtin_amdgcn_fmed3f(o[e], 0.f, 3.402823466e38f);  // max(o, 0), one instruction
           o[e] = q * q;
         }
       }
