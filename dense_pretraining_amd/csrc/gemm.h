@@ -421,8 +421,7 @@ struct EpiStore {
   NC_EPI_NO_ROW_WORK
   T* C;
   long ldc;
-  const T* res;  // optional residual, same layout as C
-  long ldr;
+  const T* res;  // optional residual, C's layout (the same leading dimension: one offset serves both)
   int M, N;
   const float* sa = nullptr;  // FP8 products: the two operands' dequantisation scales, multiplied in first
   const float* sb = nullptr;
@@ -430,7 +429,7 @@ struct EpiStore {
   static constexpr bool kTracksMax = TrackMax;
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
-    if constexpr (HasRes) return tile_load4<T>(tile_rsrc_m(res, ldr, x, M), tile_off<T>(x, p, ldr, N));
+    if constexpr (HasRes) return tile_load4<T>(tile_rsrc_m(res, ldc, x, M), tile_off<T>(x, p, ldc, N));
     else return Aux{};
   }
   // (an FP8 product's scale is applied to the accumulators before phase 1)
@@ -493,15 +492,14 @@ struct EpiAxpby {
   NC_EPI_NO_ROW_WORK
   T* C;
   long ldc;
-  const T* res;
-  long ldr;
+  const T* res;  // C's layout
   int M, N;
   float alpha, beta;
   long c_batch, r_batch;  // per-problem strides of C and res in a batched launch
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
     if constexpr (HasRes)
-      return tile_load4<T>(tile_rsrc_m(res + x.batch * r_batch, ldr, x, M), tile_off<T>(x, p, ldr, N));
+      return tile_load4<T>(tile_rsrc_m(res + x.batch * r_batch, ldc, x, M), tile_off<T>(x, p, ldc, N));
     else return Aux{};
   }
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
@@ -525,12 +523,11 @@ struct EpiDReluSq {
   NC_EPI_NO_ROW_WORK
   T* C;
   long ldc;
-  const T* act;  // a = max(u, 0)^2 as stored by the forward pass
-  long lda;
+  const T* act;  // a = max(u, 0)^2 as stored by the forward pass, C's layout
   int M, N;
   using Aux = Aux4<T>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
-    return tile_load4<T>(tile_rsrc_m(act, lda, x, M), tile_off<T>(x, p, lda, N));
+    return tile_load4<T>(tile_rsrc_m(act, ldc, x, M), tile_off<T>(x, p, ldc, N));
   }
   // The square root is the bare hardware instruction (within 1 ulp): the
   // correctly rounded library form is about 17 vector instructions, which for

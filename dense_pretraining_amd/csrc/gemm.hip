@@ -49,13 +49,13 @@ template <typename T, bool Relu, bool Track, typename Launch>
 nc_status with_store_epi(T* y, const T* res, int M, int N, const float* sa, const float* sb, uint32_t* amax,
                          Launch&& launch) {
   if (res) {
-    EpiStore<T, Relu, Track, true> e{y, N, res, N, M, N};
+    EpiStore<T, Relu, Track, true> e{y, N, res, M, N};
     e.sa = sa;
     e.sb = sb;
     e.amax = amax;
     return launch(e);
   }
-  EpiStore<T, Relu, Track, false> e{y, N, nullptr, 0, M, N};
+  EpiStore<T, Relu, Track, false> e{y, N, nullptr, M, N};
   e.sa = sa;
   e.sb = sb;
   e.amax = amax;
@@ -87,10 +87,10 @@ nc_status gemm_xwt_axpby(const T* x, const T* w, T* y, const T* res, int M, int 
   ProfScope prof(NC_NAME(T, "gemm_ns"), 2.0 * M * N * K * batch,
                  es * batch * ((double)M * K + (double)N * K + (double)M * N * (res ? 2 : 1)), st);
   if (!res) {
-    EpiAxpby<T, false> e{y, N, nullptr, N, M, N, alpha, 0.f, y_batch, 0};
+    EpiAxpby<T, false> e{y, N, nullptr, M, N, alpha, 0.f, y_batch, 0};
     return launch_gemm<T, kKc, kKc>(s, e, st);
   }
-  EpiAxpby<T, true> e{y, N, res, N, M, N, alpha, beta, y_batch, y_batch};
+  EpiAxpby<T, true> e{y, N, res, M, N, alpha, beta, y_batch, y_batch};
   return launch_gemm<T, kKc, kKc>(s, e, st);
 }
 
@@ -106,7 +106,7 @@ nc_status gemm_fp8(const uint8_t* xq, const uint8_t* wq, const float* sx, const 
   auto launch = [&](const auto& e) { return launch_gemm_f8(s, e, st); };
   if (amax_out) {
     if (!relu_sq_out || res) return NC_ERR_UNSUPPORTED;
-    EpiStore<bf16, true, true> e{y, N, nullptr, 0, M, N};
+    EpiStore<bf16, true, true> e{y, N, nullptr, M, N};
     e.sa = sx;
     e.sb = sw;
     e.amax = amax_out;
@@ -126,7 +126,7 @@ nc_status gemm_gram(const T* x, T* a, int R, int C, hipStream_t st, int batch, l
   s.b_batch = x_batch;
   const double es = sizeof(T);
   ProfScope prof(NC_NAME(T, "gemm_gram"), 2.0 * R * C * C * batch, es * batch * ((double)R * C + (double)C * C), st);
-  EpiAxpby<T, false> e{a, C, nullptr, C, C, C, 1.f, 0.f, a_batch, 0};
+  EpiAxpby<T, false> e{a, C, nullptr, C, C, 1.f, 0.f, a_batch, 0};
   return launch_gemm<T, kKo, kKo>(s, e, st);
 }
 
@@ -141,10 +141,10 @@ nc_status gemm_dyw(const T* dy, const T* w, T* dx, const T* act, int M, int N, i
   ProfScope prof(act ? NC_NAME(T, "gemm_dx_drelusq") : NC_NAME(T, "gemm_dx"), 2.0 * M * N * K,
                  es * ((double)M * N + (double)N * K + (double)M * K * (act ? 2 : 1)), st);
   if (act) {
-    EpiDReluSq<T> e{dx, K, act, K, M, K};
+    EpiDReluSq<T> e{dx, K, act, M, K};
     return launch_gemm<T, kKc, kKo>(s, e, st);
   }
-  EpiStore<T> e{dx, K, nullptr, 0, M, K};
+  EpiStore<T> e{dx, K, nullptr, M, K};
   return launch_gemm<T, kKc, kKo>(s, e, st);
 }
 

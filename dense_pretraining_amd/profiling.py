@@ -144,6 +144,7 @@ CLASSES = [
     ("gemm_dw (weight grads, split K)", r"EpiF32"),
     ("gemm_dx_drelusq (W2 input grad + dReLU^2)", r"EpiDReluSq"),
     ("gemm_lmhead_softcap", r"EpiSoftcap"),
+    ("gemm_lmhead_dx (unembedding input grad, row factors)", r"EpiRowScale"),
     ("gemm_dx (input grads)", r"ILi0ELi1ENS_8EpiStore|<0, 1, nc::EpiStore"),
     ("gemm_fwd +residual (O, W2)", r"ILi0ELi0ENS_8EpiStoreIDF16bLb0ELb0ELb1E"),
     ("gemm_fwd (QKV)", r"ILi0ELi0ENS_8EpiStoreIDF16bLb0ELb0ELb0E"),
