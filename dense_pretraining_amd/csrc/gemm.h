@@ -231,11 +231,14 @@ struct EpiCtx {
   float scale = 1.f;  // FP8 products: the operands' scale product, read once per tile
 };
 
-// A store-phase group of 4 values: its row and first column, and the parts
-// of them that are the same in every lane (ru rows and cu columns past the
-// lane's first group).
+// A store-phase group of 4 values: its row and first column, the parts of
+// them that are the same in every lane (ru rows and cu columns past the
+// lane's first group), and off, the group's byte offset in a row-major
+// output from its 32-row block's first row and the wave's first column
+// (kDmaOOB for a column at or past N): the store phase's offsets are the
+// same 16 values in every row block, so they are formed once per tile.
 struct EpiPos {
-  int row, col, ru, cu;
+  int row, col, ru, cu, off;
 };
 
 // The dequantisation scale product of an FP8 epilogue (members sa, sb), 1 otherwise.
@@ -271,6 +274,30 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
   const int lane = x.lane, lr = lane & 31, h = lane >> 5;
   const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
   float tmax = 0.f;
+  // Slab row r, chunk c sits at slab + 4 (r NCH + (c ^ (r & 15))). A phase-1
+  // write has c = 8j + 2g + h with h the lane's bit 0, so c ^ (r & 15) is
+  // (8j + 2g) ^ s1 for a per-lane s1; a phase-2 read has r = 4 it + lane / 16
+  // and c = lane % 16 + 16 k, so its address is one of four per-lane bases
+  // (it mod 4) plus a constant.
+  float* const w1 = slab + 4 * lr * NCH;
+  const int s1 = (lr & 15) ^ h;
+  const float* r2[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    r2[t] = slab + 4 * ((lane >> 4) * NCH + (((lane & 15) ^ (lane >> 4)) ^ (4 * t)));
+  // the store phase's byte offsets (EpiPos::off), one per group of a row
+  // block; a row past M is left to the row block's buffer record
+  int goff[8][NCH / 16];
+  {
+    const unsigned ld = (unsigned)epi.out_ld(), lrow = lane >> 4, lcol = 4 * (lane & 15);
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+      for (int k = 0; k < NCH / 16; ++k)
+        goff[it][k] = c0 + (int)lcol + 64 * k < epi.N
+                          ? (int)((__umul24(4 * it + lrow, ld) + lcol + 64 * k) * Epi::kOutBytes)
+                          : (int)kDmaOOB;
+  }
   // every row's state first: whatever it loads is in flight before the first store
   typename Epi::RowState rs[WTM];
 #pragma unroll
@@ -285,7 +312,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
 #pragma unroll
       for (int k = 0; k < NCH / 16; ++k)
         aux[it][k] = epi.load_aux(x, EpiPos{r0 + 32 * i + 4 * it + (lane >> 4), c0 + 4 * ((lane & 15) + 16 * k),
-                                            32 * i + 4 * it, 64 * k});
+                                            32 * i + 4 * it, 64 * k, goff[it][k]});
 #pragma unroll
     for (int j = 0; j < WTN; ++j)
 #pragma unroll
@@ -297,7 +324,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
         }
         const int cc = 8 * j + 2 * g + h;
         epi.pre(rs[i], r0 + 32 * i + lr, c0 + 4 * cc, v);
-        *reinterpret_cast<float4*>(slab + 4 * (lr * NCH + (cc ^ (lr & 15)))) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(w1 + 4 * ((8 * j + 2 * g) ^ s1)) = make_float4(v[0], v[1], v[2], v[3]);
       }
     epi.row_end(rs[i], x, i);
     // a batch of the slab's reads first, then its stores: the reads overlap
@@ -308,12 +335,10 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
       float4 q[kReadBatch][NCH / 16];
 #pragma unroll
       for (int ib = 0; ib < kReadBatch; ++ib) {
-        const int rr = 4 * (b0 + ib) + (lane >> 4);
+        const int it = b0 + ib;
 #pragma unroll
-        for (int k = 0; k < NCH / 16; ++k) {
-          const int cc = (lane & 15) + 16 * k;
-          q[ib][k] = *reinterpret_cast<const float4*>(slab + 4 * (rr * NCH + (cc ^ (rr & 15))));
-        }
+        for (int k = 0; k < NCH / 16; ++k)
+          q[ib][k] = *reinterpret_cast<const float4*>(r2[it & 3] + 4 * (4 * it * NCH + 16 * k));
       }
 #pragma unroll
       for (int ib = 0; ib < kReadBatch; ++ib) {
@@ -322,7 +347,7 @@ __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi
         for (int k = 0; k < NCH / 16; ++k) {
           const int cc = (lane & 15) + 16 * k;
           float v[4] = {q[ib][k].x, q[ib][k].y, q[ib][k].z, q[ib][k].w};
-          epi.post(x, EpiPos{r0 + 32 * i + rr, c0 + 4 * cc, 32 * i + 4 * it, 64 * k}, v, aux[it][k]);
+          epi.post(x, EpiPos{r0 + 32 * i + rr, c0 + 4 * cc, 32 * i + 4 * it, 64 * k, goff[it][k]}, v, aux[it][k]);
           if constexpr (kMax) epi.track(tmax, r0 + 32 * i + rr, c0 + 4 * cc, v);
         }
       }
@@ -353,27 +378,23 @@ __device__ __forceinline__ void aux_get(const Aux4<T>& a, float* v) {
 }
 struct NoAux {};
 
-// Branch-free epilogue I/O. A buffer resource starts at the tile origin and
-// its record ends at the matrix's last row, so a row at or past M is out of
-// the record with no test per element: the hardware drops such stores and
-// reads such loads as zero. A column at or past N gets an offset past the
-// record. With no branch per element, the slab reads and stores of a row are
-// scheduled together instead of one read, one wait, one store at a time (and
-// leaving the row test to the record takes about 110 vector instructions per
-// thread and tile out of the store phase).
+// Branch-free epilogue I/O. A buffer resource starts at the first row of a
+// wave's 32-row block and its first column, and its record ends at the
+// matrix's last row, so a row at or past M is out of the record with no test
+// per element: the hardware drops such stores and reads such loads as zero.
+// A column at or past N has an offset past the record (EpiPos::off). With no
+// branch and no address arithmetic per group, the slab reads and stores of a
+// row are scheduled together instead of one read, one wait, one store at a
+// time. Offsets within a row block: 32 ld es < 2^31 (every launcher checks
+// 256 ld es), and the rows' factor fits 24 bits.
 template <typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc_m(const T* base, long ld, const EpiCtx& x, int M) {
-  const long rem = (long)(M - x.m0) * ld * (long)sizeof(T);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base + (long)x.m0 * ld + x.n0), (short)0,
-                                           (int)(rem < (long)kDmaRecords ? rem : (long)kDmaRecords), 0x00020000);
-}
-// Byte offset of a store-phase group from the tile origin: row - m0 < 256
-// and 256 ld es < 2^31 (checked by every launcher), so both factors fit 24
-// bits and the full-rate 24-bit multiply gives the product.
-template <typename T>
-__device__ __forceinline__ int tile_off(const EpiCtx& x, const EpiPos& p, long ld, int N) {
-  const unsigned r = __umul24((unsigned)(p.row - x.m0), (unsigned)ld);
-  return (int)(p.col < N ? (r + (unsigned)(p.col - x.n0)) * (unsigned)sizeof(T) : kDmaOOB);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const T* base, long ld, const EpiCtx& x, int M,
+                                                            const EpiPos& p) {
+  const int row0 = x.m0 + x.wm + (p.ru & ~31);
+  const long rem = (long)(M - row0) * ld * (long)sizeof(T);
+  const long rec = rem < 0 ? 0L : rem < (long)kDmaRecords ? rem : (long)kDmaRecords;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base + (long)row0 * ld + x.n0 + x.wn), (short)0,
+                                           (int)rec, 0x00020000);
 }
 typedef int epi_v2i __attribute__((ext_vector_type(2)));
 typedef int epi_v4i __attribute__((ext_vector_type(4)));
@@ -427,9 +448,11 @@ struct EpiStore {
   const float* sb = nullptr;
   uint32_t* amax = nullptr;   // TrackMax: the striped maximum
   static constexpr bool kTracksMax = TrackMax;
+  static constexpr int kOutBytes = sizeof(T);
+  __device__ __forceinline__ long out_ld() const { return ldc; }
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
-    if constexpr (HasRes) return tile_load4<T>(tile_rsrc_m(res, ldc, x, M), tile_off<T>(x, p, ldc, N));
+    if constexpr (HasRes) return tile_load4<T>(block_rsrc(res, ldc, x, M, p), p.off);
     else return Aux{};
   }
   // (an FP8 product's scale is applied to the accumulators before phase 1)
@@ -449,7 +472,7 @@ struct EpiStore {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += r[e];
     }
-    tile_store4<T>(tile_rsrc_m(C, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
+    tile_store4<T>(block_rsrc(C, ldc, x, M, p), p.off, v);
   }
   // after post (v holds the stored values before rounding)
   __device__ __forceinline__ void track(float& t, int row, int col, const float* v) const {
@@ -468,6 +491,8 @@ struct EpiRowScale {
   long ldc;
   const float* q;
   int M, N;
+  static constexpr int kOutBytes = sizeof(T);
+  __device__ __forceinline__ long out_ld() const { return ldc; }
   struct RowState {
     float q;
   };
@@ -481,7 +506,7 @@ struct EpiRowScale {
   using Aux = NoAux;
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
-    tile_store4<T>(tile_rsrc_m(C, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
+    tile_store4<T>(block_rsrc(C, ldc, x, M, p), p.off, v);
   }
 };
 
@@ -496,10 +521,12 @@ struct EpiAxpby {
   int M, N;
   float alpha, beta;
   long c_batch, r_batch;  // per-problem strides of C and res in a batched launch
+  static constexpr int kOutBytes = sizeof(T);
+  __device__ __forceinline__ long out_ld() const { return ldc; }
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
     if constexpr (HasRes)
-      return tile_load4<T>(tile_rsrc_m(res + x.batch * r_batch, ldc, x, M), tile_off<T>(x, p, ldc, N));
+      return tile_load4<T>(block_rsrc(res + x.batch * r_batch, ldc, x, M, p), p.off);
     else return Aux{};
   }
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
@@ -512,7 +539,7 @@ struct EpiAxpby {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] *= alpha;
     }
-    tile_store4<T>(tile_rsrc_m(C + x.batch * c_batch, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
+    tile_store4<T>(block_rsrc(C + x.batch * c_batch, ldc, x, M, p), p.off, v);
   }
 };
 
@@ -525,9 +552,11 @@ struct EpiDReluSq {
   long ldc;
   const T* act;  // a = max(u, 0)^2 as stored by the forward pass, C's layout
   int M, N;
+  static constexpr int kOutBytes = sizeof(T);
+  __device__ __forceinline__ long out_ld() const { return ldc; }
   using Aux = Aux4<T>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
-    return tile_load4<T>(tile_rsrc_m(act, ldc, x, M), tile_off<T>(x, p, ldc, N));
+    return tile_load4<T>(block_rsrc(act, ldc, x, M, p), p.off);
   }
   // The square root is the bare hardware instruction (within 1 ulp): the
   // correctly rounded library form is about 17 vector instructions, which for
@@ -537,7 +566,7 @@ struct EpiDReluSq {
     aux_get<T>(a, av);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] *= 2.f * __builtin_amdgcn_sqrtf(av[e]);
-    tile_store4<T>(tile_rsrc_m(C, ldc, x, M), tile_off<T>(x, p, ldc, N), v);
+    tile_store4<T>(block_rsrc(C, ldc, x, M, p), p.off, v);
   }
 };
 
@@ -550,11 +579,13 @@ struct EpiF32 {
   long split_stride;
   int accumulate;
   int M, N;
+  static constexpr int kOutBytes = sizeof(float);
+  __device__ __forceinline__ long out_ld() const { return ldc; }
   using Aux = NoAux;
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc_m(C + (long)x.z * split_stride, ldc, x, M);
-    const int off = tile_off<float>(x, p, ldc, N);
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(C + (long)x.z * split_stride, ldc, x, M, p);
+    const int off = p.off;
     if (accumulate) {
       float q[4];
       aux_get<float>(tile_load4<float>(rs, off), q);
@@ -590,6 +621,10 @@ struct EpiSoftcap {
   int n_tiles;
   int M, N;
   float kc = 0.f;  // Grad: -2 c log2(e)
+  // the logits are stored in column panels with their own offsets
+  // (EpiPos::off is not used)
+  static constexpr int kOutBytes = sizeof(T);
+  __device__ __forceinline__ long out_ld() const { return 0; }
   struct RowState {
     float sum;
   };
@@ -652,7 +687,9 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(GemmShape s, Epi epi) {
   __shared__ __align__(16) T smem[2][LoadA::SIZE + LoadB::SIZE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane: uniform, so the epilogue's buffer
+  // resources (which start at the wave's rows) stay in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (s.M + BM - 1) / BM, tiles_n = (s.N + BN - 1) / BN;
   int tm, tn, z;
   gemm_tile_coords(tiles_m, tiles_n, tm, tn, z);
