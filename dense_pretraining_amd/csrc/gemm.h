@@ -263,11 +263,96 @@ struct EpiTracksMax { static constexpr bool value = false; };
 template <typename Epi>
 struct EpiTracksMax<Epi, std::void_t<decltype(Epi::kTracksMax)>> { static constexpr bool value = Epi::kTracksMax; };
 
+// Epilogues whose store phase only rounds to bf16 and stores (kPacked; no
+// second input): staged_epilogue_packed below.
+template <typename Epi, typename = void>
+struct EpiPacked { static constexpr bool value = false; };
+template <typename Epi>
+struct EpiPacked<Epi, std::void_t<decltype(Epi::kPacked)>> {
+  static constexpr bool value = Epi::kPacked && Epi::kOutBytes == 2;
+};
+
+typedef int epi_v2i __attribute__((ext_vector_type(2)));
+typedef int epi_v4i __attribute__((ext_vector_type(4)));
+
+// The staged epilogue of a kPacked epilogue: phase 1 applies epi.pre and
+// rounds to bf16 in the accumulator layout, so the slab holds bf16 (32 rows
+// of 128 columns, 8 KB a wave) and phase 2 moves half the bytes of the
+// float32 slab through LDS. A phase-2 lane reads 8 consecutive columns (one
+// 16-byte chunk) of a row, 16 lanes cover the wave's 128 columns of one row,
+// and epi.store8 writes the chunk with one 16-byte store. Slab row r, chunk c
+// sits at byte 256 r + 16 (c ^ (r & 15)): a phase-1 write (the two lane
+// halves fill the two 8-byte halves of one chunk of rows 0..31) and a phase-2
+// read (4 rows of 16 chunks) each spread over all banks. Every output column
+// count is a multiple of 8 (checked by the launchers), so a chunk lies wholly
+// inside or wholly outside the matrix.
+template <int WTM, int WTN, typename Epi, bool Scaled>
+__device__ __forceinline__ void staged_epilogue_packed(f32x16 (&c)[WTM][WTN], const Epi& epi, const EpiCtx& x,
+                                                       float* slab_f) {
+  static_assert(WTN == 4, "a slab row is the wave's 128 columns: 16 chunks of 8 bf16");
+  constexpr bool kMax = EpiTracksMax<Epi>::value;
+  const int lane = x.lane, lr = lane & 31, h = lane >> 5;
+  const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
+  float tmax = 0.f;
+  char* const slab = reinterpret_cast<char*>(slab_f);
+  // phase 1: lane (lr, h) writes half h of chunk 4j + g of row lr
+  char* const w1 = slab + 256 * lr + 8 * h;
+  const int s1 = lr & 15;
+  // phase 2: row 4 it + lane / 16, chunk lane % 16, whose slot
+  // (lane % 16) ^ (lane / 16) ^ 4 (it % 4) is one of four per-lane bases
+  const char* r2[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r2[t] = slab + 256 * (lane >> 4) + 16 * (((lane & 15) ^ (lane >> 4)) ^ (4 * t));
+  const int cq = 8 * (lane & 15);  // the lane's first store-phase column past c0
+  // store offsets from the wave's 32-row block origin, the same in every block
+  int goff[8];
+  {
+    const unsigned ld = (unsigned)epi.out_ld(), lrow = lane >> 4;
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      goff[it] = c0 + cq < epi.N ? (int)((__umul24(4 * it + lrow, ld) + (unsigned)cq) * 2u) : (int)kDmaOOB;
+  }
+  typename Epi::RowState rs[WTM];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) epi.row_begin(rs[i], r0 + 32 * i + lr);
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+    for (int j = 0; j < WTN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4] = {c[i][j][4 * g], c[i][j][4 * g + 1], c[i][j][4 * g + 2], c[i][j][4 * g + 3]};
+        if constexpr (Scaled) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= x.scale;
+        }
+        const int row = r0 + 32 * i + lr, col = c0 + 32 * j + 8 * g + 4 * h;
+        epi.pre(rs[i], row, col, v);
+        if constexpr (kMax) epi.track(tmax, row, col, v);
+        bf16x4 o;
+        o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+        *reinterpret_cast<uint2*>(w1 + 16 * ((4 * j + g) ^ s1)) = __builtin_bit_cast(uint2, o);
+      }
+    epi.row_end(rs[i], x, i);
+    uint4 q[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) q[it] = *reinterpret_cast<const uint4*>(r2[it & 3] + 1024 * it);
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      epi.store8(x, EpiPos{r0 + 32 * i + 4 * it + (lane >> 4), c0 + cq, 32 * i + 4 * it, 0, goff[it]}, q[it]);
+  }
+  if constexpr (kMax) epi.publish(tmax);
+}
+
 // Scaled: multiply the accumulators by x.scale first (FP8 products only; a
 // multiply per element costs about a microsecond of a tile's epilogue).
 template <int WTM, int WTN, typename Epi, bool Scaled = false>
 __device__ __forceinline__ void staged_epilogue(f32x16 (&c)[WTM][WTN], const Epi& epi, const EpiCtx& x,
                                                 float* slab) {
+  if constexpr (EpiPacked<Epi>::value) {
+    staged_epilogue_packed<WTM, WTN, Epi, Scaled>(c, epi, x, slab);
+    return;
+  }
   constexpr int NCH = 8 * WTN;  // 16-byte chunks per slab row
   constexpr bool kMax = EpiTracksMax<Epi>::value;
   constexpr int kReadBatch = (kMax || !std::is_empty<typename Epi::RowState>::value) ? 4 : 8;
@@ -396,8 +481,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const T* base, long
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base + (long)row0 * ld + x.n0 + x.wn), (short)0,
                                            (int)rec, 0x00020000);
 }
-typedef int epi_v2i __attribute__((ext_vector_type(2)));
-typedef int epi_v4i __attribute__((ext_vector_type(4)));
 // bf16 tiles are stored non-temporal (cache policy bit nt): an output tile is
 // written once and read by a later kernel, and streaming it past the caches
 // made the store-heavy products 3-10 % faster (the unembedding's 8.6 GB of
@@ -439,7 +522,10 @@ __device__ __forceinline__ Aux4<T> tile_load4(__amdgpu_buffer_rsrc_t rs, int off
 // order), so an epilogue without one must carry no loads at all.
 template <typename T, bool ReluSqOut = false, bool TrackMax = false, bool HasRes = false>
 struct EpiStore {
-  NC_EPI_NO_ROW_WORK
+  struct RowState {};
+  __device__ __forceinline__ void row_begin(RowState&, int) const {}
+  __device__ __forceinline__ void row_end(RowState&, const EpiCtx&, int) const {}
+  __device__ __forceinline__ void finish(const EpiCtx&) const {}
   T* C;
   long ldc;
   const T* res;  // optional residual, C's layout (the same leading dimension: one offset serves both)
@@ -449,14 +535,17 @@ struct EpiStore {
   uint32_t* amax = nullptr;   // TrackMax: the striped maximum
   static constexpr bool kTracksMax = TrackMax;
   static constexpr int kOutBytes = sizeof(T);
+  // without a residual the store phase only rounds and stores
+  static constexpr bool kPacked = !HasRes;
   __device__ __forceinline__ long out_ld() const { return ldc; }
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
     if constexpr (HasRes) return tile_load4<T>(block_rsrc(res, ldc, x, M, p), p.off);
     else return Aux{};
   }
-  // (an FP8 product's scale is applied to the accumulators before phase 1)
-  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
+  // the activation, in phase 1 (an FP8 product's scale is applied to the
+  // accumulators before it)
+  __device__ __forceinline__ void pre(RowState&, int, int, float* v) const {
     if constexpr (ReluSqOut) {
       // max(v, 0) as one median of three (fmaxf adds a canonicalising max per
       // element: 256 more vector instructions per thread and tile)
@@ -466,6 +555,8 @@ struct EpiStore {
         v[e] = r * r;
       }
     }
+  }
+  __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux& a) const {
     if constexpr (HasRes) {
       float r[4];
       aux_get<T>(a, r);
@@ -474,7 +565,12 @@ struct EpiStore {
     }
     tile_store4<T>(block_rsrc(C, ldc, x, M, p), p.off, v);
   }
-  // after post (v holds the stored values before rounding)
+  // kPacked: 8 rounded values of one row
+  __device__ __forceinline__ void store8(const EpiCtx& x, const EpiPos& p, const uint4& q) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(epi_v4i, q), block_rsrc(C, ldc, x, M, p), p.off, 0,
+                                           kStoreStream);
+  }
+  // the stored values before rounding
   __device__ __forceinline__ void track(float& t, int row, int col, const float* v) const {
     const float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
     t = row < M && col < N ? fmaxf(t, m) : t;
@@ -492,6 +588,7 @@ struct EpiRowScale {
   const float* q;
   int M, N;
   static constexpr int kOutBytes = sizeof(T);
+  static constexpr bool kPacked = true;
   __device__ __forceinline__ long out_ld() const { return ldc; }
   struct RowState {
     float q;
@@ -507,6 +604,10 @@ struct EpiRowScale {
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
     tile_store4<T>(block_rsrc(C, ldc, x, M, p), p.off, v);
+  }
+  __device__ __forceinline__ void store8(const EpiCtx& x, const EpiPos& p, const uint4& q8) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(epi_v4i, q8), block_rsrc(C, ldc, x, M, p), p.off, 0,
+                                           kStoreStream);
   }
 };
 
@@ -624,6 +725,7 @@ struct EpiSoftcap {
   // the logits are stored in column panels with their own offsets
   // (EpiPos::off is not used)
   static constexpr int kOutBytes = sizeof(T);
+  static constexpr bool kPacked = true;
   __device__ __forceinline__ long out_ld() const { return 0; }
   struct RowState {
     float sum;
@@ -668,6 +770,14 @@ struct EpiSoftcap {
     // panel index < 8 and zpanel < 2^24 (checked by the launcher): a 24-bit multiply
     const unsigned o = (__umul24(dc / kPanel, (unsigned)zpanel) + dr * kPanel + dc % kPanel) * (unsigned)sizeof(T);
     tile_store4<T>(rs, row < M && col < N ? (int)o : (int)kDmaOOB, v);
+  }
+  // kPacked: 8 columns of a row, inside one panel (8 divides kPanel)
+  __device__ __forceinline__ void store8(const EpiCtx& x, const EpiPos& p, const uint4& q) const {
+    const __amdgpu_buffer_rsrc_t rs = dma_rsrc(Z + (long)(x.n0 / kPanel) * zpanel + (long)x.m0 * kPanel);
+    const unsigned dc = (unsigned)(p.col - x.n0), dr = (unsigned)(p.row - x.m0);
+    const unsigned o = (__umul24(dc / kPanel, (unsigned)zpanel) + dr * kPanel + dc % kPanel) * (unsigned)sizeof(T);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(epi_v4i, q), rs,
+                                           p.row < M && p.col < N ? (int)o : (int)kDmaOOB, 0, kStoreStream);
   }
   __device__ __forceinline__ void finish(const EpiCtx& x) const {
     __syncthreads();
@@ -1181,6 +1291,8 @@ nc_status launch_gemm(const GemmShape& s, const Epi& epi, hipStream_t stream) {
   int tiles_m = (s.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (s.N + Cfg::BN - 1) / Cfg::BN;
   long blocks = (long)tiles_m * tiles_n * s.n_split * s.batch;
   if (blocks <= 0) return NC_OK;
+  // a packed store phase writes 8 columns at a time
+  if (EpiPacked<Epi>::value && epi.N % 8 != 0) return NC_ERR_UNSUPPORTED;
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((gemm_dma_kernel<LA, LB, Epi>), dim3((unsigned)blocks), dim3(256), 0, stream, s,
                        epi);
@@ -1198,6 +1310,7 @@ nc_status launch_gemm_f8(const GemmShape& s, const Epi& epi, hipStream_t stream)
   int tiles_m = (s.M + 255) / 256, tiles_n = (s.N + 255) / 256;
   long blocks = (long)tiles_m * tiles_n * s.n_split * s.batch;
   if (blocks <= 0) return NC_OK;
+  if (EpiPacked<Epi>::value && epi.N % 8 != 0) return NC_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((gemm_dma_kernel<kKc, kKc, Epi, true>), dim3((unsigned)blocks), dim3(256), 0, stream, s, epi);
   NC_LAUNCH_CHECK("gemm_f8");
   return NC_OK;
