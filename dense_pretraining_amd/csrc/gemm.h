@@ -535,8 +535,9 @@ struct EpiStore {
   uint32_t* amax = nullptr;   // TrackMax: the striped maximum
   static constexpr bool kTracksMax = TrackMax;
   static constexpr int kOutBytes = sizeof(T);
-  // without a residual the store phase only rounds and stores
-  static constexpr bool kPacked = !HasRes;
+  // without a residual the store phase only rounds and stores (the FP8
+  // operand's maximum tracking keeps the float32 slab: packed, it spilled)
+  static constexpr bool kPacked = !HasRes && !TrackMax;
   __device__ __forceinline__ long out_ld() const { return ldc; }
   using Aux = std::conditional_t<HasRes, Aux4<T>, NoAux>;
   __device__ __forceinline__ Aux load_aux(const EpiCtx& x, const EpiPos& p) const {
@@ -588,7 +589,8 @@ struct EpiRowScale {
   const float* q;
   int M, N;
   static constexpr int kOutBytes = sizeof(T);
-  static constexpr bool kPacked = true;
+  // the float32 slab: packed, the per-row factor's registers spilled
+  static constexpr bool kPacked = false;
   __device__ __forceinline__ long out_ld() const { return ldc; }
   struct RowState {
     float q;
