@@ -290,10 +290,9 @@ template <int WTM, int WTN, typename Epi, bool Scaled>
 __device__ __forceinline__ void staged_epilogue_packed(f32x16 (&c)[WTM][WTN], const Epi& epi, const EpiCtx& x,
                                                        float* slab_f) {
   static_assert(WTN == 4, "a slab row is the wave's 128 columns: 16 chunks of 8 bf16");
-  constexpr bool kMax = EpiTracksMax<Epi>::value;
+  static_assert(!EpiTracksMax<Epi>::value, "maximum tracking keeps the float32 slab");
   const int lane = x.lane, lr = lane & 31, h = lane >> 5;
   const int r0 = x.m0 + x.wm, c0 = x.n0 + x.wn;
-  float tmax = 0.f;
   char* const slab = reinterpret_cast<char*>(slab_f);
   // phase 1: lane (lr, h) writes half h of chunk 4j + g of row lr
   char* const w1 = slab + 256 * lr + 8 * h;
@@ -328,7 +327,6 @@ __device__ __forceinline__ void staged_epilogue_packed(f32x16 (&c)[WTM][WTN], co
         }
         const int row = r0 + 32 * i + lr, col = c0 + 32 * j + 8 * g + 4 * h;
         epi.pre(rs[i], row, col, v);
-        if constexpr (kMax) epi.track(tmax, row, col, v);
         bf16x4 o;
         o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
         *reinterpret_cast<uint2*>(w1 + 16 * ((4 * j + g) ^ s1)) = __builtin_bit_cast(uint2, o);
@@ -341,7 +339,6 @@ __device__ __forceinline__ void staged_epilogue_packed(f32x16 (&c)[WTM][WTN], co
     for (int it = 0; it < 8; ++it)
       epi.store8(x, EpiPos{r0 + 32 * i + 4 * it + (lane >> 4), c0 + cq, 32 * i + 4 * it, 0, goff[it]}, q[it]);
   }
-  if constexpr (kMax) epi.publish(tmax);
 }
 
 // Scaled: multiply the accumulators by x.scale first (FP8 products only; a
@@ -606,10 +603,6 @@ struct EpiRowScale {
   __device__ __forceinline__ Aux load_aux(const EpiCtx&, const EpiPos&) const { return Aux{}; }
   __device__ __forceinline__ void post(const EpiCtx& x, const EpiPos& p, float* v, const Aux&) const {
     tile_store4<T>(block_rsrc(C, ldc, x, M, p), p.off, v);
-  }
-  __device__ __forceinline__ void store8(const EpiCtx& x, const EpiPos& p, const uint4& q8) const {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(epi_v4i, q8), block_rsrc(C, ldc, x, M, p), p.off, 0,
-                                           kStoreStream);
   }
 };
 
