@@ -1151,11 +1151,13 @@ nc_status attn_bwd_impl(const AttnGeom& g, const T* qk, const T* v, const T* o, 
 }
 
 // Keys per decode block: one 64-key tile while the grid stays within about
-// five 2-wave blocks per CU, more tiles per block (through the 2-stage ring)
-// for longer caches.
+// two 2-wave blocks per CU, more tiles per block (through the 2-stage ring)
+// for longer caches. (A target of five blocks per CU, one tile each at the
+// benchmark's cache lengths, was 14 % slower: more blocks, each waiting on
+// one load, and more chunk partials to merge.)
 int decode_chunk_keys(int n, int BG) {
   const long work = (long)BG * ((n + 63) / 64);
-  const long nt = (work + 1279) / 1280;
+  const long nt = (work + 511) / 512;
   return 64 * (int)(nt < 1 ? 1 : nt);
 }
 
