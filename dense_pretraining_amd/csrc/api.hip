@@ -661,14 +661,36 @@ void layer_matrices(const Dims& m, const size_t* off, int l, MatSpec* out) {
   out[5] = {off[4 + 4 * l], m.d, m.F};
 }
 
+// The six kinds grouped by the shape of their tall form (rows >= columns):
+// a group's Newton-Schulz products run as one batch. group[k] is kind k's
+// group (the index of the group's first kind).
+void muon_groups(const MatSpec* ms, int* group) {
+  for (int k = 0; k < 6; ++k) {
+    group[k] = k;
+    const int rk = ms[k].R > ms[k].C ? ms[k].R : ms[k].C, ck = ms[k].R > ms[k].C ? ms[k].C : ms[k].R;
+    for (int j = 0; j < k; ++j) {
+      const int rj = ms[j].R > ms[j].C ? ms[j].R : ms[j].C, cj = ms[j].R > ms[j].C ? ms[j].C : ms[j].R;
+      if (rj == rk && cj == ck) {
+        group[k] = group[j];
+        break;
+      }
+    }
+  }
+}
+
 size_t opt_workspace_bytes(const Dims& m) {
   std::vector<size_t> off(2 + 4 * (size_t)m.L);
   param_offsets(m, off.data());
   MatSpec ms[6];
   layer_matrices(m, off.data(), 0, ms);
+  int group[6];
+  muon_groups(ms, group);
   size_t w = 0;
-  for (const MatSpec& x : ms) {
-    const size_t b = muon_work_bytes(x.R, x.C, m.L, m.es == 2);
+  for (int k = 0; k < 6; ++k) {
+    if (group[k] != k) continue;
+    int nk = 0;
+    for (int j = 0; j < 6; ++j) nk += group[j] == k;
+    const size_t b = muon_work_bytes(ms[k].R, ms[k].C, nk * m.L, m.es == 2);
     w = b > w ? b : w;
   }
   return w;
@@ -701,9 +723,18 @@ nc_status opt_step_t(const Dims& m, const nc_opt_hparams& h, T* params, const fl
   const long ls = m.L > 1 ? (long)(off[5] - off[1]) : 0;
   MatSpec ms[6];
   layer_matrices(m, off.data(), 0, ms);
-  for (const MatSpec& x : ms)
-    NC_TRY(muon_step<T>(grads + x.off, s1 + x.off, master + x.off, params + x.off, x.R, x.C, m.L, ls, h.lr_matrix,
-                        h.momentum, h.nesterov, h.wd_matrix, ws, ws_bytes, st));
+  int group[6];
+  muon_groups(ms, group);
+  for (int k = 0; k < 6; ++k) {
+    if (group[k] != k) continue;
+    MuonKind<T> kinds[6];
+    int nk = 0;
+    for (int j = 0; j < 6; ++j)
+      if (group[j] == k)
+        kinds[nk++] = MuonKind<T>{grads + ms[j].off, s1 + ms[j].off, master + ms[j].off, params + ms[j].off, ms[j].R,
+                                  ms[j].C};
+    NC_TRY(muon_step<T>(kinds, nk, m.L, ls, h.lr_matrix, h.momentum, h.nesterov, h.wd_matrix, ws, ws_bytes, st));
+  }
   return NC_OK;
 }
 

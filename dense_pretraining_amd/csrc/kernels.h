@@ -218,12 +218,23 @@ nc_status opt_init(const T* params, float* master, float* s1, size_t n, float* s
 template <typename T>
 nc_status adamw_step(const float* g, float* w, float* m, float* v, T* p, size_t n, float lr, float beta1,
                      float beta2, float eps, float wd, int step, hipStream_t st);
-// One Muon step of L matrices w [R, C] (float32 master, p its stored copy)
-// with gradients g and momenta mom, matrix l at + l * ls elements of each;
-// work: muon_work_bytes(R, C, L, bf16) bytes.
+// One kind of block matrix for a Muon step: L matrices w [R, C] (float32
+// master, p its stored copy) with gradients g and momenta mom, matrix l at
+// + l * ls elements of each.
 template <typename T>
-nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, int L, long ls, float lr, float mu,
-                    int nesterov, float wd, void* work, size_t work_bytes, hipStream_t st);
+struct MuonKind {
+  const float* g;
+  float* mom;
+  float* w;
+  T* p;
+  int R, C;
+};
+// One Muon step of nk kinds whose tall forms (rows >= columns) have the same
+// shape: their Newton-Schulz products run as one batch of nk * L matrices;
+// work: muon_work_bytes(R, C, nk * L, bf16) bytes.
+template <typename T>
+nc_status muon_step(const MuonKind<T>* kinds, int nk, int L, long ls, float lr, float mu, int nesterov, float wd,
+                    void* work, size_t work_bytes, hipStream_t st);
 size_t muon_work_bytes(int R, int C, int L, bool bf16_storage);
 
 // ------------------------------------------------------------ embedding grad (embed_bwd.hip)

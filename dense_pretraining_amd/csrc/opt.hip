@@ -294,67 +294,79 @@ size_t muon_work_bytes(int R, int C, int L, bool bf16_storage) {
 }
 
 template <typename T>
-nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, int L, long ls, float lr, float mu,
-                    int nesterov, float wd, void* work, size_t work_bytes, hipStream_t st) {
+nc_status muon_step(const MuonKind<T>* kinds, int nk, int L, long ls, float lr, float mu, int nesterov, float wd,
+                    void* work, size_t work_bytes, hipStream_t st) {
+  if (nk < 1 || L < 1 || L > 65535 || (long)nk * L > 65535 || ls % 8 != 0) return NC_ERR_UNSUPPORTED;
   // 16-byte accesses: R % 4 == C % 4 == 0, and every matrix of the batch starts 32-byte aligned
   auto al = [](const void* v) { return reinterpret_cast<uintptr_t>(v) % 32 == 0; };
-  if (R % 4 != 0 || C % 4 != 0 || L < 1 || L > 65535 || ls % 8 != 0 || !al(g) || !al(mom) || !al(w) ||
-      reinterpret_cast<uintptr_t>(p) % 16 != 0)
-    return NC_ERR_UNSUPPORTED;
-  if (work_bytes < muon_work_bytes(R, C, L, is_bf16<T>())) return NC_ERR_WORKSPACE;
-  const bool transpose = R < C;
-  const int Rt = transpose ? C : R, Ct = transpose ? R : C;  // the tall form
+  const int Rt = kinds[0].R > kinds[0].C ? kinds[0].R : kinds[0].C;  // the tall form
+  const int Ct = kinds[0].R > kinds[0].C ? kinds[0].C : kinds[0].R;
+  for (int k = 0; k < nk; ++k) {
+    const MuonKind<T>& x = kinds[k];
+    if (x.R % 4 != 0 || x.C % 4 != 0 || !al(x.g) || !al(x.mom) || !al(x.w) ||
+        reinterpret_cast<uintptr_t>(x.p) % 16 != 0)
+      return NC_ERR_UNSUPPORTED;
+    if ((x.R > x.C ? x.R : x.C) != Rt || (x.R > x.C ? x.C : x.R) != Ct) return NC_ERR_UNSUPPORTED;
+  }
+  const int NL = nk * L;
+  if (work_bytes < muon_work_bytes(Rt, Ct, NL, is_bf16<T>())) return NC_ERR_WORKSPACE;
   const long xs = (long)Rt * Ct, as = (long)Ct * Ct;
   const size_t es = sizeof(T);
   char* q = static_cast<char*>(work);
   T* xa = reinterpret_cast<T*>(q);
-  T* xb = xa + L * xs;
-  q += align_up(2 * L * (size_t)xs * es, 256);
+  T* xb = xa + NL * xs;
+  q += align_up(2 * NL * (size_t)xs * es, 256);
   T* Ab = reinterpret_cast<T*>(q);
-  T* Bb = Ab + L * as;
-  q += align_up(2 * L * (size_t)as * es, 256);
+  T* Bb = Ab + NL * as;
+  q += align_up(2 * NL * (size_t)as * es, 256);
   float* norm_part = reinterpret_cast<float*>(q);
 
-  const long n4 = (long)R * C / 4;
-  {
-    ProfScope prof("muon_momentum", 0, 12.0 * 4 * n4 * L, st);
-    hipLaunchKernelGGL(muon_mom_kernel, dim3(kNormParts, L), dim3(256), 0, st, g, mom, n4, ls, mu, nesterov,
-                       norm_part);
-    NC_LAUNCH_CHECK("muon_momentum");
-  }
-  const dim3 tiles((C + kTile - 1) / kTile, (R + kTile - 1) / kTile, L);
-  const dim3 flat(grid_of(n4, 512, 4096), L);
-  {
+  // kind k's matrices are batch entries k L .. k L + L - 1
+  const long n4 = (long)Rt * Ct / 4;
+  for (int k = 0; k < nk; ++k) {
+    const MuonKind<T>& x = kinds[k];
+    float* part = norm_part + (size_t)k * L * kNormParts;
+    {
+      ProfScope prof("muon_momentum", 0, 12.0 * 4 * n4 * L, st);
+      hipLaunchKernelGGL(muon_mom_kernel, dim3(kNormParts, L), dim3(256), 0, st, x.g, x.mom, n4, ls, mu, nesterov,
+                         part);
+      NC_LAUNCH_CHECK("muon_momentum");
+    }
+    const dim3 tiles((x.C + kTile - 1) / kTile, (x.R + kTile - 1) / kTile, L);
+    const dim3 flat(grid_of(n4, 512, 4096), L);
     ProfScope prof("muon_normalize", 0, (8.0 + es) * 4 * n4 * L, st);
-    if (transpose)
-      hipLaunchKernelGGL((muon_norm_tr_kernel<T>), tiles, dim3(256), 0, st, g, mom, ls, R, C, mu, nesterov, norm_part,
-                         xa, xs);
+    if (x.R < x.C)
+      hipLaunchKernelGGL((muon_norm_tr_kernel<T>), tiles, dim3(256), 0, st, x.g, x.mom, ls, x.R, x.C, mu, nesterov,
+                         part, xa + (long)k * L * xs, xs);
     else
-      hipLaunchKernelGGL((muon_norm_flat_kernel<T>), flat, dim3(256), 0, st, g, mom, ls, n4, mu, nesterov, norm_part,
-                         xa, xs);
+      hipLaunchKernelGGL((muon_norm_flat_kernel<T>), flat, dim3(256), 0, st, x.g, x.mom, ls, n4, mu, nesterov, part,
+                         xa + (long)k * L * xs, xs);
     NC_LAUNCH_CHECK("muon_normalize");
   }
-  // the published coefficients (a, b, c) of the quintic map, five steps, all L matrices at once
+  // the published coefficients (a, b, c) of the quintic map, five steps, every matrix of every kind at once
   const float a = 3.4445f, b = -4.7750f, c = 2.0315f;
   T* x = xa;
   T* xn = xb;
   for (int it = 0; it < 5; ++it) {
-    NC_TRY(gemm_gram<T>(x, Ab, Rt, Ct, st, L, xs, as));                          // A = X^T X
-    NC_TRY(gemm_xwt_axpby<T>(Ab, Ab, Bb, Ab, Ct, Ct, Ct, c, b, st, L, as, as, as));  // B = c A A^T + b A
-    NC_TRY(gemm_xwt_axpby<T>(x, Bb, xn, x, Rt, Ct, Ct, 1.f, a, st, L, xs, as, xs));  // X' = X B^T + a X
+    NC_TRY(gemm_gram<T>(x, Ab, Rt, Ct, st, NL, xs, as));                           // A = X^T X
+    NC_TRY(gemm_xwt_axpby<T>(Ab, Ab, Bb, Ab, Ct, Ct, Ct, c, b, st, NL, as, as, as));  // B = c A A^T + b A
+    NC_TRY(gemm_xwt_axpby<T>(x, Bb, xn, x, Rt, Ct, Ct, 1.f, a, st, NL, xs, as, xs));  // X' = X B^T + a X
     T* t = x;
     x = xn;
     xn = t;
   }
-  const float scale = R > C ? std::sqrt((float)R / (float)C) : 1.f;
-  {
+  for (int k = 0; k < nk; ++k) {
+    const MuonKind<T>& m = kinds[k];
+    const float scale = m.R > m.C ? std::sqrt((float)m.R / (float)m.C) : 1.f;
+    const dim3 tiles((m.C + kTile - 1) / kTile, (m.R + kTile - 1) / kTile, L);
+    const dim3 flat(grid_of(n4, 512, 4096), L);
     ProfScope prof("muon_apply", 0, (8.0 + 2.0 * es) * 4 * n4 * L, st);
-    if (transpose)
-      hipLaunchKernelGGL((muon_apply_tr_kernel<T>), tiles, dim3(256), 0, st, w, p, ls, x, xs, R, C, 1.f - lr * wd,
-                         lr * scale);
+    if (m.R < m.C)
+      hipLaunchKernelGGL((muon_apply_tr_kernel<T>), tiles, dim3(256), 0, st, m.w, m.p, ls, x + (long)k * L * xs, xs,
+                         m.R, m.C, 1.f - lr * wd, lr * scale);
     else
-      hipLaunchKernelGGL((muon_apply_flat_kernel<T>), flat, dim3(256), 0, st, w, p, ls, x, xs, n4, 1.f - lr * wd,
-                         lr * scale);
+      hipLaunchKernelGGL((muon_apply_flat_kernel<T>), flat, dim3(256), 0, st, m.w, m.p, ls, x + (long)k * L * xs, xs,
+                         n4, 1.f - lr * wd, lr * scale);
     NC_LAUNCH_CHECK("muon_apply");
   }
   return NC_OK;
@@ -364,8 +376,8 @@ nc_status muon_step(const float* g, float* mom, float* w, T* p, int R, int C, in
   template nc_status opt_init<T>(const T*, float*, float*, size_t, float*, size_t, hipStream_t);                   \
   template nc_status adamw_step<T>(const float*, float*, float*, float*, T*, size_t, float, float, float, float,   \
                                    float, int, hipStream_t);                                                       \
-  template nc_status muon_step<T>(const float*, float*, float*, T*, int, int, int, long, float, float, int, float, \
-                                  void*, size_t, hipStream_t);
+  template nc_status muon_step<T>(const MuonKind<T>*, int, int, long, float, float, int, float, void*, size_t,    \
+                                  hipStream_t);
 NC_INST(bf16)
 NC_INST(float)
 #undef NC_INST
